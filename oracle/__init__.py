@@ -1,0 +1,245 @@
+"""CPU oracle for SageAttention-style INT8-QK / FP8-PV attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It is a thin
+ctypes wrapper (argument marshalling, per-head slicing) around
+``sage_oracle.c``, a plain single-threaded C implementation of the quantized
+method; the arithmetic and the readings of the pages are documented there.
+It shares no code with the HIP path and imports nothing from it.
+
+Arrays are numpy; bf16 tensors are passed as ``uint16`` code arrays in the
+layout ``[B, H, N, d]`` (callers convert from other layouts first).
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sage_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libsage_oracle.so")
+_CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-Wall", "-Wextra"]
+
+_lib = None
+
+# Block / tile constants of the method (reading: 128, the only block size the
+# pages give; the key tile of the online softmax equals the K block).
+BLK = 128
+BC = 128
+P_SCALE = 448.0
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ct.CDLL(_LIB_PATH)
+        P = ct.c_void_p
+        i32, i64, f32, f64 = ct.c_int, ct.c_int64, ct.c_float, ct.c_double
+        sigs = {
+            "or_bf16_to_f32_n": [P, i64, P], "or_f32_to_bf16_n": [P, i64, P],
+            "or_e4m3_to_f32_n": [P, i64, P], "or_f32_to_e4m3_n": [P, i64, P],
+            "or_f16_to_f32_n": [P, i64, P], "or_f32_to_f16_n": [P, i64, P],
+            "or_fix30_n": [P, i64, P],
+            "or_k_mean": [P, i32, i32, P],
+            "or_quant_block": [P, i32, i32, P, P],
+            "or_quant_q": [P, i32, i32, i32, P, P, P],
+            "or_quant_k": [P, i32, i32, i32, i32, P, P, P, P],
+            "or_quant_v": [P, i32, i32, i32, P, P],
+            "or_dump_s": [P, P, i32, i32, i32, i32, i32, P],
+            "or_attn_rows": [P, P, P, P, P, P, i32, i32, P, i32, i32, f32, i32, i32, i32, P, P, P, P],
+            "or_ref64_rows": [P, P, P, i32, i32, P, i32, i32, f64, P, P],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = None
+        L.or_lambda.argtypes = [f32]
+        L.or_lambda.restype = f32
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ct.c_void_p)
+
+
+# --------------------------------------------------------------------------- codecs
+def _codec(name, x, in_dtype, out_dtype):
+    x = np.ascontiguousarray(x, dtype=in_dtype)
+    out = np.empty(x.shape, dtype=out_dtype)
+    getattr(lib(), name)(_p(x), x.size, _p(out))
+    return out
+
+
+def bf16_to_f32(x):
+    return _codec("or_bf16_to_f32_n", x, np.uint16, np.float32)
+
+
+def f32_to_bf16(x):
+    return _codec("or_f32_to_bf16_n", x, np.float32, np.uint16)
+
+
+def e4m3_to_f32(x):
+    return _codec("or_e4m3_to_f32_n", x, np.uint8, np.float32)
+
+
+def f32_to_e4m3(x):
+    return _codec("or_f32_to_e4m3_n", x, np.float32, np.uint8)
+
+
+def f16_to_f32(x):
+    return _codec("or_f16_to_f32_n", x, np.uint16, np.float32)
+
+
+def f32_to_f16(x):
+    return _codec("or_f32_to_f16_n", x, np.float32, np.uint16)
+
+
+def fix30(x):
+    return _codec("or_fix30_n", x, np.float32, np.int64)
+
+
+def lam(sm_scale: float) -> float:
+    """sm_scale * log2(e) rounded once to fp32."""
+    return float(lib().or_lambda(sm_scale))
+
+
+# --------------------------------------------------------------------- quantization
+def k_mean_head(k_head: np.ndarray) -> np.ndarray:
+    k_head = np.ascontiguousarray(k_head, dtype=np.uint16)
+    N, d = k_head.shape
+    out = np.empty(d, np.float32)
+    lib().or_k_mean(_p(k_head), N, d, _p(out))
+    return out
+
+
+def quant_block(x: np.ndarray):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, d = x.shape
+    out = np.empty((rows, d), np.int8)
+    s = np.empty(1, np.float32)
+    lib().or_quant_block(_p(x), rows, d, _p(out), _p(s))
+    return out, float(s[0])
+
+
+def quant_qk(q: np.ndarray, k: np.ndarray, blk: int = BLK, smooth: bool = True):
+    """q, k: uint16 bf16 codes [B, H, N, d].  Returns a dict with q8/k8 int8
+    [B,H,N,d], q_scale/k_scale fp32 [B,H,nblk], k_mean fp32 [B,H,d]."""
+    B, H, N, d = q.shape
+    nb = (N + blk - 1) // blk
+    q8 = np.empty((B, H, N, d), np.int8)
+    k8 = np.empty((B, H, N, d), np.int8)
+    qs = np.empty((B, H, nb), np.float32)
+    ks = np.empty((B, H, nb), np.float32)
+    km = np.empty((B, H, d), np.float32)
+    tmp = np.empty(blk * d, np.float32)
+    L = lib()
+    for b in range(B):
+        for h in range(H):
+            qh = np.ascontiguousarray(q[b, h], dtype=np.uint16)
+            kh = np.ascontiguousarray(k[b, h], dtype=np.uint16)
+            q8h = np.empty((N, d), np.int8)
+            k8h = np.empty((N, d), np.int8)
+            qsh = np.empty(nb, np.float32)
+            ksh = np.empty(nb, np.float32)
+            kmh = np.empty(d, np.float32)
+            L.or_quant_q(_p(qh), N, d, blk, _p(q8h), _p(qsh), _p(tmp))
+            L.or_quant_k(_p(kh), N, d, blk, int(smooth), _p(k8h), _p(ksh), _p(kmh), _p(tmp))
+            q8[b, h], k8[b, h], qs[b, h], ks[b, h], km[b, h] = q8h, k8h, qsh, ksh, kmh
+    return dict(q8=q8, q_scale=qs, k8=k8, k_scale=ks, k_mean=km)
+
+
+def quant_v(v: np.ndarray, pv: str = "fp8"):
+    """v: uint16 bf16 codes [B,H,N,d].  Returns v codes in natural [B,H,N,d]
+    order (uint8 e4m3 for fp8, uint16 binary16 for fp16) and v_scale [B,H,d]."""
+    B, H, N, d = v.shape
+    fp16 = pv == "fp16"
+    vq = np.empty((B, H, N, d), np.uint16 if fp16 else np.uint8)
+    vs = np.empty((B, H, d), np.float32)
+    L = lib()
+    for b in range(B):
+        for h in range(H):
+            vh = np.ascontiguousarray(v[b, h], dtype=np.uint16)
+            vqh = np.empty((N, d), vq.dtype)
+            vsh = np.empty(d, np.float32)
+            L.or_quant_v(_p(vh), N, d, int(fp16), _p(vqh), _p(vsh))
+            vq[b, h], vs[b, h] = vqh, vsh
+    return vq, vs
+
+
+# ------------------------------------------------------------------------ attention
+def dump_s(q8h: np.ndarray, k8h: np.ndarray, row0: int, nrows: int, causal: bool = False):
+    """Integer Q K^T of one head, rows [row0, row0+nrows), all keys (int32 [nrows, N])."""
+    q8h = np.ascontiguousarray(q8h, np.int8)
+    k8h = np.ascontiguousarray(k8h, np.int8)
+    N, d = k8h.shape
+    out = np.empty((nrows, N), np.int32)
+    lib().or_dump_s(_p(q8h), _p(k8h), N, d, row0, nrows, int(causal), _p(out))
+    return out
+
+
+def attn_rows_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scale: float,
+                   pv: str = "fp8", blk: int = BLK, bc: int = BC, return_ml: bool = False):
+    """Quantized attention for query rows ``rows`` of head (b, h): fp32 [len(rows), d]."""
+    q8h = np.ascontiguousarray(qz["q8"][b, h])
+    k8h = np.ascontiguousarray(qz["k8"][b, h])
+    qsh = np.ascontiguousarray(qz["q_scale"][b, h])
+    ksh = np.ascontiguousarray(qz["k_scale"][b, h])
+    vqh = np.ascontiguousarray(vq[b, h])
+    vsh = np.ascontiguousarray(vs[b, h])
+    N, d = k8h.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    out = np.empty((len(rows), d), np.float32)
+    m = np.empty(len(rows), np.float32)
+    l = np.empty(len(rows), np.float32)
+    scratch = np.empty(4 * bc + 3 * d, np.float32)
+    lib().or_attn_rows(_p(q8h), _p(qsh), _p(k8h), _p(ksh), _p(vqh), _p(vsh), N, d, _p(rows),
+                       len(rows), int(causal), float(sm_scale), int(pv == "fp16"), blk, bc,
+                       _p(out), _p(m), _p(l), _p(scratch))
+    if return_ml:
+        return out, m, l
+    return out
+
+
+def ref64_rows_head(q, k, v, b: int, h: int, rows, causal: bool, sm_scale: float):
+    """Exact softmax attention in FP64 from the bf16 inputs (uint16 codes)."""
+    qh = np.ascontiguousarray(q[b, h], np.uint16)
+    kh = np.ascontiguousarray(k[b, h], np.uint16)
+    vh = np.ascontiguousarray(v[b, h], np.uint16)
+    N, d = kh.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    out = np.empty((len(rows), d), np.float64)
+    scratch = np.empty(N, np.float64)
+    lib().or_ref64_rows(_p(qh), _p(kh), _p(vh), N, d, _p(rows), len(rows), int(causal),
+                        float(sm_scale), _p(out), _p(scratch))
+    return out
+
+
+def attention(q, k, v, causal: bool, sm_scale: float, pv: str = "fp8", rows=None):
+    """Whole oracle pipeline: quantize, then attention for ``rows`` (default all)
+    of every head.  Returns (out fp32 [B,H,len(rows),d], quantized dict, vq, vs)."""
+    B, H, N, d = q.shape
+    qz = quant_qk(q, k)
+    vq, vs = quant_v(v, pv)
+    rows = np.arange(N, dtype=np.int32) if rows is None else np.asarray(rows, np.int32)
+    out = np.empty((B, H, len(rows), d), np.float32)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = attn_rows_head(qz, vq, vs, b, h, rows, causal, sm_scale, pv)
+    return out, qz, vq, vs
