@@ -1,0 +1,178 @@
+#!/usr/bin/env python3
+"""Benchmark of libsage on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input already
+resident in HBM: sage_quant_qk (K smoothing + per-block INT8 Q/K),
+sage_quant_v (per-channel FP8 V) and sage_attn_fwd (fused INT8-QK / FP8-PV
+attention), enqueued on one stream.  The headline workload is the 720p clip
+of a 14B video DiT: B=1, H=40, N=75600 (21 x 45 x 80 latent tokens), d=128.
+
+Prints ONE JSON line:
+  value       = 4 B H N^2 d * steps / wall time of the timed steps (TOPS),
+  roofline    = the attention kernel alone: algorithmic ops per launch (4 B H N^2 d)
+                / its mean launch duration (HIP events around each launch on the
+                stream it runs on), against the dense INT8 = FP8 MFMA peak,
+  cpu_baseline= the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TOPS (4·B·H·N²·d/s) & % MFMA peak at N=32760/75600, d=128"
+PEAK_TOPS = {"fp8": 5000.0,                       # dense INT8 (QK) = dense FP8 (PV) = 5.0 POPS
+             "fp16": 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)}  # INT8 QK half + FP16 PV half
+HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def attn_ops(B, H, N, d):
+    return 4.0 * B * H * N * N * d
+
+
+def time_gpu(sage, wl, pv, steps, warmup):
+    import torch
+
+    q, k, v = wl.q, wl.k, wl.v
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        qz = sage.quant_qk(q, k)
+        vq, vs = sage.quant_v(v, pv)
+        if evs:
+            evs[1].record(stream)
+        out = sage.attn_fwd(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale, pv=pv)
+        if evs:
+            evs[2].record(stream)
+        return out
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    quant_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    return wall, quant_ms, attn_ms
+
+
+def cpu_baseline(wl, pv, target_s=12.0):
+    """The oracle as it stands (single-threaded C) on one head of the workload:
+    quantization of the whole head, then attention for R query rows against
+    all N keys; the head's quantization time is charged pro rata (R / N)."""
+    import numpy as np
+
+    import oracle
+    import synthetic_inputs as si
+
+    b, h = 0, 0
+    q, k, v = (si.bf16_codes(t[b:b + 1, h:h + 1]) for t in (wl.q, wl.k, wl.v))
+    t0 = time.perf_counter()
+    oz = oracle.quant_qk(q, k)
+    ovq, ovs = oracle.quant_v(v, pv)
+    t_quant = time.perf_counter() - t0
+    probe = np.arange(8, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.attn_rows_head(oz, ovq, ovs, 0, 0, probe, wl.causal, wl.sm_scale, pv)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    R = int(max(8, min(wl.N, target_s / max(per_row, 1e-9))))
+    rows = np.arange(wl.N - R, wl.N, dtype=np.int32) if wl.causal else np.arange(R, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.attn_rows_head(oz, ovq, ovs, 0, 0, rows, wl.causal, wl.sm_scale, pv)
+    t_attn = time.perf_counter() - t0
+    keys = (rows + 1).sum() if wl.causal else R * wl.N
+    ops = 4.0 * float(keys) * wl.d
+    t_equiv = t_attn + t_quant * R / wl.N
+    return {"value": ops / t_equiv / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": (f"head (b=0,h=0) of {wl.name}: quantization of all {wl.N} tokens "
+                       f"({t_quant:.2f} s, charged pro rata) + attention for {R} queries x "
+                       f"{'their causal keys' if wl.causal else f'{wl.N} keys'} ({t_attn:.2f} s); "
+                       "single-threaded C oracle")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="video_14b_720p")
+    ap.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (there is no multi-GPU path; "
+              "DESIGN.md describes how the work would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_attention_video_02_amd as sage
+    import synthetic_inputs as si
+
+    sage.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = si.make(args.workload, device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} causal={wl.causal} pv={args.pv}",
+          file=sys.stderr, flush=True)
+    wall, quant_ms, attn_ms = time_gpu(sage, wl, args.pv, args.steps, args.warmup)
+    ops = attn_ops(wl.B, wl.H, wl.N, wl.d)
+    ms_per_step = wall * 1e3 / args.steps
+    attn_mean = sum(attn_ms) / len(attn_ms)
+    attn_med = sorted(attn_ms)[len(attn_ms) // 2]
+    quant_mean = sum(quant_ms) / len(quant_ms)
+    achieved = ops / (attn_mean * 1e-3) / 1e12
+    peak = PEAK_TOPS[args.pv]
+    bhnd = wl.B * wl.H * wl.N * wl.d
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(f"{wl.name}/{args.pv}")
+        traffic = t.get("bytes_per_launch") if t else None
+    res = {
+        "metric": METRIC,
+        "value": ops * args.steps / wall / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp8" if args.pv == "fp8" else "int8+fp16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
+                   "causal": wl.causal, "pv": args.pv, "seed": wl.seed, "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": "attn_fwd_kernel", "ops_per_launch": ops,
+                     "mean_launch_ms": attn_mean, "median_launch_ms": attn_med},
+        "quant": {"ms": quant_mean, "bytes_two_pass": 13 * bhnd,
+                  "gbps_two_pass": 13 * bhnd / (quant_mean * 1e-3) / 1e9,
+                  "frac_hbm": 13 * bhnd / (quant_mean * 1e-3) / 1e9 / HBM_GBPS},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, args.pv, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * sage.h -- C ABI of libsage: SageAttention-style low-bit attention forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ *   O = softmax(Q K^T * sm_scale) V, computed as
+ *     1. smooth K by subtracting its per-head token mean,
+ *     2. quantize Q and K per block of 128 rows to INT8 (absmax scales) and
+ *        form Q K^T exactly in INT32 on INT8 matrix cores,
+ *     3. dequantize by q_scale * k_scale and run an exp2 online softmax in
+ *        FP32 over key tiles of 128,
+ *     4. take P to FP8 e4m3 with the static scale 448 and V to FP8 e4m3 with
+ *        per-channel scales (or both to FP16), run P V on FP8 (FP16) matrix
+ *        cores into a fresh FP32 sum per key tile, and add that into the FP32
+ *        running output (two-level accumulation).
+ *
+ * What the pages say about the method: the wxsanhe.com blog post on
+ * TurboDiffusion, section 三.1 (混合注意力) -- Q K in INT8, P V in FP8 or
+ * FP16, outlier smoothing and two-level accumulation, usable as a quantized
+ * FlashAttention; the reportify.cn SageAttention tag page, SageAttention3
+ * summary, bullet 8比特训练 -- per-block INT8 quantization and per-token
+ * quantization of P with no overhead; the txrjy.com repost of the QbitAI
+ * article, section 四个步骤极限压缩时间 -- INT8 attention with outlier
+ * smoothing.  Finer details (block sizes, rounding, the fixed-point mean,
+ * the exp2 argument order) are this library's readings, fixed below.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer allocated by the caller
+ *     (e.g. by PyTorch), except `out` of sage_get_config / sage_quant_sizes
+ *     (host).  libsage never allocates, frees, synchronises, or changes the
+ *     current device.  All work is enqueued asynchronously on `stream`
+ *     (a hipStream_t; NULL means the null stream) on the current device.
+ *   - Device buffers must be 16-byte aligned.
+ *   - Inputs Q, K, V and the output O are contiguous with d innermost, in the
+ *     layout given by `layout`: SAGE_LAYOUT_HND = [B][H][N][d],
+ *     SAGE_LAYOUT_NHD = [B][N][H][d].  Q, K, V are bf16.
+ *   - Quantized buffers are always head-major and have library-defined
+ *     layouts (below); their byte sizes come from sage_quant_sizes.
+ *     N_pad = 128 * ceil(N / 128), nblk = ceil(N / 128).
+ *   - Supported: d in {64, 128}; 1 <= N; B, H >= 1; B*H*N_pad*d < 2^40.
+ *   - Every argument is validated on the host before anything is enqueued;
+ *     a failed check returns its status code and enqueues nothing.  Launch
+ *     failures return SAGE_ERR_HIP.  Faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *   - The library holds no mutable global state; calls are thread-safe.
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_ABI_VERSION 1
+
+enum sage_status {
+    SAGE_OK = 0,
+    SAGE_ERR_NULL = -1,        /* a required pointer is NULL */
+    SAGE_ERR_INVALID = -2,     /* bad size, enum, flag, sm_scale or dump window */
+    SAGE_ERR_UNSUPPORTED = -3, /* d not in {64, 128} */
+    SAGE_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
+    SAGE_ERR_SIZE = -5,        /* the problem exceeds the supported size */
+    SAGE_ERR_HIP = -6,         /* a HIP launch failed */
+    SAGE_ERR_WORKSPACE = -7    /* workspace smaller than sage_quant_sizes asks */
+};
+
+enum sage_layout { SAGE_LAYOUT_HND = 0, SAGE_LAYOUT_NHD = 1 };
+enum sage_pv_dtype { SAGE_PV_FP8 = 0, SAGE_PV_FP16 = 1 };
+enum sage_out_dtype { SAGE_OUT_BF16 = 0, SAGE_OUT_FP32 = 1 };
+
+/* Compile-time constants of the method as built. */
+typedef struct {
+    int abi_version;     /* SAGE_ABI_VERSION */
+    int blkq;            /* rows per Q quantization block (128) */
+    int blkk;            /* rows per K quantization block (128) */
+    int bc;              /* keys per online-softmax tile (128; equals blkk) */
+    int br;              /* queries per attention workgroup (256) */
+    int stats_chunk;     /* tokens per statistics workgroup (512) */
+    float p_scale;       /* static FP8 scale of P (448, the e4m3fn maximum) */
+    float log2_p_scale;  /* fp32(log2(448)), folded into the exp2 argument */
+    int fp8_format;      /* 0 = OCP e4m3fn (max 448, no infinities) */
+} sage_config;
+
+/* Fill *out with the constants for head dimension d.
+ * Returns SAGE_OK, SAGE_ERR_NULL, or SAGE_ERR_UNSUPPORTED. */
+int sage_get_config(int d, sage_config* out);
+
+/* Indices into the sizes array of sage_quant_sizes. */
+enum sage_buffer {
+    SAGE_BUF_Q8 = 0,   /* int8  [B][H][N_pad][d]; rows >= N are 0 */
+    SAGE_BUF_QSCALE,   /* fp32  [B][H][nblk] */
+    SAGE_BUF_K8,       /* int8  [B][H][N_pad][d]; rows >= N are 0 */
+    SAGE_BUF_KSCALE,   /* fp32  [B][H][nblk] */
+    SAGE_BUF_KMEAN,    /* fp32  [B][H][d] */
+    SAGE_BUF_VQ,       /* fp8 e4m3 (1 B) or fp16 (2 B): [B][H][nblk][d][128], see below */
+    SAGE_BUF_VSCALE,   /* fp32  [B][H][d] */
+    SAGE_BUF_WS_QK,    /* workspace bytes for sage_quant_qk */
+    SAGE_BUF_WS_V,     /* workspace bytes for sage_quant_v */
+    SAGE_NBUF
+};
+
+/* Byte sizes of every buffer above for the given problem (sizes has
+ * SAGE_NBUF entries, host memory).  Returns SAGE_OK, SAGE_ERR_NULL,
+ * SAGE_ERR_INVALID, SAGE_ERR_UNSUPPORTED or SAGE_ERR_SIZE. */
+int sage_quant_sizes(int B, int H, int N, int d, int pv_dtype, size_t* sizes);
+
+/*
+ * Smooth K and quantize Q and K (per block of 128 rows, INT8).
+ *
+ * K smoothing (wxsanhe §三.1 "outlier smoothing"; txrjy 四个步骤 section): per
+ * (b, h, c), I = sum over tokens j of trunc(K[j][c] * 2^30) in wrapping
+ * 64-bit two's complement (each term saturated at +-2^62, NaN -> 0), then
+ * k_mean = fp32(fp64(I) / (fp64(N) * 2^30)).  This is the token mean on an
+ * exact 2^-30 grid, so it does not depend on summation order.
+ * Then k' = fp32(K - k_mean).
+ * Per block r of rows [128 r, min(N, 128 r + 128)) of Q (and of k'):
+ *   a = max |x| over the block's valid rows and all d channels,
+ *   scale = fp32(fp64(a) / 127), inv = a > 0 ? fp32(127 / fp64(a)) : 0,
+ *   code = clamp(round_half_even(fp32(x * inv)), -127, 127).
+ * (reportify SageAttention3 summary, 8比特训练: per-block INT8.)
+ *
+ * q, k: bf16 inputs [B,H,N,d] or [B,N,H,d] (layout).
+ * Outputs (caller-allocated, sizes from sage_quant_sizes): q8, q_scale, k8,
+ * k_scale, k_mean.  workspace: SAGE_BUF_WS_QK bytes of device scratch (no
+ * initialisation needed; contents undefined on return).
+ */
+int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, int layout,
+                  int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, float* k_mean,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Quantize V (wxsanhe §三.1: P V in FP8 or FP16).
+ * pv_dtype = SAGE_PV_FP8: per (b, h, c), a = max_j |V[j][c]|;
+ *   v_scale = fp32(fp64(a) / 448), inv = a > 0 ? fp32(448 / fp64(a)) : 0,
+ *   code = e4m3fn(round_half_even(fp32(V * inv))) (saturating).
+ * pv_dtype = SAGE_PV_FP16: code = binary16(round_half_even(V)) saturating at
+ *   +-65504; v_scale = 1.
+ * vq layout: [B][H][nblk][d][128]: for each tile of 128 keys, one row of 128
+ * codes per channel, keys permuted within the tile: key
+ *   r = 32*kb + 8*b + 4*g + q   (kb, b, q in 0..3, g in 0..1)
+ * is stored at position 64*g + 16*kb + 4*b + q.  Keys >= N are 0.
+ * (This order makes the P V operand of one lane a contiguous run.)
+ * workspace: SAGE_BUF_WS_V bytes of device scratch (fp8 path only; may be
+ * NULL with 0 bytes for fp16).
+ */
+int sage_quant_v(const void* v, int B, int H, int N, int d, int layout, int pv_dtype,
+                 void* vq, float* v_scale, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * Fused attention over the quantized operands (hunxia glossary, FlashAttention:
+ * tiled, online softmax; wxsanhe §三.1: two-level accumulation).
+ * For each query i (with sigma = fp32(q_scale * lambda), lambda =
+ * fp32(sm_scale * log2 e)), key tiles t = 0, 1, ... of 128 keys in ascending
+ * order (causal: keys j > i masked, tiles wholly above the diagonal skipped):
+ *   c = fp32(sigma * k_scale[t]);  S_j = exact int32 dot(q8_i, k8_j)
+ *   m_t = max_j fp32(S_j c);  m' = max(m, m_t);  alpha = exp2(m - m') (0 at start)
+ *   p_j = exp2(fma(S_j, c, -fp32(m' - log2 448)))     (about 448 * P_ij)
+ *   l = alpha l + sum_j p_j
+ *   T = sum_j e4m3(p_j) * v_j        (fp16 path: binary16(p_j)), fresh FP32 per tile
+ *   O = alpha O + T;  m = m'
+ * and finally out_i = O * v_scale / l.
+ * causal: 0 or 1 (top-left aligned, j <= i).  sm_scale: finite, > 0.
+ * out: [B,H,N,d] or [B,N,H,d] (layout), bf16 (out_dtype 0) or fp32 (1).
+ */
+int sage_attn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                  const void* vq, const float* v_scale, int B, int H, int N, int d, int layout,
+                  int causal, float sm_scale, int pv_dtype, void* out, int out_dtype,
+                  void* stream);
+
+/*
+ * sage_attn_fwd that also writes the raw int32 Q K^T accumulators of head
+ * (b, h), queries [row0, row0 + nrows), all keys, to s_out [nrows][N]
+ * (row-major).  With causal, only entries j <= i are written; the others are
+ * left untouched.  Same kernel source and arguments as sage_attn_fwd; the
+ * attention output is written as well.
+ */
+int sage_attn_fwd_debug(const int8_t* q8, const float* q_scale, const int8_t* k8,
+                        const float* k_scale, const void* vq, const float* v_scale, int B, int H,
+                        int N, int d, int layout, int causal, float sm_scale, int pv_dtype,
+                        void* out, int out_dtype, int b, int h, int row0, int nrows,
+                        int32_t* s_out, void* stream);
+
+/* A static, human-readable name for a status code. */
+const char* sage_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H */

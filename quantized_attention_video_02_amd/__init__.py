@@ -1,0 +1,191 @@
+"""libsage: SageAttention-style INT8-QK / FP8-PV attention on MI355X (gfx950).
+
+A thin ctypes binding over the C ABI declared in ``include/sage.h``: every step
+of the computation runs in the library's HIP kernels; this module only
+marshals arguments.  PyTorch is used for device memory and the current stream.
+
+Two-line drop-in use::
+
+    import quantized_attention_video_02_amd as sage
+    out = sage.attn(q, k, v)            # q, k, v: bf16 [B, H, N, d] on the GPU
+
+The library must be built first (``python -m quantized_attention_video_02_amd.build``);
+there is no fallback: without libsage.so every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsage.so")
+
+SAGE_OK = 0
+LAYOUTS = {"HND": 0, "NHD": 1}
+PV = {"fp8": 0, "fp16": 1}
+OUT = {torch.bfloat16: 0, torch.float32: 1}
+(BUF_Q8, BUF_QSCALE, BUF_K8, BUF_KSCALE, BUF_KMEAN, BUF_VQ, BUF_VSCALE, BUF_WS_QK,
+ BUF_WS_V, NBUF) = range(10)
+
+
+class SageError(RuntimeError):
+    pass
+
+
+class SageConfig(ct.Structure):
+    _fields_ = [("abi_version", ct.c_int), ("blkq", ct.c_int), ("blkk", ct.c_int),
+                ("bc", ct.c_int), ("br", ct.c_int), ("stats_chunk", ct.c_int),
+                ("p_scale", ct.c_float), ("log2_p_scale", ct.c_float), ("fp8_format", ct.c_int)]
+
+
+EXPORTS = ["sage_get_config", "sage_quant_sizes", "sage_quant_qk", "sage_quant_v",
+           "sage_attn_fwd", "sage_attn_fwd_debug", "sage_status_string"]
+
+_lib = None
+
+
+def lib():
+    """Load libsage.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise SageError(f"{LIB_PATH} is missing: build it with "
+                        "`python -m quantized_attention_video_02_amd.build`")
+    L = ct.CDLL(LIB_PATH)
+    P, I, F, S = ct.c_void_p, ct.c_int, ct.c_float, ct.c_size_t
+    L.sage_get_config.argtypes = [I, ct.POINTER(SageConfig)]
+    L.sage_quant_sizes.argtypes = [I, I, I, I, I, ct.POINTER(S)]
+    L.sage_quant_qk.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, S, P]
+    L.sage_quant_v.argtypes = [P, I, I, I, I, I, I, P, P, P, S, P]
+    L.sage_attn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
+    L.sage_attn_fwd_debug.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, I, I, I,
+                                      P, P]
+    for name in EXPORTS[:-1]:
+        getattr(L, name).restype = I
+    L.sage_status_string.argtypes = [I]
+    L.sage_status_string.restype = ct.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != SAGE_OK:
+        raise SageError(lib().sage_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ct.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ct.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def get_config(d: int = 128) -> dict:
+    c = SageConfig()
+    _check(lib().sage_get_config(d, ct.byref(c)))
+    return {f: getattr(c, f) for f, _ in SageConfig._fields_}
+
+
+def quant_sizes(B: int, H: int, N: int, d: int, pv: str = "fp8") -> list[int]:
+    arr = (ct.c_size_t * NBUF)()
+    _check(lib().sage_quant_sizes(B, H, N, d, PV[pv], arr))
+    return list(arr)
+
+
+def _dims(x: torch.Tensor, layout: str):
+    if x.dim() != 4:
+        raise ValueError("expected a 4-d tensor")
+    if layout == "HND":
+        B, H, N, d = x.shape
+    elif layout == "NHD":
+        B, N, H, d = x.shape
+    else:
+        raise ValueError(f"layout must be HND or NHD, not {layout!r}")
+    return B, H, N, d
+
+
+def _empty(nbytes: int, device, dtype=torch.uint8):
+    itemsize = torch.empty((), dtype=dtype).element_size()
+    return torch.empty(max(1, nbytes // itemsize), dtype=dtype, device=device)
+
+
+def quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND") -> dict:
+    """Smooth K and quantize Q, K to per-block INT8 (sage_quant_qk)."""
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise TypeError("q and k must be bfloat16")
+    if q.shape != k.shape or not q.is_contiguous() or not k.is_contiguous():
+        raise ValueError("q and k must be contiguous and of the same shape")
+    B, H, N, d = _dims(q, layout)
+    sz = quant_sizes(B, H, N, d)
+    dev = q.device
+    nblk = -(-N // 128)
+    r = dict(q8=torch.empty((B, H, nblk * 128, d), dtype=torch.int8, device=dev),
+             q_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+             k8=torch.empty((B, H, nblk * 128, d), dtype=torch.int8, device=dev),
+             k_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+             k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev),
+             workspace=_empty(sz[BUF_WS_QK], dev, torch.int64))
+    _check(lib().sage_quant_qk(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout], _ptr(r["q8"]),
+                               _ptr(r["q_scale"]), _ptr(r["k8"]), _ptr(r["k_scale"]),
+                               _ptr(r["k_mean"]), _ptr(r["workspace"]), sz[BUF_WS_QK],
+                               _stream(dev)))
+    r.update(B=B, H=H, N=N, d=d, layout=layout)
+    return r
+
+
+def quant_v(v: torch.Tensor, pv: str = "fp8", layout: str = "HND"):
+    """Quantize V (sage_quant_v): returns (vq, v_scale); vq is the library's
+    tiled [B, H, nblk, d, 128] layout with permuted keys (see sage.h)."""
+    if v.dtype != torch.bfloat16 or not v.is_contiguous():
+        raise TypeError("v must be a contiguous bfloat16 tensor")
+    B, H, N, d = _dims(v, layout)
+    sz = quant_sizes(B, H, N, d, pv)
+    dev = v.device
+    nblk = -(-N // 128)
+    vq = torch.empty((B, H, nblk, d, 128), dtype=torch.uint8 if pv == "fp8" else torch.float16,
+                     device=dev)
+    vs = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    ws = _empty(sz[BUF_WS_V], dev, torch.float32) if sz[BUF_WS_V] else None
+    _check(lib().sage_quant_v(_ptr(v), B, H, N, d, LAYOUTS[layout], PV[pv], _ptr(vq), _ptr(vs),
+                              _ptr(ws), sz[BUF_WS_V], _stream(dev)))
+    return vq, vs
+
+
+def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
+             sm_scale: float | None = None, pv: str = "fp8", out_dtype=torch.bfloat16,
+             out: torch.Tensor | None = None, debug: tuple | None = None):
+    """Fused attention over quantized operands (sage_attn_fwd).  With
+    ``debug=(b, h, row0, nrows)`` calls sage_attn_fwd_debug and also returns
+    the int32 Q K^T accumulators [nrows, N]."""
+    B, H, N, d, layout = qz["B"], qz["H"], qz["N"], qz["d"], qz["layout"]
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    shape = (B, H, N, d) if layout == "HND" else (B, N, H, d)
+    dev = qz["q8"].device
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    args = (_ptr(qz["q8"]), _ptr(qz["q_scale"]), _ptr(qz["k8"]), _ptr(qz["k_scale"]), _ptr(vq),
+            _ptr(vs), B, H, N, d, LAYOUTS[layout], int(bool(causal)), sm, PV[pv], _ptr(out),
+            OUT[out.dtype])
+    if debug is None:
+        _check(lib().sage_attn_fwd(*args, _stream(dev)))
+        return out
+    b, h, row0, nrows = debug
+    s = torch.zeros((nrows, N), dtype=torch.int32, device=dev)
+    _check(lib().sage_attn_fwd_debug(*args, b, h, row0, nrows, _ptr(s), _stream(dev)))
+    return out, s
+
+
+def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+         sm_scale: float | None = None, pv: str = "fp8", layout: str = "HND",
+         out_dtype=torch.bfloat16) -> torch.Tensor:
+    """softmax(Q K^T sm_scale) V through the quantized path (quantize, then the
+    fused kernel), all on q's device and current stream."""
+    qz = quant_qk(q, k, layout)
+    vq, vs = quant_v(v, pv, layout)
+    return attn_fwd(qz, vq, vs, causal=causal, sm_scale=sm_scale, pv=pv, out_dtype=out_dtype)
+

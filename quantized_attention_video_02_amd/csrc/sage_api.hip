@@ -1,0 +1,211 @@
+// Host side of the libsage C ABI: argument validation (entirely before any
+// launch), buffer-size arithmetic, and the kernel launches.  Declarations and
+// the meaning of every argument are in include/sage.h.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sage.h"
+#include "sage_common.h"
+
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dims(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID;
+    if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
+    const int64_t nblk = ((int64_t)N + sage::kBlk - 1) / sage::kBlk;
+    const int64_t elems = (int64_t)B * H * nblk * sage::kBlk * d;
+    if (elems >= kMaxElems) return SAGE_ERR_SIZE;
+    // grid limits: attention grid is B*H*ceil(N/256) workgroups; stats grid y is B*H
+    if ((int64_t)B * H > 65535 || (int64_t)B * H * ((N + sage::kBr - 1) / sage::kBr) >= (1ll << 31))
+        return SAGE_ERR_SIZE;
+    return SAGE_OK;
+}
+
+int check_layout(int layout) {
+    return (layout == SAGE_LAYOUT_HND || layout == SAGE_LAYOUT_NHD) ? SAGE_OK : SAGE_ERR_INVALID;
+}
+int check_pv(int pv) { return (pv == SAGE_PV_FP8 || pv == SAGE_PV_FP16) ? SAGE_OK : SAGE_ERR_INVALID; }
+
+struct Sizes {
+    size_t v[SAGE_NBUF];
+};
+
+Sizes sizes_of(int B, int H, int N, int d, int pv) {
+    const size_t nblk = ((size_t)N + sage::kBlk - 1) / sage::kBlk;
+    const size_t npad = nblk * sage::kBlk;
+    const size_t bh = (size_t)B * H;
+    const size_t nchunk = ((size_t)N + sage::kStatsChunk - 1) / sage::kStatsChunk;
+    Sizes s;
+    s.v[SAGE_BUF_Q8] = bh * npad * d;
+    s.v[SAGE_BUF_QSCALE] = bh * nblk * sizeof(float);
+    s.v[SAGE_BUF_K8] = bh * npad * d;
+    s.v[SAGE_BUF_KSCALE] = bh * nblk * sizeof(float);
+    s.v[SAGE_BUF_KMEAN] = bh * d * sizeof(float);
+    s.v[SAGE_BUF_VQ] = bh * npad * d * (pv == SAGE_PV_FP16 ? 2 : 1);
+    s.v[SAGE_BUF_VSCALE] = bh * d * sizeof(float);
+    s.v[SAGE_BUF_WS_QK] = bh * nchunk * d * sizeof(uint64_t);
+    s.v[SAGE_BUF_WS_V] = pv == SAGE_PV_FP16 ? 0 : (bh * nchunk * d + bh * d) * sizeof(float);
+    return s;
+}
+
+#define SAGE_TRY(expr)                 \
+    do {                               \
+        const int _st = (expr);        \
+        if (_st != SAGE_OK) return _st; \
+    } while (0)
+
+int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                const void* vq, const float* v_scale, int B, int H, int N, int d, int layout,
+                int causal, float sm_scale, int pv_dtype, void* out, int out_dtype, int dump,
+                int db, int dh, int row0, int nrows, int32_t* s_out, void* stream) {
+    if (!q8 || !q_scale || !k8 || !k_scale || !vq || !v_scale || !out) return SAGE_ERR_NULL;
+    if (dump && !s_out) return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_layout(layout));
+    SAGE_TRY(check_pv(pv_dtype));
+    if (causal != 0 && causal != 1) return SAGE_ERR_INVALID;
+    if (out_dtype != SAGE_OUT_BF16 && out_dtype != SAGE_OUT_FP32) return SAGE_ERR_INVALID;
+    if (!(isfinite(sm_scale) && sm_scale > 0.0f)) return SAGE_ERR_INVALID;
+    if (dump) {
+        if (db < 0 || db >= B || dh < 0 || dh >= H || row0 < 0 || nrows < 1 ||
+            (int64_t)row0 + nrows > N)
+            return SAGE_ERR_INVALID;
+        if ((int64_t)nrows * N >= kMaxElems) return SAGE_ERR_SIZE;
+    }
+    if (!aligned16(q8) || !aligned16(q_scale) || !aligned16(k8) || !aligned16(k_scale) ||
+        !aligned16(vq) || !aligned16(v_scale) || !aligned16(out) || (dump && !aligned16(s_out)))
+        return SAGE_ERR_ALIGN;
+    sage::AttnArgs a;
+    a.q8 = q8;
+    a.q_scale = q_scale;
+    a.k8 = k8;
+    a.k_scale = k_scale;
+    a.vq = vq;
+    a.v_scale = v_scale;
+    a.out = out;
+    a.s_out = s_out;
+    a.H = H;
+    a.N = N;
+    a.nblk = (N + sage::kBlk - 1) / sage::kBlk;
+    a.N_pad = a.nblk * sage::kBlk;
+    a.nqt = (N + sage::kBr - 1) / sage::kBr;
+    a.total = B * H * a.nqt;
+    a.layout = layout;
+    a.out_fp32 = out_dtype == SAGE_OUT_FP32;
+    a.lambda = (float)((double)sm_scale * 1.4426950408889634);
+    a.dbh = dump ? db * H + dh : -1;
+    a.drow0 = row0;
+    a.dnrows = nrows;
+    const hipError_t e = sage::launch_attn(a, B, d, pv_dtype == SAGE_PV_FP16, causal, dump,
+                                           (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) int sage_get_config(int d, sage_config* out) {
+    if (!out) return SAGE_ERR_NULL;
+    if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
+    out->abi_version = SAGE_ABI_VERSION;
+    out->blkq = sage::kBlk;
+    out->blkk = sage::kBlk;
+    out->bc = sage::kBc;
+    out->br = sage::kBr;
+    out->stats_chunk = sage::kStatsChunk;
+    out->p_scale = sage::kPScale;
+    out->log2_p_scale = sage::kLog2PScale;
+    out->fp8_format = 0;
+    return SAGE_OK;
+}
+
+__attribute__((visibility("default"))) int sage_quant_sizes(int B, int H, int N, int d,
+                                                            int pv_dtype, size_t* sizes) {
+    if (!sizes) return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_pv(pv_dtype));
+    const Sizes s = sizes_of(B, H, N, d, pv_dtype);
+    for (int i = 0; i < SAGE_NBUF; ++i) sizes[i] = s.v[i];
+    return SAGE_OK;
+}
+
+__attribute__((visibility("default"))) int sage_quant_qk(const void* q, const void* k, int B,
+                                                         int H, int N, int d, int layout,
+                                                         int8_t* q8, float* q_scale, int8_t* k8,
+                                                         float* k_scale, float* k_mean,
+                                                         void* workspace, size_t workspace_bytes,
+                                                         void* stream) {
+    if (!q || !k || !q8 || !q_scale || !k8 || !k_scale || !k_mean || !workspace)
+        return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_layout(layout));
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q8) || !aligned16(q_scale) ||
+        !aligned16(k8) || !aligned16(k_scale) || !aligned16(k_mean) || !aligned16(workspace))
+        return SAGE_ERR_ALIGN;
+    const Sizes s = sizes_of(B, H, N, d, SAGE_PV_FP8);
+    if (workspace_bytes < s.v[SAGE_BUF_WS_QK]) return SAGE_ERR_WORKSPACE;
+    const hipError_t e = sage::launch_quant_qk((const sage::u16*)q, (const sage::u16*)k, B, H, N,
+                                               d, layout, q8, q_scale, k8, k_scale, k_mean,
+                                               (uint64_t*)workspace, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+__attribute__((visibility("default"))) int sage_quant_v(const void* v, int B, int H, int N, int d,
+                                                        int layout, int pv_dtype, void* vq,
+                                                        float* v_scale, void* workspace,
+                                                        size_t workspace_bytes, void* stream) {
+    if (!v || !vq || !v_scale) return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_layout(layout));
+    SAGE_TRY(check_pv(pv_dtype));
+    const Sizes s = sizes_of(B, H, N, d, pv_dtype);
+    if (pv_dtype == SAGE_PV_FP8 && !workspace) return SAGE_ERR_NULL;
+    if (!aligned16(v) || !aligned16(vq) || !aligned16(v_scale) ||
+        (workspace && !aligned16(workspace)))
+        return SAGE_ERR_ALIGN;
+    if (workspace_bytes < s.v[SAGE_BUF_WS_V]) return SAGE_ERR_WORKSPACE;
+    const hipError_t e = sage::launch_quant_v((const sage::u16*)v, B, H, N, d, layout,
+                                              pv_dtype == SAGE_PV_FP16, vq, v_scale,
+                                              (float*)workspace, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+__attribute__((visibility("default"))) int sage_attn_fwd(
+    const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+    const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
+    float sm_scale, int pv_dtype, void* out, int out_dtype, void* stream) {
+    return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
+                       pv_dtype, out, out_dtype, 0, 0, 0, 0, 1, nullptr, stream);
+}
+
+__attribute__((visibility("default"))) int sage_attn_fwd_debug(
+    const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+    const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
+    float sm_scale, int pv_dtype, void* out, int out_dtype, int b, int h, int row0, int nrows,
+    int32_t* s_out, void* stream) {
+    return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
+                       pv_dtype, out, out_dtype, 1, b, h, row0, nrows, s_out, stream);
+}
+
+__attribute__((visibility("default"))) const char* sage_status_string(int status) {
+    switch (status) {
+        case SAGE_OK: return "SAGE_OK";
+        case SAGE_ERR_NULL: return "SAGE_ERR_NULL: a required pointer is NULL";
+        case SAGE_ERR_INVALID: return "SAGE_ERR_INVALID: invalid argument";
+        case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED: head dimension must be 64 or 128";
+        case SAGE_ERR_ALIGN: return "SAGE_ERR_ALIGN: device buffers must be 16-byte aligned";
+        case SAGE_ERR_SIZE: return "SAGE_ERR_SIZE: problem exceeds the supported size";
+        case SAGE_ERR_HIP: return "SAGE_ERR_HIP: a HIP launch failed";
+        case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace too small";
+        default: return "SAGE_ERR_UNKNOWN";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal definitions shared by the libsage HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned short u16;
+
+constexpr int kBlk = 128;          // rows per Q / K quantization block
+constexpr int kBc = 128;           // keys per online-softmax tile (== kBlk)
+constexpr int kBr = 256;           // queries per attention workgroup (8 waves x 32)
+constexpr int kAttnThreads = 512;  // 8 wave64s
+constexpr int kStatsChunk = 512;   // tokens per statistics workgroup
+constexpr int kQuantThreads = 256;
+constexpr float kPScale = 448.0f;
+// fp32 nearest to log2(448) = 8.807354922057604...
+constexpr float kLog2PScale = 0x1.19d5dap+3f;
+
+// Offset (in elements) of row n of head (b, h) in a [B,H,N,d] or [B,N,H,d] tensor.
+__device__ __host__ inline int64_t row_offset(int layout, int b, int h, int n, int H, int N,
+                                              int d) {
+    return layout == 0 ? ((int64_t)(b * H + h) * N + n) * d : ((int64_t)b * N + n) * H * d +
+                                                                  (int64_t)h * d;
+}
+
+__device__ inline float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ inline uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Wave-wide max of a non-negative float (all 64 lanes hold a value).
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// Arguments of the fused attention kernel (one struct, passed by value).
+struct AttnArgs {
+    const int8_t* q8;
+    const float* q_scale;
+    const int8_t* k8;
+    const float* k_scale;
+    const void* vq;
+    const float* v_scale;
+    void* out;
+    int32_t* s_out;  // debug dump (dump instantiations only)
+    int H, N, N_pad, nblk, nqt, total, layout, out_fp32;
+    float lambda;    // fp32(sm_scale * log2 e)
+    int dbh, drow0, dnrows;
+};
+
+hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
+                           int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean,
+                           uint64_t* ws, hipStream_t s);
+hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, int pv16,
+                          void* vq, float* vscale, float* ws, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal, int dump,
+                       hipStream_t s);
+
+}  // namespace sage

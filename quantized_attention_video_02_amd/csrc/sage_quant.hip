@@ -1,0 +1,371 @@
+// Smoothing and quantization pass of libsage (gfx950): HBM-bound kernels.
+//
+//   k_stats / v_stats : per (b, h, chunk of 512 tokens) partial column
+//                       statistics (exact fixed-point K sums; V absmax),
+//   k_mean / v_scale  : per (b, h, channel) combination of the partials,
+//   quant_qk          : per (b, h, block of 128 rows) INT8 codes + scale,
+//   quant_v           : per (b, h, tile of 128 keys) FP8 e4m3 (or FP16) codes,
+//                       transposed to [channel][key] with the key order the
+//                       attention kernel's P V operand expects.
+//
+// Method: wxsanhe.com TurboDiffusion post, section 三.1 (Q K to INT8, P V to
+// FP8/FP16, outlier smoothing); reportify.cn SageAttention3 summary, bullet
+// 8比特训练 (per-block INT8).  Every read is a 16-byte vector load of a row
+// chunk; consecutive lanes read consecutive chunks of a row, so each wave
+// reads whole rows.  The partial-sum layout makes every reduction order-free
+// (wrapping int64 adds, max), so results are bitwise deterministic.
+#include "sage_common.h"
+
+namespace sage {
+
+// trunc(x * 2^30) of the bf16 value with bit pattern u, saturated at +-2^62,
+// NaN -> 0 (the fixed-point grid of the K mean).
+__device__ inline uint64_t fix30_bf16(uint32_t u) {
+    const uint32_t e = (u >> 7) & 0xffu, man = u & 0x7fu;
+    const bool neg = (u >> 15) & 1u;
+    uint64_t mag;
+    if (e == 0xffu) {
+        if (man) return 0;
+        mag = 1ull << 62;
+    } else {
+        const uint32_t M = e ? (128u + man) : man;  // value = M * 2^(E - 134)
+        const int sh = (e ? (int)e : 1) - 104;      // x * 2^30 = M * 2^sh
+        if (sh > 54) mag = 1ull << 62;
+        else if (sh >= 0) mag = (uint64_t)M << sh;
+        else mag = (-sh >= 32) ? 0ull : (uint64_t)(M >> (-sh));
+    }
+    return neg ? (0ull - mag) : mag;
+}
+
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void k_stats_kernel(const u16* __restrict__ k, int H,
+                                                                int N, int layout, int nchunk,
+                                                                uint64_t* __restrict__ part) {
+    constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    constexpr int RPI = kQuantThreads / CPR;    // rows per pass
+    __shared__ uint64_t red[RPI][D];
+    const int chunk = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
+    const int n0 = chunk * kStatsChunk, n1 = min(N, n0 + kStatsChunk);
+    uint64_t acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0;
+#pragma unroll 4
+    for (int n = n0 + tr; n < n1; n += RPI) {
+        const uint4 w = *(const uint4*)(k + row_offset(layout, b, h, n, H, N, D) + cg * 8);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += fix30_bf16(ws[e] & 0xffffu);
+            acc[2 * e + 1] += fix30_bf16(ws[e] >> 16);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[tr][cg * 8 + e] = acc[e];
+    __syncthreads();
+    if (t < D) {
+        uint64_t s = 0;
+#pragma unroll 8
+        for (int r = 0; r < RPI; ++r) s += red[r][t];
+        part[((int64_t)bh * nchunk + chunk) * D + t] = s;
+    }
+}
+
+__global__ void k_mean_kernel(const uint64_t* __restrict__ part, int nchunk, int D, int total,
+                              int N, float* __restrict__ mean) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int bh = i / D, c = i % D;
+    uint64_t s = 0;
+    for (int ch = 0; ch < nchunk; ++ch) s += part[((int64_t)bh * nchunk + ch) * D + c];
+    mean[i] = (float)((double)(int64_t)s / ((double)N * 1073741824.0));
+}
+
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void v_stats_kernel(const u16* __restrict__ v, int H,
+                                                                int N, int layout, int nchunk,
+                                                                float* __restrict__ part) {
+    constexpr int CPR = D / 8;
+    constexpr int RPI = kQuantThreads / CPR;
+    __shared__ float red[RPI][D];
+    const int chunk = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
+    const int n0 = chunk * kStatsChunk, n1 = min(N, n0 + kStatsChunk);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll 4
+    for (int n = n0 + tr; n < n1; n += RPI) {
+        const uint4 w = *(const uint4*)(v + row_offset(layout, b, h, n, H, N, D) + cg * 8);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = fmaxf(acc[2 * e], bf16_bits_to_f32(ws[e] & 0x7fffu));
+            acc[2 * e + 1] = fmaxf(acc[2 * e + 1], bf16_bits_to_f32((ws[e] >> 16) & 0x7fffu));
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[tr][cg * 8 + e] = acc[e];
+    __syncthreads();
+    if (t < D) {
+        float s = 0.0f;
+        for (int r = 0; r < RPI; ++r) s = fmaxf(s, red[r][t]);
+        part[((int64_t)bh * nchunk + chunk) * D + t] = s;
+    }
+}
+
+// v_scale = fp32(a / 448); inv = fp32(448 / a) (0 for a == 0), both via fp64.
+__global__ void v_scale_kernel(const float* __restrict__ part, int nchunk, int D, int total,
+                               float* __restrict__ v_scale, float* __restrict__ v_inv) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int bh = i / D, c = i % D;
+    float a = 0.0f;
+    for (int ch = 0; ch < nchunk; ++ch) a = fmaxf(a, part[((int64_t)bh * nchunk + ch) * D + c]);
+    v_scale[i] = (float)((double)a / 448.0);
+    v_inv[i] = a > 0.0f ? (float)(448.0 / (double)a) : 0.0f;
+}
+
+// One block of 128 rows of Q (blockIdx.z == 0) or of smoothed K (z == 1).
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, int H, int N, int N_pad, int nblk,
+    int layout, const float* __restrict__ kmean, int8_t* __restrict__ q8,
+    float* __restrict__ q_scale, int8_t* __restrict__ k8, float* __restrict__ k_scale) {
+    constexpr int CPR = D / 8;
+    constexpr int RPI = kQuantThreads / CPR;
+    constexpr int IT = kBlk / RPI;
+    __shared__ float wmax[kQuantThreads / 64];
+    const int blk = blockIdx.x, bh = blockIdx.y, isk = blockIdx.z;
+    const int b = bh / H, h = bh % H;
+    const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
+    const u16* src = isk ? k : q;
+    float mu[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mu[e] = isk ? kmean[bh * D + cg * 8 + e] : 0.0f;
+    float x[IT][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int row = blk * kBlk + tr + it * RPI;
+        if (row < N) {
+            const uint4 w = *(const uint4*)(src + row_offset(layout, b, h, row, H, N, D) + cg * 8);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[it][2 * e] = bf16_bits_to_f32(ws[e] & 0xffffu) - mu[2 * e];
+                x[it][2 * e + 1] = bf16_bits_to_f32(ws[e] >> 16) - mu[2 * e + 1];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[it][e]));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[it][e] = 0.0f;
+        }
+    }
+    amax = wave_max(amax);
+    if ((t & 63) == 0) wmax[t >> 6] = amax;
+    __syncthreads();
+    float a = wmax[0];
+#pragma unroll
+    for (int i = 1; i < kQuantThreads / 64; ++i) a = fmaxf(a, wmax[i]);
+    const float inv = a > 0.0f ? (float)(127.0 / (double)a) : 0.0f;
+    int8_t* dst = isk ? k8 : q8;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int row = blk * kBlk + tr + it * RPI;
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = __builtin_rintf(x[it][e] * inv);
+            v = fminf(fmaxf(v, -127.0f), 127.0f);
+            packed[e >> 2] |= ((uint32_t)(int)v & 0xffu) << (8 * (e & 3));
+        }
+        *(uint2*)(dst + ((int64_t)bh * N_pad + row) * D + cg * 8) = make_uint2(packed[0], packed[1]);
+    }
+    if (t == 0) (isk ? k_scale : q_scale)[bh * nblk + blk] = (float)((double)a / 127.0);
+}
+
+// Position of key r (0..127) of a tile inside the tile's [channel][128] rows.
+__device__ __host__ inline int vperm_pos(int r) {
+    const int kb = r >> 5, bb = (r >> 3) & 3, g = (r >> 2) & 1, qq = r & 3;
+    return 64 * g + 16 * kb + 4 * bb + qq;
+}
+// First key of the run of 4 keys stored at positions 4w .. 4w+3.
+__device__ inline int vperm_key0(int w) {
+    const int g = w >> 4, kb = (w >> 2) & 3, bb = w & 3;
+    return 32 * kb + 8 * bb + 4 * g;
+}
+
+// V -> e4m3 codes of one tile of 128 keys, written as [D][128] (permuted keys).
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void quant_v_fp8_kernel(
+    const u16* __restrict__ v, int H, int N, int nblk, int layout, const float* __restrict__ v_inv,
+    uint8_t* __restrict__ vq) {
+    constexpr int CPR = D / 8;
+    constexpr int RPI = kQuantThreads / CPR;
+    constexpr int IT = kBc / RPI;
+    constexpr int LSTR = D + 4;  // bytes per key row in LDS (4-byte pad: conflict-free columns)
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kBc * LSTR];
+    const int blk = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
+    float inv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) inv[e] = v_inv[bh * D + cg * 8 + e];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int key = tr + it * RPI, row = blk * kBc + key;
+        uint32_t w0 = 0u, w1 = 0u;
+        if (row < N) {
+            const uint4 w = *(const uint4*)(v + row_offset(layout, b, h, row, H, N, D) + cg * 8);
+            float x[8];
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = bf16_bits_to_f32(ws[e] & 0xffffu) * inv[2 * e];
+                x[2 * e + 1] = bf16_bits_to_f32(ws[e] >> 16) * inv[2 * e + 1];
+            }
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], w0, false);
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w0, true);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], w1, false);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], w1, true);
+        }
+        *(uint32_t*)&tile[key * LSTR + cg * 8] = w0;
+        *(uint32_t*)&tile[key * LSTR + cg * 8 + 4] = w1;
+    }
+    __syncthreads();
+    uint8_t* dst = vq + ((int64_t)bh * nblk + blk) * D * kBc;
+    const int w = t & 31, key0 = vperm_key0(w);
+    for (int c4 = t >> 5; c4 < D / 4; c4 += kQuantThreads / 32) {
+        uint32_t r[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) r[kk] = *(const uint32_t*)&tile[(key0 + kk) * LSTR + 4 * c4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t o = ((r[0] >> (8 * j)) & 0xffu) | (((r[1] >> (8 * j)) & 0xffu) << 8) |
+                               (((r[2] >> (8 * j)) & 0xffu) << 16) |
+                               (((r[3] >> (8 * j)) & 0xffu) << 24);
+            *(uint32_t*)(dst + (4 * c4 + j) * kBc + 4 * w) = o;
+        }
+    }
+}
+
+// V -> binary16 codes (saturating), same tiled/permuted layout; v_scale = 1.
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void quant_v_fp16_kernel(
+    const u16* __restrict__ v, int H, int N, int nblk, int layout, u16* __restrict__ vq,
+    float* __restrict__ v_scale) {
+    constexpr int CPR = D / 8;
+    constexpr int RPI = kQuantThreads / CPR;
+    constexpr int IT = kBc / RPI;
+    constexpr int LSTR = D + 2;  // u16 elements per key row in LDS (4-byte pad)
+    __shared__ __attribute__((aligned(16))) u16 tile[kBc * LSTR];
+    const int blk = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
+    if (blk == 0 && t < D) v_scale[bh * D + t] = 1.0f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int key = tr + it * RPI, row = blk * kBc + key;
+        uint32_t o[4] = {0u, 0u, 0u, 0u};
+        if (row < N) {
+            const uint4 w = *(const uint4*)(v + row_offset(layout, b, h, row, H, N, D) + cg * 8);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = fminf(fmaxf(bf16_bits_to_f32(ws[e] & 0xffffu), -65504.0f), 65504.0f);
+                const float x1 = fminf(fmaxf(bf16_bits_to_f32(ws[e] >> 16), -65504.0f), 65504.0f);
+                const u16 h0 = __builtin_bit_cast(u16, (_Float16)x0);
+                const u16 h1 = __builtin_bit_cast(u16, (_Float16)x1);
+                o[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *(uint32_t*)&tile[key * LSTR + cg * 8 + 2 * e] = o[e];
+    }
+    __syncthreads();
+    u16* dst = vq + ((int64_t)bh * nblk + blk) * D * kBc;
+    const int w = t & 31, key0 = vperm_key0(w);
+    for (int c2 = t >> 5; c2 < D / 2; c2 += kQuantThreads / 32) {
+        uint32_t r[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) r[kk] = *(const uint32_t*)&tile[(key0 + kk) * LSTR + 2 * c2];
+        const uint2 lo = make_uint2((r[0] & 0xffffu) | (r[1] << 16), (r[2] & 0xffffu) | (r[3] << 16));
+        const uint2 hi = make_uint2((r[0] >> 16) | (r[1] & 0xffff0000u),
+                                    (r[2] >> 16) | (r[3] & 0xffff0000u));
+        *(uint2*)(dst + (2 * c2) * kBc + 4 * w) = lo;
+        *(uint2*)(dst + (2 * c2 + 1) * kBc + 4 * w) = hi;
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+static inline hipError_t launch(const void* fn, dim3 grid, dim3 block, void** args,
+                                hipStream_t s) {
+    return hipLaunchKernel(fn, grid, block, args, 0, s);
+}
+
+hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
+                           int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean,
+                           uint64_t* ws, hipStream_t s) {
+    const int nblk = (N + kBlk - 1) / kBlk, N_pad = nblk * kBlk;
+    const int nchunk = (N + kStatsChunk - 1) / kStatsChunk;
+    const int BH = B * H, total = BH * d;
+    hipError_t e;
+    {
+        void* args[] = {(void*)&k, (void*)&H, (void*)&N, (void*)&layout, (void*)&nchunk, (void*)&ws};
+        const void* fn = d == 128 ? (const void*)k_stats_kernel<128> : (const void*)k_stats_kernel<64>;
+        if ((e = launch(fn, dim3(nchunk, BH), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
+    }
+    {
+        void* args[] = {(void*)&ws, (void*)&nchunk, (void*)&d, (void*)&total, (void*)&N, (void*)&kmean};
+        if ((e = launch((const void*)k_mean_kernel, dim3((total + 255) / 256), dim3(256), args, s)) !=
+            hipSuccess)
+            return e;
+    }
+    {
+        void* args[] = {(void*)&q,  (void*)&k,  (void*)&H,     (void*)&N,  (void*)&N_pad,
+                        (void*)&nblk, (void*)&layout, (void*)&kmean, (void*)&q8, (void*)&qs,
+                        (void*)&k8, (void*)&ks};
+        const void* fn = d == 128 ? (const void*)quant_qk_kernel<128> : (const void*)quant_qk_kernel<64>;
+        if ((e = launch(fn, dim3(nblk, BH, 2), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, int pv16,
+                          void* vq, float* vscale, float* ws, hipStream_t s) {
+    const int nblk = (N + kBc - 1) / kBc;
+    const int nchunk = (N + kStatsChunk - 1) / kStatsChunk;
+    const int BH = B * H, total = BH * d;
+    hipError_t e;
+    if (pv16) {
+        void* args[] = {(void*)&v, (void*)&H, (void*)&N, (void*)&nblk, (void*)&layout, (void*)&vq,
+                        (void*)&vscale};
+        const void* fn = d == 128 ? (const void*)quant_v_fp16_kernel<128>
+                                  : (const void*)quant_v_fp16_kernel<64>;
+        return launch(fn, dim3(nblk, BH), dim3(kQuantThreads), args, s);
+    }
+    float* part = ws;
+    float* vinv = ws + (size_t)BH * nchunk * d;
+    {
+        void* args[] = {(void*)&v, (void*)&H, (void*)&N, (void*)&layout, (void*)&nchunk, (void*)&part};
+        const void* fn = d == 128 ? (const void*)v_stats_kernel<128> : (const void*)v_stats_kernel<64>;
+        if ((e = launch(fn, dim3(nchunk, BH), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
+    }
+    {
+        void* args[] = {(void*)&part, (void*)&nchunk, (void*)&d, (void*)&total, (void*)&vscale,
+                        (void*)&vinv};
+        if ((e = launch((const void*)v_scale_kernel, dim3((total + 255) / 256), dim3(256), args, s)) !=
+            hipSuccess)
+            return e;
+    }
+    {
+        void* args[] = {(void*)&v, (void*)&H, (void*)&N, (void*)&nblk, (void*)&layout, (void*)&vinv,
+                        (void*)&vq};
+        const void* fn = d == 128 ? (const void*)quant_v_fp8_kernel<128>
+                                  : (const void*)quant_v_fp8_kernel<64>;
+        if ((e = launch(fn, dim3(nblk, BH), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace sage

@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/sage.h declares, reports its constants, and rejects invalid arguments
+with the documented status codes before anything is launched."""
+import ctypes as ct
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+
+@pytest.fixture(scope="module")
+def sage():
+    import quantized_attention_video_02_amd as s
+    from quantized_attention_video_02_amd import build as b
+
+    if not os.path.exists(b.LIB_PATH):
+        b.build()
+    s.lib()
+    return s
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(sage_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(sage):
+    names = declared_functions()
+    assert set(names) == set(sage.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", sage.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for n in names:
+        assert n in exported, n
+    assert not any(e.startswith("or_") for e in exported)  # nothing of the oracle
+
+
+def test_config_matches_the_method_constants(sage):
+    import oracle
+
+    for d in (64, 128):
+        c = sage.get_config(d)
+        assert c["abi_version"] == 1
+        assert c["blkq"] == c["blkk"] == oracle.BLK == 128
+        assert c["bc"] == oracle.BC == 128 and c["br"] == 256
+        assert c["p_scale"] == oracle.P_SCALE == 448.0
+        assert np.float32(c["log2_p_scale"]) == np.float32(math.log2(448.0))
+        assert c["fp8_format"] == 0
+    with pytest.raises(sage.SageError, match="UNSUPPORTED"):
+        sage.get_config(96)
+
+
+def test_quant_sizes(sage):
+    s = sage.quant_sizes(2, 3, 300, 64, "fp8")
+    nblk, npad = 3, 384
+    assert s[sage.BUF_Q8] == s[sage.BUF_K8] == 2 * 3 * npad * 64
+    assert s[sage.BUF_QSCALE] == s[sage.BUF_KSCALE] == 2 * 3 * nblk * 4
+    assert s[sage.BUF_KMEAN] == s[sage.BUF_VSCALE] == 2 * 3 * 64 * 4
+    assert s[sage.BUF_VQ] == 2 * 3 * npad * 64
+    assert s[sage.BUF_WS_QK] == 2 * 3 * 1 * 64 * 8
+    assert s[sage.BUF_WS_V] == (2 * 3 * 64 + 2 * 3 * 64) * 4
+    s16 = sage.quant_sizes(2, 3, 300, 64, "fp16")
+    assert s16[sage.BUF_VQ] == 2 * s[sage.BUF_VQ] and s16[sage.BUF_WS_V] == 0
+
+
+def _codes(sage):
+    L = sage.lib()
+    return L, {L.sage_status_string(c).decode().split(":")[0]: c for c in range(-8, 1)}
+
+
+A = 0x10000  # a fake, 16-byte-aligned address: never dereferenced (validation fails first)
+
+
+def test_invalid_arguments_rejected_before_launch(sage):
+    L, _ = _codes(sage)
+    sz = (ct.c_size_t * sage.NBUF)()
+    assert L.sage_quant_sizes(1, 1, 0, 128, 0, sz) == -2
+    assert L.sage_quant_sizes(1, 1, 10, 96, 0, sz) == -3
+    assert L.sage_quant_sizes(1, 1, 10, 128, 2, sz) == -2
+    assert L.sage_quant_sizes(1, 1, 10, 128, 0, None) == -1
+    assert L.sage_quant_sizes(70000, 1, 10, 128, 0, sz) == -5
+    assert L.sage_quant_sizes(1, 1 << 20, 1 << 20, 128, 0, sz) == -5
+    qk = lambda q=A, N=256, d=128, lay=0, ws=A, wsb=1 << 20, q8=A: L.sage_quant_qk(
+        q, A, 1, 1, N, d, lay, q8, A, A, A, A, ws, wsb, None)
+    assert qk(q=None) == -1
+    assert qk(ws=None) == -1
+    assert qk(N=-5) == -2
+    assert qk(d=32) == -3
+    assert qk(lay=2) == -2
+    assert qk(q=A + 8) == -4
+    assert qk(q8=A + 1) == -4
+    assert qk(wsb=16) == -7
+    qv = lambda pv=0, ws=A, wsb=1 << 20, v=A: L.sage_quant_v(v, 1, 1, 256, 128, 0, pv, A, A, ws,
+                                                              wsb, None)
+    assert qv(v=None) == -1
+    assert qv(pv=3) == -2
+    assert qv(ws=None) == -1
+    assert qv(wsb=8) == -7
+    assert qv(v=A + 4) == -4
+    fwd = lambda causal=0, sm=0.1, pv=0, od=0, out=A, N=256, lay=0: L.sage_attn_fwd(
+        A, A, A, A, A, A, 1, 2, N, 128, lay, causal, sm, pv, out, od, None)
+    assert fwd(out=None) == -1
+    assert fwd(causal=2) == -2
+    assert fwd(sm=float("nan")) == -2
+    assert fwd(sm=float("inf")) == -2
+    assert fwd(sm=0.0) == -2
+    assert fwd(sm=-1.0) == -2
+    assert fwd(pv=7) == -2
+    assert fwd(od=5) == -2
+    assert fwd(N=0) == -2
+    assert fwd(lay=-1) == -2
+    assert fwd(out=A + 2) == -4
+    dbg = lambda b=0, h=0, row0=0, nrows=4, s=A: L.sage_attn_fwd_debug(
+        A, A, A, A, A, A, 1, 2, 256, 128, 0, 0, 0.1, 0, A, 0, b, h, row0, nrows, s, None)
+    assert dbg(s=None) == -1
+    assert dbg(b=1) == -2
+    assert dbg(h=2) == -2
+    assert dbg(row0=-1) == -2
+    assert dbg(nrows=0) == -2
+    assert dbg(row0=250, nrows=7) == -2
+    assert dbg(s=A + 4) == -4
+
+
+def test_status_strings(sage):
+    L = sage.lib()
+    names = [L.sage_status_string(c).decode() for c in range(0, -8, -1)]
+    assert names[0] == "SAGE_OK" and all(n.startswith("SAGE_ERR_") for n in names[1:])
+    assert L.sage_status_string(12345).decode() == "SAGE_ERR_UNKNOWN"
