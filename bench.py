@@ -113,6 +113,9 @@ def main():
     ap.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (the known-size "
+                         "reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (there is no multi-GPU path; "
@@ -131,6 +134,13 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {wl.name}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} causal={wl.causal} pv={args.pv}",
           file=sys.stderr, flush=True)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wall, quant_ms, attn_ms = time_gpu(sage, wl, args.pv, args.steps, args.warmup)
     ops = attn_ops(wl.B, wl.H, wl.N, wl.d)
     ms_per_step = wall * 1e3 / args.steps

@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/sage.h"
+#include "sage.h"
 #include "sage_common.h"
 
 

@@ -53,6 +53,153 @@ struct AttnSmem {
     static constexpr int VCPR = kBc * VES / 16;
 };
 
+// Value of lane ^ 32 combined with this lane's (v_permlane32_swap: the two
+// halves of the wave exchange registers; both results hold one value from
+// each half, so max/sum of the pair is the same on both lanes).
+__device__ inline int pair_max(int x) {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return max((int)r[0], (int)r[1]);
+}
+__device__ inline float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Key index held by lane half hh in register r of 32-key block k4 of a tile
+// (the 32x32 MFMA accumulator layout: row 8*(r/4) + 4*hh + r%4).
+__device__ inline int tile_key(int key_t, int k4, int r, int hh) {
+    return key_t + 32 * k4 + 8 * (r >> 2) + 4 * hh + (r & 3);
+}
+
+// S^T (128 keys x 32 queries) = K8 tile (LDS, rows of KSTR bytes) . Q8^T.
+template <int D, int KSTR>
+__device__ inline void qk_tile(const uint8_t* kb, const v4i* qf, v16i* S, int n, int hh) {
+    constexpr int KK = D / 32;
+    const uint8_t* krow = kb + n * KSTR + 16 * hh;
+    v4i a[2][KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) a[0][kk] = *(const v4i*)(krow + 32 * kk);
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+        if (k4 + 1 < 4) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                a[(k4 + 1) & 1][kk] = *(const v4i*)(krow + 32 * (k4 + 1) * KSTR + 32 * kk);
+        }
+        v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[k4 & 1][0], qf[0], v16i{}, 0, 0, 0);
+#pragma unroll
+        for (int kk = 1; kk < KK; ++kk)
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[k4 & 1][kk], qf[kk], acc, 0, 0, 0);
+        S[k4] = acc;
+    }
+}
+
+__device__ inline void dump_tile(const v16i* S, int32_t* srow, int key_t, int N, bool causal,
+                                 int qi, int hh) {
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = tile_key(key_t, k4, r, hh);
+            if (key < N && (!causal || key <= qi)) srow[key] = S[k4][r];
+        }
+}
+
+// Online-softmax step of one tile for this lane's query.  In: S (int32), the
+// dequantization constant c, the running max m.  Out: P (the PV B operand),
+// alpha, the partial row sum ls of this lane's 64 keys; m is updated.
+// p = exp2(fma(S, c, -(m' - log2 448))).  MASK: keys >= N (and, causal,
+// keys > qi) get p = 0 and do not enter the max.
+template <bool MASK, typename PT>
+__device__ inline void softmax_tile(v16i* S, PT* P, float c, float& m, float& alpha, float& ls,
+                                    int key_t, int N, bool causal, int qi, int hh) {
+    if (MASK) {
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = tile_key(key_t, k4, r, hh);
+                if (key >= N || (causal && key > qi)) S[k4][r] = INT_MIN;
+            }
+    }
+    int mk[4];
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+        int x = max(S[k4][0], S[k4][1]);
+#pragma unroll
+        for (int r = 2; r < 16; r += 2) x = max(x, max(S[k4][r], S[k4][r + 1]));
+        mk[k4] = x;
+    }
+    const int mx = pair_max(max(max(mk[0], mk[1]), max(mk[2], mk[3])));
+    const float mt = (MASK && mx == INT_MIN) ? -INFINITY : (float)mx * c;
+    const float mn = fmaxf(m, mt);
+    alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    const float mu = mn - kLog2PScale;
+    float part[4];
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int s = S[k4][4 * u + j];
+                p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s, c, -mu));
+                if (MASK && s == INT_MIN) p[j] = 0.0f;
+            }
+            sum += (p[0] + p[1]) + (p[2] + p[3]);
+            if constexpr (sizeof(PT) == 32 && __is_same(PT, v8i)) {
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_nondeterministic_value(0),
+                                                        false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+                P[k4 >> 1][(k4 & 1) * 4 + u] = w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) P[2 * k4 + (u >> 1)][4 * (u & 1) + j] = (_Float16)p[j];
+            }
+        }
+        part[k4] = sum;
+    }
+    ls = (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// Level 1: T = V^T tile (LDS) . P^T, a fresh fp32 accumulator per output
+// block; level 2: O = alpha O + T.
+template <int D, int VSTR>
+__device__ inline void pv_tile_fp8(const uint8_t* vb, const v8i* P, v16f* O, float alpha, int n,
+                                   int hh) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+        const uint8_t* vrow = vb + (32 * cb + n) * VSTR + 64 * hh;
+        const v8i a0 = *(const v8i*)(vrow);
+        const v8i a1 = *(const v8i*)(vrow + 32);
+        v16f T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, P[0], v16f{}, 0, 0, 0, 0, 0, 0);
+        T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, P[1], T, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) O[cb][e] = __builtin_fmaf(alpha, O[cb][e], T[e]);
+    }
+}
+
+template <int D, int VSTR>
+__device__ inline void pv_tile_fp16(const uint8_t* vb, const v8h* P, v16f* O, float alpha, int n,
+                                    int hh) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+        const uint8_t* vrow = vb + (32 * cb + n) * VSTR + 2 * 64 * hh;
+        v16f T = v16f{};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const v8h av = *(const v8h*)(vrow + 16 * u);
+            T = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, P[u], T, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) O[cb][e] = __builtin_fmaf(alpha, O[cb][e], T[e]);
+    }
+}
+
 template <int D, bool PV16, bool CAUSAL, bool DUMP>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     using SM = AttnSmem<D, PV16>;
@@ -129,124 +276,33 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         if (active && t < wave_tiles) {
             const uint8_t* kb = smem + (t & 1) * SM::STAGE;
             const uint8_t* vb = kb + SM::KBYTES;
-            // ---- S^T = K8 . Q8^T (exact int32)
             v16i S[4];
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) S[k4][e] = 0;
-                const uint8_t* krow = kb + (32 * k4 + n) * SM::KSTR + 16 * hh;
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const v4i av = *(const v4i*)(krow + 32 * kk);
-                    S[k4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, qf[kk], S[k4], 0, 0, 0);
-                }
-            }
+            qk_tile<D, SM::KSTR>(kb, qf, S, n, hh);
             const int key_t = t * kBc;
-            if (DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows) {
-                int32_t* srow = a.s_out + (int64_t)(qi - a.drow0) * N;
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key_t + 32 * k4 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        if (key < N && (!CAUSAL || key <= qi)) srow[key] = S[k4][r];
-                    }
-            }
-            const bool needmask = (tail && t == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase);
-            if (needmask) {
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key_t + 32 * k4 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        if (key >= N || (CAUSAL && key > qi)) S[k4][r] = INT_MIN;
-                    }
-            }
-            // ---- tile max on the integers (c > 0 keeps the order)
-            int mx = INT_MIN;
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = max(mx, S[k4][r]);
-            mx = max(mx, __shfl_xor(mx, 32, 64));
+            if (DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows)
+                dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
             const float c = sigma * a.k_scale[bh * a.nblk + t];
-            const float mt = (mx == INT_MIN) ? -INFINITY : (float)mx * c;
-            const float mn = fmaxf(m, mt);
-            const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
-            const float mu = mn - kLog2PScale;
-            // ---- p = exp2(S c - (m' - log2 448)), row sum, P -> FP8 / FP16
-            float ls = 0.0f;
+            const bool needmask = (tail && t == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase);
+            float alpha, ls;
             if constexpr (!PV16) {
                 v8i P[2];
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        float p[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int s = S[k4][4 * u + j];
-                            p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s, c, -mu));
-                            if (needmask && s == INT_MIN) p[j] = 0.0f;
-                            ls += p[j];
-                        }
-                        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-                        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-                        P[k4 >> 1][(k4 & 1) * 4 + u] = w;
-                    }
-                // ---- level 1: T = V^T . P^T (fresh fp32); level 2: O = alpha O + T
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    v16f T;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) T[e] = 0.0f;
-                    const uint8_t* vrow = vb + (32 * cb + n) * SM::VSTR + 64 * hh;
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const v8i av = *(const v8i*)(vrow + 32 * hf);
-                        T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, P[hf], T, 0, 0, 0, 0,
-                                                                            0, 0);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) O[cb][e] = __builtin_fmaf(alpha, O[cb][e], T[e]);
-                }
+                if (needmask) softmax_tile<true>(S, P, c, m, alpha, ls, key_t, N, CAUSAL, qi, hh);
+                else softmax_tile<false>(S, P, c, m, alpha, ls, key_t, N, CAUSAL, qi, hh);
+                pv_tile_fp8<D, SM::VSTR>(vb, P, O, alpha, n, hh);
             } else {
                 v8h P[8];
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int s = S[k4][r];
-                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s, c, -mu));
-                        if (needmask && s == INT_MIN) p = 0.0f;
-                        ls += p;
-                        P[2 * k4 + (r >> 3)][r & 7] = (_Float16)p;
-                    }
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    v16f T;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) T[e] = 0.0f;
-                    const uint8_t* vrow = vb + (32 * cb + n) * SM::VSTR + 2 * 64 * hh;
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const v8h av = *(const v8h*)(vrow + 16 * u);
-                        T = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, P[u], T, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) O[cb][e] = __builtin_fmaf(alpha, O[cb][e], T[e]);
-                }
+                if (needmask) softmax_tile<true>(S, P, c, m, alpha, ls, key_t, N, CAUSAL, qi, hh);
+                else softmax_tile<false>(S, P, c, m, alpha, ls, key_t, N, CAUSAL, qi, hh);
+                pv_tile_fp16<D, SM::VSTR>(vb, P, O, alpha, n, hh);
             }
             l = alpha * l + ls;
-            m = mn;
         }
         if (t + 1 < ntiles) swrite((t + 1) & 1);
         __syncthreads();
     }
 
     // ---- epilogue: out = O * v_scale / l (l summed over both lane halves)
-    const float lt = l + __shfl_xor(l, 32, 64);
+    const float lt = pair_sum(l);
     if (!active || qi >= N) return;
     const int64_t obase = row_offset(a.layout, b, h, qi, H, N, D);
     const float* vs = a.v_scale + bh * D;
