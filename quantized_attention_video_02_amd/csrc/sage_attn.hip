@@ -18,14 +18,25 @@
 //   O^T (d x 32 queries) += V^T tile (LDS) . P^T (registers),
 //     8 x v_mfma_f32_32x32x64_f8f6f4 (d = 128) -- O^T keeps queries on lanes,
 //     so the per-query rescale alpha is a per-lane scalar.
-// K and V tiles are staged global -> registers -> LDS, double-buffered: the
-// loads of tile t+1 are in flight while tile t is computed; one barrier per
-// tile.  LDS rows carry a 16-byte pad so the 16-byte operand reads of 8
-// consecutive lanes (8 different rows) hit distinct banks.
+// Schedule: the 8 waves form two groups, waves 0-3 and 4-7, one wave of each
+// on every SIMD.  Time is cut into slots separated by workgroup barriers; in
+// each slot one group runs its MFMA phase (P V of tile t-1, then Q K^T of tile
+// t) while the other runs its VALU phase (the softmax of its current tile), and
+// the groups swap every slot.  A wave's VALU instructions do not overlap its own
+// MFMAs, but the SIMD overlaps one wave's MFMAs with the other wave's VALU
+// work, so keeping the two waves of a SIMD in opposite phases keeps both the
+// matrix core and the VALU busy.
+// K and V tiles go straight from global memory into LDS (global_load_lds_dwordx4,
+// no register staging), double-buffered: the loads of K(t+1) and V(t) are
+// issued at the start of the slot pair that reads K(t) and V(t-1).  LDS rows
+// carry a 16-byte pad so that the operand reads of 16 consecutive lanes (16
+// rows, same column) fall in 16 distinct 16-byte slots of the 64-bank LDS.
 // The grid is remapped so that consecutive workgroups of one head run on the
 // same XCD (hardware dispatches workgroups round-robin over the 8 XCDs), so a
 // head's K/V tiles are shared through that XCD's L2.
 #include <limits.h>
+
+#include <type_traits>
 
 #include "sage_common.h"
 
@@ -38,20 +49,54 @@ __device__ inline int xcd_remap(int bid, int total) {
     return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
 }
 
+// LDS: two K tiles (128 key rows of D bytes) and two V tiles (D channel rows
+// of 128 keys x 1 or 2 bytes).  Every row carries a 16-byte pad: the 16-byte
+// operand reads of 16 consecutive lanes (16 consecutive rows, same column)
+// then fall in 16 distinct 16-byte slots of the 64-bank LDS.
 template <int D, bool PV16>
-struct AttnSmem {
-    static constexpr int KSTR = D + 16;                      // bytes per key row
+struct Lds {
     static constexpr int VES = PV16 ? 2 : 1;
-    static constexpr int VSTR = kBc * VES + 16;              // bytes per channel row
-    static constexpr int KBYTES = kBc * KSTR;
+    static constexpr int KROW = D;                 // bytes of a K row in HBM
+    static constexpr int VROW = kBc * VES;         // bytes of a V row in HBM
+    static constexpr int KSTR = KROW + 16;         // bytes of a K row in LDS
+    static constexpr int VSTR = VROW + 16;
+    static constexpr int KBYTES = kBc * KSTR;      // one K tile in LDS
     static constexpr int VBYTES = D * VSTR;
-    static constexpr int STAGE = KBYTES + VBYTES;
-    static constexpr int TOTAL = 2 * STAGE;
-    static constexpr int KCH = kBc * D / 16 / kAttnThreads;       // 16-B K chunks per thread
-    static constexpr int VCH = D * kBc * VES / 16 / kAttnThreads; // 16-B V chunks per thread
-    static constexpr int KCPR = D / 16;
-    static constexpr int VCPR = kBc * VES / 16;
+    static constexpr int VBASE = 2 * KBYTES;
+    static constexpr int TOTAL = 2 * (KBYTES + VBYTES);
+    static constexpr int KPIECES = KBYTES / 1024;  // 1 KB direct-load pieces per tile
+    static constexpr int VPIECES = VBYTES / 1024;
+    static constexpr int KHBM = kBc * KROW;        // one K tile in HBM
+    static constexpr int VHBM = D * VROW;
+    static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles must be whole 1 KB pieces");
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Source offset (bytes, inside the HBM tile) of the 16-byte chunk that lands in
+// LDS slot P of a padded tile: LDS row P / (STR/16), chunk P % (STR/16); the
+// pad chunk of each row takes a duplicate of the row's first chunk.
+template <int ROW, int STR>
+__device__ inline int slot_src(int P) {
+    constexpr int CPR = STR / 16;
+    const int row = P / CPR, c = P % CPR;
+    return row * ROW + (c < ROW / 16 ? 16 * c : 0);
+}
+
+// Direct global -> LDS copy of this wave's pieces of a tile: piece J (1 KB) is
+// written by one global_load_lds_dwordx4, lane i filling bytes [16 i, 16 i + 16).
+template <int NPIECES, int MAXP>
+__device__ inline void tile_to_lds(const uint8_t* g, uint8_t* l, int wave, const int* off) {
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) {
+        const int J = wave + 8 * j;
+        if (J < NPIECES)
+            __builtin_amdgcn_global_load_lds((const void*)(g + off[j]), (lds_void*)(l + 1024 * J),
+                                             16, 0, 0);
+    }
+}
+
+__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Value of lane ^ 32 combined with this lane's (v_permlane32_swap: the two
 // halves of the wave exchange registers; both results hold one value from
@@ -59,6 +104,11 @@ struct AttnSmem {
 __device__ inline int pair_max(int x) {
     const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
     return max((int)r[0], (int)r[1]);
+}
+__device__ inline float pair_fmax(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float pair_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -72,11 +122,13 @@ __device__ inline int tile_key(int key_t, int k4, int r, int hh) {
     return key_t + 32 * k4 + 8 * (r >> 2) + 4 * hh + (r & 3);
 }
 
-// S^T (128 keys x 32 queries) = K8 tile (LDS, rows of KSTR bytes) . Q8^T.
-template <int D, int KSTR>
+// S^T (128 keys x 32 queries) = K8 tile (LDS) . Q8^T: lane (n, hh) reads key
+// row 32 k4 + n, channels [32 kk + 16 hh, +16).
+template <int D, bool PV16>
 __device__ inline void qk_tile(const uint8_t* kb, const v4i* qf, v16i* S, int n, int hh) {
+    using L = Lds<D, PV16>;
     constexpr int KK = D / 32;
-    const uint8_t* krow = kb + n * KSTR + 16 * hh;
+    const uint8_t* krow = kb + n * L::KSTR + 16 * hh;
     v4i a[2][KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) a[0][kk] = *(const v4i*)(krow + 32 * kk);
@@ -85,7 +137,7 @@ __device__ inline void qk_tile(const uint8_t* kb, const v4i* qf, v16i* S, int n,
         if (k4 + 1 < 4) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                a[(k4 + 1) & 1][kk] = *(const v4i*)(krow + 32 * (k4 + 1) * KSTR + 32 * kk);
+                a[(k4 + 1) & 1][kk] = *(const v4i*)(krow + 32 * (k4 + 1) * L::KSTR + 32 * kk);
         }
         v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[k4 & 1][0], qf[0], v16i{}, 0, 0, 0);
 #pragma unroll
@@ -109,20 +161,47 @@ __device__ inline void dump_tile(const v16i* S, int32_t* srow, int key_t, int N,
 // Online-softmax step of one tile for this lane's query.  In: S (int32), the
 // dequantization constant c, the running max m.  Out: P (the PV B operand),
 // alpha, the partial row sum ls of this lane's 64 keys; m is updated.
-// p = exp2(fma(S, c, -(m' - log2 448))).  MASK: keys >= N (and, causal,
-// keys > qi) get p = 0 and do not enter the max.
-template <bool MASK, typename PT>
-__device__ inline void softmax_tile(v16i* S, PT* P, float c, float& m, float& alpha, float& ls,
-                                    int key_t, int N, bool causal, int qi, int hh) {
-    if (MASK) {
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = tile_key(key_t, k4, r, hh);
-                if (key >= N || (causal && key > qi)) S[k4][r] = INT_MIN;
-            }
+// p = exp2(fma(S, c, -(m' - log2 448))).  With needmask (wave-uniform), the
+// keys past `lim` (key - key_t - 4 hh > lim: beyond N, or after the query
+// when causal) become -inf: p = 0 and they do not enter the max.
+// The tile max is taken on the integers: c > 0 and rounding is monotone, so
+// max_j fp32(S_j c) = fp32(max_j S_j * c).
+// x with its bits replaced by `fill` when lim - OFF < 0 (the key at offset OFF
+// of the lane's tile run is masked): v_subrev, v_ashrrev (sign word), v_bfi.
+// Written as one ALU asm block so the compiler keeps it a branch-free 3-op
+// sequence instead of hoisting 64 compares into scalar masks.
+template <int OFF>
+__device__ inline uint32_t mask_key(uint32_t x, int lim, uint32_t fill) {
+    uint32_t w;
+    asm("v_subrev_u32 %1, %4, %2\n\t"
+        "v_ashrrev_i32 %1, 31, %1\n\t"
+        "v_bfi_b32 %0, %1, %3, %0"
+        : "+v"(x), "=&v"(w)
+        : "v"(lim), "s"(fill), "i"(OFF));
+    return x;
+}
+
+template <int K4, int R>
+struct MaskTile {
+    static constexpr int OFF = 32 * K4 + 8 * (R >> 2) + (R & 3);
+    __device__ static void apply_int(v16i* S, int lim) {
+        S[K4][R] = (int)mask_key<OFF>((uint32_t)S[K4][R], lim, 0x80000000u);
+        if constexpr (R + 1 < 16) MaskTile<K4, R + 1>::apply_int(S, lim);
+        else if constexpr (K4 + 1 < 4) MaskTile<K4 + 1, 0>::apply_int(S, lim);
     }
+    __device__ static void apply_float(v16f* F, int lim) {
+        F[K4][R] = __uint_as_float(mask_key<OFF>(__float_as_uint(F[K4][R]), lim, 0xff800000u));
+        if constexpr (R + 1 < 16) MaskTile<K4, R + 1>::apply_float(F, lim);
+        else if constexpr (K4 + 1 < 4) MaskTile<K4 + 1, 0>::apply_float(F, lim);
+    }
+};
+
+template <typename PT>
+__device__ inline void softmax_tile(v16i* S, PT* P, float c, float& m, float& alpha, float& ls,
+                                    bool needmask, int lim) {
+    // masked keys (offset 32 k4 + 8 b + q > lim, b = r / 4, q = r % 4) become
+    // INT_MIN for the max and -inf for the exponent
+    if (needmask) MaskTile<0, 0>::apply_int(S, lim);
     int mk[4];
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
@@ -132,11 +211,20 @@ __device__ inline void softmax_tile(v16i* S, PT* P, float c, float& m, float& al
         mk[k4] = x;
     }
     const int mx = pair_max(max(max(mk[0], mk[1]), max(mk[2], mk[3])));
-    const float mt = (MASK && mx == INT_MIN) ? -INFINITY : (float)mx * c;
+    const float mt = mx == INT_MIN ? -INFINITY : (float)mx * c;
+    v16f F[4];
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) F[k4][r] = (float)S[k4][r];
+    if (needmask) MaskTile<0, 0>::apply_float(F, lim);
     const float mn = fmaxf(m, mt);
     alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
     m = mn;
     const float mu = mn - kLog2PScale;
+    // c == 0 only when the whole tile's S is 0; any positive factor then gives
+    // the same argument, and a positive one keeps -inf * factor = -inf
+    const float cf = c == 0.0f ? 1.0f : c;
     float part[4];
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
@@ -145,13 +233,10 @@ __device__ inline void softmax_tile(v16i* S, PT* P, float c, float& m, float& al
         for (int u = 0; u < 4; ++u) {
             float p[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int s = S[k4][4 * u + j];
-                p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s, c, -mu));
-                if (MASK && s == INT_MIN) p[j] = 0.0f;
-            }
+            for (int j = 0; j < 4; ++j)
+                p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[k4][4 * u + j], cf, -mu));
             sum += (p[0] + p[1]) + (p[2] + p[3]);
-            if constexpr (sizeof(PT) == 32 && __is_same(PT, v8i)) {
+            if constexpr (__is_same(PT, v8i)) {
                 int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_nondeterministic_value(0),
                                                         false);
                 w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
@@ -167,32 +252,45 @@ __device__ inline void softmax_tile(v16i* S, PT* P, float c, float& m, float& al
 }
 
 // Level 1: T = V^T tile (LDS) . P^T, a fresh fp32 accumulator per output
-// block; level 2: O = alpha O + T.
-template <int D, int VSTR>
+// block; level 2: O = alpha O + T.  Lane (channel n, hh) reads V row
+// 32 cb + n, key positions [64 hh + 32 hf, +32).
+template <int D>
 __device__ inline void pv_tile_fp8(const uint8_t* vb, const v8i* P, v16f* O, float alpha, int n,
                                    int hh) {
+    using L = Lds<D, false>;
+    constexpr int CB = D / 32;
+    const uint8_t* vrow = vb + n * L::VSTR + 64 * hh;
+    // software pipeline over output blocks: the level-2 update of block cb-1
+    // is issued after the MFMAs of block cb, when T[cb-1] is complete
+    v16f T[2];
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) {
-        const uint8_t* vrow = vb + (32 * cb + n) * VSTR + 64 * hh;
-        const v8i a0 = *(const v8i*)(vrow);
-        const v8i a1 = *(const v8i*)(vrow + 32);
-        v16f T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, P[0], v16f{}, 0, 0, 0, 0, 0, 0);
-        T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, P[1], T, 0, 0, 0, 0, 0, 0);
+    for (int cb = 0; cb <= CB; ++cb) {
+        if (cb < CB) {
+            const v8i a0 = *(const v8i*)(vrow + 32 * cb * L::VSTR);
+            const v8i a1 = *(const v8i*)(vrow + 32 * cb * L::VSTR + 32);
+            T[cb & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, P[0], v16f{}, 0, 0, 0, 0, 0, 0);
+            T[cb & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, P[1], T[cb & 1], 0, 0, 0, 0, 0, 0);
+        }
+        if (cb > 0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) O[cb][e] = __builtin_fmaf(alpha, O[cb][e], T[e]);
+            for (int e = 0; e < 16; ++e)
+                O[cb - 1][e] = __builtin_fmaf(alpha, O[cb - 1][e], T[(cb - 1) & 1][e]);
+        }
     }
 }
 
-template <int D, int VSTR>
+// FP16 path: lane (n, hh) reads key positions [64 hh + 8 u, +8).
+template <int D>
 __device__ inline void pv_tile_fp16(const uint8_t* vb, const v8h* P, v16f* O, float alpha, int n,
                                     int hh) {
+    using L = Lds<D, true>;
+    const uint8_t* vrow = vb + n * L::VSTR + 128 * hh;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) {
-        const uint8_t* vrow = vb + (32 * cb + n) * VSTR + 2 * 64 * hh;
         v16f T = v16f{};
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const v8h av = *(const v8h*)(vrow + 16 * u);
+            const v8h av = *(const v8h*)(vrow + 32 * cb * L::VSTR + 16 * u);
             T = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, P[u], T, 0, 0, 0);
         }
 #pragma unroll
@@ -202,12 +300,14 @@ __device__ inline void pv_tile_fp16(const uint8_t* vb, const v8h* P, v16f* O, fl
 
 template <int D, bool PV16, bool CAUSAL, bool DUMP>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
-    using SM = AttnSmem<D, PV16>;
-    constexpr int KK = D / 32;  // 32-channel steps of the Q K^T product
-    constexpr int CB = D / 32;  // 32-channel blocks of the output
-    __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
+    using L = Lds<D, PV16>;
+    using PT = typename std::conditional<PV16, v8h, v8i>::type;
+    constexpr int NP = PV16 ? 8 : 2;
+    constexpr int KK = D / 32;
+    constexpr int CB = D / 32;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::TOTAL];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = wave >> 2;
     const int n = lane & 31, hh = lane >> 5;
     const int wg = xcd_remap(blockIdx.x, a.total);
     const int bh = wg / a.nqt;
@@ -221,11 +321,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 
     int ntiles = a.nblk;
     if (CAUSAL) ntiles = (min(N, qt * kBr + kBr) - 1) / kBc + 1;
-    const int wave_tiles = CAUSAL ? (min(N, qbase + 32) - 1) / kBc + 1 : ntiles;
     const bool tail = (N % kBc) != 0;
 
     // Q8^T operand: lane (query n, half hh) holds channels [32 kk + 16 hh, +16).
+    // (a wave whose 32 queries are all padding runs the schedule on zero codes;
+    // its rows are never written)
     v4i qf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = v4i{};
     float sigma = 0.0f;
     if (active) {
         const int8_t* qrow = a.q8 + ((int64_t)bh * a.N_pad + qi) * D + 16 * hh;
@@ -234,71 +337,104 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         sigma = a.q_scale[bh * a.nblk + qbase / kBlk] * a.lambda;
     }
 
-    const v4i* kg = (const v4i*)(a.k8 + (int64_t)bh * a.N_pad * D);
-    const v4i* vg = (const v4i*)((const uint8_t*)a.vq + (int64_t)bh * a.nblk * D * kBc * SM::VES);
-    v4i kst[SM::KCH], vst[SM::VCH];
-    auto gload = [&](int t) {
-        const v4i* kt = kg + (int64_t)t * (kBc * D / 16);
-        const v4i* vt = vg + (int64_t)t * (D * kBc * SM::VES / 16);
+    const uint8_t* kg = (const uint8_t*)a.k8 + (int64_t)bh * a.N_pad * D;
+    const uint8_t* vg = (const uint8_t*)a.vq + (int64_t)bh * a.nblk * L::VHBM;
+    constexpr int KMAXP = (L::KPIECES + 7) / 8, VMAXP = (L::VPIECES + 7) / 8;
+    int koff[KMAXP], voff[VMAXP];
 #pragma unroll
-        for (int i = 0; i < SM::KCH; ++i) kst[i] = kt[tid + kAttnThreads * i];
+    for (int j = 0; j < KMAXP; ++j) koff[j] = slot_src<L::KROW, L::KSTR>(64 * (wave + 8 * j) + lane);
 #pragma unroll
-        for (int i = 0; i < SM::VCH; ++i) vst[i] = vt[tid + kAttnThreads * i];
+    for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<L::VROW, L::VSTR>(64 * (wave + 8 * j) + lane);
+    auto load_k = [&](int t) {
+        tile_to_lds<L::KPIECES, KMAXP>(kg + (int64_t)t * L::KHBM, smem + (t & 1) * L::KBYTES, wave,
+                                       koff);
     };
-    auto swrite = [&](int buf) {
-        uint8_t* kb = smem + buf * SM::STAGE;
-        uint8_t* vb = kb + SM::KBYTES;
-#pragma unroll
-        for (int i = 0; i < SM::KCH; ++i) {
-            const int ci = tid + kAttnThreads * i;
-            *(v4i*)(kb + (ci / SM::KCPR) * SM::KSTR + (ci % SM::KCPR) * 16) = kst[i];
-        }
-#pragma unroll
-        for (int i = 0; i < SM::VCH; ++i) {
-            const int ci = tid + kAttnThreads * i;
-            *(v4i*)(vb + (ci / SM::VCPR) * SM::VSTR + (ci % SM::VCPR) * 16) = vst[i];
-        }
+    auto load_v = [&](int t) {
+        tile_to_lds<L::VPIECES, VMAXP>(vg + (int64_t)t * L::VHBM,
+                                       smem + L::VBASE + (t & 1) * L::VBYTES, wave, voff);
     };
 
-    float m = -INFINITY, l = 0.0f;
+    float m = -INFINITY, l = 0.0f, alpha = 0.0f;
     v16f O[CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) O[cb][e] = 0.0f;
+    for (int cb = 0; cb < CB; ++cb) O[cb] = v16f{};
+    v16i S[4];
+    PT P[NP];
 
-    gload(0);
-    swrite(0);
+    // Slot schedule (slots end with a workgroup barrier; loads issued at the
+    // start of slot 2t -- K(t+1), V(t) -- are waited for at the end of slot
+    // 2t+1).  Group 0: slot 2t = MFMA phase of tile t (P V of t-1, Q K^T of t),
+    // slot 2t+1 = VALU phase of tile t.  Group 1 runs one slot later.
+    auto issue_loads = [&](int t) {
+        if (t + 1 < ntiles) load_k(t + 1);
+        if (t < ntiles) load_v(t);
+    };
+    auto end_slot = [&](bool odd) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (odd) wait_vmem();
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto mfma_phase = [&](int t, bool pv, bool qk) {
+        if (pv) {
+            const uint8_t* vb = smem + L::VBASE + ((t + 1) & 1) * L::VBYTES;  // V(t-1)
+            if constexpr (PV16) pv_tile_fp16<D>(vb, P, O, alpha, n, hh);
+            else pv_tile_fp8<D>(vb, P, O, alpha, n, hh);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (qk) qk_tile<D, PV16>(smem + (t & 1) * L::KBYTES, qf, S, n, hh);
+    };
+    const int kmax = CAUSAL ? min(N - 1, qi) : N - 1;  // last key this lane's query sees
+    auto valu_phase = [&](int t) {
+        const int key_t = t * kBc;
+        if (DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows)
+            dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
+        const float c = sigma * a.k_scale[bh * a.nblk + t];
+        const bool needmask = (tail && t == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase);
+        float ls;
+        softmax_tile(S, P, c, m, alpha, ls, needmask, kmax - key_t - 4 * hh);
+        l = alpha * l + ls;
+    };
+
+    // The P V of "tile -1" (first MFMA phase) runs with P = 0 and alpha = 1
+    // against a zero-filled V buffer, so every MFMA phase has the same code.
+    alpha = 1.0f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) P[i] = PT{};
+    {
+        uint4* vz = (uint4*)(smem + L::VBASE + L::VBYTES);
+        for (int i = tid; i < L::VBYTES / 16; i += kAttnThreads) vz[i] = make_uint4(0, 0, 0, 0);
+    }
+    load_k(0);
+    wait_vmem();
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) gload(t + 1);
-        if (active && t < wave_tiles) {
-            const uint8_t* kb = smem + (t & 1) * SM::STAGE;
-            const uint8_t* vb = kb + SM::KBYTES;
-            v16i S[4];
-            qk_tile<D, SM::KSTR>(kb, qf, S, n, hh);
-            const int key_t = t * kBc;
-            if (DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows)
-                dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
-            const float c = sigma * a.k_scale[bh * a.nblk + t];
-            const bool needmask = (tail && t == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase);
-            float alpha, ls;
-            if constexpr (!PV16) {
-                v8i P[2];
-                if (needmask) softmax_tile<true>(S, P, c, m, alpha, ls, key_t, N, CAUSAL, qi, hh);
-                else softmax_tile<false>(S, P, c, m, alpha, ls, key_t, N, CAUSAL, qi, hh);
-                pv_tile_fp8<D, SM::VSTR>(vb, P, O, alpha, n, hh);
-            } else {
-                v8h P[8];
-                if (needmask) softmax_tile<true>(S, P, c, m, alpha, ls, key_t, N, CAUSAL, qi, hh);
-                else softmax_tile<false>(S, P, c, m, alpha, ls, key_t, N, CAUSAL, qi, hh);
-                pv_tile_fp16<D, SM::VSTR>(vb, P, O, alpha, n, hh);
-            }
-            l = alpha * l + ls;
+    // Both groups run every phase of every tile of the workgroup (a causal wave
+    // past its last key tile sees it fully masked: p = 0, alpha = 1, so its
+    // state is unchanged), which keeps the loop bodies free of branches.
+    if (grp == 0) {
+        for (int t = 0; t < ntiles; ++t) {
+            issue_loads(t);
+            mfma_phase(t, true, true);
+            end_slot(false);
+            valu_phase(t);
+            end_slot(true);
         }
-        if (t + 1 < ntiles) swrite((t + 1) & 1);
-        __syncthreads();
+        mfma_phase(ntiles, true, false);
+        end_slot(false);
+        end_slot(true);
+    } else {
+        issue_loads(0);
+        end_slot(false);
+        for (int t = 0; t < ntiles; ++t) {
+            mfma_phase(t, true, true);
+            end_slot(true);
+            issue_loads(t + 1);
+            valu_phase(t);
+            end_slot(false);
+        }
+        mfma_phase(ntiles, true, false);
+        end_slot(true);
     }
 
     // ---- epilogue: out = O * v_scale / l (l summed over both lane halves)
