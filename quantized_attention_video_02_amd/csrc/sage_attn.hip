@@ -122,31 +122,6 @@ __device__ inline int tile_key(int key_t, int k4, int r, int hh) {
     return key_t + 32 * k4 + 8 * (r >> 2) + 4 * hh + (r & 3);
 }
 
-// S^T (128 keys x 32 queries) = K8 tile (LDS) . Q8^T: lane (n, hh) reads key
-// row 32 k4 + n, channels [32 kk + 16 hh, +16).
-template <int D, bool PV16>
-__device__ inline void qk_tile(const uint8_t* kb, const v4i* qf, v16i* S, int n, int hh) {
-    using L = Lds<D, PV16>;
-    constexpr int KK = D / 32;
-    const uint8_t* krow = kb + n * L::KSTR + 16 * hh;
-    v4i a[2][KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) a[0][kk] = *(const v4i*)(krow + 32 * kk);
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-        if (k4 + 1 < 4) {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                a[(k4 + 1) & 1][kk] = *(const v4i*)(krow + 32 * (k4 + 1) * L::KSTR + 32 * kk);
-        }
-        v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[k4 & 1][0], qf[0], v16i{}, 0, 0, 0);
-#pragma unroll
-        for (int kk = 1; kk < KK; ++kk)
-            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[k4 & 1][kk], qf[kk], acc, 0, 0, 0);
-        S[k4] = acc;
-    }
-}
-
 __device__ inline void dump_tile(const v16i* S, int32_t* srow, int key_t, int N, bool causal,
                                  int qi, int hh) {
 #pragma unroll
@@ -196,106 +171,119 @@ struct MaskTile {
     }
 };
 
-template <typename PT>
-__device__ inline void softmax_tile(v16i* S, PT* P, float c, float& m, float& alpha, float& ls,
+// First half of the online-softmax step of one tile for this lane's query:
+// masking, the tile max (on the integers: c > 0 and rounding is monotone, so
+// max_j fp32(S_j c) = fp32(max_j S_j * c)), the new running max m and alpha,
+// and F = float(S) with masked keys at -inf.  With needmask (wave-uniform),
+// the keys past `lim` (key - key_t - 4 hh > lim: beyond N, or after the query
+// when causal) are masked.
+__device__ inline void softmax_prep(v16i* S, v16f* F, float c, float& m, float& alpha, float& mu,
                                     bool needmask, int lim) {
-    // masked keys (offset 32 k4 + 8 b + q > lim, b = r / 4, q = r % 4) become
-    // INT_MIN for the max and -inf for the exponent
     if (needmask) MaskTile<0, 0>::apply_int(S, lim);
     int mk[4];
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
         int x = max(S[k4][0], S[k4][1]);
 #pragma unroll
-        for (int r = 2; r < 16; r += 2) x = max(x, max(S[k4][r], S[k4][r + 1]));
+        for (int r = 2; r < 16; r += 2) x = max(max(x, S[k4][r]), S[k4][r + 1]);
         mk[k4] = x;
     }
     const int mx = pair_max(max(max(mk[0], mk[1]), max(mk[2], mk[3])));
     const float mt = mx == INT_MIN ? -INFINITY : (float)mx * c;
-    v16f F[4];
+    const float mn = fmaxf(m, mt);
+    alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    mu = mn - kLog2PScale;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
         for (int r = 0; r < 16; ++r) F[k4][r] = (float)S[k4][r];
     if (needmask) MaskTile<0, 0>::apply_float(F, lim);
-    const float mn = fmaxf(m, mt);
-    alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
-    const float mu = mn - kLog2PScale;
-    // c == 0 only when the whole tile's S is 0; any positive factor then gives
-    // the same argument, and a positive one keeps -inf * factor = -inf
-    const float cf = c == 0.0f ? 1.0f : c;
-    float part[4];
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            float p[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[k4][4 * u + j], cf, -mu));
-            sum += (p[0] + p[1]) + (p[2] + p[3]);
-            if constexpr (__is_same(PT, v8i)) {
-                int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_nondeterministic_value(0),
-                                                        false);
-                w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-                P[k4 >> 1][(k4 & 1) * 4 + u] = w;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) P[2 * k4 + (u >> 1)][4 * (u & 1) + j] = (_Float16)p[j];
-            }
-        }
-        part[k4] = sum;
-    }
-    ls = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
-// Level 1: T = V^T tile (LDS) . P^T, a fresh fp32 accumulator per output
-// block; level 2: O = alpha O + T.  Lane (channel n, hh) reads V row
-// 32 cb + n, key positions [64 hh + 32 hf, +32).
+// Second half, one 32-key block k4: p = exp2(fma(F, c, -mu)) (= 448 * 2^(s - m')),
+// P (FP8 e4m3 or FP16) into the P V operand, and the partial row sum.
+// c == 0 only when the whole tile's S is 0; any positive factor then gives
+// the same argument, and a positive one keeps -inf * factor = -inf.
+template <typename PT>
+__device__ inline float softmax_block(const v16f& Fk, PT* P, int k4, float cf, float mu) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(Fk[4 * u + j], cf, -mu));
+        sum += (p[0] + p[1]) + (p[2] + p[3]);
+        if constexpr (__is_same(PT, v8i)) {
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_nondeterministic_value(0),
+                                                    false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+            P[k4 >> 1][(k4 & 1) * 4 + u] = w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) P[2 * k4 + (u >> 1)][4 * (u & 1) + j] = (_Float16)p[j];
+        }
+    }
+    return sum;
+}
+
+// P V into the running output: O = alpha O + V^T P^T.  The MFMA accumulates in
+// FP32 straight into O (the rescale by alpha is skipped when every lane's
+// alpha is 1).  Lane (channel n, hh) reads V row 32 cb + n, key positions
+// [64 hh + 32 hf, +32) (FP8) or [64 hh + 8 u, +8) (FP16).
 template <int D>
-__device__ inline void pv_tile_fp8(const uint8_t* vb, const v8i* P, v16f* O, float alpha, int n,
-                                   int hh) {
+__device__ inline void pv_tile(const uint8_t* vb, const v8i* P, v16f* O, float alpha, int n,
+                               int hh) {
     using L = Lds<D, false>;
-    constexpr int CB = D / 32;
     const uint8_t* vrow = vb + n * L::VSTR + 64 * hh;
-    // software pipeline over output blocks: the level-2 update of block cb-1
-    // is issued after the MFMAs of block cb, when T[cb-1] is complete
-    v16f T[2];
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int cb = 0; cb <= CB; ++cb) {
-        if (cb < CB) {
-            const v8i a0 = *(const v8i*)(vrow + 32 * cb * L::VSTR);
-            const v8i a1 = *(const v8i*)(vrow + 32 * cb * L::VSTR + 32);
-            T[cb & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, P[0], v16f{}, 0, 0, 0, 0, 0, 0);
-            T[cb & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, P[1], T[cb & 1], 0, 0, 0, 0, 0, 0);
-        }
-        if (cb > 0) {
+        for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                O[cb - 1][e] = __builtin_fmaf(alpha, O[cb - 1][e], T[(cb - 1) & 1][e]);
-        }
+            for (int e = 0; e < 16; ++e) O[cb][e] *= alpha;
     }
-}
-
-// FP16 path: lane (n, hh) reads key positions [64 hh + 8 u, +8).
-template <int D>
-__device__ inline void pv_tile_fp16(const uint8_t* vb, const v8h* P, v16f* O, float alpha, int n,
-                                    int hh) {
-    using L = Lds<D, true>;
-    const uint8_t* vrow = vb + n * L::VSTR + 128 * hh;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) {
-        v16f T = v16f{};
+        const v8i a0 = *(const v8i*)(vrow + 32 * cb * L::VSTR);
+        const v8i a1 = *(const v8i*)(vrow + 32 * cb * L::VSTR + 32);
+        O[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, P[0], O[cb], 0, 0, 0, 0, 0, 0);
+        O[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, P[1], O[cb], 0, 0, 0, 0, 0, 0);
+    }
+}
+
+template <int D>
+__device__ inline void pv_tile(const uint8_t* vb, const v8h* P, v16f* O, float alpha, int n,
+                               int hh) {
+    using L = Lds<D, true>;
+    const uint8_t* vrow = vb + n * L::VSTR + 128 * hh;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) O[cb][e] *= alpha;
+    }
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const v8h av = *(const v8h*)(vrow + 32 * cb * L::VSTR + 16 * u);
-            T = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, P[u], T, 0, 0, 0);
+            O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, P[u], O[cb], 0, 0, 0);
         }
+}
+
+// 32-key block k4 of S^T = K8 tile . Q8^T: lane (n, hh) reads key row 32 k4 + n,
+// channels [32 kk + 16 hh, +16).
+template <int D, int KSTR>
+__device__ inline v16i qk_block(const uint8_t* kb, const v4i* qf, int k4, int n, int hh) {
+    constexpr int KK = D / 32;
+    const uint8_t* krow = kb + (32 * k4 + n) * KSTR + 16 * hh;
+    v4i av[KK];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) O[cb][e] = __builtin_fmaf(alpha, O[cb][e], T[e]);
-    }
+    for (int kk = 0; kk < KK; ++kk) av[kk] = *(const v4i*)(krow + 32 * kk);
+    v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[0], qf[0], v16i{}, 0, 0, 0);
+#pragma unroll
+    for (int kk = 1; kk < KK; ++kk) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[kk], qf[kk], acc, 0, 0, 0);
+    return acc;
 }
 
 template <int D, bool PV16, bool CAUSAL, bool DUMP>
@@ -307,7 +295,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     constexpr int CB = D / 32;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[L::TOTAL];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = wave >> 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const int wg = xcd_remap(blockIdx.x, a.total);
     const int bh = wg / a.nqt;
@@ -354,88 +342,62 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                                        smem + L::VBASE + (t & 1) * L::VBYTES, wave, voff);
     };
 
-    float m = -INFINITY, l = 0.0f, alpha = 0.0f;
+    float m = -INFINITY, l = 0.0f;
+    float alpha = 1.0f;  // alpha of the tile whose P is held (tile -1: P = 0, alpha = 1)
     v16f O[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) O[cb] = v16f{};
     v16i S[4];
     PT P[NP];
-
-    // Slot schedule (slots end with a workgroup barrier; loads issued at the
-    // start of slot 2t -- K(t+1), V(t) -- are waited for at the end of slot
-    // 2t+1).  Group 0: slot 2t = MFMA phase of tile t (P V of t-1, Q K^T of t),
-    // slot 2t+1 = VALU phase of tile t.  Group 1 runs one slot later.
-    auto issue_loads = [&](int t) {
-        if (t + 1 < ntiles) load_k(t + 1);
-        if (t < ntiles) load_v(t);
-    };
-    auto end_slot = [&](bool odd) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (odd) wait_vmem();
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto mfma_phase = [&](int t, bool pv, bool qk) {
-        if (pv) {
-            const uint8_t* vb = smem + L::VBASE + ((t + 1) & 1) * L::VBYTES;  // V(t-1)
-            if constexpr (PV16) pv_tile_fp16<D>(vb, P, O, alpha, n, hh);
-            else pv_tile_fp8<D>(vb, P, O, alpha, n, hh);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (qk) qk_tile<D, PV16>(smem + (t & 1) * L::KBYTES, qf, S, n, hh);
-    };
-    const int kmax = CAUSAL ? min(N - 1, qi) : N - 1;  // last key this lane's query sees
-    auto valu_phase = [&](int t) {
-        const int key_t = t * kBc;
-        if (DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows)
-            dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
-        const float c = sigma * a.k_scale[bh * a.nblk + t];
-        const bool needmask = (tail && t == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase);
-        float ls;
-        softmax_tile(S, P, c, m, alpha, ls, needmask, kmax - key_t - 4 * hh);
-        l = alpha * l + ls;
-    };
-
-    // The P V of "tile -1" (first MFMA phase) runs with P = 0 and alpha = 1
-    // against a zero-filled V buffer, so every MFMA phase has the same code.
-    alpha = 1.0f;
 #pragma unroll
     for (int i = 0; i < NP; ++i) P[i] = PT{};
+    const int kmax = CAUSAL ? min(N - 1, qi) : N - 1;  // last key this lane's query sees
+
+    // Software pipeline, one barrier per tile.  Iteration t:
+    //   loads in flight: K(t+2), V(t);  LDS holds K(t+1), V(t-1)
+    //   A: P V of tile t-1 (MFMA)      || mask + max + float(S) of tile t (VALU)
+    //   B: per 32-key block, Q K^T of tile t+1 (MFMA) || exp / sum / FP8 of tile t (VALU)
+    // so each wave always has independent MFMA and VALU work for the SIMD to
+    // overlap with the other wave's.  V buffer 1 is zero-filled for tile -1.
     {
         uint4* vz = (uint4*)(smem + L::VBASE + L::VBYTES);
         for (int i = tid; i < L::VBYTES / 16; i += kAttnThreads) vz[i] = make_uint4(0, 0, 0, 0);
     }
     load_k(0);
+    if (ntiles > 1) load_k(1);
     wait_vmem();
     __syncthreads();
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) S[k4] = qk_block<D, L::KSTR>(smem, qf, k4, n, hh);
+    __syncthreads();
 
-    // Both groups run every phase of every tile of the workgroup (a causal wave
-    // past its last key tile sees it fully masked: p = 0, alpha = 1, so its
-    // state is unchanged), which keeps the loop bodies free of branches.
-    if (grp == 0) {
-        for (int t = 0; t < ntiles; ++t) {
-            issue_loads(t);
-            mfma_phase(t, true, true);
-            end_slot(false);
-            valu_phase(t);
-            end_slot(true);
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 2 < ntiles) load_k(t + 2);
+        load_v(t);
+        const int key_t = t * kBc;
+        if (DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows)
+            dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
+        // A
+        pv_tile<D>(smem + L::VBASE + ((t + 1) & 1) * L::VBYTES, P, O, alpha, n, hh);
+        const float c = sigma * a.k_scale[bh * a.nblk + t];
+        const bool needmask = (tail && t == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase);
+        v16f F[4];
+        float mu;
+        softmax_prep(S, F, c, m, alpha, mu, needmask, kmax - key_t - 4 * hh);
+        const float cf = c == 0.0f ? 1.0f : c;
+        // B (the Q K^T of "tile ntiles" reads a stale buffer; its result is unused)
+        const uint8_t* kb = smem + ((t + 1) & 1) * L::KBYTES;
+        float part[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            S[k4] = qk_block<D, L::KSTR>(kb, qf, k4, n, hh);
+            part[k4] = softmax_block(F[k4], P, k4, cf, mu);
         }
-        mfma_phase(ntiles, true, false);
-        end_slot(false);
-        end_slot(true);
-    } else {
-        issue_loads(0);
-        end_slot(false);
-        for (int t = 0; t < ntiles; ++t) {
-            mfma_phase(t, true, true);
-            end_slot(true);
-            issue_loads(t + 1);
-            valu_phase(t);
-            end_slot(false);
-        }
-        mfma_phase(ntiles, true, false);
-        end_slot(true);
+        l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
+        wait_vmem();
+        __syncthreads();
     }
+    pv_tile<D>(smem + L::VBASE + ((ntiles + 1) & 1) * L::VBYTES, P, O, alpha, n, hh);
 
     // ---- epilogue: out = O * v_scale / l (l summed over both lane halves)
     const float lt = pair_sum(l);
