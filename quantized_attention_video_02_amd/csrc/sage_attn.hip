@@ -83,16 +83,29 @@ __device__ inline int slot_src(int P) {
     return row * ROW + (c < ROW / 16 ? 16 * c : 0);
 }
 
-// Direct global -> LDS copy of this wave's pieces of a tile: piece J (1 KB) is
-// written by one global_load_lds_dwordx4, lane i filling bytes [16 i, 16 i + 16).
+// One 1 KB piece of a tile, global -> LDS: global_load_lds_dwordx4 with the LDS
+// destination in M0, lane i filling bytes [16 i, 16 i + 16) of the piece.
+// Issued from asm: the compiler cannot tell these in-flight writes from the
+// other LDS buffer's reads and would otherwise wait for every copy before the
+// next LDS read.  Completion is awaited explicitly (wait_vmem before the
+// barrier that publishes the buffer).  The asm has no register outputs.
+__device__ inline void dma_piece(const uint8_t* gbase, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(gbase), "s"(lds)
+        : "memory", "m0");
+}
+
+// This wave's pieces of a tile: piece J = wave + 8 j.  g and l are uniform.
 template <int NPIECES, int MAXP>
-__device__ inline void tile_to_lds(const uint8_t* g, uint8_t* l, int wave, const int* off) {
+__device__ inline void tile_to_lds(const uint8_t* g, uint32_t l, int wave, const int* off) {
 #pragma unroll
     for (int j = 0; j < MAXP; ++j) {
         const int J = wave + 8 * j;
-        if (J < NPIECES)
-            __builtin_amdgcn_global_load_lds((const void*)(g + off[j]), (lds_void*)(l + 1024 * J),
-                                             16, 0, 0);
+        if (J < NPIECES) dma_piece(g, (uint32_t)off[j], l + 1024u * J);
     }
 }
 
@@ -333,13 +346,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     for (int j = 0; j < KMAXP; ++j) koff[j] = slot_src<L::KROW, L::KSTR>(64 * (wave + 8 * j) + lane);
 #pragma unroll
     for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<L::VROW, L::VSTR>(64 * (wave + 8 * j) + lane);
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
     auto load_k = [&](int t) {
-        tile_to_lds<L::KPIECES, KMAXP>(kg + (int64_t)t * L::KHBM, smem + (t & 1) * L::KBYTES, wave,
+        tile_to_lds<L::KPIECES, KMAXP>(kg + (int64_t)t * L::KHBM, lbase + (t & 1) * L::KBYTES, wv,
                                        koff);
     };
     auto load_v = [&](int t) {
         tile_to_lds<L::VPIECES, VMAXP>(vg + (int64_t)t * L::VHBM,
-                                       smem + L::VBASE + (t & 1) * L::VBYTES, wave, voff);
+                                       lbase + L::VBASE + (t & 1) * L::VBYTES, wv, voff);
     };
 
     float m = -INFINITY, l = 0.0f;
@@ -371,7 +386,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     for (int k4 = 0; k4 < 4; ++k4) S[k4] = qk_block<D, L::KSTR>(smem, qf, k4, n, hh);
     __syncthreads();
 
+    const float* ksrow = a.k_scale + bh * a.nblk;
+    float ks = ksrow[0];
     for (int t = 0; t < ntiles; ++t) {
+        // the dequantization constant of tile t, taken before this iteration's
+        // copies are issued (its load was issued one iteration earlier, so the
+        // wait the compiler places before this use does not cover the copies)
+        float c = sigma * ks;
+        asm volatile("" : "+v"(c));
+        ks = ksrow[min(t + 1, a.nblk - 1)];
         if (t + 2 < ntiles) load_k(t + 2);
         load_v(t);
         const int key_t = t * kBc;
@@ -379,7 +402,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
             dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
         // A
         pv_tile<D>(smem + L::VBASE + ((t + 1) & 1) * L::VBYTES, P, O, alpha, n, hh);
-        const float c = sigma * a.k_scale[bh * a.nblk + t];
         const bool needmask = (tail && t == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase);
         v16f F[4];
         float mu;
