@@ -220,16 +220,17 @@ __device__ inline void softmax_prep(v16i* S, v16f* F, float c, float& m, float& 
 // the same argument, and a positive one keeps -inf * factor = -inf.
 template <typename PT>
 __device__ inline float softmax_block(const v16f& Fk, PT* P, int k4, float cf, float mu) {
-    float sum = 0.0f;
+    float part[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         float p[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(Fk[4 * u + j], cf, -mu));
-        sum += (p[0] + p[1]) + (p[2] + p[3]);
+        part[u] = (p[0] + p[1]) + (p[2] + p[3]);
         if constexpr (__is_same(PT, v8i)) {
-            int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_nondeterministic_value(0),
-                                                    false);
+            // the first half-word write keeps the other half of its old operand;
+            // p[0]'s own register (dead after this) serves, so no zeroing move
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
             w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
             P[k4 >> 1][(k4 & 1) * 4 + u] = w;
         } else {
@@ -237,7 +238,7 @@ __device__ inline float softmax_block(const v16f& Fk, PT* P, int k4, float cf, f
             for (int j = 0; j < 4; ++j) P[2 * k4 + (u >> 1)][4 * (u & 1) + j] = (_Float16)p[j];
         }
     }
-    return sum;
+    return (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // P V into the running output: O = alpha O + V^T P^T.  The MFMA accumulates in
