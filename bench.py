@@ -17,10 +17,13 @@ Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +34,31 @@ PEAK_TOPS = {"fp8": 5000.0,                       # dense INT8 (QK) = dense FP8 
              "fp16": 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)}  # INT8 QK half + FP16 PV half
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+ATTN_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
+                for f in ("sage_attn.hip", "sage_common.h")]
+
+
+def attn_source_hash():
+    """sha256 of the attention kernel's sources: HBM byte counts measured on
+    another version of the kernel are not reported."""
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def sample_sclk(out):
+    """Current shader clock (MHz) from rocm-smi, sampled while the timed steps run."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        for card in json.loads(r.stdout).values():
+            for k, v in card.items():
+                if "sclk" in k.lower() and "speed" in k.lower():
+                    out.append(float(str(v).strip("()Mhz ")))
+    except Exception:  # the clock is context only; its absence is reported as null
+        pass
 
 
 def attn_ops(B, H, N, d):
@@ -59,15 +87,19 @@ def time_gpu(sage, wl, pv, steps, warmup):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    clocks = []
+    sampler = threading.Thread(target=sample_sclk, args=(clocks,), daemon=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    sampler.start()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sampler.join(timeout=30)
     quant_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    return wall, quant_ms, attn_ms
+    return wall, quant_ms, attn_ms, (max(clocks) if clocks else None)
 
 
 def cpu_baseline(wl, pv, target_s=12.0):
@@ -104,6 +136,47 @@ def cpu_baseline(wl, pv, target_s=12.0):
                        "single-threaded C oracle")}
 
 
+def record_traffic(workload, pv, fetch_dir, write_dir):
+    """Write profiles/traffic.json from two rocprofv3 --pmc runs of
+    `bench.py --steps 1 --warmup 0 --no-cpu-baseline --calibrate-copy` (one with
+    FETCH_SIZE, one with WRITE_SIZE; KiB per dispatch).  Each counter is scaled
+    so that the plain 1 GiB device copy in the same run reads (writes) 1 GiB."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+        return rows
+
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = per_kernel(d, counter)
+        attn = [float(r["Counter_Value"]) * 1024 for r in rows if "attn_fwd_kernel" in r["Kernel_Name"]]
+        # --calibrate-copy's device-to-device copy runs as the HIP runtime's blit kernel
+        copy = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not attn or not copy:
+            raise SystemExit(f"no attn_fwd_kernel or copy dispatch with {counter} under {d}")
+        scale = float(1 << 30) / max(copy)
+        res[counter] = (sum(attn) / len(attn) * scale, scale)
+    entry = {"kernel": "attn_fwd_kernel", "source_hash": attn_source_hash(),
+             "fetch_bytes": res["FETCH_SIZE"][0], "write_bytes": res["WRITE_SIZE"][0],
+             "bytes_per_launch": res["FETCH_SIZE"][0] + res["WRITE_SIZE"][0],
+             "fetch_scale": res["FETCH_SIZE"][1], "write_scale": res["WRITE_SIZE"][1],
+             "note": "rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by a plain "
+                     "1 GiB device copy measured in the same runs"}
+    data = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    data[f"{workload}/{pv}"] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1)
+    print(json.dumps(entry))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,7 +189,13 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (the known-size "
                          "reference for HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json for --workload/--pv from two rocprofv3 "
+                         "--pmc output folders (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, args.pv, *args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (there is no multi-GPU path; "
               "DESIGN.md describes how the work would shard). Run with --gpus 1.",
@@ -141,11 +220,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    wall, quant_ms, attn_ms = time_gpu(sage, wl, args.pv, args.steps, args.warmup)
+    wall, quant_ms, attn_ms, sclk = time_gpu(sage, wl, args.pv, args.steps, args.warmup)
     ops = attn_ops(wl.B, wl.H, wl.N, wl.d)
     ms_per_step = wall * 1e3 / args.steps
     attn_mean = sum(attn_ms) / len(attn_ms)
-    attn_med = sorted(attn_ms)[len(attn_ms) // 2]
+    srt = sorted(attn_ms)
+    attn_med = srt[len(srt) // 2]
+    attn_iqr = srt[(3 * len(srt)) // 4] - srt[len(srt) // 4]
     quant_mean = sum(quant_ms) / len(quant_ms)
     achieved = ops / (attn_mean * 1e-3) / 1e12
     peak = PEAK_TOPS[args.pv]
@@ -154,7 +235,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f).get(f"{wl.name}/{args.pv}")
-        traffic = t.get("bytes_per_launch") if t else None
+        if t and t.get("source_hash") == attn_source_hash():
+            traffic = t.get("bytes_per_launch")
     res = {
         "metric": METRIC,
         "value": ops * args.steps / wall / 1e12,
@@ -173,11 +255,19 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": "attn_fwd_kernel", "ops_per_launch": ops,
-                     "mean_launch_ms": attn_mean, "median_launch_ms": attn_med},
+                     "mean_launch_ms": attn_mean, "median_launch_ms": attn_med,
+                     "iqr_launch_ms": attn_iqr,
+                     "median_tops": ops / (attn_med * 1e-3) / 1e12,
+                     "sclk_mhz": sclk},
         "quant": {"ms": quant_mean, "bytes_two_pass": 13 * bhnd,
                   "gbps_two_pass": 13 * bhnd / (quant_mean * 1e-3) / 1e9,
                   "frac_hbm": 13 * bhnd / (quant_mean * 1e-3) / 1e9 / HBM_GBPS},
     }
+    if wl.causal:
+        # the formula above counts every (query, key) pair; the causal mask keeps N(N+1)/2
+        useful = 4.0 * wl.B * wl.H * wl.d * wl.N * (wl.N + 1) / 2
+        res["roofline"]["useful_causal_ops_per_launch"] = useful
+        res["roofline"]["useful_causal_tops"] = useful / (attn_mean * 1e-3) / 1e12
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.pv, args.cpu_seconds)

@@ -4,8 +4,12 @@
 // SageAttention3 summary, bullet 8比特训练; hunxia.com glossary entry on
 // FlashAttention): INT8 Q K^T into int32, dequantize by q_scale * k_scale,
 // exp2 online softmax in FP32 over key tiles of 128, P to FP8 e4m3 with the
-// static scale 448 (FP16 path: binary16), P V on FP8 (FP16) matrix cores into
-// a fresh FP32 sum per key tile, added into the FP32 running output.
+// static scale 448 (FP16 path: binary16), P V on FP8 (FP16) matrix cores with
+// FP32 accumulation into the running output.  The pages accumulate each tile's
+// P V in a fresh FP32 sum and add it to the output (two levels) because the
+// FP8 tensor cores they target keep fewer accumulator bits; the gfx950 MFMA
+// accumulates in full FP32, so the product is accumulated straight into the
+// rescaled output (O = alpha O + P V, one rounding per MFMA step).
 //
 // Work decomposition: one workgroup = 8 wave64s = 256 queries of one (b, h);
 // each wave owns 32 queries for the whole key sweep.  Per key tile:
@@ -13,22 +17,21 @@
 //     16 x v_mfma_i32_32x32x32_i8 (d = 128);
 //   in the 32x32 accumulator layout each lane holds one query (lane & 31) and
 //   64 of the tile's keys, so the row max / row sum stay in the lane plus one
-//   exchange with lane ^ 32, and the P values a lane produces are exactly the
-//   B operand of the P V product;
+//   exchange with lane ^ 32 (v_permlane32_swap), and the P values a lane
+//   produces are exactly the B operand of the P V product;
 //   O^T (d x 32 queries) += V^T tile (LDS) . P^T (registers),
 //     8 x v_mfma_f32_32x32x64_f8f6f4 (d = 128) -- O^T keeps queries on lanes,
 //     so the per-query rescale alpha is a per-lane scalar.
-// Schedule: the 8 waves form two groups, waves 0-3 and 4-7, one wave of each
-// on every SIMD.  Time is cut into slots separated by workgroup barriers; in
-// each slot one group runs its MFMA phase (P V of tile t-1, then Q K^T of tile
-// t) while the other runs its VALU phase (the softmax of its current tile), and
-// the groups swap every slot.  A wave's VALU instructions do not overlap its own
-// MFMAs, but the SIMD overlaps one wave's MFMAs with the other wave's VALU
-// work, so keeping the two waves of a SIMD in opposite phases keeps both the
-// matrix core and the VALU busy.
-// K and V tiles go straight from global memory into LDS (global_load_lds_dwordx4,
-// no register staging), double-buffered: the loads of K(t+1) and V(t) are
-// issued at the start of the slot pair that reads K(t) and V(t-1).  LDS rows
+// Schedule: a per-wave software pipeline with one workgroup barrier per tile.
+// Iteration t runs A = P V of tile t-1 (MFMA) and the max / alpha / float(S)
+// of tile t (VALU), then B = the Q K^T of tile t+1 (MFMA) interleaved with the
+// exp2 / row sum / FP8 packing of tile t (VALU), so every wave always holds
+// independent MFMA and VALU work.  The kernel is bound by VALU issue (about
+// 350 VALU instructions per wave and tile against 24 MFMAs), not by the
+// matrix cores.
+// K and V tiles go straight from global memory into LDS (global_load_lds_dwordx4
+// issued from asm, no register staging), double-buffered: K(t+2) and V(t) are
+// loaded during iteration t and awaited before its closing barrier.  LDS rows
 // carry a 16-byte pad so that the operand reads of 16 consecutive lanes (16
 // rows, same column) fall in 16 distinct 16-byte slots of the 64-bank LDS.
 // The grid is remapped so that consecutive workgroups of one head run on the
