@@ -21,9 +21,7 @@ import hashlib
 import json
 import math
 import os
-import subprocess
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -48,23 +46,6 @@ def attn_source_hash():
     return h.hexdigest()[:16]
 
 
-def sample_sclk(out):
-    """Current shader clock (MHz) from rocm-smi, sampled while the timed steps run."""
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                           timeout=20)
-        for card in json.loads(r.stdout).values():
-            for k, v in card.items():
-                if "sclk" in k.lower() and "speed" in k.lower():
-                    out.append(float(str(v).strip("()Mhz ")))
-    except Exception:  # the clock is context only; its absence is reported as null
-        pass
-
-
-def attn_ops(B, H, N, d):
-    return 4.0 * B * H * N * N * d
-
-
 def time_gpu(sage, wl, pv, steps, warmup):
     import torch
 
@@ -87,19 +68,15 @@ def time_gpu(sage, wl, pv, steps, warmup):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    clocks = []
-    sampler = threading.Thread(target=sample_sclk, args=(clocks,), daemon=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    sampler.start()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sampler.join(timeout=30)
     quant_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    return wall, quant_ms, attn_ms, (max(clocks) if clocks else None)
+    return wall, quant_ms, attn_ms
 
 
 def cpu_baseline(wl, pv, target_s=12.0):
@@ -220,7 +197,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    wall, quant_ms, attn_ms, sclk = time_gpu(sage, wl, args.pv, args.steps, args.warmup)
+    wall, quant_ms, attn_ms = time_gpu(sage, wl, args.pv, args.steps, args.warmup)
     ops = attn_ops(wl.B, wl.H, wl.N, wl.d)
     ms_per_step = wall * 1e3 / args.steps
     attn_mean = sum(attn_ms) / len(attn_ms)
@@ -257,8 +234,7 @@ def main():
                      "kernel": "attn_fwd_kernel", "ops_per_launch": ops,
                      "mean_launch_ms": attn_mean, "median_launch_ms": attn_med,
                      "iqr_launch_ms": attn_iqr,
-                     "median_tops": ops / (attn_med * 1e-3) / 1e12,
-                     "sclk_mhz": sclk},
+                     "median_tops": ops / (attn_med * 1e-3) / 1e12},
         "quant": {"ms": quant_mean, "bytes_two_pass": 13 * bhnd,
                   "gbps_two_pass": 13 * bhnd / (quant_mean * 1e-3) / 1e9,
                   "frac_hbm": 13 * bhnd / (quant_mean * 1e-3) / 1e9 / HBM_GBPS},
