@@ -1,0 +1,86 @@
+"""bench.py: the contract line (GPU) and the host logic behind its `traffic`
+field (CPU): counter files from two rocprofv3 --pmc runs are scaled by the
+known-size device copy and tagged with the attention kernel's source hash."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+FIELDS = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _write_counters(d, counter, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for name, kib in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": kib})
+
+
+def test_record_traffic_scales_by_the_copy_and_tags_the_source(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    gib_kib = (1 << 30) / 1024
+    # the counters see half of the copy's reads and all of its writes
+    _write_counters(tmp_path / "f", "FETCH_SIZE",
+                    [("__amd_rocclr_copyBuffer", gib_kib / 2),
+                     ("void at::native::vectorized_elementwise_kernel<4, copy>", 123.0),
+                     ("void sage::attn_fwd_kernel<128, false, false, false>(sage::AttnArgs)", 1000.0),
+                     ("void sage::attn_fwd_kernel<128, false, false, false>(sage::AttnArgs)", 3000.0)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE",
+                    [("__amd_rocclr_copyBuffer", gib_kib),
+                     ("void sage::attn_fwd_kernel<128, false, false, false>(sage::AttnArgs)", 500.0)])
+    bench.record_traffic("video_14b_720p", "fp8", str(tmp_path / "f"), str(tmp_path / "w"))
+    e = json.load(open(tmp_path / "traffic.json"))["video_14b_720p/fp8"]
+    assert e["fetch_scale"] == pytest.approx(2.0) and e["write_scale"] == pytest.approx(1.0)
+    assert e["fetch_bytes"] == pytest.approx(2000.0 * 1024 * 2.0)   # mean of the two dispatches
+    assert e["write_bytes"] == pytest.approx(500.0 * 1024)
+    assert e["bytes_per_launch"] == pytest.approx(e["fetch_bytes"] + e["write_bytes"])
+    assert e["source_hash"] == bench.attn_source_hash()
+
+
+def test_record_traffic_refuses_runs_without_the_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    _write_counters(tmp_path / "f", "FETCH_SIZE", [("void sage::attn_fwd_kernel<128>", 1.0)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE", [("void sage::attn_fwd_kernel<128>", 1.0)])
+    with pytest.raises(SystemExit):
+        bench.record_traffic("tiny", "fp8", str(tmp_path / "f"), str(tmp_path / "w"))
+
+
+def test_source_hash_covers_the_kernel_sources():
+    h = bench.attn_source_hash()
+    assert len(h) == 16 and all(os.path.exists(f) for f in bench.ATTN_SOURCES)
+    assert h == bench.attn_source_hash()
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+@pytest.mark.gpu
+def test_bench_line_keeps_the_contract():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny",
+                        "--steps", "3", "--warmup", "1", "--cpu-seconds", "0.5"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+              "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+              "roofline", "cpu_baseline"):
+        assert k in line, k
+    assert line["n_gpus"] == 1 and line["steps"] == 3 and line["value"] > 0
+    rf = line["roofline"]
+    assert rf["bound"] == "mfma" and rf["peak"] == 5000.0 and rf["unit"] == "TFLOP/s"
+    assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
+    assert line["cpu_baseline"]["kind"] == "oracle" and line["cpu_baseline"]["cores"] == 1
+    assert line["config"]["workload"] == "tiny"
