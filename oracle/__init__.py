@@ -61,7 +61,8 @@ def lib():
             "or_quant_k": [P, i32, i32, i32, i32, P, P, P, P],
             "or_quant_v": [P, i32, i32, i32, P, P],
             "or_dump_s": [P, P, i32, i32, i32, i32, i32, P],
-            "or_attn_rows": [P, P, P, P, P, P, i32, i32, P, i32, i32, f32, i32, i32, i32, P, P, P, P],
+            "or_attn_rows": [P, P, P, P, P, P, i32, i32, P, i32, i32, f32, i32, i32, i32, i32, P, P, P,
+                             P],
             "or_ref64_rows": [P, P, P, i32, i32, P, i32, i32, f64, P, P],
         }
         for name, args in sigs.items():
@@ -138,14 +139,19 @@ def quant_block(x: np.ndarray):
     return out, float(s[0])
 
 
-def quant_qk(q: np.ndarray, k: np.ndarray, blk: int = BLK, smooth: bool = True):
+def quant_qk(q: np.ndarray, k: np.ndarray, blk: int = BLK, smooth: bool = True,
+             q_gran: str = "block"):
     """q, k: uint16 bf16 codes [B, H, N, d].  Returns a dict with q8/k8 int8
-    [B,H,N,d], q_scale/k_scale fp32 [B,H,nblk], k_mean fp32 [B,H,d]."""
+    [B,H,N,d], q_scale fp32 [B,H,ceil(N/qblk)], k_scale fp32 [B,H,nblk],
+    k_mean fp32 [B,H,d] and qblk.  q_gran "block": Q blocks of blk rows like
+    K; "token": one scale per query row (qblk = 1)."""
     B, H, N, d = q.shape
+    qblk = {"block": blk, "token": 1}[q_gran]
     nb = (N + blk - 1) // blk
+    nbq = (N + qblk - 1) // qblk
     q8 = np.empty((B, H, N, d), np.int8)
     k8 = np.empty((B, H, N, d), np.int8)
-    qs = np.empty((B, H, nb), np.float32)
+    qs = np.empty((B, H, nbq), np.float32)
     ks = np.empty((B, H, nb), np.float32)
     km = np.empty((B, H, d), np.float32)
     tmp = np.empty(blk * d, np.float32)
@@ -156,13 +162,13 @@ def quant_qk(q: np.ndarray, k: np.ndarray, blk: int = BLK, smooth: bool = True):
             kh = np.ascontiguousarray(k[b, h], dtype=np.uint16)
             q8h = np.empty((N, d), np.int8)
             k8h = np.empty((N, d), np.int8)
-            qsh = np.empty(nb, np.float32)
+            qsh = np.empty(nbq, np.float32)
             ksh = np.empty(nb, np.float32)
             kmh = np.empty(d, np.float32)
-            L.or_quant_q(_p(qh), N, d, blk, _p(q8h), _p(qsh), _p(tmp))
+            L.or_quant_q(_p(qh), N, d, qblk, _p(q8h), _p(qsh), _p(tmp))
             L.or_quant_k(_p(kh), N, d, blk, int(smooth), _p(k8h), _p(ksh), _p(kmh), _p(tmp))
             q8[b, h], k8[b, h], qs[b, h], ks[b, h], km[b, h] = q8h, k8h, qsh, ksh, kmh
-    return dict(q8=q8, q_scale=qs, k8=k8, k_scale=ks, k_mean=km)
+    return dict(q8=q8, q_scale=qs, k8=k8, k_scale=ks, k_mean=km, qblk=qblk)
 
 
 def quant_v(v: np.ndarray, pv: str = "fp8"):
@@ -209,8 +215,9 @@ def attn_rows_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scal
     m = np.empty(len(rows), np.float32)
     l = np.empty(len(rows), np.float32)
     scratch = np.empty(4 * bc + 3 * d, np.float32)
+    qblk = int(qz.get("qblk", blk))
     lib().or_attn_rows(_p(q8h), _p(qsh), _p(k8h), _p(ksh), _p(vqh), _p(vsh), N, d, _p(rows),
-                       len(rows), int(causal), float(sm_scale), int(pv == "fp16"), blk, bc,
+                       len(rows), int(causal), float(sm_scale), int(pv == "fp16"), qblk, blk, bc,
                        _p(out), _p(m), _p(l), _p(scratch))
     if return_ml:
         return out, m, l
@@ -231,11 +238,12 @@ def ref64_rows_head(q, k, v, b: int, h: int, rows, causal: bool, sm_scale: float
     return out
 
 
-def attention(q, k, v, causal: bool, sm_scale: float, pv: str = "fp8", rows=None):
+def attention(q, k, v, causal: bool, sm_scale: float, pv: str = "fp8", rows=None,
+              q_gran: str = "block"):
     """Whole oracle pipeline: quantize, then attention for ``rows`` (default all)
     of every head.  Returns (out fp32 [B,H,len(rows),d], quantized dict, vq, vs)."""
     B, H, N, d = q.shape
-    qz = quant_qk(q, k)
+    qz = quant_qk(q, k, q_gran=q_gran)
     vq, vs = quant_v(v, pv)
     rows = np.arange(N, dtype=np.int32) if rows is None else np.asarray(rows, np.int32)
     out = np.empty((B, H, len(rows), d), np.float32)

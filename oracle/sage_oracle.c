@@ -300,18 +300,21 @@ OR_API float or_lambda(float sm_scale) { return (float)((double)sm_scale * 1.442
  * the 448 is folded into the exp2 argument through mu; l sums the
  * unquantized p; key tiles of bc = 128 keys in ascending order, no split;
  * the two accumulation levels are one key tile and the whole row.
- * ks is indexed by key block of blk keys, and bc == blk.
+ * qs is indexed by query block of qblk rows: qblk = 128 is the per-block
+ * quantization, qblk = 1 the per-token ("thread-level") one, reportify
+ * SageAttention3 summary, bullet 8比特训练 and wxsanhe §三.1; ks by key block of
+ * kblk keys, and bc == kblk.
  * Pinned: FP64 attention (cosine), brute force of the single-tile case,
  * P rows summing to 1 through the final (m, l), a tile-by-tile non-online
  * recomputation, constant keys and peaked rows in closed form. */
 static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
                         const void* vq, const float* vs, int N, int d, int i, int causal,
-                        float lambda, int pv_fp16, int blk, int bc, float* out, float* m_out,
-                        float* l_out, int32_t* S, float* T, float* O, float* P) {
+                        float lambda, int pv_fp16, int qblk, int kblk, int bc, float* out,
+                        float* m_out, float* l_out, int32_t* S, float* T, float* O, float* P) {
     const uint8_t* v8 = (const uint8_t*)vq;
     const uint16_t* v16 = (const uint16_t*)vq;
     const float L = or_log2_pscale();
-    const float sigma = qs[i / blk] * lambda;
+    const float sigma = qs[i / qblk] * lambda;
     const int8_t* qi = q8 + (int64_t)i * d;
     float m = -INFINITY, l = 0.0f;
     for (int c = 0; c < d; ++c) O[c] = 0.0f;
@@ -322,7 +325,7 @@ static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, con
         int j1 = j0 + bc < N ? j0 + bc : N;
         if (causal && j1 > i + 1) j1 = i + 1;
         int n = j1 - j0;
-        float c = sigma * ks[j0 / blk];
+        float c = sigma * ks[j0 / kblk];
         float mt = -INFINITY;
         for (int j = 0; j < n; ++j) {
             S[j] = or_dot_i8(qi, k8 + (int64_t)(j0 + j) * d, d);
@@ -359,15 +362,16 @@ static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, con
  * scratch must hold 4*bc + 3*d floats. */
 OR_API void or_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
                          const void* vq, const float* vs, int N, int d, const int32_t* rows,
-                         int nrows, int causal, float sm_scale, int pv_fp16, int blk, int bc,
-                         float* out, float* m_out, float* l_out, float* scratch) {
+                         int nrows, int causal, float sm_scale, int pv_fp16, int qblk,
+                         int kblk, int bc, float* out, float* m_out, float* l_out,
+                         float* scratch) {
     float lambda = or_lambda(sm_scale);
     int32_t* S = (int32_t*)scratch;
     float* P = scratch + bc;
     float* T = scratch + 2 * bc;
     float* O = T + d;
     for (int r = 0; r < nrows; ++r)
-        or_attn_row(q8, qs, k8, ks, vq, vs, N, d, rows[r], causal, lambda, pv_fp16, blk, bc,
+        or_attn_row(q8, qs, k8, ks, vq, vs, N, d, rows[r], causal, lambda, pv_fp16, qblk, kblk, bc,
                     out + (int64_t)r * d, m_out ? m_out + r : 0, l_out ? l_out + r : 0, S, T, O,
                     P);
 }

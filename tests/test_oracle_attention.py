@@ -53,16 +53,19 @@ def test_tiny_workload_vs_fp64(orc, pv):
 @pytest.mark.parametrize("pv", ["fp8", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 17, 64])
-def test_single_tile_brute_force(orc, pv, causal, N):
+@pytest.mark.parametrize("q_gran", ["block", "token"])
+def test_single_tile_brute_force(orc, pv, causal, N, q_gran):
     """N <= 64: one key tile, so the online softmax is the one-shot softmax.
     Compare with FP64 one-shot attention over the dequantized operands; the
     only gap left is P's rounding (fp16: 2^-11 relative, fp8: 2^-4)."""
     wl = si.make("tiny", N=N, H=1, seed=77 + N)
     q, k, v = (si.bf16_codes(t) for t in (wl.q, wl.k, wl.v))
-    z, vq, vs = _quantize(orc, q, k, v, pv)
+    z = orc.quant_qk(q, k, q_gran=q_gran)
+    vq, vs = orc.quant_v(v, pv)
     rows = np.arange(N)
     out = orc.attn_rows_head(z, vq, vs, 0, 0, rows, causal, wl.sm_scale, pv)
-    dq = z["q8"][0, 0].astype(np.float64) * z["q_scale"][0, 0, 0]
+    qsc = z["q_scale"][0, 0] if q_gran == "token" else np.full(N, z["q_scale"][0, 0, 0])
+    dq = z["q8"][0, 0].astype(np.float64) * qsc[:, None].astype(np.float64)
     dk = z["k8"][0, 0].astype(np.float64) * z["k_scale"][0, 0, 0]
     dv = _deq_v(orc, vq, vs, pv)[0, 0]
     s = dq @ dk.T * wl.sm_scale
@@ -82,7 +85,7 @@ def _non_online(orc, z, vq, vs, b, h, i, causal, sm_scale, pv):
     k8 = z["k8"][b, h].astype(np.int64)
     N = k8.shape[0]
     lam = np.float32(orc.lam(sm_scale))
-    sigma = np.float32(z["q_scale"][b, h, i // 128] * lam)
+    sigma = np.float32(z["q_scale"][b, h, i // z["qblk"]] * lam)
     dec = orc.f16_to_f32 if pv == "fp16" else orc.e4m3_to_f32
     enc = orc.f32_to_f16 if pv == "fp16" else orc.f32_to_e4m3
     vdec = dec(vq[b, h]).reshape(vq.shape[2:]).astype(np.float64)
@@ -109,10 +112,12 @@ def _non_online(orc, z, vq, vs, b, h, i, causal, sm_scale, pv):
 
 @pytest.mark.parametrize("pv", ["fp8", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_online_bookkeeping_matches_non_online(orc, pv, causal):
+@pytest.mark.parametrize("q_gran", ["block", "token"])
+def test_online_bookkeeping_matches_non_online(orc, pv, causal, q_gran):
     wl = si.make("tiny", N=700, H=1, seed=91)  # 6 tiles, the last ragged (60 keys)
     q, k, v = (si.bf16_codes(t) for t in (wl.q, wl.k, wl.v))
-    z, vq, vs = _quantize(orc, q, k, v, pv)
+    z = orc.quant_qk(q, k, q_gran=q_gran)
+    vq, vs = orc.quant_v(v, pv)
     rows = np.array([0, 5, 127, 128, 300, 511, 640, 699])
     out, m, l = orc.attn_rows_head(z, vq, vs, 0, 0, rows, causal, wl.sm_scale, pv, return_ml=True)
     for r, i in enumerate(rows):
@@ -261,3 +266,18 @@ def test_outlier_recipe_accuracy_is_reported(orc):
     rows = np.arange(wl.N)
     ref = np.stack([orc.ref64_rows_head(q, k, v, 0, h, rows, False, wl.sm_scale) for h in range(2)])
     assert _cos(out[0], ref) > 0.995
+
+
+@pytest.mark.parametrize("pv", ["fp8", "fp16"])
+def test_per_token_q_is_closer_to_fp64_on_outlier_tokens(orc, pv):
+    """Finer Q scales are the remedy the pages' "thread-level" quantization
+    points at: on the outlier recipe (query tokens scaled x30 share a block
+    with normal ones) per-token Q scales bring the output closer to FP64
+    attention than per-block ones."""
+    wl = si.make("outlier", B=1, H=2, N=1500, seed=4)
+    q, k, v = (si.bf16_codes(t) for t in (wl.q, wl.k, wl.v))
+    rows = np.arange(wl.N)
+    ref = np.stack([orc.ref64_rows_head(q, k, v, 0, h, rows, False, wl.sm_scale) for h in range(2)])
+    cb = _cos(orc.attention(q, k, v, False, wl.sm_scale, pv)[0][0], ref)
+    ct = _cos(orc.attention(q, k, v, False, wl.sm_scale, pv, q_gran="token")[0][0], ref)
+    assert ct > cb + 1e-3, (cb, ct)

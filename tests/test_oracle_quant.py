@@ -117,6 +117,39 @@ def test_quant_qk_blocks_and_tail(orc):
     assert np.abs(dq - ks).max() <= z["k_scale"].max() * 0.5001
 
 
+def test_per_token_q_scales(orc):
+    """Per-token Q ("thread-level" granularity): one scale per query row.  Every
+    nonzero row reaches +-127, its scale is its own absmax / 127, codes stay
+    within half a step, K is unchanged, and the row that holds a block's absmax
+    gets exactly the codes the per-block quantization gives it."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((1, 1, 300, 128)).astype(np.float32)
+    x[0, 0, 7] *= 30.0        # an outlier token, like the outlier workload's
+    x[0, 0, 200] = 0.0        # an all-zero row
+    q = _bf16(x).reshape(x.shape)
+    k = _bf16(rng.standard_normal(x.shape).astype(np.float32) + 2.0).reshape(x.shape)
+    zt = orc.quant_qk(q, k, q_gran="token")
+    zb = orc.quant_qk(q, k)
+    assert zt["q_scale"].shape == (1, 1, 300) and zt["qblk"] == 1 and zb["qblk"] == 128
+    assert np.array_equal(zt["k8"], zb["k8"]) and np.array_equal(zt["k_scale"], zb["k_scale"])
+    qf = orc.bf16_to_f32(q).reshape(x.shape)[0, 0].astype(np.float64)
+    a = np.abs(qf).max(axis=1)
+    assert np.array_equal(zt["q_scale"][0, 0], (a / 127).astype(np.float32))
+    c = zt["q8"][0, 0].astype(np.int64)
+    top = np.abs(c).max(axis=1)
+    assert np.all((top == 127) | (a == 0)) and not c[200].any()
+    deq = c * zt["q_scale"][0, 0][:, None].astype(np.float64)
+    assert np.all(np.abs(deq - qf) <= zt["q_scale"][0, 0][:, None] * 0.5001 + 1e-30)
+    for r0 in (0, 128, 256):
+        blk = qf[r0:r0 + 128]
+        i = r0 + int(np.argmax(np.abs(blk).max(axis=1)))
+        assert np.array_equal(zt["q8"][0, 0, i], zb["q8"][0, 0, i])
+    # finer scales never lose resolution: per-token error <= per-block error, row by row
+    eb = np.abs(zb["q8"][0, 0] * np.repeat(zb["q_scale"][0, 0], 128)[:300, None] - qf).max(axis=1)
+    et = np.abs(deq - qf).max(axis=1)
+    assert np.all(et <= eb * 1.0001 + 1e-12)
+
+
 def test_quant_v_fp8_and_fp16(orc):
     rng = np.random.default_rng(7)
     v = (rng.standard_normal((1, 2, 333, 64)) * rng.uniform(0.1, 10, (1, 2, 1, 64))).astype(np.float32)
