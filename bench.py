@@ -46,6 +46,12 @@ def attn_source_hash():
     return h.hexdigest()[:16]
 
 
+def attn_ops(B, H, N, d):
+    """Algorithmic work of one launch: 4 d ops per (query, key) pair, 2d INT8
+    for Q K^T and 2d FP8 (FP16) for P V."""
+    return 4.0 * B * H * N * N * d
+
+
 def time_gpu(sage, wl, pv, steps, warmup):
     import torch
 

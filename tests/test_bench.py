@@ -55,6 +55,12 @@ def test_record_traffic_refuses_runs_without_the_copy(tmp_path, monkeypatch):
         bench.record_traffic("tiny", "fp8", str(tmp_path / "f"), str(tmp_path / "w"))
 
 
+def test_algorithmic_ops_count():
+    # 4 d ops per (query, key) pair: 2d for Q K^T, 2d for P V
+    assert bench.attn_ops(1, 40, 75600, 128) == pytest.approx(1.1705e14, rel=1e-4)
+    assert bench.attn_ops(2, 3, 5, 64) == 4 * 2 * 3 * 25 * 64
+
+
 def test_source_hash_covers_the_kernel_sources():
     h = bench.attn_source_hash()
     assert len(h) == 16 and all(os.path.exists(f) for f in bench.ATTN_SOURCES)
