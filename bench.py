@@ -52,7 +52,7 @@ def attn_ops(B, H, N, d):
     return 4.0 * B * H * N * N * d
 
 
-def time_gpu(sage, wl, pv, steps, warmup):
+def time_gpu(sage, wl, pv, steps, warmup, q_gran="block"):
     import torch
 
     q, k, v = wl.q, wl.k, wl.v
@@ -61,7 +61,7 @@ def time_gpu(sage, wl, pv, steps, warmup):
     def step(evs=None):
         if evs:
             evs[0].record(stream)
-        qz = sage.quant_qk(q, k)
+        qz = sage.quant_qk(q, k, q_gran=q_gran)
         vq, vs = sage.quant_v(v, pv)
         if evs:
             evs[1].record(stream)
@@ -85,7 +85,7 @@ def time_gpu(sage, wl, pv, steps, warmup):
     return wall, quant_ms, attn_ms
 
 
-def cpu_baseline(wl, pv, target_s=12.0):
+def cpu_baseline(wl, pv, target_s=12.0, q_gran="block"):
     """The oracle as it stands (single-threaded C) on one head of the workload:
     quantization of the whole head, then attention for R query rows against
     all N keys; the head's quantization time is charged pro rata (R / N)."""
@@ -97,7 +97,7 @@ def cpu_baseline(wl, pv, target_s=12.0):
     b, h = 0, 0
     q, k, v = (si.bf16_codes(t[b:b + 1, h:h + 1]) for t in (wl.q, wl.k, wl.v))
     t0 = time.perf_counter()
-    oz = oracle.quant_qk(q, k)
+    oz = oracle.quant_qk(q, k, q_gran=q_gran)
     ovq, ovs = oracle.quant_v(v, pv)
     t_quant = time.perf_counter() - t0
     probe = np.arange(8, dtype=np.int32)
@@ -119,7 +119,11 @@ def cpu_baseline(wl, pv, target_s=12.0):
                        "single-threaded C oracle")}
 
 
-def record_traffic(workload, pv, fetch_dir, write_dir):
+def traffic_key(workload, pv, q_gran="block"):
+    return f"{workload}/{pv}" + ("" if q_gran == "block" else f"/{q_gran}")
+
+
+def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block"):
     """Write profiles/traffic.json from two rocprofv3 --pmc runs of
     `bench.py --steps 1 --warmup 0 --no-cpu-baseline --calibrate-copy` (one with
     FETCH_SIZE, one with WRITE_SIZE; KiB per dispatch).  Each counter is scaled
@@ -154,7 +158,7 @@ def record_traffic(workload, pv, fetch_dir, write_dir):
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
-    data[f"{workload}/{pv}"] = entry
+    data[traffic_key(workload, pv, q_gran)] = entry
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(data, f, indent=1)
     print(json.dumps(entry))
@@ -167,6 +171,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="video_14b_720p")
     ap.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
+    ap.add_argument("--q-gran", default="block", choices=["block", "token"],
+                    help="Q scale granularity: per block of 128 queries, or per query row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -177,7 +183,7 @@ def main():
                          "--pmc output folders (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.record_traffic:
-        record_traffic(args.workload, args.pv, *args.record_traffic)
+        record_traffic(args.workload, args.pv, *args.record_traffic, q_gran=args.q_gran)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (there is no multi-GPU path; "
@@ -203,7 +209,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    wall, quant_ms, attn_ms = time_gpu(sage, wl, args.pv, args.steps, args.warmup)
+    wall, quant_ms, attn_ms = time_gpu(sage, wl, args.pv, args.steps, args.warmup, args.q_gran)
     ops = attn_ops(wl.B, wl.H, wl.N, wl.d)
     ms_per_step = wall * 1e3 / args.steps
     attn_mean = sum(attn_ms) / len(attn_ms)
@@ -217,7 +223,7 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f).get(f"{wl.name}/{args.pv}")
+            t = json.load(f).get(traffic_key(wl.name, args.pv, args.q_gran))
         if t and t.get("source_hash") == attn_source_hash():
             traffic = t.get("bytes_per_launch")
     res = {
@@ -234,7 +240,8 @@ def main():
         "dtype": "int8+fp8" if args.pv == "fp8" else "int8+fp16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
-                   "causal": wl.causal, "pv": args.pv, "seed": wl.seed, "parallelism": "none"},
+                   "causal": wl.causal, "pv": args.pv, "q_gran": args.q_gran, "seed": wl.seed,
+                   "parallelism": "none"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": "attn_fwd_kernel", "ops_per_launch": ops,
@@ -252,7 +259,7 @@ def main():
         res["roofline"]["useful_causal_tops"] = useful / (attn_mean * 1e-3) / 1e12
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, args.pv, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, args.pv, args.cpu_seconds, args.q_gran)
     print(json.dumps(res), flush=True)
 
 

@@ -73,6 +73,12 @@ enum sage_status {
 enum sage_layout { SAGE_LAYOUT_HND = 0, SAGE_LAYOUT_NHD = 1 };
 enum sage_pv_dtype { SAGE_PV_FP8 = 0, SAGE_PV_FP16 = 1 };
 enum sage_out_dtype { SAGE_OUT_BF16 = 0, SAGE_OUT_FP32 = 1 };
+/* Granularity of the Q scales (the _ex entry points).  The pages give the
+ * per-block INT8 quantization (reportify SageAttention3 summary, bullet
+ * 8比特训练) and a finer "thread-level" one (the txrjy.com repost of the
+ * QbitAI article, section 四个步骤极限压缩时间); SAGE_QGRAN_TOKEN is the finest
+ * Q granularity: one scale per query row.  K stays per block of 128 rows. */
+enum sage_q_gran { SAGE_QGRAN_BLOCK = 0, SAGE_QGRAN_TOKEN = 1 };
 
 /* Compile-time constants of the method as built. */
 typedef struct {
@@ -110,6 +116,12 @@ enum sage_buffer {
  * SAGE_ERR_INVALID, SAGE_ERR_UNSUPPORTED or SAGE_ERR_SIZE. */
 int sage_quant_sizes(int B, int H, int N, int d, int pv_dtype, size_t* sizes);
 
+/* As sage_quant_sizes, for Q scales of granularity q_gran (sage_q_gran):
+ * with SAGE_QGRAN_TOKEN, SAGE_BUF_QSCALE is fp32 [B][H][N_pad] (rows >= N
+ * get scale 0).  Returns the codes of sage_quant_sizes; SAGE_ERR_INVALID for
+ * an unknown q_gran. */
+int sage_quant_sizes_ex(int B, int H, int N, int d, int pv_dtype, int q_gran, size_t* sizes);
+
 /*
  * Smooth K and quantize Q and K (per block of 128 rows, INT8).
  *
@@ -133,6 +145,18 @@ int sage_quant_sizes(int B, int H, int N, int d, int pv_dtype, size_t* sizes);
 int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, int layout,
                   int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, float* k_mean,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sage_quant_qk with the Q scale granularity q_gran (sage_q_gran).
+ * SAGE_QGRAN_BLOCK is sage_quant_qk.  SAGE_QGRAN_TOKEN quantizes each query
+ * row n < N on its own: a = max_c |Q[n][c]|, q_scale[b][h][n] = fp32(fp64(a)/127),
+ * codes as above with inv = fp32(127/fp64(a)); rows N..N_pad-1 get codes 0 and
+ * scale 0.  K smoothing and K quantization are unchanged.  q_scale must hold
+ * the SAGE_BUF_QSCALE bytes sage_quant_sizes_ex gives for q_gran.
+ */
+int sage_quant_qk_ex(const void* q, const void* k, int B, int H, int N, int d, int layout,
+                     int q_gran, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale,
+                     float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Quantize V (wxsanhe §三.1: P V in FP8 or FP16).
@@ -177,6 +201,17 @@ int sage_attn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, cons
                   const void* vq, const float* v_scale, int B, int H, int N, int d, int layout,
                   int causal, float sm_scale, int pv_dtype, void* out, int out_dtype,
                   void* stream);
+
+/*
+ * sage_attn_fwd over Q scales of granularity q_gran (sage_q_gran), as
+ * produced by sage_quant_qk_ex: sigma above is fp32(q_scale[b][h][i] *
+ * lambda) for SAGE_QGRAN_TOKEN (fp32(q_scale[b][h][i / 128] * lambda) for
+ * SAGE_QGRAN_BLOCK, which is sage_attn_fwd).  Same kernel, same cost.
+ */
+int sage_attn_fwd_ex(const int8_t* q8, const float* q_scale, const int8_t* k8,
+                     const float* k_scale, const void* vq, const float* v_scale, int B, int H,
+                     int N, int d, int layout, int causal, float sm_scale, int pv_dtype,
+                     int q_gran, void* out, int out_dtype, void* stream);
 
 /*
  * sage_attn_fwd that also writes the raw int32 Q K^T accumulators of head

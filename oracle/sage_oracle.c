@@ -301,9 +301,10 @@ OR_API float or_lambda(float sm_scale) { return (float)((double)sm_scale * 1.442
  * unquantized p; key tiles of bc = 128 keys in ascending order, no split;
  * the two accumulation levels are one key tile and the whole row.
  * qs is indexed by query block of qblk rows: qblk = 128 is the per-block
- * quantization, qblk = 1 the per-token ("thread-level") one, reportify
- * SageAttention3 summary, bullet 8比特训练 and wxsanhe §三.1; ks by key block of
- * kblk keys, and bc == kblk.
+ * quantization (reportify SageAttention3 summary, bullet 8比特训练), qblk = 1
+ * the per-token one, the finest reading of the "thread-level quantization" in
+ * the txrjy.com repost of the QbitAI article, section 四个步骤极限压缩时间;
+ * ks by key block of kblk keys, and bc == kblk.
  * Pinned: FP64 attention (cosine), brute force of the single-tile case,
  * P rows summing to 1 through the final (m, l), a tile-by-tile non-online
  * recomputation, constant keys and peaked rows in closed form. */

@@ -27,6 +27,7 @@ SAGE_OK = 0
 LAYOUTS = {"HND": 0, "NHD": 1}
 PV = {"fp8": 0, "fp16": 1}
 OUT = {torch.bfloat16: 0, torch.float32: 1}
+QGRAN = {"block": 0, "token": 1}
 (BUF_Q8, BUF_QSCALE, BUF_K8, BUF_KSCALE, BUF_KMEAN, BUF_VQ, BUF_VSCALE, BUF_WS_QK,
  BUF_WS_V, NBUF) = range(10)
 
@@ -41,8 +42,9 @@ class SageConfig(ct.Structure):
                 ("p_scale", ct.c_float), ("log2_p_scale", ct.c_float), ("fp8_format", ct.c_int)]
 
 
-EXPORTS = ["sage_get_config", "sage_quant_sizes", "sage_quant_qk", "sage_quant_v",
-           "sage_attn_fwd", "sage_attn_fwd_debug", "sage_status_string"]
+EXPORTS = ["sage_get_config", "sage_quant_sizes", "sage_quant_sizes_ex", "sage_quant_qk",
+           "sage_quant_qk_ex", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_ex",
+           "sage_attn_fwd_debug", "sage_status_string"]
 
 _lib = None
 
@@ -59,9 +61,12 @@ def lib():
     P, I, F, S = ct.c_void_p, ct.c_int, ct.c_float, ct.c_size_t
     L.sage_get_config.argtypes = [I, ct.POINTER(SageConfig)]
     L.sage_quant_sizes.argtypes = [I, I, I, I, I, ct.POINTER(S)]
+    L.sage_quant_sizes_ex.argtypes = [I, I, I, I, I, I, ct.POINTER(S)]
     L.sage_quant_qk.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, S, P]
+    L.sage_quant_qk_ex.argtypes = [P, P, I, I, I, I, I, I, P, P, P, P, P, P, S, P]
     L.sage_quant_v.argtypes = [P, I, I, I, I, I, I, P, P, P, S, P]
     L.sage_attn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
+    L.sage_attn_fwd_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, I, P]
     L.sage_attn_fwd_debug.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, I, I, I,
                                       P, P]
     for name in EXPORTS[:-1]:
@@ -91,9 +96,12 @@ def get_config(d: int = 128) -> dict:
     return {f: getattr(c, f) for f, _ in SageConfig._fields_}
 
 
-def quant_sizes(B: int, H: int, N: int, d: int, pv: str = "fp8") -> list[int]:
+def quant_sizes(B: int, H: int, N: int, d: int, pv: str = "fp8", q_gran: str = "block") -> list[int]:
     arr = (ct.c_size_t * NBUF)()
-    _check(lib().sage_quant_sizes(B, H, N, d, PV[pv], arr))
+    if q_gran == "block":
+        _check(lib().sage_quant_sizes(B, H, N, d, PV[pv], arr))
+    else:
+        _check(lib().sage_quant_sizes_ex(B, H, N, d, PV[pv], QGRAN[q_gran], arr))
     return list(arr)
 
 
@@ -114,27 +122,34 @@ def _empty(nbytes: int, device, dtype=torch.uint8):
     return torch.empty(max(1, nbytes // itemsize), dtype=dtype, device=device)
 
 
-def quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND") -> dict:
-    """Smooth K and quantize Q, K to per-block INT8 (sage_quant_qk)."""
+def quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", q_gran: str = "block") -> dict:
+    """Smooth K and quantize Q, K to INT8 (sage_quant_qk; sage_quant_qk_ex with
+    q_gran="token" for one Q scale per query row)."""
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
         raise TypeError("q and k must be bfloat16")
     if q.shape != k.shape or not q.is_contiguous() or not k.is_contiguous():
         raise ValueError("q and k must be contiguous and of the same shape")
+    if q_gran not in QGRAN:
+        raise ValueError(f"q_gran must be one of {list(QGRAN)}, not {q_gran!r}")
     B, H, N, d = _dims(q, layout)
-    sz = quant_sizes(B, H, N, d)
+    sz = quant_sizes(B, H, N, d, q_gran=q_gran)
     dev = q.device
     nblk = -(-N // 128)
     r = dict(q8=torch.empty((B, H, nblk * 128, d), dtype=torch.int8, device=dev),
-             q_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+             q_scale=torch.empty((B, H, nblk * 128 if q_gran == "token" else nblk),
+                                 dtype=torch.float32, device=dev),
              k8=torch.empty((B, H, nblk * 128, d), dtype=torch.int8, device=dev),
              k_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
              k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev),
              workspace=_empty(sz[BUF_WS_QK], dev, torch.int64))
-    _check(lib().sage_quant_qk(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout], _ptr(r["q8"]),
-                               _ptr(r["q_scale"]), _ptr(r["k8"]), _ptr(r["k_scale"]),
-                               _ptr(r["k_mean"]), _ptr(r["workspace"]), sz[BUF_WS_QK],
-                               _stream(dev)))
-    r.update(B=B, H=H, N=N, d=d, layout=layout)
+    bufs = (_ptr(r["q8"]), _ptr(r["q_scale"]), _ptr(r["k8"]), _ptr(r["k_scale"]),
+            _ptr(r["k_mean"]), _ptr(r["workspace"]), sz[BUF_WS_QK], _stream(dev))
+    if q_gran == "block":
+        _check(lib().sage_quant_qk(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout], *bufs))
+    else:
+        _check(lib().sage_quant_qk_ex(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout], QGRAN[q_gran],
+                                      *bufs))
+    r.update(B=B, H=H, N=N, d=d, layout=layout, q_gran=q_gran)
     return r
 
 
@@ -171,9 +186,16 @@ def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
     args = (_ptr(qz["q8"]), _ptr(qz["q_scale"]), _ptr(qz["k8"]), _ptr(qz["k_scale"]), _ptr(vq),
             _ptr(vs), B, H, N, d, LAYOUTS[layout], int(bool(causal)), sm, PV[pv], _ptr(out),
             OUT[out.dtype])
+    q_gran = qz.get("q_gran", "block")
     if debug is None:
-        _check(lib().sage_attn_fwd(*args, _stream(dev)))
+        if q_gran == "block":
+            _check(lib().sage_attn_fwd(*args, _stream(dev)))
+        else:
+            _check(lib().sage_attn_fwd_ex(*args[:14], QGRAN[q_gran], *args[14:], _stream(dev)))
         return out
+    if q_gran != "block":
+        raise ValueError("the debug dump runs with per-block Q scales (the int32 Q K^T it "
+                         "writes does not depend on them)")
     b, h, row0, nrows = debug
     s = torch.zeros((nrows, N), dtype=torch.int32, device=dev)
     _check(lib().sage_attn_fwd_debug(*args, b, h, row0, nrows, _ptr(s), _stream(dev)))
@@ -182,10 +204,10 @@ def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
 
 def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
          sm_scale: float | None = None, pv: str = "fp8", layout: str = "HND",
-         out_dtype=torch.bfloat16) -> torch.Tensor:
+         out_dtype=torch.bfloat16, q_gran: str = "block") -> torch.Tensor:
     """softmax(Q K^T sm_scale) V through the quantized path (quantize, then the
     fused kernel), all on q's device and current stream."""
-    qz = quant_qk(q, k, layout)
+    qz = quant_qk(q, k, layout, q_gran)
     vq, vs = quant_v(v, pv, layout)
     return attn_fwd(qz, vq, vs, causal=causal, sm_scale=sm_scale, pv=pv, out_dtype=out_dtype)
 

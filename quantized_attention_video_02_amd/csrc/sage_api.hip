@@ -31,19 +31,22 @@ int check_layout(int layout) {
     return (layout == SAGE_LAYOUT_HND || layout == SAGE_LAYOUT_NHD) ? SAGE_OK : SAGE_ERR_INVALID;
 }
 int check_pv(int pv) { return (pv == SAGE_PV_FP8 || pv == SAGE_PV_FP16) ? SAGE_OK : SAGE_ERR_INVALID; }
+int check_qgran(int g) {
+    return (g == SAGE_QGRAN_BLOCK || g == SAGE_QGRAN_TOKEN) ? SAGE_OK : SAGE_ERR_INVALID;
+}
 
 struct Sizes {
     size_t v[SAGE_NBUF];
 };
 
-Sizes sizes_of(int B, int H, int N, int d, int pv) {
+Sizes sizes_of(int B, int H, int N, int d, int pv, int q_gran = SAGE_QGRAN_BLOCK) {
     const size_t nblk = ((size_t)N + sage::kBlk - 1) / sage::kBlk;
     const size_t npad = nblk * sage::kBlk;
     const size_t bh = (size_t)B * H;
     const size_t nchunk = ((size_t)N + sage::kStatsChunk - 1) / sage::kStatsChunk;
     Sizes s;
     s.v[SAGE_BUF_Q8] = bh * npad * d;
-    s.v[SAGE_BUF_QSCALE] = bh * nblk * sizeof(float);
+    s.v[SAGE_BUF_QSCALE] = bh * (q_gran == SAGE_QGRAN_TOKEN ? npad : nblk) * sizeof(float);
     s.v[SAGE_BUF_K8] = bh * npad * d;
     s.v[SAGE_BUF_KSCALE] = bh * nblk * sizeof(float);
     s.v[SAGE_BUF_KMEAN] = bh * d * sizeof(float);
@@ -62,13 +65,14 @@ Sizes sizes_of(int B, int H, int N, int d, int pv) {
 
 int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                 const void* vq, const float* v_scale, int B, int H, int N, int d, int layout,
-                int causal, float sm_scale, int pv_dtype, void* out, int out_dtype, int dump,
-                int db, int dh, int row0, int nrows, int32_t* s_out, void* stream) {
+                int causal, float sm_scale, int pv_dtype, int q_gran, void* out, int out_dtype,
+                int dump, int db, int dh, int row0, int nrows, int32_t* s_out, void* stream) {
     if (!q8 || !q_scale || !k8 || !k_scale || !vq || !v_scale || !out) return SAGE_ERR_NULL;
     if (dump && !s_out) return SAGE_ERR_NULL;
     SAGE_TRY(check_dims(B, H, N, d));
     SAGE_TRY(check_layout(layout));
     SAGE_TRY(check_pv(pv_dtype));
+    SAGE_TRY(check_qgran(q_gran));
     if (causal != 0 && causal != 1) return SAGE_ERR_INVALID;
     if (out_dtype != SAGE_OUT_BF16 && out_dtype != SAGE_OUT_FP32) return SAGE_ERR_INVALID;
     if (!(isfinite(sm_scale) && sm_scale > 0.0f)) return SAGE_ERR_INVALID;
@@ -98,6 +102,7 @@ int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const 
     a.total = B * H * a.nqt;
     a.layout = layout;
     a.out_fp32 = out_dtype == SAGE_OUT_FP32;
+    a.qtok = q_gran == SAGE_QGRAN_TOKEN;
     a.lambda = (float)((double)sm_scale * 1.4426950408889634);
     a.dbh = dump ? db * H + dh : -1;
     a.drow0 = row0;
@@ -126,14 +131,46 @@ __attribute__((visibility("default"))) int sage_get_config(int d, sage_config* o
     return SAGE_OK;
 }
 
-__attribute__((visibility("default"))) int sage_quant_sizes(int B, int H, int N, int d,
-                                                            int pv_dtype, size_t* sizes) {
+__attribute__((visibility("default"))) int sage_quant_sizes_ex(int B, int H, int N, int d,
+                                                               int pv_dtype, int q_gran,
+                                                               size_t* sizes) {
     if (!sizes) return SAGE_ERR_NULL;
     SAGE_TRY(check_dims(B, H, N, d));
     SAGE_TRY(check_pv(pv_dtype));
-    const Sizes s = sizes_of(B, H, N, d, pv_dtype);
+    SAGE_TRY(check_qgran(q_gran));
+    const Sizes s = sizes_of(B, H, N, d, pv_dtype, q_gran);
     for (int i = 0; i < SAGE_NBUF; ++i) sizes[i] = s.v[i];
     return SAGE_OK;
+}
+
+__attribute__((visibility("default"))) int sage_quant_sizes(int B, int H, int N, int d,
+                                                            int pv_dtype, size_t* sizes) {
+    return sage_quant_sizes_ex(B, H, N, d, pv_dtype, SAGE_QGRAN_BLOCK, sizes);
+}
+
+__attribute__((visibility("default"))) int sage_quant_qk_ex(const void* q, const void* k, int B,
+                                                            int H, int N, int d, int layout,
+                                                            int q_gran, int8_t* q8,
+                                                            float* q_scale, int8_t* k8,
+                                                            float* k_scale, float* k_mean,
+                                                            void* workspace,
+                                                            size_t workspace_bytes,
+                                                            void* stream) {
+    if (!q || !k || !q8 || !q_scale || !k8 || !k_scale || !k_mean || !workspace)
+        return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_layout(layout));
+    SAGE_TRY(check_qgran(q_gran));
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q8) || !aligned16(q_scale) ||
+        !aligned16(k8) || !aligned16(k_scale) || !aligned16(k_mean) || !aligned16(workspace))
+        return SAGE_ERR_ALIGN;
+    const Sizes s = sizes_of(B, H, N, d, SAGE_PV_FP8, q_gran);
+    if (workspace_bytes < s.v[SAGE_BUF_WS_QK]) return SAGE_ERR_WORKSPACE;
+    const hipError_t e = sage::launch_quant_qk((const sage::u16*)q, (const sage::u16*)k, B, H, N,
+                                               d, layout, q_gran == SAGE_QGRAN_TOKEN, q8, q_scale,
+                                               k8, k_scale, k_mean, (uint64_t*)workspace,
+                                               (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
 __attribute__((visibility("default"))) int sage_quant_qk(const void* q, const void* k, int B,
@@ -142,19 +179,8 @@ __attribute__((visibility("default"))) int sage_quant_qk(const void* q, const vo
                                                          float* k_scale, float* k_mean,
                                                          void* workspace, size_t workspace_bytes,
                                                          void* stream) {
-    if (!q || !k || !q8 || !q_scale || !k8 || !k_scale || !k_mean || !workspace)
-        return SAGE_ERR_NULL;
-    SAGE_TRY(check_dims(B, H, N, d));
-    SAGE_TRY(check_layout(layout));
-    if (!aligned16(q) || !aligned16(k) || !aligned16(q8) || !aligned16(q_scale) ||
-        !aligned16(k8) || !aligned16(k_scale) || !aligned16(k_mean) || !aligned16(workspace))
-        return SAGE_ERR_ALIGN;
-    const Sizes s = sizes_of(B, H, N, d, SAGE_PV_FP8);
-    if (workspace_bytes < s.v[SAGE_BUF_WS_QK]) return SAGE_ERR_WORKSPACE;
-    const hipError_t e = sage::launch_quant_qk((const sage::u16*)q, (const sage::u16*)k, B, H, N,
-                                               d, layout, q8, q_scale, k8, k_scale, k_mean,
-                                               (uint64_t*)workspace, (hipStream_t)stream);
-    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+    return sage_quant_qk_ex(q, k, B, H, N, d, layout, SAGE_QGRAN_BLOCK, q8, q_scale, k8, k_scale,
+                            k_mean, workspace, workspace_bytes, stream);
 }
 
 __attribute__((visibility("default"))) int sage_quant_v(const void* v, int B, int H, int N, int d,
@@ -182,7 +208,15 @@ __attribute__((visibility("default"))) int sage_attn_fwd(
     const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
     float sm_scale, int pv_dtype, void* out, int out_dtype, void* stream) {
     return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
-                       pv_dtype, out, out_dtype, 0, 0, 0, 0, 1, nullptr, stream);
+                       pv_dtype, SAGE_QGRAN_BLOCK, out, out_dtype, 0, 0, 0, 0, 1, nullptr, stream);
+}
+
+__attribute__((visibility("default"))) int sage_attn_fwd_ex(
+    const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+    const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
+    float sm_scale, int pv_dtype, int q_gran, void* out, int out_dtype, void* stream) {
+    return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
+                       pv_dtype, q_gran, out, out_dtype, 0, 0, 0, 0, 1, nullptr, stream);
 }
 
 __attribute__((visibility("default"))) int sage_attn_fwd_debug(
@@ -191,7 +225,8 @@ __attribute__((visibility("default"))) int sage_attn_fwd_debug(
     float sm_scale, int pv_dtype, void* out, int out_dtype, int b, int h, int row0, int nrows,
     int32_t* s_out, void* stream) {
     return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
-                       pv_dtype, out, out_dtype, 1, b, h, row0, nrows, s_out, stream);
+                       pv_dtype, SAGE_QGRAN_BLOCK, out, out_dtype, 1, b, h, row0, nrows, s_out,
+                       stream);
 }
 
 __attribute__((visibility("default"))) const char* sage_status_string(int status) {

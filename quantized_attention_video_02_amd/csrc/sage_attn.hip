@@ -339,7 +339,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         const int8_t* qrow = a.q8 + ((int64_t)bh * a.N_pad + qi) * D + 16 * hh;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const v4i*)(qrow + 32 * kk);
-        sigma = a.q_scale[bh * a.nblk + qbase / kBlk] * a.lambda;
+        // per block: one scale for the wave's 32 queries; per token: one per lane
+        sigma = (a.qtok ? a.q_scale[(int64_t)bh * a.N_pad + qi] : a.q_scale[bh * a.nblk + qbase / kBlk]) *
+                a.lambda;
     }
 
     const uint8_t* kg = (const uint8_t*)a.k8 + (int64_t)bh * a.N_pad * D;

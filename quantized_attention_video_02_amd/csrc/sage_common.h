@@ -60,11 +60,13 @@ struct AttnArgs {
     void* out;
     int32_t* s_out;  // debug dump (dump instantiations only)
     int H, N, N_pad, nblk, nqt, total, layout, out_fp32;
+    int qtok;  // 1: q_scale per query row [bh][N_pad]; 0: per block of kBlk rows [bh][nblk]
     float lambda;    // fp32(sm_scale * log2 e)
     int dbh, drow0, dnrows;
 };
 
 hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
+                           int qtok,
                            int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean,
                            uint64_t* ws, hipStream_t s);
 hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, int pv16,

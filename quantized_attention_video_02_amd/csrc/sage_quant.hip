@@ -130,7 +130,7 @@ __global__ void v_scale_kernel(const float* __restrict__ part, int nchunk, int D
 template <int D>
 __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, int H, int N, int N_pad, int nblk,
-    int layout, const float* __restrict__ kmean, int8_t* __restrict__ q8,
+    int layout, int qtok, const float* __restrict__ kmean, int8_t* __restrict__ q8,
     float* __restrict__ q_scale, int8_t* __restrict__ k8, float* __restrict__ k_scale) {
     constexpr int CPR = D / 8;
     constexpr int RPI = kQuantThreads / CPR;
@@ -162,6 +162,32 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[it][e] = 0.0f;
         }
+    }
+    if (!isk && qtok) {
+        // one scale per query row: the row's CPR lanes are consecutive lanes of
+        // one wave, so its absmax is a butterfly over them.  Padded rows get
+        // codes 0 and scale 0.
+        int8_t* dst = q8;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int row = blk * kBlk + tr + it * RPI;
+            float ra = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ra = fmaxf(ra, fabsf(x[it][e]));
+#pragma unroll
+            for (int off = 1; off < CPR; off <<= 1) ra = fmaxf(ra, __shfl_xor(ra, off, 64));
+            const float rinv = ra > 0.0f ? (float)(127.0 / (double)ra) : 0.0f;
+            uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = __builtin_rintf(x[it][e] * rinv);
+                v = fminf(fmaxf(v, -127.0f), 127.0f);
+                packed[e >> 2] |= ((uint32_t)(int)v & 0xffu) << (8 * (e & 3));
+            }
+            *(uint2*)(dst + ((int64_t)bh * N_pad + row) * D + cg * 8) = make_uint2(packed[0], packed[1]);
+            if (cg == 0) q_scale[(int64_t)bh * N_pad + row] = (float)((double)ra / 127.0);
+        }
+        return;
     }
     amax = wave_max(amax);
     if ((t & 63) == 0) wmax[t >> 6] = amax;
@@ -304,7 +330,7 @@ static inline hipError_t launch(const void* fn, dim3 grid, dim3 block, void** ar
 }
 
 hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
-                           int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean,
+                           int qtok, int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean,
                            uint64_t* ws, hipStream_t s) {
     const int nblk = (N + kBlk - 1) / kBlk, N_pad = nblk * kBlk;
     const int nchunk = (N + kStatsChunk - 1) / kStatsChunk;
@@ -322,9 +348,10 @@ hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int 
             return e;
     }
     {
-        void* args[] = {(void*)&q,  (void*)&k,  (void*)&H,     (void*)&N,  (void*)&N_pad,
-                        (void*)&nblk, (void*)&layout, (void*)&kmean, (void*)&q8, (void*)&qs,
-                        (void*)&k8, (void*)&ks};
+        void* args[] = {(void*)&q,      (void*)&k,    (void*)&H,     (void*)&N,
+                        (void*)&N_pad,  (void*)&nblk, (void*)&layout, (void*)&qtok,
+                        (void*)&kmean,  (void*)&q8,   (void*)&qs,     (void*)&k8,
+                        (void*)&ks};
         const void* fn = d == 128 ? (const void*)quant_qk_kernel<128> : (const void*)quant_qk_kernel<64>;
         if ((e = launch(fn, dim3(nblk, BH, 2), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
     }

@@ -68,6 +68,11 @@ def test_quant_sizes(sage):
     assert s[sage.BUF_WS_V] == (2 * 3 * 64 + 2 * 3 * 64) * 4
     s16 = sage.quant_sizes(2, 3, 300, 64, "fp16")
     assert s16[sage.BUF_VQ] == 2 * s[sage.BUF_VQ] and s16[sage.BUF_WS_V] == 0
+    st = sage.quant_sizes(2, 3, 300, 64, "fp8", q_gran="token")
+    assert st[sage.BUF_QSCALE] == 2 * 3 * npad * 4   # one scale per (padded) query row
+    assert [st[i] for i in range(sage.NBUF) if i != sage.BUF_QSCALE] == \
+        [s[i] for i in range(sage.NBUF) if i != sage.BUF_QSCALE]
+    assert sage.quant_sizes(2, 3, 300, 64, "fp8", q_gran="block") == s
 
 
 def _codes(sage):
@@ -117,6 +122,17 @@ def test_invalid_arguments_rejected_before_launch(sage):
     assert fwd(N=0) == -2
     assert fwd(lay=-1) == -2
     assert fwd(out=A + 2) == -4
+    assert L.sage_quant_sizes_ex(1, 1, 10, 128, 0, 2, sz) == -2
+    assert L.sage_quant_sizes_ex(1, 1, 10, 128, 0, -1, sz) == -2
+    assert L.sage_quant_sizes_ex(1, 1, 10, 128, 0, 1, None) == -1
+    qkx = lambda g=1, q=A: L.sage_quant_qk_ex(q, A, 1, 1, 256, 128, 0, g, A, A, A, A, A, A,
+                                              1 << 20, None)
+    assert qkx(g=2) == -2
+    assert qkx(q=None) == -1
+    fwdx = lambda g=1, sm=0.1: L.sage_attn_fwd_ex(A, A, A, A, A, A, 1, 2, 256, 128, 0, 0, sm, 0,
+                                                  g, A, 0, None)
+    assert fwdx(g=3) == -2
+    assert fwdx(sm=-2.0) == -2
     dbg = lambda b=0, h=0, row0=0, nrows=4, s=A: L.sage_attn_fwd_debug(
         A, A, A, A, A, A, 1, 2, 256, 128, 0, 0, 0.1, 0, A, 0, b, h, row0, nrows, s, None)
     assert dbg(s=None) == -1

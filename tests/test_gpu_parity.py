@@ -83,7 +83,7 @@ def oracle_quant(orc, wl, pv, heads=None):
     oz = orc.quant_qk(q, k)
     ovq, ovs = orc.quant_v(v, pv)
     if heads is not None:
-        oz = {key: val[0] for key, val in oz.items()}
+        oz = {key: (val[0] if isinstance(val, np.ndarray) else val) for key, val in oz.items()}
         ovq, ovs = ovq[0], ovs[0]
     return q, k, v, oz, ovq, ovs
 
@@ -285,7 +285,8 @@ def test_full_size_sampled(sage, orc, name, pv):
     o_all, r_all, or_all = [], [], []
     for i, (b, h) in enumerate(heads):
         rows = sample_rows(wl, b, h, rng)
-        ozh = {key: val[i][None, None] for key, val in oz.items()}
+        ozh = {key: (val[i][None, None] if isinstance(val, np.ndarray) else val)
+               for key, val in oz.items()}
         o_or = orc.attn_rows_head(ozh, ovq[i][None, None], ovs[i][None, None], 0, 0, rows,
                                   wl.causal, wl.sm_scale, pv)
         o_gpu = out[b, h, torch.from_numpy(rows).long().cuda()].cpu().numpy()
@@ -300,4 +301,95 @@ def test_full_size_sampled(sage, orc, name, pv):
     if name == "outlier":
         assert abs(c_gpu - c_or) < 2e-4, (c_gpu, c_or)
     else:
+        assert c_gpu >= COS_FP64, c_gpu
+
+
+# ------------------------------------------------------- per-token Q scales
+def run_gpu_token(sage, wl, pv, layout="HND"):
+    qd, kd, vd = (_to_layout(t, layout).cuda() for t in (wl.q, wl.k, wl.v))
+    qz = sage.quant_qk(qd, kd, layout, q_gran="token")
+    vq, vs = sage.quant_v(vd, pv, layout)
+    out = sage.attn_fwd(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale, pv=pv,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return qz, vq, vs, to_hnd(out, layout)
+
+
+TOKEN_CASES = [
+    ("tiny", dict(N=300, H=2), "fp8", "HND"),
+    ("tiny", dict(N=1, H=1), "fp8", "NHD"),
+    ("tiny", dict(N=129, H=1), "fp16", "HND"),
+    ("causal_prefill", dict(B=2, H=1, N=700), "fp8", "NHD"),
+    ("outlier", dict(B=1, H=2, N=1100), "fp8", "HND"),
+    ("outlier", dict(B=1, H=2, N=1100), "fp16", "HND"),
+]
+
+
+@pytest.mark.parametrize("name,kw,pv,layout", TOKEN_CASES)
+def test_per_token_q_matches_oracle(sage, orc, name, kw, pv, layout):
+    """sage_quant_qk_ex / sage_attn_fwd_ex with one Q scale per query row:
+    codes and scales bit-exact (padded rows: codes 0, scale 0; K as with
+    per-block Q), the output within the parity bars of the oracle run with
+    the same granularity."""
+    wl = si.make(name, **kw)
+    qz, vq, vs, out = run_gpu_token(sage, wl, pv, layout)
+    out = out.cpu().numpy()
+    q, k, v = codes(wl.q), codes(wl.k), codes(wl.v)
+    oz = orc.quant_qk(q, k, q_gran="token")
+    ovq, ovs = orc.quant_v(v, pv)
+    N = wl.N
+    q8, qs = qz["q8"].cpu().numpy(), qz["q_scale"].cpu().numpy()
+    assert qs.shape == (wl.B, wl.H, -(-N // 128) * 128)
+    assert np.array_equal(q8[:, :, :N], oz["q8"]) and not q8[:, :, N:].any()
+    assert np.array_equal(qs[:, :, :N].view(np.uint32), oz["q_scale"].view(np.uint32))
+    assert not qs[:, :, N:].any()
+    assert np.array_equal(qz["k8"][:, :, :N].cpu().numpy(), oz["k8"])
+    assert np.array_equal(qz["k_scale"].cpu().numpy().view(np.uint32), oz["k_scale"].view(np.uint32))
+    rows = np.arange(N)
+    o_or = np.stack([np.stack([orc.attn_rows_head(oz, ovq, ovs, b, h, rows, wl.causal, wl.sm_scale, pv)
+                               for h in range(wl.H)]) for b in range(wl.B)])
+    assert np.isfinite(out).all()
+    err, c = np.abs(out - o_or).max(), _cos(out, o_or)
+    assert err <= MAX_ABS and c >= COS_ORACLE, (err, c)
+    if N >= 64:
+        ref = np.stack([np.stack([orc.ref64_rows_head(q, k, v, b, h, rows, wl.causal, wl.sm_scale)
+                                  for h in range(wl.H)]) for b in range(wl.B)])
+        c_gpu, c_or = _cos(out, ref), _cos(o_or, ref)
+        assert abs(c_gpu - c_or) < 2e-4, (c_gpu, c_or)
+
+
+@pytest.mark.parametrize("name,pv", [("outlier", "fp8"), ("video_14b_720p", "fp8")])
+def test_per_token_q_full_size_sampled(sage, orc, name, pv):
+    """Per-token Q at full size in the benchmark's launch configuration, on
+    sampled heads and rows (the outlier tokens included)."""
+    print(f"[full-size per-token parity] {name} pv={pv}", flush=True)
+    wl = si.make(name, device="cuda")
+    qz = sage.quant_qk(wl.q, wl.k, q_gran="token")
+    vq, vs = sage.quant_v(wl.v, pv)
+    out = sage.attn_fwd(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale, pv=pv,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (wl.B - 1, wl.H - 1)]
+    rng = np.random.default_rng(2)
+    qa, ka, va = codes(wl.q.cpu()), codes(wl.k.cpu()), codes(wl.v.cpu())
+    o_all, or_all, r_all = [], [], []
+    for b, h in heads:
+        q, k, v = (x[b, h][None, None] for x in (qa, ka, va))
+        oz = orc.quant_qk(q, k, q_gran="token")
+        ovq, ovs = orc.quant_v(v, pv)
+        assert np.array_equal(qz["q8"][b, h, :wl.N].cpu().numpy(), oz["q8"][0, 0])
+        assert np.array_equal(qz["q_scale"][b, h, :wl.N].cpu().numpy().view(np.uint32),
+                              oz["q_scale"][0, 0].view(np.uint32))
+        rows = sample_rows(wl, b, h, rng)
+        o_or = orc.attn_rows_head(oz, ovq, ovs, 0, 0, rows, wl.causal, wl.sm_scale, pv)
+        o_gpu = out[b, h, torch.from_numpy(rows).long().cuda()].cpu().numpy()
+        ref = orc.ref64_rows_head(q, k, v, 0, 0, rows, wl.causal, wl.sm_scale)
+        o_all.append(o_gpu), or_all.append(o_or), r_all.append(ref)
+    o_gpu, o_or, ref = (np.concatenate(x) for x in (o_all, or_all, r_all))
+    err, c = np.abs(o_gpu - o_or).max(), _cos(o_gpu, o_or)
+    c_gpu, c_or = _cos(o_gpu, ref), _cos(o_or, ref)
+    print(f"  max-abs {err:.3e} cos(oracle) {c:.7f} cos64 gpu {c_gpu:.6f} oracle {c_or:.6f}")
+    assert err <= MAX_ABS and c >= COS_ORACLE, (err, c)
+    assert abs(c_gpu - c_or) < 2e-4, (c_gpu, c_or)
+    if name != "outlier":
         assert c_gpu >= COS_FP64, c_gpu
