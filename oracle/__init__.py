@@ -61,8 +61,8 @@ def lib():
             "or_quant_k": [P, i32, i32, i32, i32, P, P, P, P],
             "or_quant_v": [P, i32, i32, i32, P, P],
             "or_dump_s": [P, P, i32, i32, i32, i32, i32, P],
-            "or_attn_rows": [P, P, P, P, P, P, i32, i32, P, i32, i32, f32, i32, i32, i32, i32, P, P, P,
-                             P],
+            "or_attn_rows": [P, P, P, P, P, P, i32, i32, P, i32, i32, f32, i32, i32, i32, i32, P, P,
+                             P, P, P],
             "or_ref64_rows": [P, P, P, i32, i32, P, i32, i32, f64, P, P],
         }
         for name, args in sigs.items():
@@ -201,8 +201,11 @@ def dump_s(q8h: np.ndarray, k8h: np.ndarray, row0: int, nrows: int, causal: bool
 
 
 def attn_rows_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scale: float,
-                   pv: str = "fp8", blk: int = BLK, bc: int = BC, return_ml: bool = False):
-    """Quantized attention for query rows ``rows`` of head (b, h): fp32 [len(rows), d]."""
+                   pv: str = "fp8", blk: int = BLK, bc: int = BC, return_ml: bool = False,
+                   tile_mask=None):
+    """Quantized attention for query rows ``rows`` of head (b, h): fp32 [len(rows), d].
+    tile_mask: None (dense) or uint8 [B, H, ceil(N/128), ceil(N/bc)], nonzero =
+    the query block visits the key tile."""
     q8h = np.ascontiguousarray(qz["q8"][b, h])
     k8h = np.ascontiguousarray(qz["k8"][b, h])
     qsh = np.ascontiguousarray(qz["q_scale"][b, h])
@@ -216,9 +219,13 @@ def attn_rows_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scal
     l = np.empty(len(rows), np.float32)
     scratch = np.empty(4 * bc + 3 * d, np.float32)
     qblk = int(qz.get("qblk", blk))
+    tm = None
+    if tile_mask is not None:
+        tm = np.ascontiguousarray(tile_mask[b, h], np.uint8)
+        assert tm.shape == ((N + 127) // 128, (N + bc - 1) // bc), tm.shape
     lib().or_attn_rows(_p(q8h), _p(qsh), _p(k8h), _p(ksh), _p(vqh), _p(vsh), N, d, _p(rows),
                        len(rows), int(causal), float(sm_scale), int(pv == "fp16"), qblk, blk, bc,
-                       _p(out), _p(m), _p(l), _p(scratch))
+                       None if tm is None else _p(tm), _p(out), _p(m), _p(l), _p(scratch))
     if return_ml:
         return out, m, l
     return out
@@ -239,7 +246,7 @@ def ref64_rows_head(q, k, v, b: int, h: int, rows, causal: bool, sm_scale: float
 
 
 def attention(q, k, v, causal: bool, sm_scale: float, pv: str = "fp8", rows=None,
-              q_gran: str = "block"):
+              q_gran: str = "block", tile_mask=None):
     """Whole oracle pipeline: quantize, then attention for ``rows`` (default all)
     of every head.  Returns (out fp32 [B,H,len(rows),d], quantized dict, vq, vs)."""
     B, H, N, d = q.shape
@@ -249,5 +256,6 @@ def attention(q, k, v, causal: bool, sm_scale: float, pv: str = "fp8", rows=None
     out = np.empty((B, H, len(rows), d), np.float32)
     for b in range(B):
         for h in range(H):
-            out[b, h] = attn_rows_head(qz, vq, vs, b, h, rows, causal, sm_scale, pv)
+            out[b, h] = attn_rows_head(qz, vq, vs, b, h, rows, causal, sm_scale, pv,
+                                       tile_mask=tile_mask)
     return out, qz, vq, vs

@@ -305,13 +305,21 @@ OR_API float or_lambda(float sm_scale) { return (float)((double)sm_scale * 1.442
  * the per-token one, the finest reading of the "thread-level quantization" in
  * the txrjy.com repost of the QbitAI article, section 四个步骤极限压缩时间;
  * ks by key block of kblk keys, and bc == kblk.
+ * Block-sparse tile skipping (the sparse half of sparse-linear attention,
+ * wxsanhe §三.1 and the pages' point that sparsity stacks on low-bit
+ * attention): with a tile mask, key tile t is visited only when
+ * tmask[t] != 0 for the query's block of 128 rows; a skipped tile is never
+ * seen, exactly as if all its keys were masked.  A row that visits no key has
+ * l = 0 and gets the output 0 (reading: an empty softmax contributes nothing).
  * Pinned: FP64 attention (cosine), brute force of the single-tile case,
  * P rows summing to 1 through the final (m, l), a tile-by-tile non-online
- * recomputation, constant keys and peaked rows in closed form. */
+ * recomputation, constant keys and peaked rows in closed form; with a tile
+ * mask, against FP64 attention over the visited keys only. */
 static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
                         const void* vq, const float* vs, int N, int d, int i, int causal,
-                        float lambda, int pv_fp16, int qblk, int kblk, int bc, float* out,
-                        float* m_out, float* l_out, int32_t* S, float* T, float* O, float* P) {
+                        float lambda, int pv_fp16, int qblk, int kblk, int bc,
+                        const uint8_t* tmask, float* out, float* m_out, float* l_out, int32_t* S,
+                        float* T, float* O, float* P) {
     const uint8_t* v8 = (const uint8_t*)vq;
     const uint16_t* v16 = (const uint16_t*)vq;
     const float L = or_log2_pscale();
@@ -323,6 +331,7 @@ static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, con
     for (int t = 0; t < ntiles; ++t) {
         int j0 = t * bc;
         if (causal && j0 > i) break;
+        if (tmask && !tmask[t]) continue;
         int j1 = j0 + bc < N ? j0 + bc : N;
         if (causal && j1 > i + 1) j1 = i + 1;
         int n = j1 - j0;
@@ -354,18 +363,20 @@ static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, con
         for (int cc = 0; cc < d; ++cc) O[cc] = alpha * O[cc] + T[cc];
         m = mn;
     }
-    for (int cc = 0; cc < d; ++cc) out[cc] = (O[cc] * vs[cc]) / l;
+    for (int cc = 0; cc < d; ++cc) out[cc] = l > 0.0f ? (O[cc] * vs[cc]) / l : 0.0f;
     if (m_out) *m_out = m;
     if (l_out) *l_out = l;
 }
 
 /* Rows rows[0..nrows) of one head; out [nrows][d]; m_out/l_out optional.
+ * tmask: NULL (dense) or the head's tile mask [ceil(N/128)][ntiles] (query
+ * block of 128 rows x key tile), nonzero = visit.
  * scratch must hold 4*bc + 3*d floats. */
 OR_API void or_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
                          const void* vq, const float* vs, int N, int d, const int32_t* rows,
                          int nrows, int causal, float sm_scale, int pv_fp16, int qblk,
-                         int kblk, int bc, float* out, float* m_out, float* l_out,
-                         float* scratch) {
+                         int kblk, int bc, const uint8_t* tmask, float* out, float* m_out,
+                         float* l_out, float* scratch) {
     float lambda = or_lambda(sm_scale);
     int32_t* S = (int32_t*)scratch;
     float* P = scratch + bc;
@@ -373,6 +384,7 @@ OR_API void or_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, co
     float* O = T + d;
     for (int r = 0; r < nrows; ++r)
         or_attn_row(q8, qs, k8, ks, vq, vs, N, d, rows[r], causal, lambda, pv_fp16, qblk, kblk, bc,
+                    tmask ? tmask + (int64_t)(rows[r] / 128) * ((N + bc - 1) / bc) : 0,
                     out + (int64_t)r * d, m_out ? m_out + r : 0, l_out ? l_out + r : 0, S, T, O,
                     P);
 }
