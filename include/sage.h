@@ -214,6 +214,27 @@ int sage_attn_fwd_ex(const int8_t* q8, const float* q_scale, const int8_t* k8,
                      int q_gran, void* out, int out_dtype, void* stream);
 
 /*
+ * Block-sparse attention: sage_attn_fwd_ex that visits, for each block of
+ * 128 queries, only the key tiles its mask selects (the pages present sparse
+ * attention as orthogonal to low-bit attention and stackable with it:
+ * wxsanhe §三.1; the block-sparse half of sparse-linear attention).
+ * tile_mask: device uint8 [B][H][nblk][nblk], row = query block (queries
+ * [128 r, 128 r + 128)), column = key tile (keys [128 t, 128 t + 128));
+ * nonzero = visit.  A skipped tile contributes nothing: the online softmax of
+ * the block's rows runs over the visited tiles in ascending order, exactly as
+ * if the skipped tiles' keys were masked; with causal, keys after the query
+ * stay masked as well.  A row that visits no key gets the output 0.
+ * A workgroup (256 queries) loads and computes only the tiles that one of its
+ * two query blocks visits.  Requires nblk <= 4096 (N <= 524288; else
+ * SAGE_ERR_SIZE); tile_mask 16-byte aligned.
+ */
+int sage_attn_fwd_sparse(const int8_t* q8, const float* q_scale, const int8_t* k8,
+                         const float* k_scale, const void* vq, const float* v_scale, int B, int H,
+                         int N, int d, int layout, int causal, float sm_scale, int pv_dtype,
+                         int q_gran, const uint8_t* tile_mask, void* out, int out_dtype,
+                         void* stream);
+
+/*
  * sage_attn_fwd that also writes the raw int32 Q K^T accumulators of head
  * (b, h), queries [row0, row0 + nrows), all keys, to s_out [nrows][N]
  * (row-major).  With causal, only entries j <= i are written; the others are

@@ -44,7 +44,7 @@ class SageConfig(ct.Structure):
 
 EXPORTS = ["sage_get_config", "sage_quant_sizes", "sage_quant_sizes_ex", "sage_quant_qk",
            "sage_quant_qk_ex", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_ex",
-           "sage_attn_fwd_debug", "sage_status_string"]
+           "sage_attn_fwd_sparse", "sage_attn_fwd_debug", "sage_status_string"]
 
 _lib = None
 
@@ -67,6 +67,7 @@ def lib():
     L.sage_quant_v.argtypes = [P, I, I, I, I, I, I, P, P, P, S, P]
     L.sage_attn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
     L.sage_attn_fwd_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, I, P]
+    L.sage_attn_fwd_sparse.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, I, P]
     L.sage_attn_fwd_debug.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, I, I, I,
                                       P, P]
     for name in EXPORTS[:-1]:
@@ -173,10 +174,13 @@ def quant_v(v: torch.Tensor, pv: str = "fp8", layout: str = "HND"):
 
 def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
              sm_scale: float | None = None, pv: str = "fp8", out_dtype=torch.bfloat16,
-             out: torch.Tensor | None = None, debug: tuple | None = None):
+             out: torch.Tensor | None = None, debug: tuple | None = None,
+             tile_mask: torch.Tensor | None = None):
     """Fused attention over quantized operands (sage_attn_fwd).  With
     ``debug=(b, h, row0, nrows)`` calls sage_attn_fwd_debug and also returns
-    the int32 Q K^T accumulators [nrows, N]."""
+    the int32 Q K^T accumulators [nrows, N].  With ``tile_mask`` (uint8 or
+    bool [B, H, nblk, nblk] on the device: query block x key tile, nonzero =
+    visit) calls sage_attn_fwd_sparse."""
     B, H, N, d, layout = qz["B"], qz["H"], qz["N"], qz["d"], qz["layout"]
     sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
     shape = (B, H, N, d) if layout == "HND" else (B, N, H, d)
@@ -187,6 +191,16 @@ def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
             _ptr(vs), B, H, N, d, LAYOUTS[layout], int(bool(causal)), sm, PV[pv], _ptr(out),
             OUT[out.dtype])
     q_gran = qz.get("q_gran", "block")
+    if tile_mask is not None:
+        if debug is not None:
+            raise ValueError("the debug dump runs dense")
+        nblk = -(-N // 128)
+        if tuple(tile_mask.shape) != (B, H, nblk, nblk) or tile_mask.device != dev:
+            raise ValueError(f"tile_mask must be [B, H, {nblk}, {nblk}] on {dev}")
+        tm = tile_mask.to(torch.uint8).contiguous()
+        _check(lib().sage_attn_fwd_sparse(*args[:14], QGRAN[q_gran], _ptr(tm), *args[14:],
+                                          _stream(dev)))
+        return out
     if debug is None:
         if q_gran == "block":
             _check(lib().sage_attn_fwd(*args, _stream(dev)))
@@ -204,10 +218,12 @@ def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
 
 def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
          sm_scale: float | None = None, pv: str = "fp8", layout: str = "HND",
-         out_dtype=torch.bfloat16, q_gran: str = "block") -> torch.Tensor:
+         out_dtype=torch.bfloat16, q_gran: str = "block",
+         tile_mask: torch.Tensor | None = None) -> torch.Tensor:
     """softmax(Q K^T sm_scale) V through the quantized path (quantize, then the
     fused kernel), all on q's device and current stream."""
     qz = quant_qk(q, k, layout, q_gran)
     vq, vs = quant_v(v, pv, layout)
-    return attn_fwd(qz, vq, vs, causal=causal, sm_scale=sm_scale, pv=pv, out_dtype=out_dtype)
+    return attn_fwd(qz, vq, vs, causal=causal, sm_scale=sm_scale, pv=pv, out_dtype=out_dtype,
+                    tile_mask=tile_mask)
 

@@ -65,9 +65,11 @@ Sizes sizes_of(int B, int H, int N, int d, int pv, int q_gran = SAGE_QGRAN_BLOCK
 
 int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                 const void* vq, const float* v_scale, int B, int H, int N, int d, int layout,
-                int causal, float sm_scale, int pv_dtype, int q_gran, void* out, int out_dtype,
-                int dump, int db, int dh, int row0, int nrows, int32_t* s_out, void* stream) {
+                int causal, float sm_scale, int pv_dtype, int q_gran, const uint8_t* tmask,
+                int sparse, void* out, int out_dtype, int dump, int db, int dh, int row0,
+                int nrows, int32_t* s_out, void* stream) {
     if (!q8 || !q_scale || !k8 || !k_scale || !vq || !v_scale || !out) return SAGE_ERR_NULL;
+    if (sparse && !tmask) return SAGE_ERR_NULL;
     if (dump && !s_out) return SAGE_ERR_NULL;
     SAGE_TRY(check_dims(B, H, N, d));
     SAGE_TRY(check_layout(layout));
@@ -82,8 +84,11 @@ int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const 
             return SAGE_ERR_INVALID;
         if ((int64_t)nrows * N >= kMaxElems) return SAGE_ERR_SIZE;
     }
+    if (sparse && ((int64_t)N + sage::kBc - 1) / sage::kBc > sage::kMaxSparseTiles)
+        return SAGE_ERR_SIZE;
     if (!aligned16(q8) || !aligned16(q_scale) || !aligned16(k8) || !aligned16(k_scale) ||
-        !aligned16(vq) || !aligned16(v_scale) || !aligned16(out) || (dump && !aligned16(s_out)))
+        !aligned16(vq) || !aligned16(v_scale) || !aligned16(out) || (dump && !aligned16(s_out)) ||
+        (sparse && !aligned16(tmask)))
         return SAGE_ERR_ALIGN;
     sage::AttnArgs a;
     a.q8 = q8;
@@ -103,6 +108,7 @@ int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const 
     a.layout = layout;
     a.out_fp32 = out_dtype == SAGE_OUT_FP32;
     a.qtok = q_gran == SAGE_QGRAN_TOKEN;
+    a.tmask = sparse ? tmask : nullptr;
     a.lambda = (float)((double)sm_scale * 1.4426950408889634);
     a.dbh = dump ? db * H + dh : -1;
     a.drow0 = row0;
@@ -208,7 +214,8 @@ __attribute__((visibility("default"))) int sage_attn_fwd(
     const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
     float sm_scale, int pv_dtype, void* out, int out_dtype, void* stream) {
     return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
-                       pv_dtype, SAGE_QGRAN_BLOCK, out, out_dtype, 0, 0, 0, 0, 1, nullptr, stream);
+                       pv_dtype, SAGE_QGRAN_BLOCK, nullptr, 0, out, out_dtype, 0, 0, 0, 0, 1,
+                       nullptr, stream);
 }
 
 __attribute__((visibility("default"))) int sage_attn_fwd_ex(
@@ -216,7 +223,18 @@ __attribute__((visibility("default"))) int sage_attn_fwd_ex(
     const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
     float sm_scale, int pv_dtype, int q_gran, void* out, int out_dtype, void* stream) {
     return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
-                       pv_dtype, q_gran, out, out_dtype, 0, 0, 0, 0, 1, nullptr, stream);
+                       pv_dtype, q_gran, nullptr, 0, out, out_dtype, 0, 0, 0, 0, 1, nullptr,
+                       stream);
+}
+
+__attribute__((visibility("default"))) int sage_attn_fwd_sparse(
+    const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+    const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
+    float sm_scale, int pv_dtype, int q_gran, const uint8_t* tile_mask, void* out,
+    int out_dtype, void* stream) {
+    return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
+                       pv_dtype, q_gran, tile_mask, 1, out, out_dtype, 0, 0, 0, 0, 1, nullptr,
+                       stream);
 }
 
 __attribute__((visibility("default"))) int sage_attn_fwd_debug(
@@ -225,8 +243,8 @@ __attribute__((visibility("default"))) int sage_attn_fwd_debug(
     float sm_scale, int pv_dtype, void* out, int out_dtype, int b, int h, int row0, int nrows,
     int32_t* s_out, void* stream) {
     return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
-                       pv_dtype, SAGE_QGRAN_BLOCK, out, out_dtype, 1, b, h, row0, nrows, s_out,
-                       stream);
+                       pv_dtype, SAGE_QGRAN_BLOCK, nullptr, 0, out, out_dtype, 1, b, h, row0,
+                       nrows, s_out, stream);
 }
 
 __attribute__((visibility("default"))) const char* sage_status_string(int status) {

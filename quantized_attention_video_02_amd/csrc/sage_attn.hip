@@ -303,14 +303,23 @@ __device__ inline v16i qk_block(const uint8_t* kb, const v4i* qf, int k4, int n,
     return acc;
 }
 
-template <int D, bool PV16, bool CAUSAL, bool DUMP>
+// MODE: kDense, kDump (also writes the int32 Q K^T of one head), kSparse
+// (visits only the key tiles a tile mask selects).
+enum { kDense = 0, kDump = 1, kSparse = 2 };
+
+template <int D, bool PV16, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
+    constexpr bool DUMP = MODE == kDump, SPARSE = MODE == kSparse;
     using L = Lds<D, PV16>;
     using PT = typename std::conditional<PV16, v8h, v8i>::type;
     constexpr int NP = PV16 ? 8 : 2;
     constexpr int KK = D / 32;
     constexpr int CB = D / 32;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[L::TOTAL];
+    // sparse: the key tiles this workgroup visits, ascending; bits 14 / 15 say
+    // whether the first / second 128-query block of the workgroup visits it
+    __shared__ uint16_t vlist[SPARSE ? kMaxSparseTiles : 1];
+    __shared__ int vcount;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
@@ -354,13 +363,44 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<L::VROW, L::VSTR>(64 * (wave + 8 * j) + lane);
     const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
+    // step t of the sweep works on key tile tile_at(t) (every tile when dense)
+    auto tile_at = [&](int t) {
+        return SPARSE ? __builtin_amdgcn_readfirstlane((int)(vlist[t] & 0x3fffu)) : t;
+    };
     auto load_k = [&](int t) {
-        tile_to_lds<L::KPIECES, KMAXP>(kg + (int64_t)t * L::KHBM, lbase + (t & 1) * L::KBYTES, wv,
-                                       koff);
+        tile_to_lds<L::KPIECES, KMAXP>(kg + (int64_t)tile_at(t) * L::KHBM,
+                                       lbase + (t & 1) * L::KBYTES, wv, koff);
     };
     auto load_v = [&](int t) {
-        tile_to_lds<L::VPIECES, VMAXP>(vg + (int64_t)t * L::VHBM,
+        tile_to_lds<L::VPIECES, VMAXP>(vg + (int64_t)tile_at(t) * L::VHBM,
                                        lbase + L::VBASE + (t & 1) * L::VBYTES, wv, voff);
+    };
+    if (SPARSE) {
+        // wave 0 compacts the visited tiles: tile T is visited when either of
+        // the workgroup's two query blocks has a nonzero mask byte for it
+        if (wave == 0) {
+            const int r0 = 2 * qt, nbq = a.nblk;
+            const uint8_t* m0 = a.tmask + ((int64_t)bh * nbq + r0) * a.nblk;
+            const bool has1 = r0 + 1 < nbq;
+            int cnt = 0;
+            for (int base = 0; base < ntiles; base += 64) {
+                const int T = base + lane;
+                int e = 0;
+                if (T < ntiles) e = (m0[T] != 0) | ((has1 && m0[a.nblk + T] != 0) << 1);
+                const uint64_t bal = __ballot(e != 0);
+                const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+                if (e) vlist[pos] = (uint16_t)(T | (e << 14));
+                cnt += __popcll(bal);
+            }
+            if (lane == 0) vcount = cnt;
+        }
+        __syncthreads();
+        ntiles = vcount;
+    }
+    // does this wave's query block visit step t's tile (sparse)?
+    const int vbit = 14 + (wave >= 4);
+    auto wave_visits = [&](int t) {
+        return !SPARSE || ((__builtin_amdgcn_readfirstlane((int)vlist[t]) >> vbit) & 1);
     };
 
     float m = -INFINITY, l = 0.0f;
@@ -384,7 +424,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         uint4* vz = (uint4*)(smem + L::VBASE + L::VBYTES);
         for (int i = tid; i < L::VBYTES / 16; i += kAttnThreads) vz[i] = make_uint4(0, 0, 0, 0);
     }
-    load_k(0);
+    if (!SPARSE || ntiles > 0) load_k(0);
     if (ntiles > 1) load_k(1);
     wait_vmem();
     __syncthreads();
@@ -393,25 +433,32 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     __syncthreads();
 
     const float* ksrow = a.k_scale + bh * a.nblk;
-    float ks = ksrow[0];
+    float ks = (!SPARSE || ntiles > 0) ? ksrow[tile_at(0)] : 0.0f;
     for (int t = 0; t < ntiles; ++t) {
         // the dequantization constant of tile t, taken before this iteration's
         // copies are issued (its load was issued one iteration earlier, so the
         // wait the compiler places before this use does not cover the copies)
         float c = sigma * ks;
         asm volatile("" : "+v"(c));
-        ks = ksrow[min(t + 1, a.nblk - 1)];
+        ks = ksrow[SPARSE ? tile_at(min(t + 1, ntiles - 1)) : min(t + 1, a.nblk - 1)];
+        const int T = tile_at(t);
         if (t + 2 < ntiles) load_k(t + 2);
         load_v(t);
-        const int key_t = t * kBc;
+        const int key_t = T * kBc;
         if (DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows)
             dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
         // A
         pv_tile<D>(smem + L::VBASE + ((t + 1) & 1) * L::VBYTES, P, O, alpha, n, hh);
-        const bool needmask = (tail && t == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase);
+        // a tile this wave's query block does not visit is masked whole: with
+        // p = 0 and alpha = 1 it changes nothing, as if never seen
+        const bool visits = wave_visits(t);
+        const bool needmask = (tail && T == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase) ||
+                              !visits;
         v16f F[4];
         float mu;
-        softmax_prep(S, F, c, m, alpha, mu, needmask, kmax - key_t - 4 * hh);
+        softmax_prep(S, F, c, m, alpha, mu, needmask, visits ? kmax - key_t - 4 * hh : -1);
+        // no key seen yet (m = -inf): any finite mu keeps p = exp2(-inf) = 0
+        if (SPARSE && m == -INFINITY) mu = 0.0f;
         const float cf = c == 0.0f ? 1.0f : c;
         // B (the Q K^T of "tile ntiles" reads a stale buffer; its result is unused)
         const uint8_t* kb = smem + ((t + 1) & 1) * L::KBYTES;
@@ -439,7 +486,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
             const int c0 = 32 * cb + 8 * r4 + 4 * hh;
             float o[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = (O[cb][4 * r4 + j] * vs[c0 + j]) / lt;
+            for (int j = 0; j < 4; ++j)
+                o[j] = (SPARSE && !(lt > 0.0f)) ? 0.0f : (O[cb][4 * r4 + j] * vs[c0 + j]) / lt;
             if (a.out_fp32) {
                 *(float4*)((float*)a.out + obase + c0) = make_float4(o[0], o[1], o[2], o[3]);
             } else {
@@ -450,22 +498,29 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         }
 }
 
-template <int D, bool PV16, bool CAUSAL, bool DUMP>
+template <int D, bool PV16, bool CAUSAL, int MODE>
 static const void* attn_fn() {
-    return (const void*)attn_fwd_kernel<D, PV16, CAUSAL, DUMP>;
+    return (const void*)attn_fwd_kernel<D, PV16, CAUSAL, MODE>;
+}
+
+template <int D, bool PV16, int MODE>
+static const void* attn_fn_rt(bool causal) {
+    return causal ? attn_fn<D, PV16, true, MODE>() : attn_fn<D, PV16, false, MODE>();
 }
 
 template <int D, bool PV16>
-static const void* attn_fn_rt(bool causal, bool dump) {
-    if (causal) return dump ? attn_fn<D, PV16, true, true>() : attn_fn<D, PV16, true, false>();
-    return dump ? attn_fn<D, PV16, false, true>() : attn_fn<D, PV16, false, false>();
+static const void* attn_fn_rt(bool causal, int mode) {
+    if (mode == kDump) return attn_fn_rt<D, PV16, kDump>(causal);
+    if (mode == kSparse) return attn_fn_rt<D, PV16, kSparse>(causal);
+    return attn_fn_rt<D, PV16, kDense>(causal);
 }
 
 hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal, int dump,
                        hipStream_t s) {
+    const int mode = dump ? kDump : (args.tmask ? kSparse : kDense);
     const void* fn;
-    if (d == 128) fn = pv16 ? attn_fn_rt<128, true>(causal, dump) : attn_fn_rt<128, false>(causal, dump);
-    else fn = pv16 ? attn_fn_rt<64, true>(causal, dump) : attn_fn_rt<64, false>(causal, dump);
+    if (d == 128) fn = pv16 ? attn_fn_rt<128, true>(causal, mode) : attn_fn_rt<128, false>(causal, mode);
+    else fn = pv16 ? attn_fn_rt<64, true>(causal, mode) : attn_fn_rt<64, false>(causal, mode);
     AttnArgs a = args;
     void* kargs[] = {(void*)&a};
     return hipLaunchKernel(fn, dim3(a.total), dim3(kAttnThreads), kargs, 0, s);

@@ -18,6 +18,7 @@ constexpr int kBlk = 128;          // rows per Q / K quantization block
 constexpr int kBc = 128;           // keys per online-softmax tile (== kBlk)
 constexpr int kBr = 256;           // queries per attention workgroup (8 waves x 32)
 constexpr int kAttnThreads = 512;  // 8 wave64s
+constexpr int kMaxSparseTiles = 4096;  // key tiles a sparse launch may list (N <= 524288)
 constexpr int kStatsChunk = 512;   // tokens per statistics workgroup
 constexpr int kQuantThreads = 256;
 constexpr float kPScale = 448.0f;
@@ -61,6 +62,7 @@ struct AttnArgs {
     int32_t* s_out;  // debug dump (dump instantiations only)
     int H, N, N_pad, nblk, nqt, total, layout, out_fp32;
     int qtok;  // 1: q_scale per query row [bh][N_pad]; 0: per block of kBlk rows [bh][nblk]
+    const uint8_t* tmask;  // NULL (dense) or [B*H][nblk][nblk]: query block x key tile, nonzero = visit
     float lambda;    // fp32(sm_scale * log2 e)
     int dbh, drow0, dnrows;
 };

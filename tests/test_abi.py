@@ -133,6 +133,13 @@ def test_invalid_arguments_rejected_before_launch(sage):
                                                   g, A, 0, None)
     assert fwdx(g=3) == -2
     assert fwdx(sm=-2.0) == -2
+    sp = lambda tm=A, N=256, g=0: L.sage_attn_fwd_sparse(A, A, A, A, A, A, 1, 2, N, 128, 0, 0, 0.1,
+                                                         0, g, tm, A, 0, None)
+    assert sp(tm=None) == -1
+    assert sp(tm=A + 3) == -4
+    assert sp(g=5) == -2
+    assert sp(N=4096 * 128 + 1) == -5      # more key tiles than a sparse launch can list
+    assert sp(N=4096 * 128, tm=A + 3) == -4   # the size passes; validation stops at alignment
     dbg = lambda b=0, h=0, row0=0, nrows=4, s=A: L.sage_attn_fwd_debug(
         A, A, A, A, A, A, 1, 2, 256, 128, 0, 0, 0.1, 0, A, 0, b, h, row0, nrows, s, None)
     assert dbg(s=None) == -1

@@ -393,3 +393,104 @@ def test_per_token_q_full_size_sampled(sage, orc, name, pv):
     assert abs(c_gpu - c_or) < 2e-4, (c_gpu, c_or)
     if name != "outlier":
         assert c_gpu >= COS_FP64, c_gpu
+
+
+# ------------------------------------------------------ block-sparse tile skipping
+def make_tile_mask(B, H, N, kind, seed=0, keep=0.5):
+    """uint8 [B, H, nblk, nblk] (query block x key tile, nonzero = visit)."""
+    nb = -(-N // 128)
+    rng = np.random.default_rng(seed)
+    i, j = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    if kind == "ones":
+        m = np.ones((B, H, nb, nb), bool)
+    elif kind == "random":
+        m = rng.random((B, H, nb, nb)) < keep
+    elif kind == "band":                       # a local window plus the first tile
+        m = np.broadcast_to((np.abs(i - j) <= 1) | (j == 0), (B, H, nb, nb)).copy()
+    elif kind == "split":                      # the two query blocks of a workgroup differ
+        m = np.broadcast_to(((i % 2 == 0) & (j % 2 == 0)) | ((i % 2 == 1) & (j % 3 == 1)),
+                            (B, H, nb, nb)).copy()
+    elif kind == "empty_rows":                 # some query blocks visit nothing at all
+        m = rng.random((B, H, nb, nb)) < keep
+        m[:, :, 1] = False
+        m[:, :, -1] = False
+    else:
+        raise ValueError(kind)
+    return m.astype(np.uint8)
+
+
+SPARSE_CASES = [
+    ("tiny", dict(N=1000, H=2), "fp8", "HND", "random", "block"),
+    ("tiny", dict(N=1000, H=2), "fp8", "HND", "ones", "block"),
+    ("tiny", dict(N=700, H=1), "fp16", "NHD", "random", "block"),
+    ("tiny", dict(N=1000, H=2), "fp8", "HND", "empty_rows", "block"),
+    ("tiny", dict(N=900, H=2), "fp8", "HND", "split", "token"),
+    ("causal_prefill", dict(B=2, H=1, N=900), "fp8", "HND", "random", "block"),
+    ("causal_prefill", dict(B=1, H=2, N=1000), "fp8", "NHD", "band", "block"),
+    ("outlier", dict(B=1, H=2, N=1100), "fp8", "HND", "band", "block"),
+]
+
+
+@pytest.mark.parametrize("name,kw,pv,layout,kind,q_gran", SPARSE_CASES)
+def test_sparse_matches_oracle(sage, orc, name, kw, pv, layout, kind, q_gran):
+    """sage_attn_fwd_sparse against the oracle run with the same tile mask;
+    an all-ones mask reproduces the dense kernel bit for bit; query blocks
+    that visit nothing get exact zeros."""
+    wl = si.make(name, **kw)
+    mask = make_tile_mask(wl.B, wl.H, wl.N, kind, seed=7)
+    qd, kd, vd = (_to_layout(t, layout).cuda() for t in (wl.q, wl.k, wl.v))
+    qz = sage.quant_qk(qd, kd, layout, q_gran=q_gran)
+    vq, vs = sage.quant_v(vd, pv, layout)
+    out = sage.attn_fwd(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale, pv=pv,
+                        out_dtype=torch.float32, tile_mask=torch.from_numpy(mask).cuda())
+    dense = sage.attn_fwd(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale, pv=pv,
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out, dense = to_hnd(out, layout).cpu().numpy(), to_hnd(dense, layout).cpu().numpy()
+    q, k, v = codes(wl.q), codes(wl.k), codes(wl.v)
+    oz = orc.quant_qk(q, k, q_gran=q_gran)
+    ovq, ovs = orc.quant_v(v, pv)
+    rows = np.arange(wl.N)
+    o_or = np.stack([np.stack([orc.attn_rows_head(oz, ovq, ovs, b, h, rows, wl.causal, wl.sm_scale,
+                                                  pv, tile_mask=mask)
+                               for h in range(wl.H)]) for b in range(wl.B)])
+    assert np.isfinite(out).all()
+    err, c = np.abs(out - o_or).max(), _cos(out, o_or)
+    assert err <= MAX_ABS and c >= COS_ORACLE, (err, c)
+    if kind == "ones":
+        assert np.array_equal(out, dense)
+    empty = o_or.reshape(wl.B, wl.H, wl.N, -1).any(axis=-1) == 0
+    assert not out[empty].any()
+    if kind == "empty_rows":
+        assert empty.any()
+
+
+def test_sparse_full_size_sampled(sage, orc):
+    """video_14b_720p with a band-plus-random tile mask (about 1/4 of the
+    tiles), in the benchmark's launch configuration, on sampled heads/rows."""
+    print("[full-size sparse parity] video_14b_720p pv=fp8", flush=True)
+    wl = si.make("video_14b_720p", device="cuda")
+    mask = make_tile_mask(wl.B, wl.H, wl.N, "random", seed=3, keep=0.2)
+    mask |= make_tile_mask(wl.B, wl.H, wl.N, "band")
+    qz = sage.quant_qk(wl.q, wl.k)
+    vq, vs = sage.quant_v(wl.v, "fp8")
+    out = sage.attn_fwd(qz, vq, vs, sm_scale=wl.sm_scale, out_dtype=torch.float32,
+                        tile_mask=torch.from_numpy(mask).cuda())
+    torch.cuda.synchronize()
+    heads = [(0, 0), (0, wl.H - 1)]
+    rng = np.random.default_rng(4)
+    qa, ka, va = codes(wl.q.cpu()), codes(wl.k.cpu()), codes(wl.v.cpu())
+    o_all, or_all = [], []
+    for b, h in heads:
+        q, k, v = (x[b, h][None, None] for x in (qa, ka, va))
+        oz = orc.quant_qk(q, k)
+        ovq, ovs = orc.quant_v(v, "fp8")
+        rows = sample_rows(wl, b, h, rng)
+        o_or = orc.attn_rows_head(oz, ovq, ovs, 0, 0, rows, False, wl.sm_scale, "fp8",
+                                  tile_mask=mask[b:b + 1, h:h + 1])
+        o_all.append(out[b, h, torch.from_numpy(rows).long().cuda()].cpu().numpy())
+        or_all.append(o_or)
+    o_gpu, o_or = np.concatenate(o_all), np.concatenate(or_all)
+    err, c = np.abs(o_gpu - o_or).max(), _cos(o_gpu, o_or)
+    print(f"  max-abs {err:.3e} cos(oracle) {c:.7f} kept {mask.mean():.3f} of the tiles")
+    assert err <= MAX_ABS and c >= COS_ORACLE, (err, c)
