@@ -52,7 +52,36 @@ def attn_ops(B, H, N, d):
     return 4.0 * B * H * N * N * d
 
 
-def time_gpu(sage, wl, pv, steps, warmup, q_gran="block"):
+def tile_mask_for(wl, keep, seed=11):
+    """A seeded block-sparse tile mask (query block x key tile): each tile is
+    kept with probability `keep`, plus a local band (|i - j| <= 1) and the
+    first key tile, the shape of a sliding-window-plus-sink pattern."""
+    import numpy as np
+
+    nb = -(-wl.N // 128)
+    rng = np.random.default_rng(seed)
+    i, j = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    m = rng.random((wl.B, wl.H, nb, nb)) < keep
+    m |= ((np.abs(i - j) <= 1) | (j == 0))[None, None]
+    if wl.causal:
+        m &= (j <= i)[None, None]
+    return m.astype(np.uint8)
+
+
+def visited_ops(wl, mask):
+    """Algorithmic work of a sparse launch: 4 d ops per visited (query, key)
+    pair (causal: pairs with key <= query)."""
+    import numpy as np
+
+    nb = mask.shape[-1]
+    sizes = np.minimum(128, wl.N - 128 * np.arange(nb)).astype(np.float64)
+    pairs = sizes[:, None] * sizes[None, :]
+    if wl.causal:  # diagonal tiles hold s (s + 1) / 2 causal pairs
+        pairs[np.arange(nb), np.arange(nb)] = sizes * (sizes + 1) / 2
+    return 4.0 * wl.d * float((mask.astype(np.float64) * pairs).sum())
+
+
+def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None):
     import torch
 
     q, k, v = wl.q, wl.k, wl.v
@@ -65,7 +94,8 @@ def time_gpu(sage, wl, pv, steps, warmup, q_gran="block"):
         vq, vs = sage.quant_v(v, pv)
         if evs:
             evs[1].record(stream)
-        out = sage.attn_fwd(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale, pv=pv)
+        out = sage.attn_fwd(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale, pv=pv,
+                            tile_mask=tile_mask)
         if evs:
             evs[2].record(stream)
         return out
@@ -173,6 +203,9 @@ def main():
     ap.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
     ap.add_argument("--q-gran", default="block", choices=["block", "token"],
                     help="Q scale granularity: per block of 128 queries, or per query row")
+    ap.add_argument("--tile-keep", type=float, default=None,
+                    help="block-sparse run: keep each (query block, key tile) with this "
+                         "probability, plus a local band and the first tile")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -209,15 +242,22 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    wall, quant_ms, attn_ms = time_gpu(sage, wl, args.pv, args.steps, args.warmup, args.q_gran)
+    tmask = None
+    if args.tile_keep is not None:
+        mask_np = tile_mask_for(wl, args.tile_keep)
+        tmask = torch.from_numpy(mask_np).cuda()
+    wall, quant_ms, attn_ms = time_gpu(sage, wl, args.pv, args.steps, args.warmup, args.q_gran,
+                                       tmask)
     ops = attn_ops(wl.B, wl.H, wl.N, wl.d)
+    # roofline work: all pairs when dense; the visited pairs of a sparse run
+    work = ops if tmask is None else visited_ops(wl, mask_np)
     ms_per_step = wall * 1e3 / args.steps
     attn_mean = sum(attn_ms) / len(attn_ms)
     srt = sorted(attn_ms)
     attn_med = srt[len(srt) // 2]
     attn_iqr = srt[(3 * len(srt)) // 4] - srt[len(srt) // 4]
     quant_mean = sum(quant_ms) / len(quant_ms)
-    achieved = ops / (attn_mean * 1e-3) / 1e12
+    achieved = work / (attn_mean * 1e-3) / 1e12
     peak = PEAK_TOPS[args.pv]
     bhnd = wl.B * wl.H * wl.N * wl.d
     traffic = None
@@ -244,15 +284,21 @@ def main():
                    "parallelism": "none"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "attn_fwd_kernel", "ops_per_launch": ops,
+                     "kernel": "attn_fwd_kernel", "ops_per_launch": work,
                      "mean_launch_ms": attn_mean, "median_launch_ms": attn_med,
                      "iqr_launch_ms": attn_iqr,
-                     "median_tops": ops / (attn_med * 1e-3) / 1e12},
+                     "median_tops": work / (attn_med * 1e-3) / 1e12},
         "quant": {"ms": quant_mean, "bytes_two_pass": 13 * bhnd,
                   "gbps_two_pass": 13 * bhnd / (quant_mean * 1e-3) / 1e9,
                   "frac_hbm": 13 * bhnd / (quant_mean * 1e-3) / 1e9 / HBM_GBPS},
     }
-    if wl.causal:
+    if tmask is not None:
+        # value stays the metric's formula over all N^2 pairs (dense-equivalent);
+        # the roofline counts the visited pairs only
+        res["config"]["tile_keep"] = float(mask_np.mean())
+        res["config"]["value_is"] = "dense-equivalent (4 B H N^2 d / s) of a block-sparse run"
+        res["roofline"]["traffic"] = None
+    if wl.causal and tmask is None:
         # the formula above counts every (query, key) pair; the causal mask keeps N(N+1)/2
         useful = 4.0 * wl.B * wl.H * wl.d * wl.N * (wl.N + 1) / 2
         res["roofline"]["useful_causal_ops_per_launch"] = useful

@@ -363,16 +363,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<L::VROW, L::VSTR>(64 * (wave + 8 * j) + lane);
     const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    // step t of the sweep works on key tile tile_at(t) (every tile when dense)
-    auto tile_at = [&](int t) {
-        return SPARSE ? __builtin_amdgcn_readfirstlane((int)(vlist[t] & 0x3fffu)) : t;
+    // step t of the sweep works on key tile T (every tile when dense: T = t);
+    // the tile goes to LDS slot t & 1
+    auto load_k = [&](int t, int T) {
+        tile_to_lds<L::KPIECES, KMAXP>(kg + (int64_t)T * L::KHBM, lbase + (t & 1) * L::KBYTES, wv,
+                                       koff);
     };
-    auto load_k = [&](int t) {
-        tile_to_lds<L::KPIECES, KMAXP>(kg + (int64_t)tile_at(t) * L::KHBM,
-                                       lbase + (t & 1) * L::KBYTES, wv, koff);
-    };
-    auto load_v = [&](int t) {
-        tile_to_lds<L::VPIECES, VMAXP>(vg + (int64_t)tile_at(t) * L::VHBM,
+    auto load_v = [&](int t, int T) {
+        tile_to_lds<L::VPIECES, VMAXP>(vg + (int64_t)T * L::VHBM,
                                        lbase + L::VBASE + (t & 1) * L::VBYTES, wv, voff);
     };
     if (SPARSE) {
@@ -397,11 +395,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         __syncthreads();
         ntiles = vcount;
     }
-    // does this wave's query block visit step t's tile (sparse)?
+    // sparse: list entries of steps t, t+1, t+2 in scalar registers; the entry
+    // of step t+3 is read from LDS early in step t and shifted in at its end,
+    // so no list read sits on the path to a copy's address
     const int vbit = 14 + (wave >= 4);
-    auto wave_visits = [&](int t) {
-        return !SPARSE || ((__builtin_amdgcn_readfirstlane((int)vlist[t]) >> vbit) & 1);
+    auto entry = [&](int t) {
+        return (SPARSE && t < ntiles) ? __builtin_amdgcn_readfirstlane((int)vlist[t]) : 0;
     };
+    int e0 = entry(0), e1 = entry(1), e2 = entry(2);
 
     float m = -INFINITY, l = 0.0f;
     float alpha = 1.0f;  // alpha of the tile whose P is held (tile -1: P = 0, alpha = 1)
@@ -424,8 +425,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         uint4* vz = (uint4*)(smem + L::VBASE + L::VBYTES);
         for (int i = tid; i < L::VBYTES / 16; i += kAttnThreads) vz[i] = make_uint4(0, 0, 0, 0);
     }
-    if (!SPARSE || ntiles > 0) load_k(0);
-    if (ntiles > 1) load_k(1);
+    if (!SPARSE || ntiles > 0) load_k(0, SPARSE ? (e0 & 0x3fff) : 0);
+    if (ntiles > 1) load_k(1, SPARSE ? (e1 & 0x3fff) : 1);
     wait_vmem();
     __syncthreads();
 #pragma unroll
@@ -433,17 +434,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     __syncthreads();
 
     const float* ksrow = a.k_scale + bh * a.nblk;
-    float ks = (!SPARSE || ntiles > 0) ? ksrow[tile_at(0)] : 0.0f;
+    float ks = (!SPARSE || ntiles > 0) ? ksrow[SPARSE ? (e0 & 0x3fff) : 0] : 0.0f;
     for (int t = 0; t < ntiles; ++t) {
         // the dequantization constant of tile t, taken before this iteration's
         // copies are issued (its load was issued one iteration earlier, so the
         // wait the compiler places before this use does not cover the copies)
         float c = sigma * ks;
         asm volatile("" : "+v"(c));
-        ks = ksrow[SPARSE ? tile_at(min(t + 1, ntiles - 1)) : min(t + 1, a.nblk - 1)];
-        const int T = tile_at(t);
-        if (t + 2 < ntiles) load_k(t + 2);
-        load_v(t);
+        const int T = SPARSE ? (e0 & 0x3fff) : t;
+        ks = ksrow[SPARSE ? (t + 1 < ntiles ? (e1 & 0x3fff) : T) : min(t + 1, a.nblk - 1)];
+        const uint32_t e3raw = (SPARSE && t + 3 < ntiles) ? vlist[t + 3] : 0u;
+        if (t + 2 < ntiles) load_k(t + 2, SPARSE ? (e2 & 0x3fff) : t + 2);
+        load_v(t, T);
         const int key_t = T * kBc;
         if (DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows)
             dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         pv_tile<D>(smem + L::VBASE + ((t + 1) & 1) * L::VBYTES, P, O, alpha, n, hh);
         // a tile this wave's query block does not visit is masked whole: with
         // p = 0 and alpha = 1 it changes nothing, as if never seen
-        const bool visits = wave_visits(t);
+        const bool visits = !SPARSE || ((e0 >> vbit) & 1);
         const bool needmask = (tail && T == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase) ||
                               !visits;
         v16f F[4];
@@ -469,6 +471,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
             part[k4] = softmax_block(F[k4], P, k4, cf, mu);
         }
         l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
+        if (SPARSE) {
+            e0 = e1;
+            e1 = e2;
+            e2 = __builtin_amdgcn_readfirstlane((int)e3raw);
+        }
         wait_vmem();
         __syncthreads();
     }

@@ -61,6 +61,27 @@ def test_algorithmic_ops_count():
     assert bench.attn_ops(2, 3, 5, 64) == 4 * 2 * 3 * 25 * 64
 
 
+def test_visited_ops_closed_forms():
+    import numpy as np
+
+    import synthetic_inputs as si
+
+    wl = si.make("tiny", N=300)
+    full = np.ones((1, 2, 3, 3), np.uint8)
+    assert bench.visited_ops(wl, full) == bench.attn_ops(1, 2, 300, 128)   # ragged tiles
+    half = full.copy()
+    half[:, :, :, 1] = 0                                                   # drop key tile 1
+    assert bench.visited_ops(wl, half) == 4 * 128 * 2 * 300 * (300 - 128)
+    wc = si.make("causal_prefill", B=1, H=1, N=300)
+    m = bench.tile_mask_for(wc, 1.0)
+    assert m.shape == (1, 1, 3, 3) and not np.triu(m[0, 0], 1).any()      # nothing above the diagonal
+    assert bench.visited_ops(wc, m) == 4 * 128 * 300 * 301 / 2            # N (N + 1) / 2 pairs
+    wl = si.make("tiny")
+    m = bench.tile_mask_for(wl, 0.0)                                       # band + first tile only
+    i, j = np.meshgrid(np.arange(8), np.arange(8), indexing="ij")
+    assert np.array_equal(m[0, 0].astype(bool), (abs(i - j) <= 1) | (j == 0))
+
+
 def test_source_hash_covers_the_kernel_sources():
     h = bench.attn_source_hash()
     assert len(h) == 16 and all(os.path.exists(f) for f in bench.ATTN_SOURCES)
