@@ -50,18 +50,41 @@ __global__ __launch_bounds__(kQuantThreads) void k_stats_kernel(const u16* __res
     uint64_t acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0;
+    // Fast path: while every value of a load has |x| < 2^18, each term
+    // trunc(x 2^30) is an integer below 2^48 and the fp64 chain
+    // bf16 -> fp32 -> fp64, * 2^30, trunc, + is exact; a thread adds at most
+    // 512 / RPI <= 32 such terms per channel, below 2^53, so its fp64 sum is the
+    // exact integer.  Loads holding larger values, infinities or NaNs take
+    // the integer path (saturation, NaN -> 0), the same function of the data.
+    double accd[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) accd[e] = 0.0;
+    static_assert(kStatsChunk / RPI <= 32, "fp64 partial sums must stay below 2^53");
 #pragma unroll 4
     for (int n = n0 + tr; n < n1; n += RPI) {
         const uint4 w = *(const uint4*)(k + row_offset(layout, b, h, n, H, N, D) + cg * 8);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        bool big = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += fix30_bf16(ws[e] & 0xffffu);
-            acc[2 * e + 1] += fix30_bf16(ws[e] >> 16);
+        for (int e = 0; e < 4; ++e)
+            big |= ((ws[e] & 0x7fffu) >= 0x4880u) | (((ws[e] >> 16) & 0x7fffu) >= 0x4880u);
+        if (!big) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                accd[2 * e] += __builtin_trunc((double)__uint_as_float(ws[e] << 16) * 1073741824.0);
+                accd[2 * e + 1] += __builtin_trunc((double)__uint_as_float(ws[e] & 0xffff0000u) *
+                                                   1073741824.0);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += fix30_bf16(ws[e] & 0xffffu);
+                acc[2 * e + 1] += fix30_bf16(ws[e] >> 16);
+            }
         }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[tr][cg * 8 + e] = acc[e];
+    for (int e = 0; e < 8; ++e) red[tr][cg * 8 + e] = acc[e] + (uint64_t)(int64_t)accd[e];
     __syncthreads();
     if (t < D) {
         uint64_t s = 0;
@@ -71,14 +94,26 @@ __global__ __launch_bounds__(kQuantThreads) void k_stats_kernel(const u16* __res
     }
 }
 
-__global__ void k_mean_kernel(const uint64_t* __restrict__ part, int nchunk, int D, int total,
-                              int N, float* __restrict__ mean) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total) return;
-    const int bh = i / D, c = i % D;
+// Combination kernels: workgroup (b*h, group of 32 channels), 256 threads =
+// 32 channels x 8 chunk lanes; lane j adds chunks j, j + 8, ... (coalesced
+// across the 32 channels), then the 8 lane results are combined in LDS.
+constexpr int kCombCh = 32, kCombLanes = kQuantThreads / kCombCh;
+
+__global__ __launch_bounds__(kQuantThreads) void k_mean_kernel(const uint64_t* __restrict__ part,
+                                                               int nchunk, int D, int N,
+                                                               float* __restrict__ mean) {
+    __shared__ uint64_t red[kCombLanes][kCombCh];
+    const int bh = blockIdx.x, c = blockIdx.y * kCombCh + threadIdx.x % kCombCh;
+    const int j = threadIdx.x / kCombCh;
     uint64_t s = 0;
-    for (int ch = 0; ch < nchunk; ++ch) s += part[((int64_t)bh * nchunk + ch) * D + c];
-    mean[i] = (float)((double)(int64_t)s / ((double)N * 1073741824.0));
+    for (int ch = j; ch < nchunk; ch += kCombLanes) s += part[((int64_t)bh * nchunk + ch) * D + c];
+    red[j][threadIdx.x % kCombCh] = s;
+    __syncthreads();
+    if (j == 0) {
+#pragma unroll
+        for (int r = 1; r < kCombLanes; ++r) s += red[r][threadIdx.x];
+        mean[bh * D + c] = (float)((double)(int64_t)s / ((double)N * 1073741824.0));
+    }
 }
 
 template <int D>
@@ -115,15 +150,25 @@ __global__ __launch_bounds__(kQuantThreads) void v_stats_kernel(const u16* __res
 }
 
 // v_scale = fp32(a / 448); inv = fp32(448 / a) (0 for a == 0), both via fp64.
-__global__ void v_scale_kernel(const float* __restrict__ part, int nchunk, int D, int total,
-                               float* __restrict__ v_scale, float* __restrict__ v_inv) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total) return;
-    const int bh = i / D, c = i % D;
+__global__ __launch_bounds__(kQuantThreads) void v_scale_kernel(const float* __restrict__ part,
+                                                                int nchunk, int D,
+                                                                float* __restrict__ v_scale,
+                                                                float* __restrict__ v_inv) {
+    __shared__ float red[kCombLanes][kCombCh];
+    const int bh = blockIdx.x, c = blockIdx.y * kCombCh + threadIdx.x % kCombCh;
+    const int j = threadIdx.x / kCombCh;
     float a = 0.0f;
-    for (int ch = 0; ch < nchunk; ++ch) a = fmaxf(a, part[((int64_t)bh * nchunk + ch) * D + c]);
-    v_scale[i] = (float)((double)a / 448.0);
-    v_inv[i] = a > 0.0f ? (float)(448.0 / (double)a) : 0.0f;
+    for (int ch = j; ch < nchunk; ch += kCombLanes)
+        a = fmaxf(a, part[((int64_t)bh * nchunk + ch) * D + c]);
+    red[j][threadIdx.x % kCombCh] = a;
+    __syncthreads();
+    if (j == 0) {
+#pragma unroll
+        for (int r = 1; r < kCombLanes; ++r) a = fmaxf(a, red[r][threadIdx.x]);
+        const int i = bh * D + c;
+        v_scale[i] = (float)((double)a / 448.0);
+        v_inv[i] = a > 0.0f ? (float)(448.0 / (double)a) : 0.0f;
+    }
 }
 
 // One block of 128 rows of Q (blockIdx.z == 0) or of smoothed K (z == 1).
@@ -334,7 +379,7 @@ hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int 
                            uint64_t* ws, hipStream_t s) {
     const int nblk = (N + kBlk - 1) / kBlk, N_pad = nblk * kBlk;
     const int nchunk = (N + kStatsChunk - 1) / kStatsChunk;
-    const int BH = B * H, total = BH * d;
+    const int BH = B * H;
     hipError_t e;
     {
         void* args[] = {(void*)&k, (void*)&H, (void*)&N, (void*)&layout, (void*)&nchunk, (void*)&ws};
@@ -342,9 +387,9 @@ hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int 
         if ((e = launch(fn, dim3(nchunk, BH), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
     }
     {
-        void* args[] = {(void*)&ws, (void*)&nchunk, (void*)&d, (void*)&total, (void*)&N, (void*)&kmean};
-        if ((e = launch((const void*)k_mean_kernel, dim3((total + 255) / 256), dim3(256), args, s)) !=
-            hipSuccess)
+        void* args[] = {(void*)&ws, (void*)&nchunk, (void*)&d, (void*)&N, (void*)&kmean};
+        if ((e = launch((const void*)k_mean_kernel, dim3(BH, d / kCombCh), dim3(kQuantThreads), args,
+                        s)) != hipSuccess)
             return e;
     }
     {
@@ -362,7 +407,7 @@ hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, 
                           void* vq, float* vscale, float* ws, hipStream_t s) {
     const int nblk = (N + kBc - 1) / kBc;
     const int nchunk = (N + kStatsChunk - 1) / kStatsChunk;
-    const int BH = B * H, total = BH * d;
+    const int BH = B * H;
     hipError_t e;
     if (pv16) {
         void* args[] = {(void*)&v, (void*)&H, (void*)&N, (void*)&nblk, (void*)&layout, (void*)&vq,
@@ -379,10 +424,9 @@ hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, 
         if ((e = launch(fn, dim3(nchunk, BH), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
     }
     {
-        void* args[] = {(void*)&part, (void*)&nchunk, (void*)&d, (void*)&total, (void*)&vscale,
-                        (void*)&vinv};
-        if ((e = launch((const void*)v_scale_kernel, dim3((total + 255) / 256), dim3(256), args, s)) !=
-            hipSuccess)
+        void* args[] = {(void*)&part, (void*)&nchunk, (void*)&d, (void*)&vscale, (void*)&vinv};
+        if ((e = launch((const void*)v_scale_kernel, dim3(BH, d / kCombCh), dim3(kQuantThreads), args,
+                        s)) != hipSuccess)
             return e;
     }
     {

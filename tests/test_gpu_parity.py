@@ -494,3 +494,23 @@ def test_sparse_full_size_sampled(sage, orc):
     err, c = np.abs(o_gpu - o_or).max(), _cos(o_gpu, o_or)
     print(f"  max-abs {err:.3e} cos(oracle) {c:.7f} kept {mask.mean():.3f} of the tiles")
     assert err <= MAX_ABS and c >= COS_ORACLE, (err, c)
+
+
+def test_k_mean_exact_with_large_and_special_values(sage, orc):
+    """The K statistics take an fp64 fast path while every value of a load is
+    below 2^18 and the saturating integer path otherwise: mix both (large
+    finite values, +-inf, NaN) into some rows; the K mean stays bit-exact."""
+    wl = si.make("tiny", N=1500, H=2, seed=23)
+    k = codes(wl.k).copy()
+    rng = np.random.default_rng(5)
+    specials = np.array([0x4880, 0xC880, 0x4F00, 0xCF00, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80, 0x7FC1,
+                         0x4A00, 0x0001, 0x8001], np.uint16)
+    rows = rng.choice(wl.N, 40, replace=False)
+    for i, r in enumerate(rows):
+        k[0, i % 2, r, rng.integers(0, 128, 3)] = specials[i % len(specials)]
+    kt = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).cuda()
+    qz = sage.quant_qk(wl.q.cuda(), kt)
+    torch.cuda.synchronize()
+    got = qz["k_mean"].cpu().numpy()
+    ref = np.stack([orc.k_mean_head(k[0, h]) for h in range(2)])[None]
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
