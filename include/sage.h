@@ -224,9 +224,9 @@ int sage_attn_fwd_ex(const int8_t* q8, const float* q_scale, const int8_t* k8,
  * the block's rows runs over the visited tiles in ascending order, exactly as
  * if the skipped tiles' keys were masked; with causal, keys after the query
  * stay masked as well.  A row that visits no key gets the output 0.
- * A workgroup (256 queries) loads and computes only the tiles that one of its
- * two query blocks visits.  Requires nblk <= 4096 (N <= 524288; else
- * SAGE_ERR_SIZE); tile_mask 16-byte aligned.
+ * A workgroup (one query block; two with FP16 P V at d = 128) loads and
+ * computes only the tiles its block(s) visit.  Requires nblk <= 2048
+ * (N <= 262144; else SAGE_ERR_SIZE); tile_mask 16-byte aligned.
  */
 int sage_attn_fwd_sparse(const int8_t* q8, const float* q_scale, const int8_t* k8,
                          const float* k_scale, const void* vq, const float* v_scale, int B, int H,

@@ -103,8 +103,8 @@ int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const 
     a.N = N;
     a.nblk = (N + sage::kBlk - 1) / sage::kBlk;
     a.N_pad = a.nblk * sage::kBlk;
-    a.nqt = (N + sage::kBr - 1) / sage::kBr;
-    a.total = B * H * a.nqt;
+    // a.nqt / a.total (workgroups per head / in all) are set by the launcher,
+    // which knows the workgroup size of the variant it picks
     a.layout = layout;
     a.out_fp32 = out_dtype == SAGE_OUT_FP32;
     a.qtok = q_gran == SAGE_QGRAN_TOKEN;

@@ -102,12 +102,12 @@ __device__ inline void dma_piece(const uint8_t* gbase, uint32_t voff, uint32_t l
         : "memory", "m0");
 }
 
-// This wave's pieces of a tile: piece J = wave + 8 j.  g and l are uniform.
-template <int NPIECES, int MAXP>
+// This wave's pieces of a tile: piece J = wave + NW j.  g and l are uniform.
+template <int NPIECES, int MAXP, int NW>
 __device__ inline void tile_to_lds(const uint8_t* g, uint32_t l, int wave, const int* off) {
 #pragma unroll
     for (int j = 0; j < MAXP; ++j) {
-        const int J = wave + 8 * j;
+        const int J = wave + NW * j;
         if (J < NPIECES) dma_piece(g, (uint32_t)off[j], l + 1024u * J);
     }
 }
@@ -307,9 +307,20 @@ __device__ inline v16i qk_block(const uint8_t* kb, const v4i* qf, int k4, int n,
 // (visits only the key tiles a tile mask selects).
 enum { kDense = 0, kDump = 1, kSparse = 2 };
 
+// Waves per workgroup: 8 (256 queries, one workgroup per CU), or 4 (128
+// queries = one query block, two workgroups per CU) for the sparse sweep, so
+// that a workgroup's tile list is its own block's and no wave computes tiles
+// its block skips (FP16 P V at d = 128 keeps 8: its LDS fits one per CU).
+template <int D, bool PV16, int MODE>
+constexpr int attn_waves() {
+    return (MODE == kSparse && !(PV16 && D == 128)) ? 4 : 8;
+}
+
 template <int D, bool PV16, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__((64 * attn_waves<D, PV16, MODE>()), (8 / attn_waves<D, PV16, MODE>()))
+void attn_fwd_kernel(AttnArgs a) {
     constexpr bool DUMP = MODE == kDump, SPARSE = MODE == kSparse;
+    constexpr int NW = attn_waves<D, PV16, MODE>(), NT = 64 * NW, BR = 32 * NW;
     using L = Lds<D, PV16>;
     using PT = typename std::conditional<PV16, v8h, v8i>::type;
     constexpr int NP = PV16 ? 8 : 2;
@@ -329,12 +340,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     if (CAUSAL) qt = a.nqt - 1 - qt;  // longest rows first
     const int H = a.H, N = a.N;
     const int b = bh / H, h = bh - b * H;
-    const int qbase = qt * kBr + wave * 32;
+    const int qbase = qt * BR + wave * 32;
     const bool active = qbase < N;
     const int qi = qbase + n;
 
     int ntiles = a.nblk;
-    if (CAUSAL) ntiles = (min(N, qt * kBr + kBr) - 1) / kBc + 1;
+    if (CAUSAL) ntiles = (min(N, qt * BR + BR) - 1) / kBc + 1;
     const bool tail = (N % kBc) != 0;
 
     // Q8^T operand: lane (query n, half hh) holds channels [32 kk + 16 hh, +16).
@@ -355,31 +366,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 
     const uint8_t* kg = (const uint8_t*)a.k8 + (int64_t)bh * a.N_pad * D;
     const uint8_t* vg = (const uint8_t*)a.vq + (int64_t)bh * a.nblk * L::VHBM;
-    constexpr int KMAXP = (L::KPIECES + 7) / 8, VMAXP = (L::VPIECES + 7) / 8;
+    constexpr int KMAXP = (L::KPIECES + NW - 1) / NW, VMAXP = (L::VPIECES + NW - 1) / NW;
     int koff[KMAXP], voff[VMAXP];
 #pragma unroll
-    for (int j = 0; j < KMAXP; ++j) koff[j] = slot_src<L::KROW, L::KSTR>(64 * (wave + 8 * j) + lane);
+    for (int j = 0; j < KMAXP; ++j) koff[j] = slot_src<L::KROW, L::KSTR>(64 * (wave + NW * j) + lane);
 #pragma unroll
-    for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<L::VROW, L::VSTR>(64 * (wave + 8 * j) + lane);
+    for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<L::VROW, L::VSTR>(64 * (wave + NW * j) + lane);
     const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     // step t of the sweep works on key tile T (every tile when dense: T = t);
     // the tile goes to LDS slot t & 1
     auto load_k = [&](int t, int T) {
-        tile_to_lds<L::KPIECES, KMAXP>(kg + (int64_t)T * L::KHBM, lbase + (t & 1) * L::KBYTES, wv,
-                                       koff);
+        tile_to_lds<L::KPIECES, KMAXP, NW>(kg + (int64_t)T * L::KHBM, lbase + (t & 1) * L::KBYTES,
+                                           wv, koff);
     };
     auto load_v = [&](int t, int T) {
-        tile_to_lds<L::VPIECES, VMAXP>(vg + (int64_t)T * L::VHBM,
-                                       lbase + L::VBASE + (t & 1) * L::VBYTES, wv, voff);
+        tile_to_lds<L::VPIECES, VMAXP, NW>(vg + (int64_t)T * L::VHBM,
+                                           lbase + L::VBASE + (t & 1) * L::VBYTES, wv, voff);
     };
     if (SPARSE) {
-        // wave 0 compacts the visited tiles: tile T is visited when either of
-        // the workgroup's two query blocks has a nonzero mask byte for it
+        // wave 0 compacts the visited tiles: tile T is visited when one of the
+        // workgroup's query blocks (one or two) has a nonzero mask byte for it
         if (wave == 0) {
-            const int r0 = 2 * qt, nbq = a.nblk;
+            const int r0 = qt * (NW / 4), nbq = a.nblk;
             const uint8_t* m0 = a.tmask + ((int64_t)bh * nbq + r0) * a.nblk;
-            const bool has1 = r0 + 1 < nbq;
+            const bool has1 = NW == 8 && r0 + 1 < nbq;
             int cnt = 0;
             for (int base = 0; base < ntiles; base += 64) {
                 const int T = base + lane;
@@ -423,7 +434,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     // overlap with the other wave's.  V buffer 1 is zero-filled for tile -1.
     {
         uint4* vz = (uint4*)(smem + L::VBASE + L::VBYTES);
-        for (int i = tid; i < L::VBYTES / 16; i += kAttnThreads) vz[i] = make_uint4(0, 0, 0, 0);
+        for (int i = tid; i < L::VBYTES / 16; i += NT) vz[i] = make_uint4(0, 0, 0, 0);
     }
     if (!SPARSE || ntiles > 0) load_k(0, SPARSE ? (e0 & 0x3fff) : 0);
     if (ntiles > 1) load_k(1, SPARSE ? (e1 & 0x3fff) : 1);
@@ -522,6 +533,11 @@ static const void* attn_fn_rt(bool causal, int mode) {
     return attn_fn_rt<D, PV16, kDense>(causal);
 }
 
+static int waves_of(int d, int pv16, int mode) {
+    if (d == 128) return pv16 ? attn_waves<128, true, kSparse>() : attn_waves<128, false, kSparse>();
+    return pv16 ? attn_waves<64, true, kSparse>() : attn_waves<64, false, kSparse>();
+}
+
 hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal, int dump,
                        hipStream_t s) {
     const int mode = dump ? kDump : (args.tmask ? kSparse : kDense);
@@ -529,8 +545,11 @@ hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal,
     if (d == 128) fn = pv16 ? attn_fn_rt<128, true>(causal, mode) : attn_fn_rt<128, false>(causal, mode);
     else fn = pv16 ? attn_fn_rt<64, true>(causal, mode) : attn_fn_rt<64, false>(causal, mode);
     AttnArgs a = args;
+    const int nw = mode == kSparse ? waves_of(d, pv16, mode) : 8;
+    a.nqt = (a.N + 32 * nw - 1) / (32 * nw);
+    a.total = B * a.H * a.nqt;
     void* kargs[] = {(void*)&a};
-    return hipLaunchKernel(fn, dim3(a.total), dim3(kAttnThreads), kargs, 0, s);
+    return hipLaunchKernel(fn, dim3(a.total), dim3(64 * nw), kargs, 0, s);
 }
 
 }  // namespace sage

@@ -16,9 +16,9 @@ typedef unsigned short u16;
 
 constexpr int kBlk = 128;          // rows per Q / K quantization block
 constexpr int kBc = 128;           // keys per online-softmax tile (== kBlk)
-constexpr int kBr = 256;           // queries per attention workgroup (8 waves x 32)
+constexpr int kBr = 256;           // queries per dense attention workgroup (8 waves x 32)
 constexpr int kAttnThreads = 512;  // 8 wave64s
-constexpr int kMaxSparseTiles = 4096;  // key tiles a sparse launch may list (N <= 524288)
+constexpr int kMaxSparseTiles = 2048;  // key tiles a sparse launch may list (N <= 262144)
 constexpr int kStatsChunk = 512;   // tokens per statistics workgroup
 constexpr int kQuantThreads = 256;
 constexpr float kPScale = 448.0f;

@@ -138,8 +138,8 @@ def test_invalid_arguments_rejected_before_launch(sage):
     assert sp(tm=None) == -1
     assert sp(tm=A + 3) == -4
     assert sp(g=5) == -2
-    assert sp(N=4096 * 128 + 1) == -5      # more key tiles than a sparse launch can list
-    assert sp(N=4096 * 128, tm=A + 3) == -4   # the size passes; validation stops at alignment
+    assert sp(N=2048 * 128 + 1) == -5      # more key tiles than a sparse launch can list
+    assert sp(N=2048 * 128, tm=A + 3) == -4   # the size passes; validation stops at alignment
     dbg = lambda b=0, h=0, row0=0, nrows=4, s=A: L.sage_attn_fwd_debug(
         A, A, A, A, A, A, 1, 2, 256, 128, 0, 0, 0.1, 0, A, 0, b, h, row0, nrows, s, None)
     assert dbg(s=None) == -1
