@@ -516,6 +516,116 @@ void attn_fwd_kernel(AttnArgs a) {
         }
 }
 
+// Non-pipelined sweep with 12 waves (384 queries) per workgroup, three per
+// SIMD, for d = 64: at d = 64 a wave needs about 135 VGPRs without the
+// software pipeline, so a third wave per SIMD fits and hides more latency than
+// the pipeline does (+24 % per query measured against the 8-wave kernel on
+// the d = 64 outlier workload).  Per tile: Q K^T, softmax, rescale and P V in
+// program order; K(t+1) and V(t+1) load into the other slot meanwhile.  Same
+// arithmetic per query as attn_fwd_kernel, so the outputs are identical.
+template <int D, bool PV16, int NW>
+__global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
+    using L = Lds<D, PV16>;
+    using PT = typename std::conditional<PV16, v8h, v8i>::type;
+    constexpr int NP = PV16 ? 8 : 2;
+    constexpr int BR = 32 * NW, KK = D / 32, CB = D / 32;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (L::KBYTES + L::VBYTES)];
+    constexpr int VB = 2 * L::KBYTES;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hh = lane >> 5;
+    const int wg = xcd_remap(blockIdx.x, a.total);
+    const int bh = wg / a.nqt;
+    const int qt = wg - bh * a.nqt;
+    const int H = a.H, N = a.N;
+    const int b = bh / H, h = bh - b * H;
+    const int qbase = qt * BR + wave * 32;
+    const bool active = qbase < N;
+    const int qi = qbase + n;
+    const int ntiles = a.nblk;
+    const bool tail = (N % kBc) != 0;
+    v4i qf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = v4i{};
+    float sigma = 0.0f;
+    if (active) {
+        const int8_t* qrow = a.q8 + ((int64_t)bh * a.N_pad + qi) * D + 16 * hh;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const v4i*)(qrow + 32 * kk);
+        sigma = (a.qtok ? a.q_scale[(int64_t)bh * a.N_pad + qi] : a.q_scale[bh * a.nblk + qbase / kBlk]) *
+                a.lambda;
+    }
+    const uint8_t* kg = (const uint8_t*)a.k8 + (int64_t)bh * a.N_pad * D;
+    const uint8_t* vg = (const uint8_t*)a.vq + (int64_t)bh * a.nblk * L::VHBM;
+    constexpr int KMAXP = (L::KPIECES + NW - 1) / NW, VMAXP = (L::VPIECES + NW - 1) / NW;
+    int koff[KMAXP], voff[VMAXP];
+#pragma unroll
+    for (int j = 0; j < KMAXP; ++j) koff[j] = slot_src<L::KROW, L::KSTR>(64 * (wave + NW * j) + lane);
+#pragma unroll
+    for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<L::VROW, L::VSTR>(64 * (wave + NW * j) + lane);
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto load_kv = [&](int t) {
+        tile_to_lds<L::KPIECES, KMAXP, NW>(kg + (int64_t)t * L::KHBM, lbase + (t & 1) * L::KBYTES,
+                                           wv, koff);
+        tile_to_lds<L::VPIECES, VMAXP, NW>(vg + (int64_t)t * L::VHBM,
+                                           lbase + VB + (t & 1) * L::VBYTES, wv, voff);
+    };
+    float m = -INFINITY, l = 0.0f;
+    v16f O[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) O[cb] = v16f{};
+    PT P[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) P[i] = PT{};
+    const int kmax = N - 1;
+    load_kv(0);
+    wait_vmem();
+    __syncthreads();
+    typedef __attribute__((address_space(4))) const float cfloat;
+    cfloat* ksrow = (cfloat*)(a.k_scale + bh * a.nblk);
+    for (int t = 0; t < ntiles; ++t) {
+        const float c = sigma * ksrow[t];
+        if (t + 1 < ntiles) load_kv(t + 1);
+        const int key_t = t * kBc;
+        const uint8_t* kb = smem + (t & 1) * L::KBYTES;
+        v16i S[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) S[k4] = qk_block<D, L::KSTR>(kb, qf, k4, n, hh);
+        const bool needmask = tail && t == a.nblk - 1;
+        v16f F[4];
+        float mu, alpha;
+        softmax_prep(S, F, c, m, alpha, mu, needmask, kmax - key_t - 4 * hh);
+        const float cf = c == 0.0f ? 1.0f : c;
+        float part[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) part[k4] = softmax_block(F[k4], P, k4, cf, mu);
+        l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
+        pv_tile<D>(smem + VB + (t & 1) * L::VBYTES, P, O, alpha, n, hh);
+        wait_vmem();
+        __syncthreads();
+    }
+    const float lt = pair_sum(l);
+    if (!active || qi >= N) return;
+    const int64_t obase = row_offset(a.layout, b, h, qi, H, N, D);
+    const float* vs = a.v_scale + bh * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int c0 = 32 * cb + 8 * r4 + 4 * hh;
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = (O[cb][4 * r4 + j] * vs[c0 + j]) / lt;
+            if (a.out_fp32) {
+                *(float4*)((float*)a.out + obase + c0) = make_float4(o[0], o[1], o[2], o[3]);
+            } else {
+                const uint32_t w0 = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+                const uint32_t w1 = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+                *(uint2*)((u16*)a.out + obase + c0) = make_uint2(w0, w1);
+            }
+        }
+}
+
 template <int D, bool PV16, bool CAUSAL, int MODE>
 static const void* attn_fn() {
     return (const void*)attn_fwd_kernel<D, PV16, CAUSAL, MODE>;
@@ -533,6 +643,24 @@ static const void* attn_fn_rt(bool causal, int mode) {
     return attn_fn_rt<D, PV16, kDense>(causal);
 }
 
+// The 12-wave d = 64 sweep processes about 1.24x the queries per unit time of
+// the 8-wave one in steady state (measured), but its workgroups are 1.5x
+// larger: use it when its rounds of workgroups over the CUs do not lose that.
+static bool np12_pays(int bh, int N) {
+    static int ncu = 0;
+    if (ncu == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            ncu = v;
+        else
+            ncu = 256;
+    }
+    const int64_t w8 = (int64_t)bh * ((N + 255) / 256), w12 = (int64_t)bh * ((N + 383) / 384);
+    const int64_t r8 = (w8 + ncu - 1) / ncu, r12 = (w12 + ncu - 1) / ncu;
+    return r12 * 150 < r8 * 124;   // r12 * 1.5 / 1.24 < r8
+}
+
 static int waves_of(int d, int pv16, int mode) {
     if (d == 128) return pv16 ? attn_waves<128, true, kSparse>() : attn_waves<128, false, kSparse>();
     return pv16 ? attn_waves<64, true, kSparse>() : attn_waves<64, false, kSparse>();
@@ -545,7 +673,11 @@ hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal,
     if (d == 128) fn = pv16 ? attn_fn_rt<128, true>(causal, mode) : attn_fn_rt<128, false>(causal, mode);
     else fn = pv16 ? attn_fn_rt<64, true>(causal, mode) : attn_fn_rt<64, false>(causal, mode);
     AttnArgs a = args;
-    const int nw = mode == kSparse ? waves_of(d, pv16, mode) : 8;
+    int nw = mode == kSparse ? waves_of(d, pv16, mode) : 8;
+    if (mode == kDense && !causal && d == 64 && np12_pays(B * a.H, a.N)) {
+        nw = 12;
+        fn = pv16 ? (const void*)attn_np_kernel<64, true, 12> : (const void*)attn_np_kernel<64, false, 12>;
+    }
     a.nqt = (a.N + 32 * nw - 1) / (32 * nw);
     a.total = B * a.H * a.nqt;
     void* kargs[] = {(void*)&a};

@@ -514,3 +514,24 @@ def test_k_mean_exact_with_large_and_special_values(sage, orc):
     got = qz["k_mean"].cpu().numpy()
     ref = np.stack([orc.k_mean_head(k[0, h]) for h in range(2)])[None]
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("pv", ["fp8", "fp16"])
+def test_d64_many_heads_matches_oracle(sage, orc, pv):
+    """d = 64 with many heads: the launcher runs the 12-wave (384-query)
+    non-pipelined sweep here (its rounds over the CUs beat the 8-wave ones);
+    sampled heads against the oracle, every row, ragged N."""
+    print(f"[d=64 many heads] pv={pv}", flush=True)
+    wl = si.make("outlier", B=1, H=256, N=1000, seed=31)
+    qz, vq, vs, out = run_gpu(sage, wl, pv)
+    out = out.cpu().numpy()
+    heads = [(0, 0), (0, 97), (0, 255)]
+    q, k, v, oz, ovq, ovs = oracle_quant(orc, wl, pv, heads)
+    rows = np.arange(wl.N)
+    for i, (b, h) in enumerate(heads):
+        ozh = {key: (val[i][None, None] if isinstance(val, np.ndarray) else val)
+               for key, val in oz.items()}
+        o_or = orc.attn_rows_head(ozh, ovq[i][None, None], ovs[i][None, None], 0, 0, rows, False,
+                                  wl.sm_scale, pv)
+        err, c = np.abs(out[b, h] - o_or).max(), _cos(out[b, h], o_or)
+        assert err <= MAX_ABS and c >= COS_ORACLE, (h, err, c)
