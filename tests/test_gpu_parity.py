@@ -535,3 +535,75 @@ def test_d64_many_heads_matches_oracle(sage, orc, pv):
                                   wl.sm_scale, pv)
         err, c = np.abs(out[b, h] - o_or).max(), _cos(out[b, h], o_or)
         assert err <= MAX_ABS and c >= COS_ORACLE, (h, err, c)
+
+
+# --------------------------------------------------------- degenerate inputs
+def _bf16_tensor(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("pv", ["fp8", "fp16"])
+def test_degenerate_inputs(sage, orc, pv):
+    """Constant keys (smoothed K is exactly 0, so k_scale = 0 and the
+    dequantization constant c = 0), an all-zero Q, an all-zero V and a zero V
+    channel, each against the oracle and against its closed form."""
+    rng = np.random.default_rng(41)
+    N, d = 700, 128
+    q = rng.standard_normal((1, 4, N, d)).astype(np.float32)
+    k = rng.standard_normal((1, 4, N, d)).astype(np.float32)
+    v = rng.standard_normal((1, 4, N, d)).astype(np.float32)
+    k[0, 0] = rng.standard_normal(d)[None, :]      # head 0: every key the same
+    q[0, 1] = 0.0                                  # head 1: Q all zero
+    v[0, 2] = 0.0                                  # head 2: V all zero
+    v[0, 3, :, 5] = 0.0                            # head 3: one zero V channel
+    qt, kt, vt = (_bf16_tensor(x).cuda() for x in (q, k, v))
+    qz = sage.quant_qk(qt, kt)
+    vq, vs = sage.quant_v(vt, pv)
+    sm = 1.0 / math.sqrt(d)
+    out = sage.attn_fwd(qz, vq, vs, sm_scale=sm, pv=pv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.isfinite(out).all()
+    qc, kc, vc = (codes(_bf16_tensor(x)) for x in (q, k, v))
+    oz = orc.quant_qk(qc, kc)
+    ovq, ovs = orc.quant_v(vc, pv)
+    assert np.array_equal(qz["k8"][:, :, :N].cpu().numpy(), oz["k8"])
+    assert not oz["k8"][0, 0].any() and oz["k_scale"][0, 0].max() == 0.0
+    rows = np.arange(N)
+    for h in range(4):
+        o_or = orc.attn_rows_head(oz, ovq, ovs, 0, h, rows, False, sm, pv)
+        err = np.abs(out[0, h] - o_or).max()
+        assert err <= MAX_ABS, (h, err)
+    dec = orc.f16_to_f32 if pv == "fp16" else orc.e4m3_to_f32
+    vdq = dec(ovq[0]).reshape(4, N, d).astype(np.float64) * ovs[0][:, None, :]
+    # constant keys and zero Q: every score is equal, so O = the mean of the dequantized V
+    for h in (0, 1):
+        assert np.allclose(out[0, h], vdq[h].mean(axis=0)[None, :], rtol=1e-5, atol=1e-6), h
+    assert not out[0, 2].any()
+    assert not out[0, 3, :, 5].any()
+
+
+def test_maximum_sequence_length(sage, orc):
+    """N = 2^20 keys (8192 key tiles; offsets beyond 2^31 bytes per tensor
+    pair): quantization of sampled heads bit-exact, sampled rows (first,
+    last, middle, ragged) against the oracle."""
+    print("[max size] B=1 H=2 N=2^20 d=128", flush=True)
+    N = 1 << 20
+    wl = si.make("tiny", N=N, H=2, seed=43, device="cuda")
+    qz = sage.quant_qk(wl.q, wl.k)
+    vq, vs = sage.quant_v(wl.v, "fp8")
+    out = sage.attn_fwd(qz, vq, vs, sm_scale=wl.sm_scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 300_001, N // 2, N - 129, N - 2, N - 1], np.int32)
+    for h in range(2):
+        q, k, v = (codes(t[0:1, h:h + 1].cpu()) for t in (wl.q, wl.k, wl.v))
+        oz = orc.quant_qk(q, k)
+        ovq, ovs = orc.quant_v(v, "fp8")
+        assert np.array_equal(qz["k8"][0, h, :N].cpu().numpy(), oz["k8"][0, 0])
+        assert np.array_equal(qz["k_mean"][0, h].cpu().numpy().view(np.uint32),
+                              oz["k_mean"][0, 0].view(np.uint32))
+        o_or = orc.attn_rows_head(oz, ovq, ovs, 0, 0, rows, False, wl.sm_scale, "fp8")
+        o_gpu = out[0, h, torch.from_numpy(rows).long().cuda()].cpu().numpy()
+        err, c = np.abs(o_gpu - o_or).max(), _cos(o_gpu, o_or)
+        print(f"  head {h}: max-abs {err:.3e} cos {c:.7f}", flush=True)
+        assert err <= MAX_ABS and c >= COS_ORACLE, (h, err, c)
