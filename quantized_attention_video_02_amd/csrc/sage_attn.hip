@@ -11,8 +11,10 @@
 // accumulates in full FP32, so the product is accumulated straight into the
 // rescaled output (O = alpha O + P V, one rounding per MFMA step).
 //
-// Work decomposition: one workgroup = 8 wave64s = 256 queries of one (b, h);
-// each wave owns 32 queries for the whole key sweep.  Per key tile:
+// Work decomposition: one workgroup = 8 wave64s = 256 queries of one (b, h)
+// (4 waves = one 128-query block for the block-sparse sweep; 12 waves for the
+// non-pipelined d = 64 sweep); each wave owns 32 queries for the whole key
+// sweep.  Per key tile:
 //   S^T (128 keys x 32 queries) = K8 tile (LDS) . Q8^T (registers),
 //     16 x v_mfma_i32_32x32x32_i8 (d = 128);
 //   in the 32x32 accumulator layout each lane holds one query (lane & 31) and
@@ -45,7 +47,9 @@
 
 namespace sage {
 
-
+// The hardware hands workgroup IDs to the 8 XCDs round-robin (bid % 8).
+// Renumber so that XCD x runs a contiguous range of logical workgroups:
+// consecutive Q tiles of one head then share that XCD's L2 for K and V.
 __device__ inline int xcd_remap(int bid, int total) {
     constexpr int nx = 8;
     const int q = total / nx, r = total % nx, x = bid % nx, s = bid / nx;
@@ -149,14 +153,6 @@ __device__ inline void dump_tile(const v16i* S, int32_t* srow, int key_t, int N,
         }
 }
 
-// Online-softmax step of one tile for this lane's query.  In: S (int32), the
-// dequantization constant c, the running max m.  Out: P (the PV B operand),
-// alpha, the partial row sum ls of this lane's 64 keys; m is updated.
-// p = exp2(fma(S, c, -(m' - log2 448))).  With needmask (wave-uniform), the
-// keys past `lim` (key - key_t - 4 hh > lim: beyond N, or after the query
-// when causal) become -inf: p = 0 and they do not enter the max.
-// The tile max is taken on the integers: c > 0 and rounding is monotone, so
-// max_j fp32(S_j c) = fp32(max_j S_j * c).
 // x with its bits replaced by `fill` when lim - OFF < 0 (the key at offset OFF
 // of the lane's tile run is masked): v_subrev, v_ashrrev (sign word), v_bfi.
 // Written as one ALU asm block so the compiler keeps it a branch-free 3-op
@@ -303,6 +299,50 @@ __device__ inline v16i qk_block(const uint8_t* kb, const v4i* qf, int k4, int n,
     return acc;
 }
 
+// Q8^T operand of this lane (query qi, half hh: channels [32 kk + 16 hh, +16))
+// and the row's dequantization factor q_scale * lambda.  A wave whose 32
+// queries are all padding runs the sweep on zero codes; its rows are never
+// written.
+template <int D>
+__device__ inline float load_q(const AttnArgs& a, int bh, int qbase, int qi, int hh, bool active,
+                               v4i* qf) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) qf[kk] = v4i{};
+    if (!active) return 0.0f;
+    const int8_t* qrow = a.q8 + ((int64_t)bh * a.N_pad + qi) * D + 16 * hh;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) qf[kk] = *(const v4i*)(qrow + 32 * kk);
+    // per block: one scale for the wave's 32 queries; per token: one per lane
+    const float qs = a.qtok ? a.q_scale[(int64_t)bh * a.N_pad + qi] : a.q_scale[bh * a.nblk + qbase / kBlk];
+    return qs * a.lambda;
+}
+
+// Output row qi = O^T column * v_scale / lt, this lane's half of the channels
+// (32 cb + 8 r4 + 4 hh + j).  ZERO_EMPTY: a row that saw no key (lt = 0) is 0.
+template <int D, bool ZERO_EMPTY>
+__device__ inline void store_row(const AttnArgs& a, const v16f* O, float lt, int b, int h, int bh,
+                                 int qi, int hh) {
+    const int64_t obase = row_offset(a.layout, b, h, qi, a.H, a.N, D);
+    const float* vs = a.v_scale + bh * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int c0 = 32 * cb + 8 * r4 + 4 * hh;
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = (ZERO_EMPTY && !(lt > 0.0f)) ? 0.0f : (O[cb][4 * r4 + j] * vs[c0 + j]) / lt;
+            if (a.out_fp32) {
+                *(float4*)((float*)a.out + obase + c0) = make_float4(o[0], o[1], o[2], o[3]);
+            } else {
+                const uint32_t w0 = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+                const uint32_t w1 = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+                *(uint2*)((u16*)a.out + obase + c0) = make_uint2(w0, w1);
+            }
+        }
+}
+
 // MODE: kDense, kDump (also writes the int32 Q K^T of one head), kSparse
 // (visits only the key tiles a tile mask selects).
 enum { kDense = 0, kDump = 1, kSparse = 2 };
@@ -348,21 +388,8 @@ void attn_fwd_kernel(AttnArgs a) {
     if (CAUSAL) ntiles = (min(N, qt * BR + BR) - 1) / kBc + 1;
     const bool tail = (N % kBc) != 0;
 
-    // Q8^T operand: lane (query n, half hh) holds channels [32 kk + 16 hh, +16).
-    // (a wave whose 32 queries are all padding runs the schedule on zero codes;
-    // its rows are never written)
     v4i qf[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = v4i{};
-    float sigma = 0.0f;
-    if (active) {
-        const int8_t* qrow = a.q8 + ((int64_t)bh * a.N_pad + qi) * D + 16 * hh;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const v4i*)(qrow + 32 * kk);
-        // per block: one scale for the wave's 32 queries; per token: one per lane
-        sigma = (a.qtok ? a.q_scale[(int64_t)bh * a.N_pad + qi] : a.q_scale[bh * a.nblk + qbase / kBlk]) *
-                a.lambda;
-    }
+    const float sigma = load_q<D>(a, bh, qbase, qi, hh, active, qf);
 
     const uint8_t* kg = (const uint8_t*)a.k8 + (int64_t)bh * a.N_pad * D;
     const uint8_t* vg = (const uint8_t*)a.vq + (int64_t)bh * a.nblk * L::VHBM;
@@ -495,25 +522,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // ---- epilogue: out = O * v_scale / l (l summed over both lane halves)
     const float lt = pair_sum(l);
     if (!active || qi >= N) return;
-    const int64_t obase = row_offset(a.layout, b, h, qi, H, N, D);
-    const float* vs = a.v_scale + bh * D;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int c0 = 32 * cb + 8 * r4 + 4 * hh;
-            float o[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = (SPARSE && !(lt > 0.0f)) ? 0.0f : (O[cb][4 * r4 + j] * vs[c0 + j]) / lt;
-            if (a.out_fp32) {
-                *(float4*)((float*)a.out + obase + c0) = make_float4(o[0], o[1], o[2], o[3]);
-            } else {
-                const uint32_t w0 = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-                const uint32_t w1 = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-                *(uint2*)((u16*)a.out + obase + c0) = make_uint2(w0, w1);
-            }
-        }
+    store_row<D, SPARSE>(a, O, lt, b, h, bh, qi, hh);
 }
 
 // Non-pipelined sweep with 12 waves (384 queries) per workgroup, three per
@@ -544,16 +553,7 @@ __global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
     const int ntiles = a.nblk;
     const bool tail = (N % kBc) != 0;
     v4i qf[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = v4i{};
-    float sigma = 0.0f;
-    if (active) {
-        const int8_t* qrow = a.q8 + ((int64_t)bh * a.N_pad + qi) * D + 16 * hh;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const v4i*)(qrow + 32 * kk);
-        sigma = (a.qtok ? a.q_scale[(int64_t)bh * a.N_pad + qi] : a.q_scale[bh * a.nblk + qbase / kBlk]) *
-                a.lambda;
-    }
+    const float sigma = load_q<D>(a, bh, qbase, qi, hh, active, qf);
     const uint8_t* kg = (const uint8_t*)a.k8 + (int64_t)bh * a.N_pad * D;
     const uint8_t* vg = (const uint8_t*)a.vq + (int64_t)bh * a.nblk * L::VHBM;
     constexpr int KMAXP = (L::KPIECES + NW - 1) / NW, VMAXP = (L::VPIECES + NW - 1) / NW;
@@ -606,24 +606,7 @@ __global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
     }
     const float lt = pair_sum(l);
     if (!active || qi >= N) return;
-    const int64_t obase = row_offset(a.layout, b, h, qi, H, N, D);
-    const float* vs = a.v_scale + bh * D;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int c0 = 32 * cb + 8 * r4 + 4 * hh;
-            float o[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = (O[cb][4 * r4 + j] * vs[c0 + j]) / lt;
-            if (a.out_fp32) {
-                *(float4*)((float*)a.out + obase + c0) = make_float4(o[0], o[1], o[2], o[3]);
-            } else {
-                const uint32_t w0 = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-                const uint32_t w1 = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-                *(uint2*)((u16*)a.out + obase + c0) = make_uint2(w0, w1);
-            }
-        }
+    store_row<D, false>(a, O, lt, b, h, bh, qi, hh);
 }
 
 template <int D, bool PV16, bool CAUSAL, int MODE>
@@ -661,7 +644,7 @@ static bool np12_pays(int bh, int N) {
     return r12 * 150 < r8 * 124;   // r12 * 1.5 / 1.24 < r8
 }
 
-static int waves_of(int d, int pv16, int mode) {
+static int sparse_waves(int d, int pv16) {
     if (d == 128) return pv16 ? attn_waves<128, true, kSparse>() : attn_waves<128, false, kSparse>();
     return pv16 ? attn_waves<64, true, kSparse>() : attn_waves<64, false, kSparse>();
 }
@@ -673,7 +656,7 @@ hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal,
     if (d == 128) fn = pv16 ? attn_fn_rt<128, true>(causal, mode) : attn_fn_rt<128, false>(causal, mode);
     else fn = pv16 ? attn_fn_rt<64, true>(causal, mode) : attn_fn_rt<64, false>(causal, mode);
     AttnArgs a = args;
-    int nw = mode == kSparse ? waves_of(d, pv16, mode) : 8;
+    int nw = mode == kSparse ? sparse_waves(d, pv16) : 8;
     if (mode == kDense && !causal && d == 64 && np12_pays(B * a.H, a.N)) {
         nw = 12;
         fn = pv16 ? (const void*)attn_np_kernel<64, true, 12> : (const void*)attn_np_kernel<64, false, 12>;
