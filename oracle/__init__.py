@@ -58,11 +58,13 @@ def lib():
             "or_k_mean": [P, i32, i32, P],
             "or_quant_block": [P, i32, i32, P, P],
             "or_quant_q": [P, i32, i32, i32, P, P, P],
+            "or_quant_q_smooth": [P, i32, i32, i32, P, P, P, P],
+            "or_q_smooth_bias": [P, P, P, i32, i32, f32, P],
             "or_quant_k": [P, i32, i32, i32, i32, P, P, P, P],
             "or_quant_v": [P, i32, i32, i32, P, P],
             "or_dump_s": [P, P, i32, i32, i32, i32, i32, P],
             "or_attn_rows": [P, P, P, P, P, P, i32, i32, P, i32, i32, f32, i32, i32, i32, i32, P, P,
-                             P, P, P],
+                             P, P, P, P],
             "or_ref64_rows": [P, P, P, i32, i32, P, i32, i32, f64, P, P],
         }
         for name, args in sigs.items():
@@ -140,12 +142,15 @@ def quant_block(x: np.ndarray):
 
 
 def quant_qk(q: np.ndarray, k: np.ndarray, blk: int = BLK, smooth: bool = True,
-             q_gran: str = "block"):
+             q_gran: str = "block", q_smooth: bool = False):
     """q, k: uint16 bf16 codes [B, H, N, d].  Returns a dict with q8/k8 int8
     [B,H,N,d], q_scale fp32 [B,H,ceil(N/qblk)], k_scale fp32 [B,H,nblk],
     k_mean fp32 [B,H,d] and qblk.  q_gran "block": Q blocks of blk rows like
-    K; "token": one scale per query row (qblk = 1)."""
+    K; "token": one scale per query row (qblk = 1).  q_smooth: Q is smoothed
+    by its per-block token mean first (q_mean fp32 [B,H,nblk,d] is added to
+    the dict; the scores need smooth_bias then)."""
     B, H, N, d = q.shape
+    assert blk == BLK or not q_smooth
     qblk = {"block": blk, "token": 1}[q_gran]
     nb = (N + blk - 1) // blk
     nbq = (N + qblk - 1) // qblk
@@ -154,6 +159,7 @@ def quant_qk(q: np.ndarray, k: np.ndarray, blk: int = BLK, smooth: bool = True,
     qs = np.empty((B, H, nbq), np.float32)
     ks = np.empty((B, H, nb), np.float32)
     km = np.empty((B, H, d), np.float32)
+    qm = np.empty((B, H, nb, d), np.float32)
     tmp = np.empty(blk * d, np.float32)
     L = lib()
     for b in range(B):
@@ -165,10 +171,36 @@ def quant_qk(q: np.ndarray, k: np.ndarray, blk: int = BLK, smooth: bool = True,
             qsh = np.empty(nbq, np.float32)
             ksh = np.empty(nb, np.float32)
             kmh = np.empty(d, np.float32)
-            L.or_quant_q(_p(qh), N, d, qblk, _p(q8h), _p(qsh), _p(tmp))
+            if q_smooth:
+                qmh = np.empty((nb, d), np.float32)
+                L.or_quant_q_smooth(_p(qh), N, d, qblk, _p(q8h), _p(qsh), _p(qmh), _p(tmp))
+                qm[b, h] = qmh
+            else:
+                L.or_quant_q(_p(qh), N, d, qblk, _p(q8h), _p(qsh), _p(tmp))
             L.or_quant_k(_p(kh), N, d, blk, int(smooth), _p(k8h), _p(ksh), _p(kmh), _p(tmp))
             q8[b, h], k8[b, h], qs[b, h], ks[b, h], km[b, h] = q8h, k8h, qsh, ksh, kmh
-    return dict(q8=q8, q_scale=qs, k8=k8, k_scale=ks, k_mean=km, qblk=qblk)
+    out = dict(q8=q8, q_scale=qs, k8=k8, k_scale=ks, k_mean=km, qblk=qblk)
+    if q_smooth:
+        out["q_mean"] = qm
+    return out
+
+
+def smooth_bias(qz: dict, k: np.ndarray, sm_scale: float) -> np.ndarray:
+    """The Q-smoothing correction of every head: fp32 [B, H, nblk, N] (block
+    r, key j) from qz["q_mean"], qz["k_mean"] and the bf16 K codes."""
+    B, H, N, d = k.shape
+    nb = (N + BLK - 1) // BLK
+    out = np.empty((B, H, nb, N), np.float32)
+    L = lib()
+    for b in range(B):
+        for h in range(H):
+            qmh = np.ascontiguousarray(qz["q_mean"][b, h], np.float32)
+            kh = np.ascontiguousarray(k[b, h], np.uint16)
+            kmh = np.ascontiguousarray(qz["k_mean"][b, h], np.float32)
+            bh = np.empty((nb, N), np.float32)
+            L.or_q_smooth_bias(_p(qmh), _p(kh), _p(kmh), N, d, float(sm_scale), _p(bh))
+            out[b, h] = bh
+    return out
 
 
 def quant_v(v: np.ndarray, pv: str = "fp8"):
@@ -202,10 +234,11 @@ def dump_s(q8h: np.ndarray, k8h: np.ndarray, row0: int, nrows: int, causal: bool
 
 def attn_rows_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scale: float,
                    pv: str = "fp8", blk: int = BLK, bc: int = BC, return_ml: bool = False,
-                   tile_mask=None):
+                   tile_mask=None, bias=None):
     """Quantized attention for query rows ``rows`` of head (b, h): fp32 [len(rows), d].
     tile_mask: None (dense) or uint8 [B, H, ceil(N/128), ceil(N/bc)], nonzero =
-    the query block visits the key tile."""
+    the query block visits the key tile.  bias: None, or the Q-smoothing
+    correction fp32 [B, H, ceil(N/128), N] of smooth_bias."""
     q8h = np.ascontiguousarray(qz["q8"][b, h])
     k8h = np.ascontiguousarray(qz["k8"][b, h])
     qsh = np.ascontiguousarray(qz["q_scale"][b, h])
@@ -223,9 +256,14 @@ def attn_rows_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scal
     if tile_mask is not None:
         tm = np.ascontiguousarray(tile_mask[b, h], np.uint8)
         assert tm.shape == ((N + 127) // 128, (N + bc - 1) // bc), tm.shape
+    bs = None
+    if bias is not None:
+        bs = np.ascontiguousarray(bias[b, h], np.float32)
+        assert bs.shape == ((N + 127) // 128, N), bs.shape
     lib().or_attn_rows(_p(q8h), _p(qsh), _p(k8h), _p(ksh), _p(vqh), _p(vsh), N, d, _p(rows),
                        len(rows), int(causal), float(sm_scale), int(pv == "fp16"), qblk, blk, bc,
-                       None if tm is None else _p(tm), _p(out), _p(m), _p(l), _p(scratch))
+                       None if tm is None else _p(tm), None if bs is None else _p(bs), _p(out),
+                       _p(m), _p(l), _p(scratch))
     if return_ml:
         return out, m, l
     return out
@@ -246,16 +284,19 @@ def ref64_rows_head(q, k, v, b: int, h: int, rows, causal: bool, sm_scale: float
 
 
 def attention(q, k, v, causal: bool, sm_scale: float, pv: str = "fp8", rows=None,
-              q_gran: str = "block", tile_mask=None):
+              q_gran: str = "block", tile_mask=None, q_smooth: bool = False):
     """Whole oracle pipeline: quantize, then attention for ``rows`` (default all)
-    of every head.  Returns (out fp32 [B,H,len(rows),d], quantized dict, vq, vs)."""
+    of every head.  Returns (out fp32 [B,H,len(rows),d], quantized dict, vq, vs);
+    with q_smooth the dict also holds the correction under "bias"."""
     B, H, N, d = q.shape
-    qz = quant_qk(q, k, q_gran=q_gran)
+    qz = quant_qk(q, k, q_gran=q_gran, q_smooth=q_smooth)
+    if q_smooth:
+        qz["bias"] = smooth_bias(qz, k, sm_scale)
     vq, vs = quant_v(v, pv)
     rows = np.arange(N, dtype=np.int32) if rows is None else np.asarray(rows, np.int32)
     out = np.empty((B, H, len(rows), d), np.float32)
     for b in range(B):
         for h in range(H):
             out[b, h] = attn_rows_head(qz, vq, vs, b, h, rows, causal, sm_scale, pv,
-                                       tile_mask=tile_mask)
+                                       tile_mask=tile_mask, bias=qz.get("bias"))
     return out, qz, vq, vs

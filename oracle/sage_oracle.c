@@ -3,7 +3,9 @@
  *
  * A plain, slow, single-threaded CPU implementation of SageAttention-style
  * low-bit attention, O = softmax(Q K^T * sm_scale) V, computed the quantized
- * way: K smoothed by its per-head token mean, Q and K quantized per block of
+ * way: K smoothed by its per-head token mean (optionally Q by its per-block
+ * token mean, with the mean's share of the scores restored in FP32), Q and K
+ * quantized per block of
  * rows to INT8 for an exact integer Q K^T, an exp2 online softmax in FP32 over
  * key tiles, P taken to FP8 e4m3 (or FP16) with a static scale, V taken to
  * FP8 e4m3 with per-channel scales (or FP16), and P V accumulated in two
@@ -204,6 +206,36 @@ OR_API void or_quant_q(const uint16_t* q, int N, int d, int blk, int8_t* q8, flo
     }
 }
 
+/* Q of one head with smoothing: per block r of 128 rows, qmean[r][c] is the
+ * block's token mean of channel c, taken exactly as the K mean (or_k_mean over
+ * the block's rows); q' = fp32(Q - qmean[r]) (one rounding) is quantized to
+ * INT8 per qblk rows (qblk = 128: one scale per block; qblk = 1: one per row).
+ * The mean's share of each score comes back through or_q_smooth_bias.
+ * Reading: the pages name "outlier smoothing" without saying which operand
+ * it applies to; this is the same per-channel mean subtraction as for K, over
+ * the query block that shares a scale, with its contribution q̄·k' restored in
+ * FP32 so the scores still approximate Q K^T (subtracting a query's mean is
+ * not softmax-invariant, unlike the key mean).  Pinned: block means against
+ * FP64 numpy, reconstruction codes * scale + mean ~ Q, the FP64 attention
+ * cosine on Q-offset inputs with and without it. */
+OR_API void or_quant_q_smooth(const uint16_t* q, int N, int d, int qblk, int8_t* q8, float* qs,
+                              float* qmean /* [nb][d] */, float* tmp /* 128*d */) {
+    int nb = (N + 127) / 128;
+    for (int r = 0; r < nb; ++r) {
+        int r0 = r * 128, rows = (N - r0 < 128) ? N - r0 : 128;
+        float* qm = qmean + (int64_t)r * d;
+        or_k_mean(q + (int64_t)r0 * d, rows, d, qm);
+        for (int i = 0; i < rows; ++i)
+            for (int c = 0; c < d; ++c)
+                tmp[i * d + c] = or_bf16_to_f32(q[(int64_t)(r0 + i) * d + c]) - qm[c];
+        if (qblk == 1)
+            for (int i = 0; i < rows; ++i)
+                or_quant_block(tmp + (int64_t)i * d, 1, d, q8 + (int64_t)(r0 + i) * d, &qs[r0 + i]);
+        else
+            or_quant_block(tmp, rows, d, q8 + (int64_t)r0 * d, &qs[r]);
+    }
+}
+
 /* K of one head: k' = fp32(K - mu) (one rounding), then per-block INT8 as
  * for Q.  smooth == 0 skips the mean (mu = 0): a switch for the tests that
  * show what smoothing buys; the method always smooths. */
@@ -277,6 +309,28 @@ static float or_log2_pscale(void) { return (float)log2(448.0); }
 /* sm_scale * log2(e), rounded once to fp32 (the exp2-domain softmax scale). */
 OR_API float or_lambda(float sm_scale) { return (float)((double)sm_scale * 1.4426950408889634); }
 
+/* The Q-smoothing correction of one head: for query block r and key j,
+ *   bias[r][j] = fp32(acc * lambda),  acc = fma chain over c = 0 .. d-1 of
+ *   qmean[r][c] * k'[j][c] starting from 0 (fp32, ascending c),
+ *   k'[j][c] = fp32(K[j][c] - kmean[c])  (the smoothed K the quantizer sees).
+ * It is the block mean's part q̄·k' of every score of the block, in the exp2
+ * units of the attention (lambda = sm_scale log2 e).  Pinned against FP64
+ * numpy within the fp32 dot-product error bound; zero means give 0. */
+OR_API void or_q_smooth_bias(const float* qmean, const uint16_t* k, const float* kmean, int N,
+                             int d, float sm_scale, float* bias /* [nb][N] */) {
+    float lambda = or_lambda(sm_scale);
+    int nb = (N + 127) / 128;
+    for (int r = 0; r < nb; ++r)
+        for (int j = 0; j < N; ++j) {
+            float acc = 0.0f;
+            for (int c = 0; c < d; ++c) {
+                float kp = or_bf16_to_f32(k[(int64_t)j * d + c]) - kmean[c];
+                acc = fmaf(qmean[(int64_t)r * d + c], kp, acc);
+            }
+            bias[(int64_t)r * N + j] = acc * lambda;
+        }
+}
+
 /* One query row i of one head.  Online softmax in the exp2 domain over key
  * tiles [t*bc, (t+1)*bc) in ascending t; with causal, keys j > i are masked
  * and tiles wholly above the diagonal are never visited.
@@ -293,6 +347,10 @@ OR_API float or_lambda(float sm_scale) { return (float)((double)sm_scale * 1.442
  *   T_c   = sum_j dec(pq_j) * dec(v_jc)      level 1: a fresh fp32 sum per tile
  *   O_c   = fp32(fp32(alpha * O_c) + T_c)    level 2: the running fp32 accumulator
  * Epilogue: out_c = fp32( fp32(O_c * v_scale_c) / l ).
+ * With Q smoothing (bias = the row's block row of or_q_smooth_bias), the
+ * score carries the block mean's share and the exponent is taken from it:
+ *   s_j = fma(S_j, c, bias_j);  m_t = max_j s_j;  p_j = exp2(fp32(s_j - mu))
+ * (m', alpha, mu, l and the rest unchanged).
  *
  * Readings: the static P scale is 448 (the e4m3fn maximum: the running max
  * makes every p <= 1, so 448 p fills the FP8 range with no per-token
@@ -318,8 +376,8 @@ OR_API float or_lambda(float sm_scale) { return (float)((double)sm_scale * 1.442
 static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
                         const void* vq, const float* vs, int N, int d, int i, int causal,
                         float lambda, int pv_fp16, int qblk, int kblk, int bc,
-                        const uint8_t* tmask, float* out, float* m_out, float* l_out, int32_t* S,
-                        float* T, float* O, float* P) {
+                        const uint8_t* tmask, const float* bias, float* out, float* m_out,
+                        float* l_out, int32_t* S, float* T, float* O, float* P) {
     const uint8_t* v8 = (const uint8_t*)vq;
     const uint16_t* v16 = (const uint16_t*)vq;
     const float L = or_log2_pscale();
@@ -339,7 +397,7 @@ static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, con
         float mt = -INFINITY;
         for (int j = 0; j < n; ++j) {
             S[j] = or_dot_i8(qi, k8 + (int64_t)(j0 + j) * d, d);
-            float s = (float)S[j] * c;
+            float s = bias ? fmaf((float)S[j], c, bias[j0 + j]) : (float)S[j] * c;
             if (s > mt) mt = s;
         }
         float mn = m > mt ? m : mt;
@@ -347,7 +405,8 @@ static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, con
         float mu = mn - L;
         float psum = 0.0f;
         for (int j = 0; j < n; ++j) {
-            float p = exp2f(fmaf((float)S[j], c, -mu));
+            float p = bias ? exp2f(fmaf((float)S[j], c, bias[j0 + j]) - mu)
+                           : exp2f(fmaf((float)S[j], c, -mu));
             psum += p;
             P[j] = pv_fp16 ? or_f16_to_f32(or_f32_to_f16(p)) : or_e4m3_to_f32(or_f32_to_e4m3(p));
         }
@@ -371,12 +430,14 @@ static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, con
 /* Rows rows[0..nrows) of one head; out [nrows][d]; m_out/l_out optional.
  * tmask: NULL (dense) or the head's tile mask [ceil(N/128)][ntiles] (query
  * block of 128 rows x key tile), nonzero = visit.
+ * bias: NULL, or the head's Q-smoothing correction [ceil(N/128)][N] from
+ * or_q_smooth_bias (row i uses row i / 128).
  * scratch must hold 4*bc + 3*d floats. */
 OR_API void or_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
                          const void* vq, const float* vs, int N, int d, const int32_t* rows,
                          int nrows, int causal, float sm_scale, int pv_fp16, int qblk,
-                         int kblk, int bc, const uint8_t* tmask, float* out, float* m_out,
-                         float* l_out, float* scratch) {
+                         int kblk, int bc, const uint8_t* tmask, const float* bias,
+                         float* out, float* m_out, float* l_out, float* scratch) {
     float lambda = or_lambda(sm_scale);
     int32_t* S = (int32_t*)scratch;
     float* P = scratch + bc;
@@ -385,7 +446,7 @@ OR_API void or_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, co
     for (int r = 0; r < nrows; ++r)
         or_attn_row(q8, qs, k8, ks, vq, vs, N, d, rows[r], causal, lambda, pv_fp16, qblk, kblk, bc,
                     tmask ? tmask + (int64_t)(rows[r] / 128) * ((N + bc - 1) / bc) : 0,
-                    out + (int64_t)r * d, m_out ? m_out + r : 0, l_out ? l_out + r : 0, S, T, O,
+                    bias ? bias + (int64_t)(rows[r] / 128) * N : 0, out + (int64_t)r * d, m_out ? m_out + r : 0, l_out ? l_out + r : 0, S, T, O,
                     P);
 }
 

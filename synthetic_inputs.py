@@ -21,6 +21,9 @@ per-(batch, head, channel) offset o ~ N(0, sigma^2) shared by all tokens
 (sigma = 3, or 2 for the causal case).  Outlier case: Q, K, V ~ N(0, 1); per
 (b, h) round(1% of d) = 1 channel of K gets o ~ N(0, 20^2), and
 round(0.5% of N) query tokens are multiplied by 30 (chosen without replacement).
+Optional ``q_sigma`` (any workload): Q also gets a per-(batch, head, channel)
+offset ~ N(0, q_sigma^2) shared by all tokens, drawn after everything above
+(the inputs that Q smoothing is for; without it nothing changes).
 """
 from __future__ import annotations
 
@@ -60,7 +63,8 @@ def default_seed(name: str) -> int:
     return 1000 + ORDER.index(name)
 
 
-def make(name: str, seed: int | None = None, device="cpu", B=None, H=None, N=None) -> Workload:
+def make(name: str, seed: int | None = None, device="cpu", B=None, H=None, N=None,
+         q_sigma: float | None = None) -> Workload:
     """Generate workload ``name`` (sizes may be overridden for reduced tests)."""
     B0, H0, N0, d, causal, sigma, kind = WORKLOADS[name]
     B = B0 if B is None else B
@@ -90,6 +94,8 @@ def make(name: str, seed: int | None = None, device="cpu", B=None, H=None, N=Non
         scale = torch.ones((B, H, N), device=device, dtype=torch.float32)
         scale.scatter_(-1, outl, 30.0)
         q *= scale.unsqueeze(-1)
+    if q_sigma is not None:
+        q += torch.randn((B, H, 1, d), generator=g, device=device, dtype=torch.float32) * q_sigma
     return Workload(name=name, B=B, H=H, N=N, d=d, causal=causal, sm_scale=1.0 / math.sqrt(d),
                     seed=seed, q=q.to(torch.bfloat16), k=k.to(torch.bfloat16),
                     v=v.to(torch.bfloat16), outlier_tokens=outl)
