@@ -235,6 +235,49 @@ int sage_attn_fwd_sparse(const int8_t* q8, const float* q_scale, const int8_t* k
                          void* stream);
 
 /*
+ * Q smoothing (the pages' outlier smoothing -- wxsanhe §三.1, txrjy.com
+ * QbitAI repost, section 四个步骤极限压缩时间 -- applied to Q as well as K).
+ * Queries that share a per-channel offset waste the INT8 range of Q on it;
+ * subtracting each 128-query block's channel means before quantizing keeps the
+ * range for what varies.  Unlike the K mean, the Q mean changes the scores
+ * (by q_mean . k_j per key), so that share is put back in FP32:
+ *   1. sage_quant_qk_smooth: as sage_quant_qk_ex, except that Q is first
+ *      smoothed: q_mean[b][h][r][c] = the mean of channel c over block r's
+ *      valid rows, taken on the K mean's exact 2^-30 grid
+ *      (fp32(fp64(I) / (fp64(rows) 2^30)), I the wrapping int64 sum of
+ *      trunc(x 2^30)); the codes quantize fp32(Q - q_mean[r]) (block or token
+ *      scales as q_gran says).  q_mean: fp32 [B][H][nblk][d].
+ *   2. sage_q_smooth_bias: bias[b][h][r][j] = fp32(acc * lambda), acc the fp32
+ *      fused-multiply-add chain over c = 0 .. d-1 (ascending, from 0) of
+ *      q_mean[r][c] * fp32(K[j][c] - k_mean[c]); lambda = fp32(sm_scale *
+ *      log2 e).  bias: fp32 [B][H][nblk][N_pad]; keys j >= N get 0.  k is
+ *      the same bf16 K (same layout) that sage_quant_qk_smooth read.
+ *   3. sage_attn_fwd_smooth: as sage_attn_fwd_ex (tile_mask == NULL) or
+ *      sage_attn_fwd_sparse (tile_mask != NULL), with the scores of query i
+ *      (block r = i / 128) and key j taken as
+ *        s_j = fma(S_j, c, bias[r][j]),  m_t = max_j s_j,
+ *        p_j = exp2(fp32(s_j - mu))
+ *      (m', alpha, mu, l, P and the epilogue unchanged).  sm_scale must be the
+ *      one the bias was computed with.  About 20 % more vector work per score
+ *      than the unsmoothed kernel.
+ * sage_qsmooth_sizes gives the byte sizes of q_mean and bias (host pointers).
+ * Errors: as the functions they extend; NULL q_mean / bias -> SAGE_ERR_NULL;
+ * sage_q_smooth_bias: bias elements >= 2^40 -> SAGE_ERR_SIZE.
+ */
+int sage_qsmooth_sizes(int B, int H, int N, int d, size_t* q_mean_bytes, size_t* bias_bytes);
+int sage_quant_qk_smooth(const void* q, const void* k, int B, int H, int N, int d, int layout,
+                         int q_gran, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale,
+                         float* k_mean, float* q_mean, void* workspace, size_t workspace_bytes,
+                         void* stream);
+int sage_q_smooth_bias(const float* q_mean, const void* k, const float* k_mean, int B, int H,
+                       int N, int d, int layout, float sm_scale, float* bias, void* stream);
+int sage_attn_fwd_smooth(const int8_t* q8, const float* q_scale, const int8_t* k8,
+                         const float* k_scale, const void* vq, const float* v_scale, int B, int H,
+                         int N, int d, int layout, int causal, float sm_scale, int pv_dtype,
+                         int q_gran, const float* bias, const uint8_t* tile_mask, void* out,
+                         int out_dtype, void* stream);
+
+/*
  * sage_attn_fwd that also writes the raw int32 Q K^T accumulators of head
  * (b, h), queries [row0, row0 + nrows), all keys, to s_out [nrows][N]
  * (row-major).  With causal, only entries j <= i are written; the others are

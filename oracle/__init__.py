@@ -59,7 +59,7 @@ def lib():
             "or_quant_block": [P, i32, i32, P, P],
             "or_quant_q": [P, i32, i32, i32, P, P, P],
             "or_quant_q_smooth": [P, i32, i32, i32, P, P, P, P],
-            "or_q_smooth_bias": [P, P, P, i32, i32, f32, P],
+            "or_q_smooth_bias": [P, P, P, i32, i32, f32, i32, i32, P],
             "or_quant_k": [P, i32, i32, i32, i32, P, P, P, P],
             "or_quant_v": [P, i32, i32, i32, P, P],
             "or_dump_s": [P, P, i32, i32, i32, i32, i32, P],
@@ -185,21 +185,26 @@ def quant_qk(q: np.ndarray, k: np.ndarray, blk: int = BLK, smooth: bool = True,
     return out
 
 
-def smooth_bias(qz: dict, k: np.ndarray, sm_scale: float) -> np.ndarray:
+def smooth_bias(qz: dict, k: np.ndarray, sm_scale: float, blocks=None) -> np.ndarray:
     """The Q-smoothing correction of every head: fp32 [B, H, nblk, N] (block
-    r, key j) from qz["q_mean"], qz["k_mean"] and the bf16 K codes."""
+    r, key j) from qz["q_mean"], qz["k_mean"] and the bf16 K codes.  With
+    ``blocks`` (a list of block indices) only those rows are computed; the
+    others are left NaN."""
     B, H, N, d = k.shape
     nb = (N + BLK - 1) // BLK
-    out = np.empty((B, H, nb, N), np.float32)
+    blocks = range(nb) if blocks is None else sorted(set(int(r) for r in blocks))
+    out = np.full((B, H, nb, N), np.nan, np.float32)
     L = lib()
     for b in range(B):
         for h in range(H):
             qmh = np.ascontiguousarray(qz["q_mean"][b, h], np.float32)
             kh = np.ascontiguousarray(k[b, h], np.uint16)
             kmh = np.ascontiguousarray(qz["k_mean"][b, h], np.float32)
-            bh = np.empty((nb, N), np.float32)
-            L.or_q_smooth_bias(_p(qmh), _p(kh), _p(kmh), N, d, float(sm_scale), _p(bh))
-            out[b, h] = bh
+            row = np.empty(N, np.float32)
+            for r in blocks:
+                L.or_q_smooth_bias(_p(qmh), _p(kh), _p(kmh), N, d, float(sm_scale), r, r + 1,
+                                   _p(row))
+                out[b, h, r] = row
     return out
 
 

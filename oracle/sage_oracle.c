@@ -317,17 +317,17 @@ OR_API float or_lambda(float sm_scale) { return (float)((double)sm_scale * 1.442
  * units of the attention (lambda = sm_scale log2 e).  Pinned against FP64
  * numpy within the fp32 dot-product error bound; zero means give 0. */
 OR_API void or_q_smooth_bias(const float* qmean, const uint16_t* k, const float* kmean, int N,
-                             int d, float sm_scale, float* bias /* [nb][N] */) {
+                             int d, float sm_scale, int r0, int r1,
+                             float* bias /* [r1 - r0][N]: blocks r0 .. r1-1 */) {
     float lambda = or_lambda(sm_scale);
-    int nb = (N + 127) / 128;
-    for (int r = 0; r < nb; ++r)
+    for (int r = r0; r < r1; ++r)
         for (int j = 0; j < N; ++j) {
             float acc = 0.0f;
             for (int c = 0; c < d; ++c) {
                 float kp = or_bf16_to_f32(k[(int64_t)j * d + c]) - kmean[c];
                 acc = fmaf(qmean[(int64_t)r * d + c], kp, acc);
             }
-            bias[(int64_t)r * N + j] = acc * lambda;
+            bias[(int64_t)(r - r0) * N + j] = acc * lambda;
         }
 }
 

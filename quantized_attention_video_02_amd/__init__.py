@@ -44,7 +44,9 @@ class SageConfig(ct.Structure):
 
 EXPORTS = ["sage_get_config", "sage_quant_sizes", "sage_quant_sizes_ex", "sage_quant_qk",
            "sage_quant_qk_ex", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_ex",
-           "sage_attn_fwd_sparse", "sage_attn_fwd_debug", "sage_status_string"]
+           "sage_attn_fwd_sparse", "sage_attn_fwd_debug", "sage_qsmooth_sizes",
+           "sage_quant_qk_smooth", "sage_q_smooth_bias", "sage_attn_fwd_smooth",
+           "sage_status_string"]
 
 _lib = None
 
@@ -70,6 +72,10 @@ def lib():
     L.sage_attn_fwd_sparse.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, I, P]
     L.sage_attn_fwd_debug.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, I, I, I,
                                       P, P]
+    L.sage_qsmooth_sizes.argtypes = [I, I, I, I, ct.POINTER(S), ct.POINTER(S)]
+    L.sage_quant_qk_smooth.argtypes = [P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, S, P]
+    L.sage_q_smooth_bias.argtypes = [P, P, P, I, I, I, I, I, F, P, P]
+    L.sage_attn_fwd_smooth.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, P, I, P]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = I
     L.sage_status_string.argtypes = [I]
@@ -123,9 +129,20 @@ def _empty(nbytes: int, device, dtype=torch.uint8):
     return torch.empty(max(1, nbytes // itemsize), dtype=dtype, device=device)
 
 
-def quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", q_gran: str = "block") -> dict:
+def qsmooth_sizes(B: int, H: int, N: int, d: int) -> tuple[int, int]:
+    """Bytes of q_mean and of the Q-smoothing correction (sage_qsmooth_sizes)."""
+    a, b = ct.c_size_t(), ct.c_size_t()
+    _check(lib().sage_qsmooth_sizes(B, H, N, d, ct.byref(a), ct.byref(b)))
+    return a.value, b.value
+
+
+def quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", q_gran: str = "block",
+             q_smooth: bool = False, sm_scale: float | None = None) -> dict:
     """Smooth K and quantize Q, K to INT8 (sage_quant_qk; sage_quant_qk_ex with
-    q_gran="token" for one Q scale per query row)."""
+    q_gran="token" for one Q scale per query row).  q_smooth: Q is smoothed by
+    its per-block mean too (sage_quant_qk_smooth) and the correction of the
+    scores is computed for ``sm_scale`` (sage_q_smooth_bias; default
+    1/sqrt(d)); attn_fwd then has to run with the same sm_scale."""
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
         raise TypeError("q and k must be bfloat16")
     if q.shape != k.shape or not q.is_contiguous() or not k.is_contiguous():
@@ -145,7 +162,16 @@ def quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", q_gran: str 
              workspace=_empty(sz[BUF_WS_QK], dev, torch.int64))
     bufs = (_ptr(r["q8"]), _ptr(r["q_scale"]), _ptr(r["k8"]), _ptr(r["k_scale"]),
             _ptr(r["k_mean"]), _ptr(r["workspace"]), sz[BUF_WS_QK], _stream(dev))
-    if q_gran == "block":
+    if q_smooth:
+        sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+        r["q_mean"] = torch.empty((B, H, nblk, d), dtype=torch.float32, device=dev)
+        r["bias"] = torch.empty((B, H, nblk, nblk * 128), dtype=torch.float32, device=dev)
+        _check(lib().sage_quant_qk_smooth(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout],
+                                          QGRAN[q_gran], *bufs[:5], _ptr(r["q_mean"]), *bufs[5:]))
+        _check(lib().sage_q_smooth_bias(_ptr(r["q_mean"]), _ptr(k), _ptr(r["k_mean"]), B, H, N, d,
+                                        LAYOUTS[layout], sm, _ptr(r["bias"]), _stream(dev)))
+        r["bias_sm_scale"] = sm
+    elif q_gran == "block":
         _check(lib().sage_quant_qk(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout], *bufs))
     else:
         _check(lib().sage_quant_qk_ex(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout], QGRAN[q_gran],
@@ -180,7 +206,8 @@ def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
     ``debug=(b, h, row0, nrows)`` calls sage_attn_fwd_debug and also returns
     the int32 Q K^T accumulators [nrows, N].  With ``tile_mask`` (uint8 or
     bool [B, H, nblk, nblk] on the device: query block x key tile, nonzero =
-    visit) calls sage_attn_fwd_sparse."""
+    visit) calls sage_attn_fwd_sparse.  When ``qz`` comes from quant_qk with
+    q_smooth, calls sage_attn_fwd_smooth (dense or with the tile mask)."""
     B, H, N, d, layout = qz["B"], qz["H"], qz["N"], qz["d"], qz["layout"]
     sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
     shape = (B, H, N, d) if layout == "HND" else (B, N, H, d)
@@ -191,6 +218,7 @@ def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
             _ptr(vs), B, H, N, d, LAYOUTS[layout], int(bool(causal)), sm, PV[pv], _ptr(out),
             OUT[out.dtype])
     q_gran = qz.get("q_gran", "block")
+    tm = None
     if tile_mask is not None:
         if debug is not None:
             raise ValueError("the debug dump runs dense")
@@ -198,6 +226,16 @@ def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
         if tuple(tile_mask.shape) != (B, H, nblk, nblk) or tile_mask.device != dev:
             raise ValueError(f"tile_mask must be [B, H, {nblk}, {nblk}] on {dev}")
         tm = tile_mask.to(torch.uint8).contiguous()
+    if "bias" in qz:
+        if debug is not None:
+            raise ValueError("the debug dump runs without Q smoothing")
+        if sm != qz["bias_sm_scale"]:
+            raise ValueError(f"the Q-smoothing correction was computed for sm_scale "
+                             f"{qz['bias_sm_scale']}, not {sm}")
+        _check(lib().sage_attn_fwd_smooth(*args[:14], QGRAN[q_gran], _ptr(qz["bias"]), _ptr(tm),
+                                          *args[14:], _stream(dev)))
+        return out
+    if tm is not None:
         _check(lib().sage_attn_fwd_sparse(*args[:14], QGRAN[q_gran], _ptr(tm), *args[14:],
                                           _stream(dev)))
         return out
@@ -219,10 +257,10 @@ def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
 def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
          sm_scale: float | None = None, pv: str = "fp8", layout: str = "HND",
          out_dtype=torch.bfloat16, q_gran: str = "block",
-         tile_mask: torch.Tensor | None = None) -> torch.Tensor:
+         tile_mask: torch.Tensor | None = None, q_smooth: bool = False) -> torch.Tensor:
     """softmax(Q K^T sm_scale) V through the quantized path (quantize, then the
     fused kernel), all on q's device and current stream."""
-    qz = quant_qk(q, k, layout, q_gran)
+    qz = quant_qk(q, k, layout, q_gran, q_smooth=q_smooth, sm_scale=sm_scale)
     vq, vs = quant_v(v, pv, layout)
     return attn_fwd(qz, vq, vs, causal=causal, sm_scale=sm_scale, pv=pv, out_dtype=out_dtype,
                     tile_mask=tile_mask)

@@ -66,9 +66,10 @@ Sizes sizes_of(int B, int H, int N, int d, int pv, int q_gran = SAGE_QGRAN_BLOCK
 int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
                 const void* vq, const float* v_scale, int B, int H, int N, int d, int layout,
                 int causal, float sm_scale, int pv_dtype, int q_gran, const uint8_t* tmask,
-                int sparse, void* out, int out_dtype, int dump, int db, int dh, int row0,
-                int nrows, int32_t* s_out, void* stream) {
+                int sparse, const float* bias, int smooth, void* out, int out_dtype, int dump,
+                int db, int dh, int row0, int nrows, int32_t* s_out, void* stream) {
     if (!q8 || !q_scale || !k8 || !k_scale || !vq || !v_scale || !out) return SAGE_ERR_NULL;
+    if (smooth && !bias) return SAGE_ERR_NULL;
     if (sparse && !tmask) return SAGE_ERR_NULL;
     if (dump && !s_out) return SAGE_ERR_NULL;
     SAGE_TRY(check_dims(B, H, N, d));
@@ -88,7 +89,7 @@ int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const 
         return SAGE_ERR_SIZE;
     if (!aligned16(q8) || !aligned16(q_scale) || !aligned16(k8) || !aligned16(k_scale) ||
         !aligned16(vq) || !aligned16(v_scale) || !aligned16(out) || (dump && !aligned16(s_out)) ||
-        (sparse && !aligned16(tmask)))
+        (sparse && !aligned16(tmask)) || (smooth && !aligned16(bias)))
         return SAGE_ERR_ALIGN;
     sage::AttnArgs a;
     a.q8 = q8;
@@ -109,6 +110,7 @@ int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const 
     a.out_fp32 = out_dtype == SAGE_OUT_FP32;
     a.qtok = q_gran == SAGE_QGRAN_TOKEN;
     a.tmask = sparse ? tmask : nullptr;
+    a.bias = smooth ? bias : nullptr;
     a.lambda = (float)((double)sm_scale * 1.4426950408889634);
     a.dbh = dump ? db * H + dh : -1;
     a.drow0 = row0;
@@ -154,6 +156,33 @@ __attribute__((visibility("default"))) int sage_quant_sizes(int B, int H, int N,
     return sage_quant_sizes_ex(B, H, N, d, pv_dtype, SAGE_QGRAN_BLOCK, sizes);
 }
 
+namespace {
+
+int quant_qk_common(const void* q, const void* k, int B, int H, int N, int d, int layout,
+                    int q_gran, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale,
+                    float* k_mean, int smooth, float* q_mean, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (!q || !k || !q8 || !q_scale || !k8 || !k_scale || !k_mean || !workspace ||
+        (smooth && !q_mean))
+        return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_layout(layout));
+    SAGE_TRY(check_qgran(q_gran));
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q8) || !aligned16(q_scale) ||
+        !aligned16(k8) || !aligned16(k_scale) || !aligned16(k_mean) || !aligned16(workspace) ||
+        (smooth && !aligned16(q_mean)))
+        return SAGE_ERR_ALIGN;
+    const Sizes s = sizes_of(B, H, N, d, SAGE_PV_FP8, q_gran);
+    if (workspace_bytes < s.v[SAGE_BUF_WS_QK]) return SAGE_ERR_WORKSPACE;
+    const hipError_t e = sage::launch_quant_qk((const sage::u16*)q, (const sage::u16*)k, B, H, N,
+                                               d, layout, q_gran == SAGE_QGRAN_TOKEN, q8, q_scale,
+                                               k8, k_scale, k_mean, smooth ? q_mean : nullptr,
+                                               (uint64_t*)workspace, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+}  // namespace
+
 __attribute__((visibility("default"))) int sage_quant_qk_ex(const void* q, const void* k, int B,
                                                             int H, int N, int d, int layout,
                                                             int q_gran, int8_t* q8,
@@ -162,20 +191,47 @@ __attribute__((visibility("default"))) int sage_quant_qk_ex(const void* q, const
                                                             void* workspace,
                                                             size_t workspace_bytes,
                                                             void* stream) {
-    if (!q || !k || !q8 || !q_scale || !k8 || !k_scale || !k_mean || !workspace)
-        return SAGE_ERR_NULL;
+    return quant_qk_common(q, k, B, H, N, d, layout, q_gran, q8, q_scale, k8, k_scale, k_mean, 0,
+                           nullptr, workspace, workspace_bytes, stream);
+}
+
+__attribute__((visibility("default"))) int sage_qsmooth_sizes(int B, int H, int N, int d,
+                                                              size_t* q_mean_bytes,
+                                                              size_t* bias_bytes) {
+    if (!q_mean_bytes || !bias_bytes) return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    const size_t nblk = ((size_t)N + sage::kBlk - 1) / sage::kBlk;
+    const size_t bh = (size_t)B * H;
+    *q_mean_bytes = bh * nblk * d * sizeof(float);
+    *bias_bytes = bh * nblk * nblk * sage::kBlk * sizeof(float);
+    return SAGE_OK;
+}
+
+__attribute__((visibility("default"))) int sage_quant_qk_smooth(
+    const void* q, const void* k, int B, int H, int N, int d, int layout, int q_gran, int8_t* q8,
+    float* q_scale, int8_t* k8, float* k_scale, float* k_mean, float* q_mean, void* workspace,
+    size_t workspace_bytes, void* stream) {
+    return quant_qk_common(q, k, B, H, N, d, layout, q_gran, q8, q_scale, k8, k_scale, k_mean, 1,
+                           q_mean, workspace, workspace_bytes, stream);
+}
+
+__attribute__((visibility("default"))) int sage_q_smooth_bias(const float* q_mean, const void* k,
+                                                              const float* k_mean, int B, int H,
+                                                              int N, int d, int layout,
+                                                              float sm_scale, float* bias,
+                                                              void* stream) {
+    if (!q_mean || !k || !k_mean || !bias) return SAGE_ERR_NULL;
     SAGE_TRY(check_dims(B, H, N, d));
     SAGE_TRY(check_layout(layout));
-    SAGE_TRY(check_qgran(q_gran));
-    if (!aligned16(q) || !aligned16(k) || !aligned16(q8) || !aligned16(q_scale) ||
-        !aligned16(k8) || !aligned16(k_scale) || !aligned16(k_mean) || !aligned16(workspace))
+    if (!(isfinite(sm_scale) && sm_scale > 0.0f)) return SAGE_ERR_INVALID;
+    const int64_t nblk = ((int64_t)N + sage::kBlk - 1) / sage::kBlk;
+    if ((int64_t)B * H * nblk * nblk * sage::kBlk >= kMaxElems || nblk > 65535 * 32)
+        return SAGE_ERR_SIZE;
+    if (!aligned16(q_mean) || !aligned16(k) || !aligned16(k_mean) || !aligned16(bias))
         return SAGE_ERR_ALIGN;
-    const Sizes s = sizes_of(B, H, N, d, SAGE_PV_FP8, q_gran);
-    if (workspace_bytes < s.v[SAGE_BUF_WS_QK]) return SAGE_ERR_WORKSPACE;
-    const hipError_t e = sage::launch_quant_qk((const sage::u16*)q, (const sage::u16*)k, B, H, N,
-                                               d, layout, q_gran == SAGE_QGRAN_TOKEN, q8, q_scale,
-                                               k8, k_scale, k_mean, (uint64_t*)workspace,
-                                               (hipStream_t)stream);
+    const float lambda = (float)((double)sm_scale * 1.4426950408889634);
+    const hipError_t e = sage::launch_q_bias(q_mean, (const sage::u16*)k, k_mean, B, H, N, d,
+                                             layout, lambda, bias, (hipStream_t)stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
@@ -214,8 +270,8 @@ __attribute__((visibility("default"))) int sage_attn_fwd(
     const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
     float sm_scale, int pv_dtype, void* out, int out_dtype, void* stream) {
     return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
-                       pv_dtype, SAGE_QGRAN_BLOCK, nullptr, 0, out, out_dtype, 0, 0, 0, 0, 1,
-                       nullptr, stream);
+                       pv_dtype, SAGE_QGRAN_BLOCK, nullptr, 0, nullptr, 0, out, out_dtype, 0, 0, 0,
+                       0, 1, nullptr, stream);
 }
 
 __attribute__((visibility("default"))) int sage_attn_fwd_ex(
@@ -223,8 +279,8 @@ __attribute__((visibility("default"))) int sage_attn_fwd_ex(
     const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
     float sm_scale, int pv_dtype, int q_gran, void* out, int out_dtype, void* stream) {
     return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
-                       pv_dtype, q_gran, nullptr, 0, out, out_dtype, 0, 0, 0, 0, 1, nullptr,
-                       stream);
+                       pv_dtype, q_gran, nullptr, 0, nullptr, 0, out, out_dtype, 0, 0, 0, 0, 1,
+                       nullptr, stream);
 }
 
 __attribute__((visibility("default"))) int sage_attn_fwd_sparse(
@@ -233,8 +289,18 @@ __attribute__((visibility("default"))) int sage_attn_fwd_sparse(
     float sm_scale, int pv_dtype, int q_gran, const uint8_t* tile_mask, void* out,
     int out_dtype, void* stream) {
     return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
-                       pv_dtype, q_gran, tile_mask, 1, out, out_dtype, 0, 0, 0, 0, 1, nullptr,
-                       stream);
+                       pv_dtype, q_gran, tile_mask, 1, nullptr, 0, out, out_dtype, 0, 0, 0, 0, 1,
+                       nullptr, stream);
+}
+
+__attribute__((visibility("default"))) int sage_attn_fwd_smooth(
+    const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+    const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
+    float sm_scale, int pv_dtype, int q_gran, const float* bias, const uint8_t* tile_mask,
+    void* out, int out_dtype, void* stream) {
+    return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
+                       pv_dtype, q_gran, tile_mask, tile_mask != nullptr, bias, 1, out, out_dtype,
+                       0, 0, 0, 0, 1, nullptr, stream);
 }
 
 __attribute__((visibility("default"))) int sage_attn_fwd_debug(
@@ -243,8 +309,8 @@ __attribute__((visibility("default"))) int sage_attn_fwd_debug(
     float sm_scale, int pv_dtype, void* out, int out_dtype, int b, int h, int row0, int nrows,
     int32_t* s_out, void* stream) {
     return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
-                       pv_dtype, SAGE_QGRAN_BLOCK, nullptr, 0, out, out_dtype, 1, b, h, row0,
-                       nrows, s_out, stream);
+                       pv_dtype, SAGE_QGRAN_BLOCK, nullptr, 0, nullptr, 0, out, out_dtype, 1, b,
+                       h, row0, nrows, s_out, stream);
 }
 
 __attribute__((visibility("default"))) const char* sage_status_string(int status) {

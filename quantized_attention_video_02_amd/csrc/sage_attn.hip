@@ -189,8 +189,39 @@ struct MaskTile {
 // and F = float(S) with masked keys at -inf.  With needmask (wave-uniform),
 // the keys past `lim` (key - key_t - 4 hh > lim: beyond N, or after the query
 // when causal) are masked.
-__device__ inline void softmax_prep(v16i* S, v16f* F, float c, float& m, float& alpha, float& mu,
-                                    bool needmask, int lim) {
+// With Q smoothing (brow = this lane's block row of the tile's correction in
+// LDS): F = s = fma(float(S), c, bias) and the max is taken over s.
+template <bool QSM>
+__device__ inline void softmax_prep(v16i* S, v16f* F, float c, const uint8_t* brow, float& m,
+                                    float& alpha, float& mu, bool needmask, int lim, int hh) {
+    if constexpr (QSM) {
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // keys 32 k4 + 8 i + 4 hh + (0..3): registers 4 i .. 4 i + 3
+                const float4 bb = *(const float4*)(brow + 4 * (32 * k4 + 8 * i + 4 * hh));
+                F[k4][4 * i + 0] = __builtin_fmaf((float)S[k4][4 * i + 0], c, bb.x);
+                F[k4][4 * i + 1] = __builtin_fmaf((float)S[k4][4 * i + 1], c, bb.y);
+                F[k4][4 * i + 2] = __builtin_fmaf((float)S[k4][4 * i + 2], c, bb.z);
+                F[k4][4 * i + 3] = __builtin_fmaf((float)S[k4][4 * i + 3], c, bb.w);
+            }
+        if (needmask) MaskTile<0, 0>::apply_float(F, lim);
+        float mk[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            float x = fmaxf(F[k4][0], F[k4][1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) x = fmaxf(fmaxf(x, F[k4][r]), F[k4][r + 1]);
+            mk[k4] = x;
+        }
+        const float mt = pair_fmax(fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3])));
+        const float mn = fmaxf(m, mt);
+        alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        mu = mn - kLog2PScale;
+        return;
+    }
     if (needmask) MaskTile<0, 0>::apply_int(S, lim);
     int mk[4];
 #pragma unroll
@@ -217,14 +248,17 @@ __device__ inline void softmax_prep(v16i* S, v16f* F, float c, float& m, float& 
 // P (FP8 e4m3 or FP16) into the P V operand, and the partial row sum.
 // c == 0 only when the whole tile's S is 0; any positive factor then gives
 // the same argument, and a positive one keeps -inf * factor = -inf.
-template <typename PT>
+// With Q smoothing F already holds s: p = exp2(fp32(s - mu)).
+template <bool QSM, typename PT>
 __device__ inline float softmax_block(const v16f& Fk, PT* P, int k4, float cf, float mu) {
     float part[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         float p[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(Fk[4 * u + j], cf, -mu));
+        for (int j = 0; j < 4; ++j)
+            p[j] = __builtin_amdgcn_exp2f(QSM ? Fk[4 * u + j] - mu
+                                              : __builtin_fmaf(Fk[4 * u + j], cf, -mu));
         part[u] = (p[0] + p[1]) + (p[2] + p[3]);
         if constexpr (__is_same(PT, v8i)) {
             // the first half-word write keeps the other half of its old operand;
@@ -344,7 +378,8 @@ __device__ inline void store_row(const AttnArgs& a, const v16f* O, float lt, int
 }
 
 // MODE: kDense, kDump (also writes the int32 Q K^T of one head), kSparse
-// (visits only the key tiles a tile mask selects).
+// (visits only the key tiles a tile mask selects).  QSM: Q smoothing, the
+// scores carry the per-(query block, key) correction a.bias.
 enum { kDense = 0, kDump = 1, kSparse = 2 };
 
 // Waves per workgroup: 8 (256 queries, one workgroup per CU), or 4 (128
@@ -356,17 +391,23 @@ constexpr int attn_waves() {
     return (MODE == kSparse && !(PV16 && D == 128)) ? 4 : 8;
 }
 
-template <int D, bool PV16, bool CAUSAL, int MODE>
+// LDS bytes of one slot of the correction tile: one 512-byte row (128 keys)
+// per 128-query block of the workgroup, a whole 1 KB copy piece in any case.
+constexpr int kBiasSlot = 1024;
+
+template <int D, bool PV16, bool CAUSAL, int MODE, bool QSM>
 __global__ __launch_bounds__((64 * attn_waves<D, PV16, MODE>()), (8 / attn_waves<D, PV16, MODE>()))
 void attn_fwd_kernel(AttnArgs a) {
     constexpr bool DUMP = MODE == kDump, SPARSE = MODE == kSparse;
+    static_assert(!(QSM && DUMP), "the dump runs without Q smoothing");
     constexpr int NW = attn_waves<D, PV16, MODE>(), NT = 64 * NW, BR = 32 * NW;
     using L = Lds<D, PV16>;
     using PT = typename std::conditional<PV16, v8h, v8i>::type;
     constexpr int NP = PV16 ? 8 : 2;
     constexpr int KK = D / 32;
     constexpr int CB = D / 32;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::TOTAL];
+    constexpr int BBASE = L::TOTAL;  // correction tiles (Q smoothing), two slots
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::TOTAL + (QSM ? 2 * kBiasSlot : 0)];
     // sparse: the key tiles this workgroup visits, ascending; bits 14 / 15 say
     // whether the first / second 128-query block of the workgroup visits it
     __shared__ uint16_t vlist[SPARSE ? kMaxSparseTiles : 1];
@@ -410,6 +451,21 @@ void attn_fwd_kernel(AttnArgs a) {
     auto load_v = [&](int t, int T) {
         tile_to_lds<L::VPIECES, VMAXP, NW>(vg + (int64_t)T * L::VHBM,
                                            lbase + L::VBASE + (t & 1) * L::VBYTES, wv, voff);
+    };
+    // Q smoothing: the correction rows of the workgroup's query blocks for key
+    // tile T, one 1 KB piece issued by the last wave: lanes 0-31 copy the
+    // first block's 512 bytes, lanes 32-63 the second block's (the first
+    // again when the workgroup has one block or its second is past the end)
+    const uint8_t* bg = nullptr;
+    uint32_t boff = 0;
+    if (QSM) {
+        const int r0 = qt * (NW / 4);
+        const int r1 = (NW == 8 && r0 + 1 < a.nblk) ? r0 + 1 : r0;
+        bg = (const uint8_t*)(a.bias + ((int64_t)bh * a.nblk + r0) * a.N_pad);
+        boff = (uint32_t)((hh ? (r1 - r0) : 0) * a.N_pad * 4 + 16 * n);
+    }
+    auto load_bias = [&](int t, int T) {
+        if (QSM && wv == NW - 1) dma_piece(bg + (int64_t)T * 512, boff, lbase + BBASE + (t & 1) * kBiasSlot);
     };
     if (SPARSE) {
         // wave 0 compacts the visited tiles: tile T is visited when one of the
@@ -465,6 +521,7 @@ void attn_fwd_kernel(AttnArgs a) {
     }
     if (!SPARSE || ntiles > 0) load_k(0, SPARSE ? (e0 & 0x3fff) : 0);
     if (ntiles > 1) load_k(1, SPARSE ? (e1 & 0x3fff) : 1);
+    if (!SPARSE || ntiles > 0) load_bias(0, SPARSE ? (e0 & 0x3fff) : 0);
     wait_vmem();
     __syncthreads();
 #pragma unroll
@@ -484,6 +541,7 @@ void attn_fwd_kernel(AttnArgs a) {
         const uint32_t e3raw = (SPARSE && t + 3 < ntiles) ? vlist[t + 3] : 0u;
         if (t + 2 < ntiles) load_k(t + 2, SPARSE ? (e2 & 0x3fff) : t + 2);
         load_v(t, T);
+        if (t + 1 < ntiles) load_bias(t + 1, SPARSE ? (e1 & 0x3fff) : t + 1);
         const int key_t = T * kBc;
         if (DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows)
             dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
@@ -496,7 +554,8 @@ void attn_fwd_kernel(AttnArgs a) {
                               !visits;
         v16f F[4];
         float mu;
-        softmax_prep(S, F, c, m, alpha, mu, needmask, visits ? kmax - key_t - 4 * hh : -1);
+        softmax_prep<QSM>(S, F, c, smem + BBASE + (t & 1) * kBiasSlot + (wave >> 2) * 512, m, alpha,
+                          mu, needmask, visits ? kmax - key_t - 4 * hh : -1, hh);
         // no key seen yet (m = -inf): any finite mu keeps p = exp2(-inf) = 0
         if (SPARSE && m == -INFINITY) mu = 0.0f;
         const float cf = c == 0.0f ? 1.0f : c;
@@ -506,7 +565,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) {
             S[k4] = qk_block<D, L::KSTR>(kb, qf, k4, n, hh);
-            part[k4] = softmax_block(F[k4], P, k4, cf, mu);
+            part[k4] = softmax_block<QSM>(F[k4], P, k4, cf, mu);
         }
         l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
         if (SPARSE) {
@@ -594,11 +653,11 @@ __global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
         const bool needmask = tail && t == a.nblk - 1;
         v16f F[4];
         float mu, alpha;
-        softmax_prep(S, F, c, m, alpha, mu, needmask, kmax - key_t - 4 * hh);
+        softmax_prep<false>(S, F, c, nullptr, m, alpha, mu, needmask, kmax - key_t - 4 * hh, hh);
         const float cf = c == 0.0f ? 1.0f : c;
         float part[4];
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) part[k4] = softmax_block(F[k4], P, k4, cf, mu);
+        for (int k4 = 0; k4 < 4; ++k4) part[k4] = softmax_block<false>(F[k4], P, k4, cf, mu);
         l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
         pv_tile<D>(smem + VB + (t & 1) * L::VBYTES, P, O, alpha, n, hh);
         wait_vmem();
@@ -609,21 +668,22 @@ __global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
     store_row<D, false>(a, O, lt, b, h, bh, qi, hh);
 }
 
-template <int D, bool PV16, bool CAUSAL, int MODE>
+template <int D, bool PV16, bool CAUSAL, int MODE, bool QSM>
 static const void* attn_fn() {
-    return (const void*)attn_fwd_kernel<D, PV16, CAUSAL, MODE>;
+    return (const void*)attn_fwd_kernel<D, PV16, CAUSAL, MODE, QSM>;
 }
 
-template <int D, bool PV16, int MODE>
+template <int D, bool PV16, int MODE, bool QSM>
 static const void* attn_fn_rt(bool causal) {
-    return causal ? attn_fn<D, PV16, true, MODE>() : attn_fn<D, PV16, false, MODE>();
+    return causal ? attn_fn<D, PV16, true, MODE, QSM>() : attn_fn<D, PV16, false, MODE, QSM>();
 }
 
 template <int D, bool PV16>
-static const void* attn_fn_rt(bool causal, int mode) {
-    if (mode == kDump) return attn_fn_rt<D, PV16, kDump>(causal);
-    if (mode == kSparse) return attn_fn_rt<D, PV16, kSparse>(causal);
-    return attn_fn_rt<D, PV16, kDense>(causal);
+static const void* attn_fn_rt(bool causal, int mode, bool qsm) {
+    if (mode == kDump) return attn_fn_rt<D, PV16, kDump, false>(causal);
+    if (mode == kSparse)
+        return qsm ? attn_fn_rt<D, PV16, kSparse, true>(causal) : attn_fn_rt<D, PV16, kSparse, false>(causal);
+    return qsm ? attn_fn_rt<D, PV16, kDense, true>(causal) : attn_fn_rt<D, PV16, kDense, false>(causal);
 }
 
 // The 12-wave d = 64 sweep processes about 1.24x the queries per unit time of
@@ -652,12 +712,15 @@ static int sparse_waves(int d, int pv16) {
 hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal, int dump,
                        hipStream_t s) {
     const int mode = dump ? kDump : (args.tmask ? kSparse : kDense);
+    const bool qsm = args.bias != nullptr && !dump;
     const void* fn;
-    if (d == 128) fn = pv16 ? attn_fn_rt<128, true>(causal, mode) : attn_fn_rt<128, false>(causal, mode);
-    else fn = pv16 ? attn_fn_rt<64, true>(causal, mode) : attn_fn_rt<64, false>(causal, mode);
+    if (d == 128)
+        fn = pv16 ? attn_fn_rt<128, true>(causal, mode, qsm) : attn_fn_rt<128, false>(causal, mode, qsm);
+    else
+        fn = pv16 ? attn_fn_rt<64, true>(causal, mode, qsm) : attn_fn_rt<64, false>(causal, mode, qsm);
     AttnArgs a = args;
     int nw = mode == kSparse ? sparse_waves(d, pv16) : 8;
-    if (mode == kDense && !causal && d == 64 && np12_pays(B * a.H, a.N)) {
+    if (mode == kDense && !qsm && !causal && d == 64 && np12_pays(B * a.H, a.N)) {
         nw = 12;
         fn = pv16 ? (const void*)attn_np_kernel<64, true, 12> : (const void*)attn_np_kernel<64, false, 12>;
     }

@@ -63,6 +63,7 @@ struct AttnArgs {
     int H, N, N_pad, nblk, nqt, total, layout, out_fp32;
     int qtok;  // 1: q_scale per query row [bh][N_pad]; 0: per block of kBlk rows [bh][nblk]
     const uint8_t* tmask;  // NULL (dense) or [B*H][nblk][nblk]: query block x key tile, nonzero = visit
+    const float* bias;     // NULL, or the Q-smoothing correction [B*H][nblk][N_pad] (exp2 units)
     float lambda;    // fp32(sm_scale * log2 e)
     int dbh, drow0, dnrows;
 };
@@ -70,7 +71,9 @@ struct AttnArgs {
 hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
                            int qtok,
                            int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean,
-                           uint64_t* ws, hipStream_t s);
+                           float* qmean, uint64_t* ws, hipStream_t s);
+hipError_t launch_q_bias(const float* qmean, const u16* k, const float* kmean, int B, int H, int N,
+                         int d, int layout, float lambda, float* bias, hipStream_t s);
 hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, int pv16,
                           void* vq, float* vscale, float* ws, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal, int dump,

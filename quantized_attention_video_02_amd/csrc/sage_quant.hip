@@ -3,7 +3,9 @@
 //   k_stats / v_stats : per (b, h, chunk of 512 tokens) partial column
 //                       statistics (exact fixed-point K sums; V absmax),
 //   k_mean / v_scale  : per (b, h, channel) combination of the partials,
-//   quant_qk          : per (b, h, block of 128 rows) INT8 codes + scale,
+//   quant_qk          : per (b, h, block of 128 rows) INT8 codes + scale
+//                       (optionally Q smoothed by the block's token mean),
+//   q_bias            : the Q-smoothing correction q_mean . k' per (block, key),
 //   quant_v           : per (b, h, tile of 128 keys) FP8 e4m3 (or FP16) codes,
 //                       transposed to [channel][key] with the key order the
 //                       attention kernel's P V operand expects.
@@ -171,16 +173,32 @@ __global__ __launch_bounds__(kQuantThreads) void v_scale_kernel(const float* __r
     }
 }
 
+// trunc(x * 2^30) saturated at +-2^62, NaN -> 0 (the grid of the K mean), for
+// an fp32 x: the fp64 product is exact (a power-of-two scaling).
+__device__ inline uint64_t fix30_f32(float x) {
+    if (x != x) return 0;
+    const double t = (double)x * 1073741824.0;
+    if (t >= 4611686018427387904.0) return 1ull << 62;
+    if (t <= -4611686018427387904.0) return 0ull - (1ull << 62);
+    return (uint64_t)(int64_t)t;
+}
+
 // One block of 128 rows of Q (blockIdx.z == 0) or of smoothed K (z == 1).
+// qmean != NULL: Q is smoothed first by the block's channel means, taken on
+// the K mean's exact 2^-30 grid over the block's valid rows; the means go to
+// qmean [bh][nblk][D].
 template <int D>
 __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, int H, int N, int N_pad, int nblk,
     int layout, int qtok, const float* __restrict__ kmean, int8_t* __restrict__ q8,
-    float* __restrict__ q_scale, int8_t* __restrict__ k8, float* __restrict__ k_scale) {
+    float* __restrict__ q_scale, int8_t* __restrict__ k8, float* __restrict__ k_scale,
+    float* __restrict__ qmean) {
     constexpr int CPR = D / 8;
     constexpr int RPI = kQuantThreads / CPR;
     constexpr int IT = kBlk / RPI;
     __shared__ float wmax[kQuantThreads / 64];
+    __shared__ uint64_t red[RPI][D];
+    __shared__ float bmean[D];
     const int blk = blockIdx.x, bh = blockIdx.y, isk = blockIdx.z;
     const int b = bh / H, h = bh % H;
     const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
@@ -189,7 +207,6 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) mu[e] = isk ? kmean[bh * D + cg * 8 + e] : 0.0f;
     float x[IT][8];
-    float amax = 0.0f;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int row = blk * kBlk + tr + it * RPI;
@@ -201,13 +218,48 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
                 x[it][2 * e] = bf16_bits_to_f32(ws[e] & 0xffffu) - mu[2 * e];
                 x[it][2 * e + 1] = bf16_bits_to_f32(ws[e] >> 16) - mu[2 * e + 1];
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[it][e]));
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[it][e] = 0.0f;
         }
     }
+    if (!isk && qmean) {
+        // block means: exact wrapping int64 sums of trunc(x 2^30) per channel
+        // (padded rows hold 0 and add 0), combined over the RPI row lanes
+        uint64_t acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0;
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += fix30_f32(x[it][e]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[tr][cg * 8 + e] = acc[e];
+        __syncthreads();
+        if (t < D) {
+            uint64_t sum = 0;
+#pragma unroll 8
+            for (int r = 0; r < RPI; ++r) sum += red[r][t];
+            const int nrows = min(kBlk, N - blk * kBlk);
+            const float m = (float)((double)(int64_t)sum / ((double)nrows * 1073741824.0));
+            bmean[t] = m;
+            qmean[((int64_t)bh * nblk + blk) * D + t] = m;
+        }
+        __syncthreads();
+        float qm[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qm[e] = bmean[cg * 8 + e];
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+            if (blk * kBlk + tr + it * RPI < N)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[it][e] -= qm[e];
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[it][e]));
     if (!isk && qtok) {
         // one scale per query row: the row's CPR lanes are consecutive lanes of
         // one wave, so its absmax is a butterfly over them.  Padded rows get
@@ -255,6 +307,56 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
         *(uint2*)(dst + ((int64_t)bh * N_pad + row) * D + cg * 8) = make_uint2(packed[0], packed[1]);
     }
     if (t == 0) (isk ? k_scale : q_scale)[bh * nblk + blk] = (float)((double)a / 127.0);
+}
+
+// Q-smoothing correction: bias[bh][r][j] = fp32(acc * lambda) with acc the
+// fp32 fma chain over c = 0 .. D-1 (ascending) of qmean[bh][r][c] * k'[j][c],
+// k' = fp32(K - kmean).  One thread per key j (k'_j held in registers), the
+// query blocks r of this workgroup's slice in groups of kBiasGroup; the means
+// are uniform across the workgroup (scalar loads).  Keys j in [N, N_pad) get 0.
+constexpr int kBiasSlice = 32, kBiasGroup = 8;
+
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void q_bias_kernel(
+    const float* __restrict__ qmean, const u16* __restrict__ k, const float* __restrict__ kmean,
+    int H, int N, int N_pad, int nblk, int layout, float lambda, float* __restrict__ bias) {
+    const int j = blockIdx.x * kQuantThreads + threadIdx.x;
+    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int r0 = blockIdx.z * kBiasSlice, r1 = min(nblk, r0 + kBiasSlice);
+    float kp[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) kp[c] = 0.0f;
+    if (j < N) {
+        const u16* row = k + row_offset(layout, b, h, j, H, N, D);
+#pragma unroll
+        for (int c8 = 0; c8 < D / 8; ++c8) {
+            const uint4 w = *(const uint4*)(row + 8 * c8);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kp[8 * c8 + 2 * e] = bf16_bits_to_f32(ws[e] & 0xffffu) - kmean[bh * D + 8 * c8 + 2 * e];
+                kp[8 * c8 + 2 * e + 1] =
+                    bf16_bits_to_f32(ws[e] >> 16) - kmean[bh * D + 8 * c8 + 2 * e + 1];
+            }
+        }
+    }
+    for (int rg = r0; rg < r1; rg += kBiasGroup) {
+        float acc[kBiasGroup];
+        const float* qm[kBiasGroup];
+#pragma unroll
+        for (int g = 0; g < kBiasGroup; ++g) {
+            acc[g] = 0.0f;
+            qm[g] = qmean + ((int64_t)bh * nblk + min(rg + g, r1 - 1)) * D;
+        }
+#pragma unroll
+        for (int c = 0; c < D; ++c)
+#pragma unroll
+            for (int g = 0; g < kBiasGroup; ++g) acc[g] = __builtin_fmaf(qm[g][c], kp[c], acc[g]);
+        if (j < N_pad)
+#pragma unroll
+            for (int g = 0; g < kBiasGroup; ++g)
+                if (rg + g < r1) bias[((int64_t)bh * nblk + rg + g) * N_pad + j] = acc[g] * lambda;
+    }
 }
 
 // Position of key r (0..127) of a tile inside the tile's [channel][128] rows.
@@ -376,7 +478,7 @@ static inline hipError_t launch(const void* fn, dim3 grid, dim3 block, void** ar
 
 hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
                            int qtok, int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean,
-                           uint64_t* ws, hipStream_t s) {
+                           float* qmean, uint64_t* ws, hipStream_t s) {
     const int nblk = (N + kBlk - 1) / kBlk, N_pad = nblk * kBlk;
     const int nchunk = (N + kStatsChunk - 1) / kStatsChunk;
     const int BH = B * H;
@@ -396,11 +498,22 @@ hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int 
         void* args[] = {(void*)&q,      (void*)&k,    (void*)&H,     (void*)&N,
                         (void*)&N_pad,  (void*)&nblk, (void*)&layout, (void*)&qtok,
                         (void*)&kmean,  (void*)&q8,   (void*)&qs,     (void*)&k8,
-                        (void*)&ks};
+                        (void*)&ks,     (void*)&qmean};
         const void* fn = d == 128 ? (const void*)quant_qk_kernel<128> : (const void*)quant_qk_kernel<64>;
         if ((e = launch(fn, dim3(nblk, BH, 2), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_q_bias(const float* qmean, const u16* k, const float* kmean, int B, int H, int N,
+                         int d, int layout, float lambda, float* bias, hipStream_t s) {
+    const int nblk = (N + kBlk - 1) / kBlk, N_pad = nblk * kBlk;
+    void* args[] = {(void*)&qmean, (void*)&k,     (void*)&kmean,  (void*)&H,      (void*)&N,
+                    (void*)&N_pad, (void*)&nblk, (void*)&layout, (void*)&lambda, (void*)&bias};
+    const void* fn = d == 128 ? (const void*)q_bias_kernel<128> : (const void*)q_bias_kernel<64>;
+    const dim3 grid((N_pad + kQuantThreads - 1) / kQuantThreads, B * H,
+                    (nblk + kBiasSlice - 1) / kBiasSlice);
+    return launch(fn, grid, dim3(kQuantThreads), args, s);
 }
 
 hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, int pv16,

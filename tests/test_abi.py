@@ -75,6 +75,12 @@ def test_quant_sizes(sage):
     assert sage.quant_sizes(2, 3, 300, 64, "fp8", q_gran="block") == s
 
 
+def test_qsmooth_sizes(sage):
+    qm, bias = sage.qsmooth_sizes(2, 3, 300, 64)
+    assert qm == 2 * 3 * 3 * 64 * 4                  # [B][H][nblk][d] fp32
+    assert bias == 2 * 3 * 3 * 384 * 4               # [B][H][nblk][N_pad] fp32
+
+
 def _codes(sage):
     L = sage.lib()
     return L, {L.sage_status_string(c).decode().split(":")[0]: c for c in range(-8, 1)}
@@ -140,6 +146,30 @@ def test_invalid_arguments_rejected_before_launch(sage):
     assert sp(g=5) == -2
     assert sp(N=2048 * 128 + 1) == -5      # more key tiles than a sparse launch can list
     assert sp(N=2048 * 128, tm=A + 3) == -4   # the size passes; validation stops at alignment
+    a_, b_ = ct.c_size_t(), ct.c_size_t()
+    assert L.sage_qsmooth_sizes(1, 1, 10, 128, None, ct.byref(b_)) == -1
+    assert L.sage_qsmooth_sizes(1, 1, 0, 128, ct.byref(a_), ct.byref(b_)) == -2
+    qks = lambda qm=A, g=0, q=A: L.sage_quant_qk_smooth(q, A, 1, 1, 256, 128, 0, g, A, A, A, A, A,
+                                                       qm, A, 1 << 20, None)
+    assert qks(qm=None) == -1
+    assert qks(qm=A + 8) == -4
+    assert qks(g=4) == -2
+    assert qks(q=None) == -1
+    qb = lambda qm=A, sm=0.1, N=256, bias=A, H=1: L.sage_q_smooth_bias(qm, A, A, 1, H, N, 128, 0, sm,
+                                                                       bias, None)
+    assert qb(qm=None) == -1
+    assert qb(bias=None) == -1
+    assert qb(sm=0.0) == -2
+    assert qb(sm=float("nan")) == -2
+    assert qb(bias=A + 4) == -4
+    assert qb(N=1 << 20, H=4096) == -5      # the correction alone would be 2^40+ floats
+    sm_ = lambda bias=A, tm=None, g=0, N=256: L.sage_attn_fwd_smooth(
+        A, A, A, A, A, A, 1, 2, N, 128, 0, 0, 0.1, 0, g, bias, tm, A, 0, None)
+    assert sm_(bias=None) == -1
+    assert sm_(bias=A + 4) == -4
+    assert sm_(g=3) == -2
+    assert sm_(tm=A + 3) == -4
+    assert sm_(tm=A, N=2048 * 128 + 1) == -5
     dbg = lambda b=0, h=0, row0=0, nrows=4, s=A: L.sage_attn_fwd_debug(
         A, A, A, A, A, A, 1, 2, 256, 128, 0, 0, 0.1, 0, A, 0, b, h, row0, nrows, s, None)
     assert dbg(s=None) == -1
