@@ -242,14 +242,15 @@ int sage_attn_fwd_sparse(const int8_t* q8, const float* q_scale, const int8_t* k
  * range for what varies.  Unlike the K mean, the Q mean changes the scores
  * (by q_mean . k_j per key), so that share is put back in FP32:
  *   1. sage_quant_qk_smooth: as sage_quant_qk_ex, except that Q is first
- *      smoothed: q_mean[b][h][r][c] = the mean of channel c over block r's
+ *      smoothed: q_mean[b][h][c][r] = the mean of channel c over block r's
  *      valid rows, taken on the K mean's exact 2^-30 grid
  *      (fp32(fp64(I) / (fp64(rows) 2^30)), I the wrapping int64 sum of
- *      trunc(x 2^30)); the codes quantize fp32(Q - q_mean[r]) (block or token
- *      scales as q_gran says).  q_mean: fp32 [B][H][nblk][d].
+ *      trunc(x 2^30)); the codes quantize fp32(Q - q_mean[.][r]) (block or
+ *      token scales as q_gran says).  q_mean: fp32 [B][H][d][nbp],
+ *      channel-major, nbp = 16 ceil(nblk / 16); entries r >= nblk are 0.
  *   2. sage_q_smooth_bias: bias[b][h][r][j] = fp32(acc * lambda), acc the fp32
  *      fused-multiply-add chain over c = 0 .. d-1 (ascending, from 0) of
- *      q_mean[r][c] * fp32(K[j][c] - k_mean[c]); lambda = fp32(sm_scale *
+ *      q_mean[c][r] * fp32(K[j][c] - k_mean[c]); lambda = fp32(sm_scale *
  *      log2 e).  bias: fp32 [B][H][nblk][N_pad]; keys j >= N get 0.  k is
  *      the same bf16 K (same layout) that sage_quant_qk_smooth read.
  *   3. sage_attn_fwd_smooth: as sage_attn_fwd_ex (tile_mask == NULL) or

@@ -140,7 +140,8 @@ def quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", q_gran: str 
              q_smooth: bool = False, sm_scale: float | None = None) -> dict:
     """Smooth K and quantize Q, K to INT8 (sage_quant_qk; sage_quant_qk_ex with
     q_gran="token" for one Q scale per query row).  q_smooth: Q is smoothed by
-    its per-block mean too (sage_quant_qk_smooth) and the correction of the
+    its per-block mean too (sage_quant_qk_smooth; q_mean is channel-major
+    [B, H, d, nbp]) and the correction of the
     scores is computed for ``sm_scale`` (sage_q_smooth_bias; default
     1/sqrt(d)); attn_fwd then has to run with the same sm_scale."""
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
@@ -164,7 +165,8 @@ def quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", q_gran: str 
             _ptr(r["k_mean"]), _ptr(r["workspace"]), sz[BUF_WS_QK], _stream(dev))
     if q_smooth:
         sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
-        r["q_mean"] = torch.empty((B, H, nblk, d), dtype=torch.float32, device=dev)
+        nbp = -(-nblk // 16) * 16
+        r["q_mean"] = torch.empty((B, H, d, nbp), dtype=torch.float32, device=dev)
         r["bias"] = torch.empty((B, H, nblk, nblk * 128), dtype=torch.float32, device=dev)
         _check(lib().sage_quant_qk_smooth(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout],
                                           QGRAN[q_gran], *bufs[:5], _ptr(r["q_mean"]), *bufs[5:]))

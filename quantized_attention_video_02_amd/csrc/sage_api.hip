@@ -202,7 +202,8 @@ __attribute__((visibility("default"))) int sage_qsmooth_sizes(int B, int H, int 
     SAGE_TRY(check_dims(B, H, N, d));
     const size_t nblk = ((size_t)N + sage::kBlk - 1) / sage::kBlk;
     const size_t bh = (size_t)B * H;
-    *q_mean_bytes = bh * nblk * d * sizeof(float);
+    const size_t nbp = (nblk + sage::kBiasBlocks - 1) / sage::kBiasBlocks * sage::kBiasBlocks;
+    *q_mean_bytes = bh * d * nbp * sizeof(float);
     *bias_bytes = bh * nblk * nblk * sage::kBlk * sizeof(float);
     return SAGE_OK;
 }

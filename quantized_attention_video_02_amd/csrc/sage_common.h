@@ -18,6 +18,10 @@ constexpr int kBlk = 128;          // rows per Q / K quantization block
 constexpr int kBc = 128;           // keys per online-softmax tile (== kBlk)
 constexpr int kBr = 256;           // queries per dense attention workgroup (8 waves x 32)
 constexpr int kAttnThreads = 512;  // 8 wave64s
+// Q-smoothing correction kernel: keys per thread, query blocks per register
+// group (q_mean is padded to a multiple of this many blocks), blocks per
+// workgroup slice.
+constexpr int kBiasKeys = 4, kBiasBlocks = 16, kBiasSlice = 128;
 constexpr int kMaxSparseTiles = 2048;  // key tiles a sparse launch may list (N <= 262144)
 constexpr int kStatsChunk = 512;   // tokens per statistics workgroup
 constexpr int kQuantThreads = 256;

@@ -186,8 +186,9 @@ __device__ inline uint64_t fix30_f32(float x) {
 // One block of 128 rows of Q (blockIdx.z == 0) or of smoothed K (z == 1).
 // qmean != NULL: Q is smoothed first by the block's channel means, taken on
 // the K mean's exact 2^-30 grid over the block's valid rows; the means go to
-// qmean [bh][nblk][D].
-template <int D>
+// qmean [bh][D][nbp] (channel-major, blocks padded to nbp = 16 ceil(nblk/16)
+// with zeros).
+template <int D, bool QSM>
 __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, int H, int N, int N_pad, int nblk,
     int layout, int qtok, const float* __restrict__ kmean, int8_t* __restrict__ q8,
@@ -197,11 +198,12 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
     constexpr int RPI = kQuantThreads / CPR;
     constexpr int IT = kBlk / RPI;
     __shared__ float wmax[kQuantThreads / 64];
-    __shared__ uint64_t red[RPI][D];
-    __shared__ float bmean[D];
+    __shared__ uint64_t red[QSM ? RPI : 1][D];
+    __shared__ float bmean[QSM ? D : 1];
     const int blk = blockIdx.x, bh = blockIdx.y, isk = blockIdx.z;
     const int b = bh / H, h = bh % H;
     const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
+    const int nbp = (nblk + kBiasBlocks - 1) / kBiasBlocks * kBiasBlocks;
     const u16* src = isk ? k : q;
     float mu[8];
 #pragma unroll
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
             for (int e = 0; e < 8; ++e) x[it][e] = 0.0f;
         }
     }
-    if (!isk && qmean) {
+    if (QSM && !isk) {
         // block means: exact wrapping int64 sums of trunc(x 2^30) per channel
         // (padded rows hold 0 and add 0), combined over the RPI row lanes
         uint64_t acc[8];
@@ -243,7 +245,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
             const int nrows = min(kBlk, N - blk * kBlk);
             const float m = (float)((double)(int64_t)sum / ((double)nrows * 1073741824.0));
             bmean[t] = m;
-            qmean[((int64_t)bh * nblk + blk) * D + t] = m;
+            float* col = qmean + ((int64_t)bh * D + t) * nbp;
+            col[blk] = m;
+            if (blk == nblk - 1)
+                for (int r = nblk; r < nbp; ++r) col[r] = 0.0f;
         }
         __syncthreads();
         float qm[8];
@@ -310,52 +315,85 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
 }
 
 // Q-smoothing correction: bias[bh][r][j] = fp32(acc * lambda) with acc the
-// fp32 fma chain over c = 0 .. D-1 (ascending) of qmean[bh][r][c] * k'[j][c],
-// k' = fp32(K - kmean).  One thread per key j (k'_j held in registers), the
-// query blocks r of this workgroup's slice in groups of kBiasGroup; the means
-// are uniform across the workgroup (scalar loads).  Keys j in [N, N_pad) get 0.
-constexpr int kBiasSlice = 32, kBiasGroup = 8;
-
+// fp32 fma chain over c = 0 .. D-1 (ascending) of qmean[r][c] * k'[j][c],
+// k' = fp32(K - kmean).  A thread owns kBiasKeys consecutive keys and
+// kBiasBlocks query blocks at a time (64 accumulators), so each mean feeds 4
+// fused multiply-adds.  The means of the current 16 blocks (qmean is
+// channel-major: [c][16 blocks] is one contiguous 64-byte run per channel)
+// are staged in LDS and read as broadcasts, 4 blocks per 16-byte read.  K is
+// re-read per group of blocks in chunks of 32 channels (from L2: a workgroup
+// covers 1024 keys = 256 KB at d = 128).  Keys j in [N, N_pad) get 0.
 template <int D>
 __global__ __launch_bounds__(kQuantThreads) void q_bias_kernel(
     const float* __restrict__ qmean, const u16* __restrict__ k, const float* __restrict__ kmean,
     int H, int N, int N_pad, int nblk, int layout, float lambda, float* __restrict__ bias) {
-    const int j = blockIdx.x * kQuantThreads + threadIdx.x;
+    constexpr int CH = 32;  // channels per chunk
+    __shared__ __attribute__((aligned(16))) float qs[D][kBiasBlocks];
+    const int j0 = (blockIdx.x * kQuantThreads + threadIdx.x) * kBiasKeys;
     const int bh = blockIdx.y, b = bh / H, h = bh % H;
-    const int r0 = blockIdx.z * kBiasSlice, r1 = min(nblk, r0 + kBiasSlice);
-    float kp[D];
+    const int nbp = (nblk + kBiasBlocks - 1) / kBiasBlocks * kBiasBlocks;
+    const int s0 = blockIdx.z * kBiasSlice, s1 = min(nbp, s0 + kBiasSlice);
+    const float* km = kmean + bh * D;
+    for (int r0 = s0; r0 < s1; r0 += kBiasBlocks) {
+        __syncthreads();  // the previous group's reads of qs are done
+        for (int i = threadIdx.x; i < D * kBiasBlocks / 4; i += kQuantThreads) {
+            const int c = i / (kBiasBlocks / 4), q4 = i % (kBiasBlocks / 4);
+            *(float4*)&qs[c][4 * q4] = *(const float4*)(qmean + ((int64_t)bh * D + c) * nbp + r0 + 4 * q4);
+        }
+        __syncthreads();
+        float acc[kBiasBlocks][kBiasKeys];
 #pragma unroll
-    for (int c = 0; c < D; ++c) kp[c] = 0.0f;
-    if (j < N) {
-        const u16* row = k + row_offset(layout, b, h, j, H, N, D);
+        for (int g = 0; g < kBiasBlocks; ++g)
 #pragma unroll
-        for (int c8 = 0; c8 < D / 8; ++c8) {
-            const uint4 w = *(const uint4*)(row + 8 * c8);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            for (int e = 0; e < kBiasKeys; ++e) acc[g][e] = 0.0f;
+        for (int cc = 0; cc < D; cc += CH) {
+            float kp[kBiasKeys][CH];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kp[8 * c8 + 2 * e] = bf16_bits_to_f32(ws[e] & 0xffffu) - kmean[bh * D + 8 * c8 + 2 * e];
-                kp[8 * c8 + 2 * e + 1] =
-                    bf16_bits_to_f32(ws[e] >> 16) - kmean[bh * D + 8 * c8 + 2 * e + 1];
+            for (int e = 0; e < kBiasKeys; ++e) {
+                const int j = j0 + e;
+                if (j < N) {
+                    const u16* row = k + row_offset(layout, b, h, j, H, N, D) + cc;
+#pragma unroll
+                    for (int c8 = 0; c8 < CH / 8; ++c8) {
+                        const uint4 w = *(const uint4*)(row + 8 * c8);
+                        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            kp[e][8 * c8 + 2 * u] = bf16_bits_to_f32(ws[u] & 0xffffu) - km[cc + 8 * c8 + 2 * u];
+                            kp[e][8 * c8 + 2 * u + 1] =
+                                bf16_bits_to_f32(ws[u] >> 16) - km[cc + 8 * c8 + 2 * u + 1];
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) kp[e][c] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                float qv[kBiasBlocks];
+#pragma unroll
+                for (int q4 = 0; q4 < kBiasBlocks / 4; ++q4) {
+                    const float4 f = *(const float4*)&qs[cc + c][4 * q4];
+                    qv[4 * q4] = f.x;
+                    qv[4 * q4 + 1] = f.y;
+                    qv[4 * q4 + 2] = f.z;
+                    qv[4 * q4 + 3] = f.w;
+                }
+#pragma unroll
+                for (int g = 0; g < kBiasBlocks; ++g)
+#pragma unroll
+                    for (int e = 0; e < kBiasKeys; ++e)
+                        acc[g][e] = __builtin_fmaf(qv[g], kp[e][c], acc[g][e]);
             }
         }
-    }
-    for (int rg = r0; rg < r1; rg += kBiasGroup) {
-        float acc[kBiasGroup];
-        const float* qm[kBiasGroup];
+        if (j0 < N_pad)
 #pragma unroll
-        for (int g = 0; g < kBiasGroup; ++g) {
-            acc[g] = 0.0f;
-            qm[g] = qmean + ((int64_t)bh * nblk + min(rg + g, r1 - 1)) * D;
-        }
-#pragma unroll
-        for (int c = 0; c < D; ++c)
-#pragma unroll
-            for (int g = 0; g < kBiasGroup; ++g) acc[g] = __builtin_fmaf(qm[g][c], kp[c], acc[g]);
-        if (j < N_pad)
-#pragma unroll
-            for (int g = 0; g < kBiasGroup; ++g)
-                if (rg + g < r1) bias[((int64_t)bh * nblk + rg + g) * N_pad + j] = acc[g] * lambda;
+            for (int g = 0; g < kBiasBlocks; ++g)
+                if (r0 + g < nblk)
+                    *(float4*)(bias + ((int64_t)bh * nblk + r0 + g) * N_pad + j0) =
+                        make_float4(acc[g][0] * lambda, acc[g][1] * lambda, acc[g][2] * lambda,
+                                    acc[g][3] * lambda);
     }
 }
 
@@ -499,7 +537,10 @@ hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int 
                         (void*)&N_pad,  (void*)&nblk, (void*)&layout, (void*)&qtok,
                         (void*)&kmean,  (void*)&q8,   (void*)&qs,     (void*)&k8,
                         (void*)&ks,     (void*)&qmean};
-        const void* fn = d == 128 ? (const void*)quant_qk_kernel<128> : (const void*)quant_qk_kernel<64>;
+        const void* fn = qmean ? (d == 128 ? (const void*)quant_qk_kernel<128, true>
+                                           : (const void*)quant_qk_kernel<64, true>)
+                               : (d == 128 ? (const void*)quant_qk_kernel<128, false>
+                                           : (const void*)quant_qk_kernel<64, false>);
         if ((e = launch(fn, dim3(nblk, BH, 2), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
     }
     return hipSuccess;
@@ -511,8 +552,9 @@ hipError_t launch_q_bias(const float* qmean, const u16* k, const float* kmean, i
     void* args[] = {(void*)&qmean, (void*)&k,     (void*)&kmean,  (void*)&H,      (void*)&N,
                     (void*)&N_pad, (void*)&nblk, (void*)&layout, (void*)&lambda, (void*)&bias};
     const void* fn = d == 128 ? (const void*)q_bias_kernel<128> : (const void*)q_bias_kernel<64>;
-    const dim3 grid((N_pad + kQuantThreads - 1) / kQuantThreads, B * H,
-                    (nblk + kBiasSlice - 1) / kBiasSlice);
+    const int nbp = (nblk + kBiasBlocks - 1) / kBiasBlocks * kBiasBlocks;
+    const dim3 grid((N_pad + kQuantThreads * kBiasKeys - 1) / (kQuantThreads * kBiasKeys), B * H,
+                    (nbp + kBiasSlice - 1) / kBiasSlice);
     return launch(fn, grid, dim3(kQuantThreads), args, s);
 }
 

@@ -77,7 +77,7 @@ def test_quant_sizes(sage):
 
 def test_qsmooth_sizes(sage):
     qm, bias = sage.qsmooth_sizes(2, 3, 300, 64)
-    assert qm == 2 * 3 * 3 * 64 * 4                  # [B][H][nblk][d] fp32
+    assert qm == 2 * 3 * 64 * 16 * 4                 # [B][H][d][16 ceil(nblk/16)] fp32
     assert bias == 2 * 3 * 3 * 384 * 4               # [B][H][nblk][N_pad] fp32
 
 

@@ -44,8 +44,17 @@ def _bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
 
 
+def _q_mean(qz):
+    """The GPU's channel-major, block-padded q_mean as [B, H, nblk, d]; the
+    padding must be 0."""
+    m = qz["q_mean"].cpu().numpy()
+    nblk = -(-qz["N"] // 128)
+    assert not m[..., nblk:].any()
+    return np.ascontiguousarray(np.swapaxes(m[..., :nblk], -1, -2))
+
+
 def _check_quant(qz, oz, obias, N):
-    g = lambda key: qz[key].cpu().numpy()
+    g = lambda key: _q_mean(qz) if key == "q_mean" else qz[key].cpu().numpy()
     assert np.array_equal(g("q8")[:, :, :N], oz["q8"]) and not g("q8")[:, :, N:].any()
     assert np.array_equal(g("k8")[:, :, :N], oz["k8"])
     for key in ("q_scale", "k_scale", "k_mean", "q_mean"):
@@ -166,8 +175,9 @@ def test_qsmooth_full_size_sampled(sage, orc):
         blocks = sorted({0, 1, nblk - 1, int(rng.integers(2, nblk - 1))})
         obias = orc.smooth_bias(oz, k, wl.sm_scale, blocks=blocks)
         assert np.array_equal(qz["q8"][b, h, :N].cpu().numpy(), oz["q8"][0, 0])
-        for key in ("q_scale", "k_scale", "k_mean", "q_mean"):
+        for key in ("q_scale", "k_scale", "k_mean"):
             assert np.array_equal(_bits(qz[key][b, h].cpu().numpy()), _bits(oz[key][0, 0])), key
+        assert np.array_equal(_bits(_q_mean(qz)[b, h]), _bits(oz["q_mean"][0, 0]))
         assert np.array_equal(_bits(qz["bias"][b, h, blocks, :N].cpu().numpy()),
                               _bits(obias[0, 0, blocks]))
         ovq, ovs = orc.quant_v(v, "fp8")
