@@ -81,7 +81,7 @@ def visited_ops(wl, mask):
     return 4.0 * wl.d * float((mask.astype(np.float64) * pairs).sum())
 
 
-def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None):
+def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None, q_smooth=False):
     import torch
 
     q, k, v = wl.q, wl.k, wl.v
@@ -90,7 +90,7 @@ def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None):
     def step(evs=None):
         if evs:
             evs[0].record(stream)
-        qz = sage.quant_qk(q, k, q_gran=q_gran)
+        qz = sage.quant_qk(q, k, q_gran=q_gran, q_smooth=q_smooth, sm_scale=wl.sm_scale)
         vq, vs = sage.quant_v(v, pv)
         if evs:
             evs[1].record(stream)
@@ -115,10 +115,12 @@ def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None):
     return wall, quant_ms, attn_ms
 
 
-def cpu_baseline(wl, pv, target_s=12.0, q_gran="block"):
+def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False):
     """The oracle as it stands (single-threaded C) on one head of the workload:
     quantization of the whole head, then attention for R query rows against
-    all N keys; the head's quantization time is charged pro rata (R / N)."""
+    all N keys; the head's quantization time is charged pro rata (R / N).
+    With Q smoothing the correction rows of the blocks the R rows use are
+    computed too (charged to the quantization at the rate per block)."""
     import numpy as np
 
     import oracle
@@ -127,26 +129,42 @@ def cpu_baseline(wl, pv, target_s=12.0, q_gran="block"):
     b, h = 0, 0
     q, k, v = (si.bf16_codes(t[b:b + 1, h:h + 1]) for t in (wl.q, wl.k, wl.v))
     t0 = time.perf_counter()
-    oz = oracle.quant_qk(q, k, q_gran=q_gran)
+    oz = oracle.quant_qk(q, k, q_gran=q_gran, q_smooth=q_smooth)
     ovq, ovs = oracle.quant_v(v, pv)
     t_quant = time.perf_counter() - t0
+    nblk = -(-wl.N // 128)
+    bias, t_bias = None, 0.0
     probe = np.arange(8, dtype=np.int32)
+    if q_smooth:
+        t0 = time.perf_counter()
+        bias = oracle.smooth_bias(oz, k, wl.sm_scale, blocks=[0])
+        t_bias = time.perf_counter() - t0                       # one block row
     t0 = time.perf_counter()
-    oracle.attn_rows_head(oz, ovq, ovs, 0, 0, probe, wl.causal, wl.sm_scale, pv)
+    oracle.attn_rows_head(oz, ovq, ovs, 0, 0, probe, wl.causal, wl.sm_scale, pv, bias=bias)
     per_row = (time.perf_counter() - t0) / len(probe)
-    R = int(max(8, min(wl.N, target_s / max(per_row, 1e-9))))
+    R = int(max(8, min(wl.N, target_s / max(per_row + t_bias / 128, 1e-9))))
     rows = np.arange(wl.N - R, wl.N, dtype=np.int32) if wl.causal else np.arange(R, dtype=np.int32)
+    if q_smooth:
+        used = sorted(set((rows // 128).tolist()))
+        t0 = time.perf_counter()
+        bias = oracle.smooth_bias(oz, k, wl.sm_scale, blocks=used)
+        t_bias = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.attn_rows_head(oz, ovq, ovs, 0, 0, rows, wl.causal, wl.sm_scale, pv)
+    oracle.attn_rows_head(oz, ovq, ovs, 0, 0, rows, wl.causal, wl.sm_scale, pv, bias=bias)
     t_attn = time.perf_counter() - t0
     keys = (rows + 1).sum() if wl.causal else R * wl.N
     ops = 4.0 * float(keys) * wl.d
+    # the whole head's quantization pro rata; the correction for the used
+    # blocks, pro rata of their rows
     t_equiv = t_attn + t_quant * R / wl.N
+    if q_smooth:
+        t_equiv += t_bias * R / (len(used) * 128)
     return {"value": ops / t_equiv / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
             "sample": (f"head (b=0,h=0) of {wl.name}: quantization of all {wl.N} tokens "
                        f"({t_quant:.2f} s, charged pro rata) + attention for {R} queries x "
-                       f"{'their causal keys' if wl.causal else f'{wl.N} keys'} ({t_attn:.2f} s); "
-                       "single-threaded C oracle")}
+                       f"{'their causal keys' if wl.causal else f'{wl.N} keys'} ({t_attn:.2f} s)"
+                       + (f"; Q-smoothing correction of their blocks ({t_bias:.2f} s, pro rata)"
+                          if q_smooth else "") + "; single-threaded C oracle")}
 
 
 def traffic_key(workload, pv, q_gran="block"):
@@ -206,6 +224,12 @@ def main():
     ap.add_argument("--tile-keep", type=float, default=None,
                     help="block-sparse run: keep each (query block, key tile) with this "
                          "probability, plus a local band and the first tile")
+    ap.add_argument("--q-smooth", action="store_true",
+                    help="Q smoothing: per-block Q means, the FP32 score correction, and the "
+                         "attention variant that adds it (all inside the timed step)")
+    ap.add_argument("--q-sigma", type=float, default=None,
+                    help="give the workload's queries a per-channel offset of this sigma "
+                         "(the inputs Q smoothing is for)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -231,7 +255,7 @@ def main():
 
     sage.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    wl = si.make(args.workload, device="cuda")
+    wl = si.make(args.workload, device="cuda", q_sigma=args.q_sigma)
     torch.cuda.synchronize()
     print(f"[bench] {wl.name}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} causal={wl.causal} pv={args.pv}",
           file=sys.stderr, flush=True)
@@ -247,7 +271,7 @@ def main():
         mask_np = tile_mask_for(wl, args.tile_keep)
         tmask = torch.from_numpy(mask_np).cuda()
     wall, quant_ms, attn_ms = time_gpu(sage, wl, args.pv, args.steps, args.warmup, args.q_gran,
-                                       tmask)
+                                       tmask, args.q_smooth)
     ops = attn_ops(wl.B, wl.H, wl.N, wl.d)
     # roofline work: all pairs when dense; the visited pairs of a sparse run
     work = ops if tmask is None else visited_ops(wl, mask_np)
@@ -264,7 +288,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f).get(traffic_key(wl.name, args.pv, args.q_gran))
-        if t and t.get("source_hash") == attn_source_hash():
+        if t and t.get("source_hash") == attn_source_hash() and not args.q_smooth:
             traffic = t.get("bytes_per_launch")
     res = {
         "metric": METRIC,
@@ -292,6 +316,15 @@ def main():
                   "gbps_two_pass": 13 * bhnd / (quant_mean * 1e-3) / 1e9,
                   "frac_hbm": 13 * bhnd / (quant_mean * 1e-3) / 1e9 / HBM_GBPS},
     }
+    if args.q_smooth or args.q_sigma is not None:
+        res["config"]["q_smooth"] = bool(args.q_smooth)
+        res["config"]["q_sigma"] = args.q_sigma
+    if args.q_smooth:
+        # the quantization phase now includes the correction kernel: its
+        # bytes are not the two-pass count above
+        res["quant"]["note"] = "includes the Q-smoothing correction kernel (VALU-bound)"
+        res["quant"].pop("gbps_two_pass")
+        res["quant"].pop("frac_hbm")
     if tmask is not None:
         # value stays the metric's formula over all N^2 pairs (dense-equivalent);
         # the roofline counts the visited pairs only
@@ -305,7 +338,8 @@ def main():
         res["roofline"]["useful_causal_tops"] = useful / (attn_mean * 1e-3) / 1e12
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, args.pv, args.cpu_seconds, args.q_gran)
+        res["cpu_baseline"] = cpu_baseline(wl, args.pv, args.cpu_seconds, args.q_gran,
+                                           args.q_smooth)
     print(json.dumps(res), flush=True)
 
 
