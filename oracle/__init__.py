@@ -19,7 +19,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "sage_oracle.c")
+_SRCS = [os.path.join(_HERE, "sage_oracle.c"), os.path.join(_HERE, "sage_oracle_mx.c")]
 _LIB_PATH = os.path.join(_HERE, "libsage_oracle.so")
 _CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
            "-Wall", "-Wextra"]
@@ -35,17 +35,22 @@ P_SCALE = 448.0
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no FMA contraction, no fast-math)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    if force or _stale():
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+def _stale() -> bool:
+    return not os.path.exists(_LIB_PATH) or any(
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(src) for src in _SRCS)
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        if _stale():
             build(force=True)
         L = ct.CDLL(_LIB_PATH)
         P = ct.c_void_p
@@ -66,6 +71,11 @@ def lib():
             "or_attn_rows": [P, P, P, P, P, P, i32, i32, P, i32, i32, f32, i32, i32, i32, i32, P, P,
                              P, P, P, P],
             "or_ref64_rows": [P, P, P, i32, i32, P, i32, i32, f64, P, P],
+            "or_f32_to_mx_n": [i32, P, i64, P], "or_mx_to_f32_n": [i32, P, i64, P],
+            "or_mx_blocks_n": [i32, P, i64, P, P],
+            "or_mx_quant_rows": [i32, P, P, i32, i32, P, P, P],
+            "or_mx_quant_v": [i32, P, i32, i32, P, P, P],
+            "or_mx_attn_rows": [i32, P, P, P, P, P, P, i32, i32, P, i32, i32, f32, P, P, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -73,6 +83,8 @@ def lib():
             fn.restype = None
         L.or_lambda.argtypes = [f32]
         L.or_lambda.restype = f32
+        L.or_mx_dot.argtypes = [i32, P, P, P, P, i32]
+        L.or_mx_dot.restype = f32
         _lib = L
     return _lib
 
@@ -305,3 +317,116 @@ def attention(q, k, v, causal: bool, sm_scale: float, pv: str = "fp8", rows=None
             out[b, h] = attn_rows_head(qz, vq, vs, b, h, rows, causal, sm_scale, pv,
                                        tile_mask=tile_mask, bias=qz.get("bias"))
     return out, qz, vq, vs
+
+
+# ---------------------------------------------------------- microscaled variant
+MX_FMT = {"mxfp4": 4, "mxfp6": 6}
+
+
+def f32_to_mx(x, fmt="mxfp6"):
+    """fp32 -> MX element codes (one per byte): E2M1 for mxfp4, E2M3 for mxfp6."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().or_f32_to_mx_n(MX_FMT[fmt], _p(x), x.size, _p(out))
+    return out
+
+
+def mx_to_f32(c, fmt="mxfp6"):
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    out = np.empty(c.shape, np.float32)
+    lib().or_mx_to_f32_n(MX_FMT[fmt], _p(c), c.size, _p(out))
+    return out
+
+
+def mx_blocks(x, fmt="mxfp6"):
+    """MX quantization of consecutive blocks of 32 fp32 values: (codes uint8
+    [..., 32] one element code per byte, E8M0 bytes [...])."""
+    x = np.ascontiguousarray(x, np.float32).reshape(-1, 32)
+    codes = np.empty(x.shape, np.uint8)
+    eb = np.empty(x.shape[0], np.uint8)
+    lib().or_mx_blocks_n(MX_FMT[fmt], _p(x), x.shape[0], _p(codes), _p(eb))
+    return codes, eb
+
+
+def mx_dequant(codes, ebytes, fmt="mxfp6"):
+    """Values of element codes times 2^(e - 127); ebytes broadcast against codes."""
+    return mx_to_f32(codes, fmt).astype(np.float64) * np.exp2(ebytes.astype(np.float64) - 127.0)
+
+
+def mx_quant_qk(q: np.ndarray, k: np.ndarray, fmt="mxfp6"):
+    """q, k: uint16 bf16 codes [B, H, N, d].  MX per token and 32 channels,
+    K smoothed by its token mean first.  Returns q_c/k_c (one element code per
+    byte, [B,H,N,d]), q_e/k_e (E8M0 bytes [B,H,N,d/32]) and k_mean."""
+    B, H, N, d = q.shape
+    f = MX_FMT[fmt]
+    out = {key: np.empty((B, H, N, d), np.uint8) for key in ("q_c", "k_c")}
+    out.update({key: np.empty((B, H, N, d // 32), np.uint8) for key in ("q_e", "k_e")})
+    out["k_mean"] = np.empty((B, H, d), np.float32)
+    out["fmt"] = fmt
+    tmp = np.empty(d, np.float32)
+    L = lib()
+    for b in range(B):
+        for h in range(H):
+            qh = np.ascontiguousarray(q[b, h], np.uint16)
+            kh = np.ascontiguousarray(k[b, h], np.uint16)
+            km = np.empty(d, np.float32)
+            L.or_k_mean(_p(kh), N, d, _p(km))
+            for key, src, mean in (("q", qh, None), ("k", kh, km)):
+                c = np.empty((N, d), np.uint8)
+                e = np.empty((N, d // 32), np.uint8)
+                L.or_mx_quant_rows(f, _p(src), None if mean is None else _p(mean), N, d, _p(c),
+                                   _p(e), _p(tmp))
+                out[key + "_c"][b, h], out[key + "_e"][b, h] = c, e
+            out["k_mean"][b, h] = km
+    return out
+
+
+def mx_quant_v(v: np.ndarray, fmt="mxfp6"):
+    """v: uint16 bf16 codes [B,H,N,d].  MX per channel and 32 keys:
+    (v_c codes [B,H,N,d], v_e E8M0 bytes [B,H,ceil(N/32),d])."""
+    B, H, N, d = v.shape
+    nb = (N + 31) // 32
+    vc = np.empty((B, H, N, d), np.uint8)
+    ve = np.empty((B, H, nb, d), np.uint8)
+    tmp = np.empty(32, np.float32)
+    for b in range(B):
+        for h in range(H):
+            vh = np.ascontiguousarray(v[b, h], np.uint16)
+            c = np.empty((N, d), np.uint8)
+            e = np.empty((nb, d), np.uint8)
+            lib().or_mx_quant_v(MX_FMT[fmt], _p(vh), N, d, _p(c), _p(e), _p(tmp))
+            vc[b, h], ve[b, h] = c, e
+    return vc, ve
+
+
+def mx_attn_rows_head(mz: dict, v_c, v_e, b: int, h: int, rows, causal: bool, sm_scale: float,
+                      return_ml: bool = False):
+    """MX attention for query rows ``rows`` of head (b, h): fp32 [len(rows), d]."""
+    hd = {key: np.ascontiguousarray(mz[key][b, h]) for key in ("q_c", "q_e", "k_c", "k_e")}
+    vch, veh = np.ascontiguousarray(v_c[b, h]), np.ascontiguousarray(v_e[b, h])
+    N, d = hd["k_c"].shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    out = np.empty((len(rows), d), np.float32)
+    m = np.empty(len(rows), np.float32)
+    l = np.empty(len(rows), np.float32)
+    scratch = np.empty(3 * 128 + 2 * d, np.float32)
+    lib().or_mx_attn_rows(MX_FMT[mz["fmt"]], _p(hd["q_c"]), _p(hd["q_e"]), _p(hd["k_c"]),
+                          _p(hd["k_e"]), _p(vch), _p(veh), N, d, _p(rows), len(rows), int(causal),
+                          float(sm_scale), _p(out), _p(m), _p(l), _p(scratch))
+    if return_ml:
+        return out, m, l
+    return out
+
+
+def mx_attention(q, k, v, causal: bool, sm_scale: float, rows=None, fmt="mxfp6"):
+    """Whole MX pipeline for ``rows`` (default all) of every head: (out fp32
+    [B,H,len(rows),d], quantized dict, v_c, v_e)."""
+    B, H, N, d = q.shape
+    mz = mx_quant_qk(q, k, fmt)
+    vc, ve = mx_quant_v(v, fmt)
+    rows = np.arange(N, dtype=np.int32) if rows is None else np.asarray(rows, np.int32)
+    out = np.empty((B, H, len(rows), d), np.float32)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = mx_attn_rows_head(mz, vc, ve, b, h, rows, causal, sm_scale)
+    return out, mz, vc, ve
