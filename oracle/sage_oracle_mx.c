@@ -29,10 +29,17 @@
  *   - S_j = the exact value of sum_b 2^(eq_b + ek_b) sum_{c in b} q_c k_c,
  *     rounded once to fp32 (every partial product and sum is exact).
  *   - softmax in the exp2 domain as in the INT8 path with c = lambda and no
- *     static P scale (P's scale is per block):  m_t = max_j fp32(S_j lambda),
- *     m' = max(m, m_t), alpha = exp2(fp32(m - m')) (0 at start), mu = m',
- *     p_j = exp2(fma(S_j, lambda, -mu)) <= 1, l = fp32(alpha l) + sum p_j
- *     (unquantized p, ascending j).
+ *     static P scale (P's scale is per block):  m_t = max_j RD(S_j lambda)
+ *     (the product rounded toward -infinity), m' = max(m, m_t),
+ *     alpha = exp2(fp32(m - m')) (0 at start), mu = m',
+ *     p_j = exp2(fma(S_j, lambda, -mu)), l = fp32(alpha l) + sum p_j
+ *     (unquantized p, ascending j).  The subtracted maximum cancels in the
+ *     exact result; rounding it down makes the largest element's exponent
+ *     argument >= 0, so its p is at least 1 (at most one ulp above) and the
+ *     scale of its P block is 2^-2 whichever way an exp2 rounds just
+ *     below 1; rounded to nearest, that block's scale would depend on the
+ *     last bit of exp2 (p = 1 - 2^-24 gives exponent -3 and saturates the
+ *     element to 0.9375).
  *   - P: per block of 32 keys, amax = max p_j, codes elem(p_j / 2^e) as above.
  *   - P V in two levels as in the INT8 path: T = fp32 sum over the tile's
  *     keys (ascending) of dec(p~) dec(v~), O = fp32(fp32(alpha O) + T);
@@ -188,6 +195,8 @@ OR_API void or_mx_attn_rows(int fmt, const uint8_t* qc, const uint8_t* qe, const
                 S[j] = or_mx_dot(fmt, qc + (int64_t)i * d, qe + (int64_t)i * nq,
                                  kc + (int64_t)(j0 + j) * d, ke + (int64_t)(j0 + j) * nq, d);
                 float s = S[j] * lambda;
+                /* round down: the double product of two floats is exact */
+                if ((double)s > (double)S[j] * (double)lambda) s = nextafterf(s, -INFINITY);
                 if (s > mt) mt = s;
             }
             const float mn = m > mt ? m : mt;

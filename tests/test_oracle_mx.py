@@ -131,7 +131,8 @@ def test_single_tile_against_fp64_over_dequantized(orc, fmt, N):
 
 
 def _non_online(orc, mz, vc, ve, i, causal, sm_scale, fmt):
-    """Row i tile by tile: each tile against its running max, P blocks of 32
+    """Row i tile by tile: each tile against its running max (S lambda rounded
+    toward -infinity), P blocks of 32
     quantized by the oracle's block rule, tiles combined at the end with
     weights 2^(M_t - M)."""
     N, d = mz["q_c"].shape[2:]
@@ -147,7 +148,10 @@ def _non_online(orc, mz, vc, ve, i, causal, sm_scale, fmt):
     M = np.float32(-np.inf)
     for t0 in range(0, n_keys, 128):
         St = S[t0:t0 + 128]
-        M = max(M, (St * lam).astype(np.float32).max())
+        exact = St.astype(np.float64) * np.float64(lam)           # exact products
+        rd = exact.astype(np.float32)
+        rd = np.where(rd > exact, np.nextafter(rd, np.float32(-np.inf)), rd)  # toward -inf
+        M = max(M, rd.max())
         arg = (St.astype(np.float64) * np.float64(lam) - np.float64(M)).astype(np.float32)
         p = np.exp2(arg.astype(np.float64)).astype(np.float32)
         pq = np.zeros(len(p))
@@ -179,6 +183,34 @@ def test_online_bookkeeping_matches_non_online(orc, fmt, causal):
         # may flip at a block-rounding boundary, so the bound is loose but far
         # below a wrong tile, scale or block
         assert np.abs(out[r] - ref).max() <= 2e-3 * np.abs(ref).max() + 1e-5, (i, np.abs(out[r] - ref).max())
+
+
+@pytest.mark.parametrize("fmt", list(FMTS))
+def test_largest_probability_is_exactly_one(orc, fmt):
+    """With the running maximum rounded down, the row's largest p is in
+    [1, 1 + 2^-23): its P block takes scale 2^-2 and it dequantizes to exactly
+    1.  One key tile (N = 128) and V = the identity, so out[i, j] l = P~_ij.
+    Rounded to nearest, the maximum leaves p = 1 - 2^-24 on part of the rows,
+    whose block then saturates the element to 0.9375."""
+    N = d = 128
+    wl = si.make("tiny", N=N, H=1, seed=5)
+    q, k = si.bf16_codes(wl.q), si.bf16_codes(wl.k)
+    v = np.zeros((1, 1, N, d), np.uint16)
+    v[0, 0, np.arange(N), np.arange(N)] = 0x3F80                 # bf16 1.0
+    mz = orc.mx_quant_qk(q, k, fmt)
+    vc, ve = orc.mx_quant_v(v, fmt)
+    assert np.all(orc.mx_dequant(vc[0, 0], np.repeat(ve[0, 0], 32, axis=0), fmt) == np.eye(N))
+    rows = np.arange(N)
+    out, m, l = orc.mx_attn_rows_head(mz, vc, ve, 0, 0, rows, False, wl.sm_scale, return_ml=True)
+    pq = out.astype(np.float64) * l[:, None]
+    top = pq.max(axis=1)
+    assert np.all(np.abs(top - 1.0) <= 2.0**-22), top[np.abs(top - 1.0) > 2.0**-22]
+    # the rounded-down maximum: m <= max S lambda < m + one ulp of m
+    S = (orc.mx_dequant(mz["q_c"][0, 0], np.repeat(mz["q_e"][0, 0], 32, axis=1), fmt) @
+         orc.mx_dequant(mz["k_c"][0, 0], np.repeat(mz["k_e"][0, 0], 32, axis=1), fmt).T)
+    exact = S.astype(np.float32).astype(np.float64).max(axis=1) * np.float64(orc.lam(wl.sm_scale))
+    assert np.all(m.astype(np.float64) <= exact)
+    assert np.all(np.nextafter(m, np.float32(np.inf)).astype(np.float64) > exact)
 
 
 def test_fp64_cosine_orders_the_formats(orc):
