@@ -279,6 +279,48 @@ int sage_attn_fwd_smooth(const int8_t* q8, const float* q_scale, const int8_t* k
                          int out_dtype, void* stream);
 
 /*
+ * Microscaled attention, MXFP6 (reportify.cn SageAttention3 summary, bullet
+ * FP4量化创新: microscaling FP4 attention; MXFP4 rated less accurate there).
+ * The gfx950 matrix cores take MX operands with E8M0 block scales of 32
+ * (OCP Microscaling), FP4 and FP6 at the same rate; this path uses FP6 E2M3
+ * elements (3 mantissa bits): with E2M1 (FP4) the cosine against FP64
+ * attention drops to ~0.97 on Gaussian inputs, with E2M3 it stays ~0.998.
+ * Every MX block of 32 elements is stored as 32 bytes: the 24 bytes of the
+ * 32 packed E2M3 codes (element 2i at bits [12i, 12i + 6) is value i of the
+ * block, element 2i + 1 is value 16 + i: the packing of
+ * v_cvt_scalef32_2xpk16_fp6_f32), the E8M0 scale byte at offset 24, then 7
+ * zero bytes.  Block rule: e = floor(log2(amax)) - 2, codes =
+ * E2M3(x / 2^e) rounded to nearest even and saturated at 7.5, byte e + 127;
+ * a block with amax < 2^-100 is all zero with byte 0.
+ *   sage_quant_qk_mx: K smoothed as in sage_quant_qk (k_mean, same
+ *     workspace), then Q and K' per row and 32 channels:
+ *     q6, k6 [B][H][N_pad][d] bytes (d / 32 blocks per row), rows >= N 0.
+ *   sage_quant_v_mx: V per channel and 32 keys: v6 [B][H][nblk][d][128]
+ *     bytes: for each tile of 128 keys, one 128-byte row per channel holding
+ *     the tile's 4 key blocks in key order; keys >= N are 0.
+ *   sage_attn_fwd_mx: S_j = Q6 . K6_j with the block scales (fp32 from the
+ *     matrix core); m_t = max_j S_j lambda rounded toward -infinity,
+ *     m' = max(m, m_t), alpha = exp2(m - m'), p_j = exp2(fma(S_j, lambda,
+ *     -m')) (the largest is in [1, 1 + 2^-23), so its P block always takes
+ *     scale 2^-2), l = alpha l + sum p_j; P per query and 32 consecutive
+ *     keys of a tile to MXFP6 by the block rule; O = alpha O + P6 V6;
+ *     out = O / l.  Layout, causal, sm_scale, out / out_dtype as for
+ *     sage_attn_fwd; d = 64 or 128.
+ * Errors as for the INT8 / FP8 entry points (status codes, nothing
+ * launched on an invalid argument).
+ * Buffer sizes: q6 and k6 as SAGE_BUF_Q8, v6 as SAGE_BUF_VQ with
+ * SAGE_PV_FP8, workspace as SAGE_BUF_WS_QK (sage_quant_sizes).
+ */
+int sage_quant_qk_mx(const void* q, const void* k, int B, int H, int N, int d, int layout,
+                     uint8_t* q6, uint8_t* k6, float* k_mean, void* workspace,
+                     size_t workspace_bytes, void* stream);
+int sage_quant_v_mx(const void* v, int B, int H, int N, int d, int layout, uint8_t* v6,
+                    void* stream);
+int sage_attn_fwd_mx(const uint8_t* q6, const uint8_t* k6, const uint8_t* v6, int B, int H, int N,
+                     int d, int layout, int causal, float sm_scale, void* out, int out_dtype,
+                     void* stream);
+
+/*
  * sage_attn_fwd that also writes the raw int32 Q K^T accumulators of head
  * (b, h), queries [row0, row0 + nrows), all keys, to s_out [nrows][N]
  * (row-major).  With causal, only entries j <= i are written; the others are

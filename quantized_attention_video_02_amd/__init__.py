@@ -46,7 +46,7 @@ EXPORTS = ["sage_get_config", "sage_quant_sizes", "sage_quant_sizes_ex", "sage_q
            "sage_quant_qk_ex", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_ex",
            "sage_attn_fwd_sparse", "sage_attn_fwd_debug", "sage_qsmooth_sizes",
            "sage_quant_qk_smooth", "sage_q_smooth_bias", "sage_attn_fwd_smooth",
-           "sage_status_string"]
+           "sage_quant_qk_mx", "sage_quant_v_mx", "sage_attn_fwd_mx", "sage_status_string"]
 
 _lib = None
 
@@ -76,6 +76,9 @@ def lib():
     L.sage_quant_qk_smooth.argtypes = [P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, S, P]
     L.sage_q_smooth_bias.argtypes = [P, P, P, I, I, I, I, I, F, P, P]
     L.sage_attn_fwd_smooth.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, P, I, P]
+    L.sage_quant_qk_mx.argtypes = [P, P, I, I, I, I, I, P, P, P, P, S, P]
+    L.sage_quant_v_mx.argtypes = [P, I, I, I, I, I, P, P]
+    L.sage_attn_fwd_mx.argtypes = [P, P, P, I, I, I, I, I, I, F, P, I, P]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = I
     L.sage_status_string.argtypes = [I]
@@ -267,3 +270,67 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
     return attn_fwd(qz, vq, vs, causal=causal, sm_scale=sm_scale, pv=pv, out_dtype=out_dtype,
                     tile_mask=tile_mask)
 
+
+# ------------------------------------------------------------- MXFP6 path
+def quant_qk_mx(q: torch.Tensor, k: torch.Tensor, layout: str = "HND") -> dict:
+    """Smooth K, then Q and K to MXFP6 (sage_quant_qk_mx): q6, k6 uint8
+    [B, H, N_pad, d] (32-byte MX blocks, see sage.h), k_mean."""
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise TypeError("q and k must be bfloat16")
+    if q.shape != k.shape or not q.is_contiguous() or not k.is_contiguous():
+        raise ValueError("q and k must be contiguous and of the same shape")
+    B, H, N, d = _dims(q, layout)
+    sz = quant_sizes(B, H, N, d)
+    dev = q.device
+    nblk = -(-N // 128)
+    r = dict(q6=torch.empty((B, H, nblk * 128, d), dtype=torch.uint8, device=dev),
+             k6=torch.empty((B, H, nblk * 128, d), dtype=torch.uint8, device=dev),
+             k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev),
+             workspace=_empty(sz[BUF_WS_QK], dev, torch.int64))
+    _check(lib().sage_quant_qk_mx(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout], _ptr(r["q6"]),
+                                  _ptr(r["k6"]), _ptr(r["k_mean"]), _ptr(r["workspace"]),
+                                  sz[BUF_WS_QK], _stream(dev)))
+    r.update(B=B, H=H, N=N, d=d, layout=layout)
+    return r
+
+
+def quant_v_mx(v: torch.Tensor, layout: str = "HND") -> torch.Tensor:
+    """V to MXFP6 (sage_quant_v_mx): uint8 [B, H, nblk, d, 128]."""
+    if v.dtype != torch.bfloat16 or not v.is_contiguous():
+        raise TypeError("v must be a contiguous bfloat16 tensor")
+    B, H, N, d = _dims(v, layout)
+    nblk = -(-N // 128)
+    v6 = torch.empty((B, H, nblk, d, 128), dtype=torch.uint8, device=v.device)
+    _check(lib().sage_quant_v_mx(_ptr(v), B, H, N, d, LAYOUTS[layout], _ptr(v6), _stream(v.device)))
+    return v6
+
+
+def attn_fwd_mx(mz: dict, v6: torch.Tensor, causal: bool = False, sm_scale: float | None = None,
+                out_dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """MXFP6 attention over quantized operands (sage_attn_fwd_mx)."""
+    B, H, N, d, layout = mz["B"], mz["H"], mz["N"], mz["d"], mz["layout"]
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    shape = (B, H, N, d) if layout == "HND" else (B, N, H, d)
+    dev = mz["q6"].device
+    nblk = -(-N // 128)
+    if v6.dtype != torch.uint8 or tuple(v6.shape) != (B, H, nblk, d, 128) or \
+            not v6.is_contiguous() or v6.device != dev:
+        raise ValueError(f"v6 must be contiguous uint8 [{B}, {H}, {nblk}, {d}, 128] on {dev}")
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    elif tuple(out.shape) != shape or out.dtype not in OUT or not out.is_contiguous() or \
+            out.device != dev:
+        raise ValueError(f"out must be contiguous {shape} (bfloat16 or float32) on {dev}")
+    _check(lib().sage_attn_fwd_mx(_ptr(mz["q6"]), _ptr(mz["k6"]), _ptr(v6), B, H, N, d,
+                                  LAYOUTS[layout], int(bool(causal)), sm, _ptr(out),
+                                  OUT[out.dtype], _stream(dev)))
+    return out
+
+
+def attn_mx(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+            sm_scale: float | None = None, layout: str = "HND",
+            out_dtype=torch.bfloat16) -> torch.Tensor:
+    """softmax(Q K^T sm_scale) V through the MXFP6 path."""
+    mz = quant_qk_mx(q, k, layout)
+    v6 = quant_v_mx(v, layout)
+    return attn_fwd_mx(mz, v6, causal=causal, sm_scale=sm_scale, out_dtype=out_dtype)

@@ -314,6 +314,65 @@ __attribute__((visibility("default"))) int sage_attn_fwd_debug(
                        h, row0, nrows, s_out, stream);
 }
 
+__attribute__((visibility("default"))) int sage_quant_qk_mx(const void* q, const void* k, int B,
+                                                            int H, int N, int d, int layout,
+                                                            uint8_t* q6, uint8_t* k6,
+                                                            float* k_mean, void* workspace,
+                                                            size_t workspace_bytes,
+                                                            void* stream) {
+    if (!q || !k || !q6 || !k6 || !k_mean || !workspace) return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_layout(layout));
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q6) || !aligned16(k6) || !aligned16(k_mean) ||
+        !aligned16(workspace))
+        return SAGE_ERR_ALIGN;
+    const Sizes s = sizes_of(B, H, N, d, SAGE_PV_FP8);
+    if (workspace_bytes < s.v[SAGE_BUF_WS_QK]) return SAGE_ERR_WORKSPACE;
+    const hipError_t e = sage::launch_quant_qk_mx((const sage::u16*)q, (const sage::u16*)k, B, H, N,
+                                                  d, layout, q6, k6, k_mean, (uint64_t*)workspace,
+                                                  (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+__attribute__((visibility("default"))) int sage_quant_v_mx(const void* v, int B, int H, int N, int d,
+                                                           int layout, uint8_t* v6, void* stream) {
+    if (!v || !v6) return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_layout(layout));
+    if (!aligned16(v) || !aligned16(v6)) return SAGE_ERR_ALIGN;
+    const hipError_t e = sage::launch_quant_v_mx((const sage::u16*)v, B, H, N, d, layout, v6,
+                                                 (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+__attribute__((visibility("default"))) int sage_attn_fwd_mx(const uint8_t* q6, const uint8_t* k6,
+                                                            const uint8_t* v6, int B, int H, int N,
+                                                            int d, int layout, int causal,
+                                                            float sm_scale, void* out,
+                                                            int out_dtype, void* stream) {
+    if (!q6 || !k6 || !v6 || !out) return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_layout(layout));
+    if (causal != 0 && causal != 1) return SAGE_ERR_INVALID;
+    if (out_dtype != SAGE_OUT_BF16 && out_dtype != SAGE_OUT_FP32) return SAGE_ERR_INVALID;
+    if (!(isfinite(sm_scale) && sm_scale > 0.0f)) return SAGE_ERR_INVALID;
+    if (!aligned16(q6) || !aligned16(k6) || !aligned16(v6) || !aligned16(out)) return SAGE_ERR_ALIGN;
+    sage::AttnArgs a = {};
+    a.q8 = (const int8_t*)q6;
+    a.k8 = (const int8_t*)k6;
+    a.vq = v6;
+    a.out = out;
+    a.H = H;
+    a.N = N;
+    a.nblk = (N + sage::kBlk - 1) / sage::kBlk;
+    a.N_pad = a.nblk * sage::kBlk;
+    a.layout = layout;
+    a.out_fp32 = out_dtype == SAGE_OUT_FP32;
+    a.lambda = (float)((double)sm_scale * 1.4426950408889634);
+    const hipError_t e = sage::launch_attn_mx(a, B, d, causal, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
 __attribute__((visibility("default"))) const char* sage_status_string(int status) {
     switch (status) {
         case SAGE_OK: return "SAGE_OK";

@@ -118,6 +118,11 @@ __device__ inline void tile_to_lds(const uint8_t* g, uint32_t l, int wave, const
 
 __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// An empty use of x at this point of the program: everything that computes x
+// happens before it.  (In a __device__ function: the host pass never
+// generates code for it.)
+__device__ inline void consume(const v16f& x) { asm volatile("" ::"v"(x)); }
+
 // Value of lane ^ 32 combined with this lane's (v_permlane32_swap: the two
 // halves of the wave exchange registers; both results hold one value from
 // each half, so max/sum of the pair is the same on both lanes).
@@ -577,6 +582,9 @@ void attn_fwd_kernel(AttnArgs a) {
         __syncthreads();
     }
     pv_tile<D>(smem + L::VBASE + ((ntiles + 1) & 1) * L::VBYTES, P, O, alpha, n, hh);
+    // the final P V completes while every lane is active (see attn_mx_kernel)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) consume(O[cb]);
 
     // ---- epilogue: out = O * v_scale / l (l summed over both lane halves)
     const float lt = pair_sum(l);
@@ -663,9 +671,284 @@ __global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
         wait_vmem();
         __syncthreads();
     }
+    // the last P V completes while every lane is active (see attn_mx_kernel)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) consume(O[cb]);
     const float lt = pair_sum(l);
     if (!active || qi >= N) return;
     store_row<D, false>(a, O, lt, b, h, bh, qi, hh);
+}
+
+// ------------------------------------------------------------ MXFP6 attention
+// Q, K, P and V in MXFP6 (E2M3 elements, one E8M0 scale per 32 along the
+// reduction; each 32-element block stored as 32 bytes: 24 code bytes, the
+// scale byte at offset 24), Q K^T and P V on v_mfma_scale_f32_32x32x64_f8f6f4
+// (FP6 operands, the FP4 rate), the online softmax in FP32 between them.
+// The matrix core applies the block scales, so S arrives as fp32 and the
+// epilogue needs no V scale.
+//
+// Key order: LDS row 32 k4 + n of a K tile holds tile key mx_row_key(k4, n),
+// so accumulator register r of lane half hh in block k4 is key
+// 32 (k4 / 2) + 16 k4 + 32 hh + r.  A lane's 32 values of the 64-key chunk
+// u = k4 / 2 are then the consecutive keys 64 u + 32 hh + [0, 32): one MX
+// block of P per lane and chunk, packed from S[2u] (first 16) and S[2u+1]
+// (second 16) in the order the V blocks are packed.
+// x y rounded toward -infinity (x = -inf gives -inf): the product rounded
+// to nearest, stepped down one ulp when it came out above the exact product.
+__device__ inline float mul_round_down(float x, float y) {
+    const float p = x * y;
+    if (!(__builtin_fmaf(x, y, -p) < 0.0f)) return p;
+    const uint32_t u = __float_as_uint(p);
+    return p > 0.0f ? __uint_as_float(u - 1u) : p < 0.0f ? __uint_as_float(u + 1u) : -0x1p-149f;
+}
+
+__device__ inline int mx_row_key(int k4, int n) {
+    return 32 * (k4 >> 1) + 16 * k4 + 32 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
+}
+
+template <int K4, int R>
+struct MaskTileMx {
+    static constexpr int OFF = 32 * (K4 >> 1) + 16 * K4 + R;
+    __device__ static void apply(v16f* F, int lim) {
+        F[K4][R] = __uint_as_float(mask_key<OFF>(__float_as_uint(F[K4][R]), lim, 0xff800000u));
+        if constexpr (R + 1 < 16) MaskTileMx<K4, R + 1>::apply(F, lim);
+        else if constexpr (K4 + 1 < 4) MaskTileMx<K4 + 1, 0>::apply(F, lim);
+    }
+};
+
+// 32-key block k4 of S^T = K6 tile . Q6^T (fp32, block scales applied): lane
+// (n, hh) reads LDS row 32 k4 + n, MX block 2 kk + hh of each 64-channel chunk.
+template <int D, int KSTR>
+__device__ inline v16f qk_mx(const uint8_t* kb, const v8i* qv, int k4, int n, int hh) {
+    const uint8_t* krow = kb + (32 * k4 + n) * KSTR + 32 * hh;
+    v16f acc = v16f{};
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) {
+        const v8i av = *(const v8i*)(krow + 64 * kk);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qv[kk], acc, 2, 2, 0, av[6], 0,
+                                                              qv[kk][6]);
+    }
+    return acc;
+}
+
+// P V into the running output: O = alpha O + V^T P^T.  Lane (channel n, hh)
+// reads V row 32 cb + n, MX block 2 u + hh (keys 64 u + 32 hh + [0, 32)).
+template <int D>
+__device__ inline void pv_mx(const uint8_t* vb, const v8i* P, const int* pe, v16f* O, float alpha,
+                             int n, int hh) {
+    using L = Lds<D, false>;
+    const uint8_t* vrow = vb + n * L::VSTR + 32 * hh;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) O[cb][e] *= alpha;
+    }
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const v8i av = *(const v8i*)(vrow + 32 * cb * L::VSTR + 64 * u);
+            O[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, P[u], O[cb], 2, 2, 0, av[6], 0,
+                                                                    pe[u]);
+        }
+}
+
+// One MX block of P: 32 probabilities (pa: keys +0..15, pb: +16..31) with
+// the block exponent e (scale 2^e; a zero block comes with scale 2^127, so
+// every code is 0).
+__device__ inline v8i pack_p_mx(const v16f& pa, const v16f& pb, float scale) {
+    v6i r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(pa, pb, scale);
+    // multi-pass conversion: its sources stay live past it, so the result
+    // registers cannot overlap them.  The result passes through the same
+    // empty asm, which orders it after the conversion (an asm without that
+    // dependence may be scheduled before it and protect nothing).
+    asm volatile("" : "+v"(r) : "v"(pa), "v"(pb), "v"(scale));
+    v8i o = v8i{};
+#pragma unroll
+    for (int i = 0; i < 6; ++i) o[i] = r[i];
+    return o;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attn_mx_kernel(AttnArgs a) {
+    constexpr int NW = 8, NT = 64 * NW, BR = 32 * NW;
+    using L = Lds<D, false>;
+    constexpr int CB = D / 32;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::TOTAL];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hh = lane >> 5;
+    const int wg = xcd_remap(blockIdx.x, a.total);
+    const int bh = wg / a.nqt;
+    int qt = wg - bh * a.nqt;
+    if (CAUSAL) qt = a.nqt - 1 - qt;  // longest rows first
+    const int H = a.H, N = a.N;
+    const int b = bh / H, h = bh - b * H;
+    const int qbase = qt * BR + wave * 32;
+    const bool active = qbase < N;
+    const int qi = qbase + n;
+    int ntiles = a.nblk;
+    if (CAUSAL) ntiles = (min(N, qt * BR + BR) - 1) / kBc + 1;
+    const bool tail = (N % kBc) != 0;
+
+    // Q6^T operand: lane (query qi, hh) holds MX block 2 kk + hh of each
+    // 64-channel chunk (codes and the scale dword); zero for padding waves
+    v8i qv[D / 64];
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) qv[kk] = v8i{};
+    if (active) {
+        const uint8_t* qrow = (const uint8_t*)a.q8 + ((int64_t)bh * a.N_pad + qi) * D + 32 * hh;
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk) qv[kk] = *(const v8i*)(qrow + 64 * kk);
+    }
+    const float lam = a.lambda;
+
+    const uint8_t* kg = (const uint8_t*)a.k8 + (int64_t)bh * a.N_pad * D;
+    const uint8_t* vg = (const uint8_t*)a.vq + (int64_t)bh * a.nblk * L::VHBM;
+    constexpr int KMAXP = (L::KPIECES + NW - 1) / NW, VMAXP = (L::VPIECES + NW - 1) / NW;
+    // K: LDS row R = 32 k4 + n takes tile key mx_row_key(k4, n)
+    int koff[KMAXP], voff[VMAXP];
+#pragma unroll
+    for (int j = 0; j < KMAXP; ++j) {
+        constexpr int CPR = L::KSTR / 16;
+        const int P = 64 * (wave + NW * j) + lane, R = P / CPR, c = P % CPR;
+        const int key = mx_row_key(R >> 5, R & 31);
+        koff[j] = key * L::KROW + (c < L::KROW / 16 ? 16 * c : 0);
+    }
+#pragma unroll
+    for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<L::VROW, L::VSTR>(64 * (wave + NW * j) + lane);
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto load_k = [&](int t) {
+        tile_to_lds<L::KPIECES, KMAXP, NW>(kg + (int64_t)t * L::KHBM, lbase + (t & 1) * L::KBYTES, wv,
+                                           koff);
+    };
+    auto load_v = [&](int t) {
+        tile_to_lds<L::VPIECES, VMAXP, NW>(vg + (int64_t)t * L::VHBM,
+                                           lbase + L::VBASE + (t & 1) * L::VBYTES, wv, voff);
+    };
+
+    float m = -INFINITY, l = 0.0f;
+    float alpha = 1.0f;  // alpha of the tile whose P is held (tile -1: P = 0, alpha = 1)
+    v16f O[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) O[cb] = v16f{};
+    v16f S[4];
+    v8i P[2] = {v8i{}, v8i{}};
+    int pe[2] = {0, 0};
+    const int kmax = CAUSAL ? min(N - 1, qi) : N - 1;
+
+    // Same software pipeline as the INT8 / FP8 kernel; V buffer 1 is
+    // zero-filled for tile -1 (P = 0 must not meet stale bytes)
+    {
+        uint4* vz = (uint4*)(smem + L::VBASE + L::VBYTES);
+        for (int i = tid; i < L::VBYTES / 16; i += NT) vz[i] = make_uint4(0, 0, 0, 0);
+    }
+    load_k(0);
+    if (ntiles > 1) load_k(1);
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) S[k4] = qk_mx<D, L::KSTR>(smem, qv, k4, n, hh);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 2 < ntiles) load_k(t + 2);
+        load_v(t);
+        const int key_t = t * kBc;
+        // A
+        pv_mx<D>(smem + L::VBASE + ((t + 1) & 1) * L::VBYTES, P, pe, O, alpha, n, hh);
+        const bool needmask = (tail && t == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase);
+        if (needmask) MaskTileMx<0, 0>::apply(S, kmax - key_t - 32 * hh);
+        float mk[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            float x = fmaxf(S[k4][0], S[k4][1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) x = fmaxf(fmaxf(x, S[k4][r]), S[k4][r + 1]);
+            mk[k4] = x;
+        }
+        // row max over both lane halves (lambda > 0: max(S) lambda = max(S lambda)),
+        // rounded down: the largest element's exponent argument is then >= 0
+        // and its p at least 1, so its block's exponent cannot hang on how
+        // exp2 rounds just below 1
+        const float mt = mul_round_down(pair_fmax(fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3]))), lam);
+        const float mn = fmaxf(m, mt);
+        alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        const float mu = mn;
+        // P block exponents: the block's largest p is the p of its largest S
+        float sc[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(fmaxf(mk[2 * u], mk[2 * u + 1]), lam, -mu));
+            const bool zero = !(pmax >= 0x1p-100f);
+            const int e = (int)((__float_as_uint(pmax) >> 23) & 0xffu) - 129;
+            sc[u] = __uint_as_float(zero ? (254u << 23) : (uint32_t)(e + 127) << 23);
+            pe[u] = zero ? 0 : e + 127;
+        }
+        // B: the exponentials of tile t, interleaved with Q K^T of tile t+1
+        // into the same registers (the Q K^T of "tile ntiles" reads a stale
+        // buffer; its result is unused)
+        const uint8_t* kb = smem + ((t + 1) & 1) * L::KBYTES;
+        float part[4];
+        v16f pa;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            v16f p;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k4][r], lam, -mu));
+            float s4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s4[u] = (p[4 * u] + p[4 * u + 1]) + (p[4 * u + 2] + p[4 * u + 3]);
+            part[k4] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+            S[k4] = qk_mx<D, L::KSTR>(kb, qv, k4, n, hh);
+            if (k4 & 1) P[k4 >> 1] = pack_p_mx(pa, p, sc[k4 >> 1]);
+            else pa = p;
+        }
+        l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
+        wait_vmem();
+        __syncthreads();
+    }
+    pv_mx<D>(smem + L::VBASE + ((ntiles + 1) & 1) * L::VBYTES, P, pe, O, alpha, n, hh);
+    // The matrix instructions read operands from all 64 lanes, but the
+    // operand moves feeding them obey EXEC: the final P V must complete
+    // before the exit below turns padding-query lanes off, so its results
+    // are consumed here, where every lane is active.
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) consume(O[cb]);
+
+    const float lt = pair_sum(l);
+    if (!active || qi >= N) return;
+    const int64_t obase = row_offset(a.layout, b, h, qi, H, N, D);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int c0 = 32 * cb + 8 * r4 + 4 * hh;
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = O[cb][4 * r4 + j] / lt;
+            if (a.out_fp32) {
+                *(float4*)((float*)a.out + obase + c0) = make_float4(o[0], o[1], o[2], o[3]);
+            } else {
+                const uint32_t w0 = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+                const uint32_t w1 = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+                *(uint2*)((u16*)a.out + obase + c0) = make_uint2(w0, w1);
+            }
+        }
+}
+
+hipError_t launch_attn_mx(const AttnArgs& args, int B, int d, int causal, hipStream_t s) {
+    AttnArgs a = args;
+    a.nqt = (a.N + 255) / 256;
+    a.total = B * a.H * a.nqt;
+    const void* fn;
+    if (d == 128) fn = causal ? (const void*)attn_mx_kernel<128, true> : (const void*)attn_mx_kernel<128, false>;
+    else fn = causal ? (const void*)attn_mx_kernel<64, true> : (const void*)attn_mx_kernel<64, false>;
+    void* kargs[] = {(void*)&a};
+    return hipLaunchKernel(fn, dim3(a.total), dim3(512), kargs, 0, s);
 }
 
 template <int D, bool PV16, bool CAUSAL, int MODE, bool QSM>

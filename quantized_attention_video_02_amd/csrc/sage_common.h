@@ -12,6 +12,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef int v6i __attribute__((ext_vector_type(6)));
 typedef unsigned short u16;
 
 constexpr int kBlk = 128;          // rows per Q / K quantization block
@@ -78,6 +79,11 @@ hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int 
                            float* qmean, uint64_t* ws, hipStream_t s);
 hipError_t launch_q_bias(const float* qmean, const u16* k, const float* kmean, int B, int H, int N,
                          int d, int layout, float lambda, float* bias, hipStream_t s);
+hipError_t launch_quant_qk_mx(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
+                              uint8_t* q6, uint8_t* k6, float* kmean, uint64_t* ws, hipStream_t s);
+hipError_t launch_quant_v_mx(const u16* v, int B, int H, int N, int d, int layout, uint8_t* v6,
+                             hipStream_t s);
+hipError_t launch_attn_mx(const AttnArgs& args, int B, int d, int causal, hipStream_t s);
 hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, int pv16,
                           void* vq, float* vscale, float* ws, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal, int dump,

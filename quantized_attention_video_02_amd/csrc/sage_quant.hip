@@ -508,6 +508,126 @@ __global__ __launch_bounds__(kQuantThreads) void quant_v_fp16_kernel(
     }
 }
 
+// ------------------------------------------------------- MXFP6 quantization
+// MX blocks of 32 elements in E2M3 (FP6) with one E8M0 scale (OCP
+// Microscaling): e = floor(log2(amax)) - 2 (2 = the largest E2M3 exponent);
+// a block with amax below 2^-100 (zero included) is all zero codes with
+// scale byte 0.  Each block is stored as 32 bytes: the 24 bytes of 32 packed
+// E2M3 codes as v_cvt_scalef32_2xpk16_fp6_f32 lays them out (element 2i from
+// the first 16 values, 2i + 1 from the second 16), the E8M0 byte at offset
+// 24 (the scale operand of the matrix instruction, read with the codes), 7
+// zero bytes.
+
+// Codes and scale byte of one block of 32 fp32 values (x[0..15] first,
+// x[16..31] second); returns the 8 dwords of the stored block.
+__device__ inline v8i mx6_block(const float* x) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    v8i out = v8i{};
+    if (!(amax >= 0x1p-100f)) return out;  // zeros, scale byte 0
+    const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 2;
+    const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
+    v16f a, b;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        a[i] = x[i];
+        b[i] = x[16 + i];
+    }
+    v6i r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, scale);
+    // the conversion is multi-pass: keep its sources (scale included) live
+    // past it so that the register allocator cannot give the result
+    // registers that overlap them.  The result passes through the empty asm,
+    // which orders the asm after the conversion.
+    asm volatile("" : "+v"(r) : "v"(a), "v"(b), "v"(scale));
+#pragma unroll
+    for (int i = 0; i < 6; ++i) out[i] = r[i];
+    out[6] = e + 127;
+    return out;
+}
+
+// Q (blockIdx.z == 0) or smoothed K (z == 1) to MXFP6 per row and 32
+// channels: one thread per (row, block), rows >= N zero.  Output rows of D
+// bytes, [bh][N_pad][D].
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void quant_qk_mx_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, int H, int N, int N_pad, int layout,
+    const float* __restrict__ kmean, uint8_t* __restrict__ q6, uint8_t* __restrict__ k6) {
+    constexpr int NB = D / 32;
+    const int idx = blockIdx.x * kQuantThreads + threadIdx.x;
+    const int row = idx / NB, blk = idx % NB;
+    const int bh = blockIdx.y, b = bh / H, h = bh % H, isk = blockIdx.z;
+    if (row >= N_pad) return;
+    v8i out = v8i{};
+    if (row < N) {
+        const u16* src = (isk ? k : q) + row_offset(layout, b, h, row, H, N, D) + 32 * blk;
+        float x[32];
+#pragma unroll
+        for (int c8 = 0; c8 < 4; ++c8) {
+            const uint4 w = *(const uint4*)(src + 8 * c8);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                x[8 * c8 + 2 * u] = bf16_bits_to_f32(ws[u] & 0xffffu);
+                x[8 * c8 + 2 * u + 1] = bf16_bits_to_f32(ws[u] >> 16);
+            }
+        }
+        if (isk) {
+            const float* km = kmean + bh * D + 32 * blk;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) x[i] -= km[i];
+        }
+        out = mx6_block(x);
+    }
+    uint8_t* dst = (isk ? k6 : q6) + ((int64_t)bh * N_pad + row) * D + 32 * blk;
+    *(uint4*)dst = make_uint4(out[0], out[1], out[2], out[3]);
+    *(uint4*)(dst + 16) = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+// V to MXFP6 per channel and 32 keys, one tile of 128 keys per workgroup:
+// the tile is staged in LDS channel-major (fp32), then one thread per
+// (channel, block of 32 keys) packs its block.  Output [bh][nblk][D][128]
+// bytes: channel row = the tile's 4 key blocks of 32 bytes; keys >= N are 0.
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void quant_v_mx_kernel(
+    const u16* __restrict__ v, int H, int N, int nblk, int layout, uint8_t* __restrict__ v6) {
+    constexpr int CPR = D / 8;
+    constexpr int RPI = kQuantThreads / CPR;
+    constexpr int LSTR = kBc + 4;  // floats per channel row in LDS (pad: fewer bank conflicts)
+    __shared__ float tile[D * LSTR];
+    const int blk = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
+    for (int key = tr; key < kBc; key += RPI) {
+        const int row = blk * kBc + key;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        if (row < N) {
+            const uint4 w = *(const uint4*)(v + row_offset(layout, b, h, row, H, N, D) + cg * 8);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = bf16_bits_to_f32(ws[e] & 0xffffu);
+                x[2 * e + 1] = bf16_bits_to_f32(ws[e] >> 16);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[(cg * 8 + e) * LSTR + key] = x[e];
+    }
+    __syncthreads();
+    uint8_t* dst = v6 + ((int64_t)bh * nblk + blk) * D * kBc;
+    for (int i = t; i < D * 4; i += kQuantThreads) {
+        const int c = i >> 2, kb = i & 3;
+        float x[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) x[j] = tile[c * LSTR + 32 * kb + j];
+        const v8i out = mx6_block(x);
+        uint8_t* o = dst + c * kBc + 32 * kb;
+        *(uint4*)o = make_uint4(out[0], out[1], out[2], out[3]);
+        *(uint4*)(o + 16) = make_uint4(out[4], out[5], out[6], out[7]);
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 static inline hipError_t launch(const void* fn, dim3 grid, dim3 block, void** args,
                                 hipStream_t s) {
@@ -556,6 +676,39 @@ hipError_t launch_q_bias(const float* qmean, const u16* k, const float* kmean, i
     const dim3 grid((N_pad + kQuantThreads * kBiasKeys - 1) / (kQuantThreads * kBiasKeys), B * H,
                     (nbp + kBiasSlice - 1) / kBiasSlice);
     return launch(fn, grid, dim3(kQuantThreads), args, s);
+}
+
+hipError_t launch_quant_qk_mx(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
+                              uint8_t* q6, uint8_t* k6, float* kmean, uint64_t* ws, hipStream_t s) {
+    const int nblk = (N + kBlk - 1) / kBlk, N_pad = nblk * kBlk;
+    const int nchunk = (N + kStatsChunk - 1) / kStatsChunk;
+    const int BH = B * H;
+    hipError_t e;
+    {
+        void* args[] = {(void*)&k, (void*)&H, (void*)&N, (void*)&layout, (void*)&nchunk, (void*)&ws};
+        const void* fn = d == 128 ? (const void*)k_stats_kernel<128> : (const void*)k_stats_kernel<64>;
+        if ((e = launch(fn, dim3(nchunk, BH), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
+    }
+    {
+        void* args[] = {(void*)&ws, (void*)&nchunk, (void*)&d, (void*)&N, (void*)&kmean};
+        if ((e = launch((const void*)k_mean_kernel, dim3(BH, d / kCombCh), dim3(kQuantThreads), args,
+                        s)) != hipSuccess)
+            return e;
+    }
+    void* args[] = {(void*)&q, (void*)&k, (void*)&H, (void*)&N, (void*)&N_pad, (void*)&layout,
+                    (void*)&kmean, (void*)&q6, (void*)&k6};
+    const void* fn = d == 128 ? (const void*)quant_qk_mx_kernel<128> : (const void*)quant_qk_mx_kernel<64>;
+    const int items = N_pad * (d / 32);
+    return launch(fn, dim3((items + kQuantThreads - 1) / kQuantThreads, BH, 2), dim3(kQuantThreads),
+                  args, s);
+}
+
+hipError_t launch_quant_v_mx(const u16* v, int B, int H, int N, int d, int layout, uint8_t* v6,
+                             hipStream_t s) {
+    const int nblk = (N + kBc - 1) / kBc;
+    void* args[] = {(void*)&v, (void*)&H, (void*)&N, (void*)&nblk, (void*)&layout, (void*)&v6};
+    const void* fn = d == 128 ? (const void*)quant_v_mx_kernel<128> : (const void*)quant_v_mx_kernel<64>;
+    return launch(fn, dim3(nblk, B * H), dim3(kQuantThreads), args, s);
 }
 
 hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, int pv16,

@@ -27,3 +27,36 @@ def to_hnd(x: torch.Tensor, layout: str) -> torch.Tensor:
 def codes(x: torch.Tensor) -> np.ndarray:
     """bf16 tensor (any device) -> uint16 numpy codes, same shape."""
     return x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def mx6_unpack_blocks(raw: np.ndarray):
+    """[..., 32] bytes (one stored MX block each) -> (codes uint8 [..., 32] in
+    value order, E8M0 bytes [...], padding bytes [..., 7]).  Layout from the
+    header: bits [6p, 6p + 6) of the first 24 bytes (little endian) hold
+    element p; element 2i is value i, element 2i + 1 is value 16 + i; byte
+    24 is the scale, bytes 25..31 are zero."""
+    raw = np.ascontiguousarray(raw, np.uint8)
+    bits = np.unpackbits(raw[..., :24], axis=-1, bitorder="little")      # [..., 192]
+    el = bits.reshape(raw.shape[:-1] + (32, 6))
+    elem = (el * (1 << np.arange(6))).sum(-1).astype(np.uint8)         # element p
+    codes = np.empty_like(elem)
+    codes[..., :16] = elem[..., 0::2]
+    codes[..., 16:] = elem[..., 1::2]
+    return codes, raw[..., 24], raw[..., 25:]
+
+
+def mx6_rows(x6: np.ndarray, N: int):
+    """q6 / k6 [B,H,N_pad,d] bytes -> (codes [B,H,N,d], E8M0 [B,H,N,d/32], pad)."""
+    B, H, Np, d = x6.shape
+    c, e, pad = mx6_unpack_blocks(x6.reshape(B, H, Np, d // 32, 32))
+    return c.reshape(B, H, Np, d)[:, :, :N], e[:, :, :N], pad
+
+
+def mx6_v(v6: np.ndarray, N: int):
+    """v6 [B,H,nblk,d,128] bytes -> (codes [B,H,N,d] in key order, E8M0
+    [B,H,ceil(N/32),d], pad)."""
+    B, H, nblk, d, _ = v6.shape
+    c, e, pad = mx6_unpack_blocks(v6.reshape(B, H, nblk, d, 4, 32))
+    c = np.transpose(c.reshape(B, H, nblk, d, 128), (0, 1, 2, 4, 3)).reshape(B, H, nblk * 128, d)
+    e = np.transpose(e, (0, 1, 2, 4, 3)).reshape(B, H, nblk * 4, d)
+    return c[:, :, :N], e[:, :, :-(-N // 32)], pad

@@ -186,3 +186,25 @@ def test_status_strings(sage):
     names = [L.sage_status_string(c).decode() for c in range(0, -8, -1)]
     assert names[0] == "SAGE_OK" and all(n.startswith("SAGE_ERR_") for n in names[1:])
     assert L.sage_status_string(12345).decode() == "SAGE_ERR_UNKNOWN"
+
+
+def test_mx6_layout_reader_round_trip():
+    """The tests' reader of the MX6 block layout against a packer written
+    from the same header text in the opposite direction."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from sage_layouts import mx6_unpack_blocks
+
+    rng = np.random.default_rng(0)
+    vals = rng.integers(0, 64, (5, 32)).astype(np.uint8)
+    scales = rng.integers(0, 256, 5).astype(np.uint8)
+    raw = np.zeros((5, 32), np.uint8)
+    for b in range(5):
+        word = 0
+        for i in range(16):
+            word |= int(vals[b, i]) << (12 * i)            # element 2i = value i
+            word |= int(vals[b, 16 + i]) << (12 * i + 6)   # element 2i + 1 = value 16 + i
+        raw[b, :24] = np.frombuffer(word.to_bytes(24, "little"), np.uint8)
+        raw[b, 24] = scales[b]
+    c, e, pad = mx6_unpack_blocks(raw)
+    assert np.array_equal(c, vals) and np.array_equal(e, scales) and not pad.any()
