@@ -7,6 +7,9 @@ sage_quant_v (per-channel FP8 V) and sage_attn_fwd (fused INT8-QK / FP8-PV
 attention), enqueued on one stream.  The headline workload is the 720p clip
 of a 14B video DiT: B=1, H=40, N=75600 (21 x 45 x 80 latent tokens), d=128.
 
+--mx runs the microscaled path instead: sage_quant_qk_mx, sage_quant_v_mx and
+sage_attn_fwd_mx (Q, K, P and V in MXFP6), priced against the dense FP6 peak.
+
 Prints ONE JSON line:
   value       = 4 B H N^2 d * steps / wall time of the timed steps (TOPS),
   roofline    = the attention kernel alone: algorithmic ops per launch (4 B H N^2 d)
@@ -29,7 +32,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention TOPS (4·B·H·N²·d/s) & % MFMA peak at N=32760/75600, d=128"
 PEAK_TOPS = {"fp8": 5000.0,                       # dense INT8 (QK) = dense FP8 (PV) = 5.0 POPS
-             "fp16": 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)}  # INT8 QK half + FP16 PV half
+             "fp16": 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0),  # INT8 QK half + FP16 PV half
+             "mxfp6": 10100.0}                    # dense FP6 (= FP4) MFMA, both products
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 ATTN_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
@@ -81,7 +85,8 @@ def visited_ops(wl, mask):
     return 4.0 * wl.d * float((mask.astype(np.float64) * pairs).sum())
 
 
-def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None, q_smooth=False):
+def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None, q_smooth=False,
+             mx=False):
     import torch
 
     q, k, v = wl.q, wl.k, wl.v
@@ -90,12 +95,18 @@ def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None, q_smoo
     def step(evs=None):
         if evs:
             evs[0].record(stream)
-        qz = sage.quant_qk(q, k, q_gran=q_gran, q_smooth=q_smooth, sm_scale=wl.sm_scale)
-        vq, vs = sage.quant_v(v, pv)
+        if mx:
+            mz, v6 = sage.quant_qk_mx(q, k), sage.quant_v_mx(v)
+        else:
+            qz = sage.quant_qk(q, k, q_gran=q_gran, q_smooth=q_smooth, sm_scale=wl.sm_scale)
+            vq, vs = sage.quant_v(v, pv)
         if evs:
             evs[1].record(stream)
-        out = sage.attn_fwd(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale, pv=pv,
-                            tile_mask=tile_mask)
+        if mx:
+            out = sage.attn_fwd_mx(mz, v6, causal=wl.causal, sm_scale=wl.sm_scale)
+        else:
+            out = sage.attn_fwd(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale, pv=pv,
+                                tile_mask=tile_mask)
         if evs:
             evs[2].record(stream)
         return out
@@ -115,12 +126,13 @@ def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None, q_smoo
     return wall, quant_ms, attn_ms
 
 
-def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False):
+def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False, mx=False):
     """The oracle as it stands (single-threaded C) on one head of the workload:
     quantization of the whole head, then attention for R query rows against
     all N keys; the head's quantization time is charged pro rata (R / N).
     With Q smoothing the correction rows of the blocks the R rows use are
-    computed too (charged to the quantization at the rate per block)."""
+    computed too (charged to the quantization at the rate per block).  With
+    mx the oracle's MXFP6 quantization and attention."""
     import numpy as np
 
     import oracle
@@ -129,9 +141,20 @@ def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False):
     b, h = 0, 0
     q, k, v = (si.bf16_codes(t[b:b + 1, h:h + 1]) for t in (wl.q, wl.k, wl.v))
     t0 = time.perf_counter()
-    oz = oracle.quant_qk(q, k, q_gran=q_gran, q_smooth=q_smooth)
-    ovq, ovs = oracle.quant_v(v, pv)
+    if mx:
+        mz = oracle.mx_quant_qk(q, k)
+        vc, ve = oracle.mx_quant_v(v)
+    else:
+        oz = oracle.quant_qk(q, k, q_gran=q_gran, q_smooth=q_smooth)
+        ovq, ovs = oracle.quant_v(v, pv)
     t_quant = time.perf_counter() - t0
+
+    def attn_rows(rows, bias):
+        if mx:
+            return oracle.mx_attn_rows_head(mz, vc, ve, 0, 0, rows, wl.causal, wl.sm_scale)
+        return oracle.attn_rows_head(oz, ovq, ovs, 0, 0, rows, wl.causal, wl.sm_scale, pv,
+                                     bias=bias)
+
     nblk = -(-wl.N // 128)
     bias, t_bias = None, 0.0
     probe = np.arange(8, dtype=np.int32)
@@ -140,7 +163,7 @@ def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False):
         bias = oracle.smooth_bias(oz, k, wl.sm_scale, blocks=[0])
         t_bias = time.perf_counter() - t0                       # one block row
     t0 = time.perf_counter()
-    oracle.attn_rows_head(oz, ovq, ovs, 0, 0, probe, wl.causal, wl.sm_scale, pv, bias=bias)
+    attn_rows(probe, bias)
     per_row = (time.perf_counter() - t0) / len(probe)
     R = int(max(8, min(wl.N, target_s / max(per_row + t_bias / 128, 1e-9))))
     rows = np.arange(wl.N - R, wl.N, dtype=np.int32) if wl.causal else np.arange(R, dtype=np.int32)
@@ -150,7 +173,7 @@ def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False):
         bias = oracle.smooth_bias(oz, k, wl.sm_scale, blocks=used)
         t_bias = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.attn_rows_head(oz, ovq, ovs, 0, 0, rows, wl.causal, wl.sm_scale, pv, bias=bias)
+    attn_rows(rows, bias)
     t_attn = time.perf_counter() - t0
     keys = (rows + 1).sum() if wl.causal else R * wl.N
     ops = 4.0 * float(keys) * wl.d
@@ -164,14 +187,19 @@ def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False):
                        f"({t_quant:.2f} s, charged pro rata) + attention for {R} queries x "
                        f"{'their causal keys' if wl.causal else f'{wl.N} keys'} ({t_attn:.2f} s)"
                        + (f"; Q-smoothing correction of their blocks ({t_bias:.2f} s, pro rata)"
-                          if q_smooth else "") + "; single-threaded C oracle")}
+                          if q_smooth else "") + ("; MXFP6 path" if mx else "")
+                       + "; single-threaded C oracle")}
 
 
 def traffic_key(workload, pv, q_gran="block"):
     return f"{workload}/{pv}" + ("" if q_gran == "block" else f"/{q_gran}")
 
 
-def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block"):
+def attn_kernel_name(mx):
+    return "attn_mx_kernel" if mx else "attn_fwd_kernel"
+
+
+def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False):
     """Write profiles/traffic.json from two rocprofv3 --pmc runs of
     `bench.py --steps 1 --warmup 0 --no-cpu-baseline --calibrate-copy` (one with
     FETCH_SIZE, one with WRITE_SIZE; KiB per dispatch).  Each counter is scaled
@@ -187,16 +215,17 @@ def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block"):
         return rows
 
     res = {}
+    kname = attn_kernel_name(mx)
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = per_kernel(d, counter)
-        attn = [float(r["Counter_Value"]) * 1024 for r in rows if "attn_fwd_kernel" in r["Kernel_Name"]]
+        attn = [float(r["Counter_Value"]) * 1024 for r in rows if kname in r["Kernel_Name"]]
         # --calibrate-copy's device-to-device copy runs as the HIP runtime's blit kernel
         copy = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]]
         if not attn or not copy:
-            raise SystemExit(f"no attn_fwd_kernel or copy dispatch with {counter} under {d}")
+            raise SystemExit(f"no {kname} or copy dispatch with {counter} under {d}")
         scale = float(1 << 30) / max(copy)
         res[counter] = (sum(attn) / len(attn) * scale, scale)
-    entry = {"kernel": "attn_fwd_kernel", "source_hash": attn_source_hash(),
+    entry = {"kernel": kname, "source_hash": attn_source_hash(),
              "fetch_bytes": res["FETCH_SIZE"][0], "write_bytes": res["WRITE_SIZE"][0],
              "bytes_per_launch": res["FETCH_SIZE"][0] + res["WRITE_SIZE"][0],
              "fetch_scale": res["FETCH_SIZE"][1], "write_scale": res["WRITE_SIZE"][1],
@@ -206,7 +235,7 @@ def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block"):
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
-    data[traffic_key(workload, pv, q_gran)] = entry
+    data[traffic_key(workload, "mxfp6" if mx else pv, q_gran)] = entry
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(data, f, indent=1)
     print(json.dumps(entry))
@@ -230,6 +259,9 @@ def main():
     ap.add_argument("--q-sigma", type=float, default=None,
                     help="give the workload's queries a per-channel offset of this sigma "
                          "(the inputs Q smoothing is for)")
+    ap.add_argument("--mx", action="store_true",
+                    help="the microscaled path: Q, K, P and V in MXFP6 (sage_quant_qk_mx, "
+                         "sage_quant_v_mx, sage_attn_fwd_mx)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -240,8 +272,13 @@ def main():
                          "--pmc output folders (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.record_traffic:
-        record_traffic(args.workload, args.pv, *args.record_traffic, q_gran=args.q_gran)
+        record_traffic(args.workload, args.pv, *args.record_traffic, q_gran=args.q_gran, mx=args.mx)
         return
+    if args.mx and (args.q_smooth or args.tile_keep is not None or args.q_gran != "block"
+                    or args.pv != "fp8"):
+        print("bench.py: --mx runs the MXFP6 path alone (no --q-smooth, --tile-keep, "
+              "--q-gran token or --pv fp16)", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (there is no multi-GPU path; "
               "DESIGN.md describes how the work would shard). Run with --gpus 1.",
@@ -257,7 +294,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = si.make(args.workload, device="cuda", q_sigma=args.q_sigma)
     torch.cuda.synchronize()
-    print(f"[bench] {wl.name}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} causal={wl.causal} pv={args.pv}",
+    fmt = "mxfp6" if args.mx else args.pv
+    print(f"[bench] {wl.name}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} causal={wl.causal} path={fmt}",
           file=sys.stderr, flush=True)
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -271,7 +309,7 @@ def main():
         mask_np = tile_mask_for(wl, args.tile_keep)
         tmask = torch.from_numpy(mask_np).cuda()
     wall, quant_ms, attn_ms = time_gpu(sage, wl, args.pv, args.steps, args.warmup, args.q_gran,
-                                       tmask, args.q_smooth)
+                                       tmask, args.q_smooth, args.mx)
     ops = attn_ops(wl.B, wl.H, wl.N, wl.d)
     # roofline work: all pairs when dense; the visited pairs of a sparse run
     work = ops if tmask is None else visited_ops(wl, mask_np)
@@ -282,12 +320,16 @@ def main():
     attn_iqr = srt[(3 * len(srt)) // 4] - srt[len(srt) // 4]
     quant_mean = sum(quant_ms) / len(quant_ms)
     achieved = work / (attn_mean * 1e-3) / 1e12
-    peak = PEAK_TOPS[args.pv]
+    peak = PEAK_TOPS[fmt]
     bhnd = wl.B * wl.H * wl.N * wl.d
+    # quantization bytes, two-pass count: K read twice (statistics, then
+    # codes), Q and V once as bf16, the codes written once; the INT8/FP8 path
+    # also reads V twice (per-channel scale first): 13 BHNd, MX: 11 BHNd
+    qbytes = (11 if args.mx else 13) * bhnd
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f).get(traffic_key(wl.name, args.pv, args.q_gran))
+            t = json.load(f).get(traffic_key(wl.name, fmt, args.q_gran))
         if t and t.get("source_hash") == attn_source_hash() and not args.q_smooth:
             traffic = t.get("bytes_per_launch")
     res = {
@@ -301,20 +343,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8+fp8" if args.pv == "fp8" else "int8+fp16",
+        "dtype": {"fp8": "int8+fp8", "fp16": "int8+fp16", "mxfp6": "mxfp6"}[fmt],
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
-                   "causal": wl.causal, "pv": args.pv, "q_gran": args.q_gran, "seed": wl.seed,
+                   "causal": wl.causal, "pv": fmt, "q_gran": "mx32" if args.mx else args.q_gran,
+                   "seed": wl.seed,
                    "parallelism": "none"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "attn_fwd_kernel", "ops_per_launch": work,
+                     "kernel": attn_kernel_name(args.mx), "ops_per_launch": work,
                      "mean_launch_ms": attn_mean, "median_launch_ms": attn_med,
                      "iqr_launch_ms": attn_iqr,
                      "median_tops": work / (attn_med * 1e-3) / 1e12},
-        "quant": {"ms": quant_mean, "bytes_two_pass": 13 * bhnd,
-                  "gbps_two_pass": 13 * bhnd / (quant_mean * 1e-3) / 1e9,
-                  "frac_hbm": 13 * bhnd / (quant_mean * 1e-3) / 1e9 / HBM_GBPS},
+        "quant": {"ms": quant_mean, "bytes_two_pass": qbytes,
+                  "gbps_two_pass": qbytes / (quant_mean * 1e-3) / 1e9,
+                  "frac_hbm": qbytes / (quant_mean * 1e-3) / 1e9 / HBM_GBPS},
     }
     if args.q_smooth or args.q_sigma is not None:
         res["config"]["q_smooth"] = bool(args.q_smooth)
@@ -339,7 +382,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.pv, args.cpu_seconds, args.q_gran,
-                                           args.q_smooth)
+                                           args.q_smooth, args.mx)
     print(json.dumps(res), flush=True)
 
 

@@ -55,6 +55,36 @@ def test_record_traffic_refuses_runs_without_the_copy(tmp_path, monkeypatch):
         bench.record_traffic("tiny", "fp8", str(tmp_path / "f"), str(tmp_path / "w"))
 
 
+def test_record_traffic_of_the_mx_kernel(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    gib_kib = (1 << 30) / 1024
+    rows = [("__amd_rocclr_copyBuffer", gib_kib),
+            ("void sage::attn_fwd_kernel<128, false, false, 0, false>(sage::AttnArgs)", 9.0),
+            ("void sage::attn_mx_kernel<128, false>(sage::AttnArgs)", 700.0)]
+    _write_counters(tmp_path / "f", "FETCH_SIZE", rows)
+    _write_counters(tmp_path / "w", "WRITE_SIZE", rows)
+    bench.record_traffic("video_14b_720p", "fp8", str(tmp_path / "f"), str(tmp_path / "w"), mx=True)
+    data = json.load(open(tmp_path / "traffic.json"))
+    assert list(data) == ["video_14b_720p/mxfp6"]
+    e = data["video_14b_720p/mxfp6"]
+    assert e["kernel"] == "attn_mx_kernel" and e["fetch_bytes"] == pytest.approx(700.0 * 1024)
+
+
+def test_cpu_baseline_of_the_mx_path():
+    import synthetic_inputs as si
+
+    wl = si.make("tiny", N=300, H=1)
+    r = bench.cpu_baseline(wl, "fp8", target_s=0.2, mx=True)
+    assert r["value"] > 0 and r["kind"] == "oracle" and r["cores"] == 1
+    assert "MXFP6" in r["sample"]
+
+
+def test_mx_refuses_the_other_variants():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--mx", "--q-smooth"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "MXFP6" in r.stderr
+
+
 def test_algorithmic_ops_count():
     # 4 d ops per (query, key) pair: 2d for Q K^T, 2d for P V
     assert bench.attn_ops(1, 40, 75600, 128) == pytest.approx(1.1705e14, rel=1e-4)
@@ -111,3 +141,16 @@ def test_bench_line_keeps_the_contract():
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
     assert line["cpu_baseline"]["kind"] == "oracle" and line["cpu_baseline"]["cores"] == 1
     assert line["config"]["workload"] == "tiny"
+
+
+@pytest.mark.gpu
+def test_mx_bench_line():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--mx",
+                        "--steps", "3", "--warmup", "1", "--cpu-seconds", "0.5"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    rf = line["roofline"]
+    assert line["dtype"] == "mxfp6" and rf["kernel"] == "attn_mx_kernel"
+    assert rf["peak"] == 10100.0 and rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
+    assert "MXFP6" in line["cpu_baseline"]["sample"]
