@@ -6,8 +6,9 @@ The codecs are pinned by invariants a wrong table or rounding rule breaks
 ties between neighbours, saturation, sign symmetry); the block rule by its
 bounds and the exponent from numpy's frexp; the MX dot product by exact
 rational arithmetic; the attention by a single tile against FP64 attention
-over the dequantized operands, a tile-by-tile non-online recomputation, and
-its FP64 cosine.
+over the dequantized operands, a tile-by-tile non-online recomputation, the
+largest probability of each row dequantizing to exactly 1 (the running
+maximum rounded down), and its FP64 cosine.
 """
 from fractions import Fraction
 
