@@ -19,7 +19,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "sage_oracle.c"), os.path.join(_HERE, "sage_oracle_mx.c")]
+_SRCS = [os.path.join(_HERE, "sage_oracle.c"), os.path.join(_HERE, "sage_oracle_mx.c"),
+         os.path.join(_HERE, "sage_oracle_bwd.c")]
 _LIB_PATH = os.path.join(_HERE, "libsage_oracle.so")
 _CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
            "-Wall", "-Wextra"]
@@ -76,6 +77,11 @@ def lib():
             "or_mx_quant_rows": [i32, P, P, i32, i32, P, P, P],
             "or_mx_quant_v": [i32, P, i32, i32, P, P, P],
             "or_mx_attn_rows": [i32, P, P, P, P, P, P, i32, i32, P, i32, i32, f32, P, P, P, P],
+            "or_bf16_to_f16f_n": [P, i64, P],
+            "or_bwd_prep": [P, P, i32, i32, P, P, P],
+            "or_bwd_dq_block": [P, P, P, P, P, P, P, P, i32, i32, i32, f32, i32, P, P],
+            "or_bwd_dkdv_block": [P, P, P, P, P, P, P, P, P, P, i32, i32, i32, f32, i32, P, P, P],
+            "or_bwd_ref64": [P, P, P, P, i32, i32, i32, f64, P, P, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -85,6 +91,8 @@ def lib():
         L.or_lambda.restype = f32
         L.or_mx_dot.argtypes = [i32, P, P, P, P, i32]
         L.or_mx_dot.restype = f32
+        L.or_bwd_tile_pd.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, f32, i32, i32, P, P]
+        L.or_bwd_tile_pd.restype = i32
         _lib = L
     return _lib
 
@@ -430,3 +438,118 @@ def mx_attention(q, k, v, causal: bool, sm_scale: float, rows=None, fmt="mxfp6")
         for h in range(H):
             out[b, h] = mx_attn_rows_head(mz, vc, ve, b, h, rows, causal, sm_scale)
     return out, mz, vc, ve
+
+
+# ------------------------------------------------------------- 8-bit backward
+def lse2_from_ml(m, l):
+    """The forward's log-sum-exp in the exp2 domain: lse2 = fp32(mu + log2(l))
+    with mu = fp32(m - log2 448) (log2 rounded once to fp32)."""
+    mu = (np.asarray(m, np.float32) - np.float32(np.log2(P_SCALE))).astype(np.float32)
+    return (mu + np.log2(np.asarray(l, np.float64)).astype(np.float32)).astype(np.float32)
+
+
+def train_forward_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scale: float):
+    """The training forward for ``rows`` of head (b, h): the bf16 output (uint16
+    codes, as a training step keeps it) and lse2 per row."""
+    out, m, l = attn_rows_head(qz, vq, vs, b, h, rows, causal, sm_scale, "fp8", return_ml=True)
+    return f32_to_bf16(out), lse2_from_ml(m, l)
+
+
+def bwd_prep_head(o, dO):
+    """Per head (uint16 bf16 [N, d] each): D [N] fp32, dO FP8 codes [N, d] and
+    the per-block FP8 scales [ceil(N/128)]."""
+    o = np.ascontiguousarray(o, np.uint16)
+    dO = np.ascontiguousarray(dO, np.uint16)
+    N, d = dO.shape
+    Dq = np.empty(N, np.float32)
+    do8 = np.empty((N, d), np.uint8)
+    s_do = np.empty(-(-N // BLK), np.float32)
+    lib().or_bwd_prep(_p(o), _p(dO), N, d, _p(Dq), _p(do8), _p(s_do))
+    return Dq, do8, s_do
+
+
+def _f16f(x):
+    x = np.ascontiguousarray(x, np.uint16)
+    out = np.empty(x.shape, np.float32)
+    lib().or_bf16_to_f16f_n(_p(x), x.size, _p(out))
+    return out
+
+
+def bwd_head(qz: dict, v, o, dO, lse2, b: int, h: int, causal: bool, sm_scale: float,
+             qblocks=None, kblocks=None):
+    """The 8-bit backward of head (b, h) (sage_oracle_bwd.c): dq for the query
+    blocks ``qblocks`` and dk, dv for the key blocks ``kblocks`` (default all),
+    as dicts block -> fp32 [rows, d].  v, o, dO: uint16 bf16 [N, d] of the
+    head; lse2 [N] from train_forward_head (only the rows the blocks need
+    are read: dq of a query block needs its rows, dk/dv all rows)."""
+    q8 = np.ascontiguousarray(qz["q8"][b, h])
+    k8 = np.ascontiguousarray(qz["k8"][b, h])
+    qs = np.ascontiguousarray(qz["q_scale"][b, h])
+    ks = np.ascontiguousarray(qz["k_scale"][b, h])
+    N, d = k8.shape
+    nblk = -(-N // BLK)
+    v16, do16 = _f16f(v), _f16f(dO)
+    Dq, do8, s_do = bwd_prep_head(o, dO)
+    lse2 = np.ascontiguousarray(lse2, np.float32)
+    scratch = np.empty(2 * BLK * BLK + BLK * BLK // 4 + d, np.float32)
+    L = lib()
+    dq, dk, dv = {}, {}, {}
+    for qb in (range(nblk) if qblocks is None else qblocks):
+        rows = min(BLK, N - qb * BLK)
+        out = np.empty((rows, d), np.float32)
+        L.or_bwd_dq_block(_p(q8), _p(qs), _p(k8), _p(ks), _p(v16), _p(do16), _p(lse2), _p(Dq), N, d,
+                          int(causal), float(sm_scale), int(qb), _p(out), _p(scratch))
+        dq[qb] = out
+    for kb in (range(nblk) if kblocks is None else kblocks):
+        rows = min(BLK, N - kb * BLK)
+        ok, ov = np.empty((rows, d), np.float32), np.empty((rows, d), np.float32)
+        L.or_bwd_dkdv_block(_p(q8), _p(qs), _p(k8), _p(ks), _p(v16), _p(do16), _p(do8), _p(s_do),
+                            _p(lse2), _p(Dq), N, d, int(causal), float(sm_scale), int(kb), _p(ok),
+                            _p(ov), _p(scratch))
+        dk[kb], dv[kb] = ok, ov
+    return dq, dk, dv
+
+
+def bwd_tile_head(qz: dict, v, o, dO, lse2, b: int, h: int, causal: bool, sm_scale: float,
+                  qb: int, kb: int):
+    """P and dS (fp32 [rows of qb, keys of kb]) of one tile pair of the backward,
+    or None when the pair is wholly masked."""
+    q8 = np.ascontiguousarray(qz["q8"][b, h])
+    k8 = np.ascontiguousarray(qz["k8"][b, h])
+    qs = np.ascontiguousarray(qz["q_scale"][b, h])
+    ks = np.ascontiguousarray(qz["k_scale"][b, h])
+    N, d = k8.shape
+    v16, do16 = _f16f(v), _f16f(dO)
+    Dq, _, _ = bwd_prep_head(o, dO)
+    nq, nk = min(BLK, N - qb * BLK), min(BLK, N - kb * BLK)
+    P = np.empty((nq, nk), np.float32)
+    dS = np.empty((nq, nk), np.float32)
+    ok = lib().or_bwd_tile_pd(_p(q8), _p(qs), _p(k8), _p(ks), _p(v16), _p(do16),
+                              _p(np.ascontiguousarray(lse2, np.float32)), _p(Dq), N, d, int(causal),
+                              float(sm_scale), int(qb), int(kb), _p(P), _p(dS))
+    return (P, dS) if ok else None
+
+
+def train_step_head(q, k, v, dO, b: int, h: int, causal: bool, sm_scale: float):
+    """Whole training step of one small head through the oracle: quantization,
+    forward (all rows), backward (all blocks).  Returns (o bf16 codes [N, d],
+    lse2 [N], dq, dk, dv fp32 [N, d])."""
+    qz = quant_qk(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1])
+    vq, vs = quant_v(v[b:b + 1, h:h + 1], "fp8")
+    N = q.shape[2]
+    o, lse2 = train_forward_head(qz, vq, vs, 0, 0, np.arange(N), causal, sm_scale)
+    dq, dk, dv = bwd_head(qz, v[b, h], o, dO[b, h], lse2, 0, 0, causal, sm_scale)
+    cat = lambda dct: np.concatenate([dct[i] for i in sorted(dct)])
+    return o, lse2, cat(dq), cat(dk), cat(dv)
+
+
+def bwd_ref64_head(q, k, v, dO, b: int, h: int, causal: bool, sm_scale: float):
+    """FP64 gradients of plain softmax attention (no quantization) for head
+    (b, h): dq, dk, dv [N, d]."""
+    qh, kh, vh, dh = (np.ascontiguousarray(x[b, h], np.uint16) for x in (q, k, v, dO))
+    N, d = qh.shape
+    dq, dk, dv = (np.empty((N, d), np.float64) for _ in range(3))
+    scratch = np.empty(2 * N, np.float64)
+    lib().or_bwd_ref64(_p(qh), _p(kh), _p(vh), _p(dh), N, d, int(causal), float(sm_scale), _p(dq),
+                       _p(dk), _p(dv), _p(scratch))
+    return dq, dk, dv

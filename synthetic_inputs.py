@@ -24,6 +24,10 @@ round(0.5% of N) query tokens are multiplied by 30 (chosen without replacement).
 Optional ``q_sigma`` (any workload): Q also gets a per-(batch, head, channel)
 offset ~ N(0, q_sigma^2) shared by all tokens, drawn after everything above
 (the inputs that Q smoothing is for; without it nothing changes).
+
+``output_grad`` gives a workload the upstream gradient of its attention
+output for the backward pass: dO ~ N(0, 1) of the output's shape, bf16, from
+its own generator seeded with the workload's seed + 500000.
 """
 from __future__ import annotations
 
@@ -99,6 +103,17 @@ def make(name: str, seed: int | None = None, device="cpu", B=None, H=None, N=Non
     return Workload(name=name, B=B, H=H, N=N, d=d, causal=causal, sm_scale=1.0 / math.sqrt(d),
                     seed=seed, q=q.to(torch.bfloat16), k=k.to(torch.bfloat16),
                     v=v.to(torch.bfloat16), outlier_tokens=outl)
+
+
+def output_grad(wl: Workload, layout: str = "HND") -> torch.Tensor:
+    """The upstream gradient dO ~ N(0, 1) of ``wl``'s output, bf16, [B, H, N, d]
+    (HND) or [B, N, H, d] (NHD), on the device of ``wl.q``."""
+    dev = wl.q.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 500000)
+    do = torch.randn((wl.B, wl.H, wl.N, wl.d), generator=g, device=dev, dtype=torch.float32)
+    do = do.to(torch.bfloat16)
+    return do if layout == "HND" else do.permute(0, 2, 1, 3).contiguous()
 
 
 def bf16_codes(t: torch.Tensor):
