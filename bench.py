@@ -37,7 +37,7 @@ PEAK_TOPS = {"fp8": 5000.0,                       # dense INT8 (QK) = dense FP8 
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 ATTN_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
-                for f in ("sage_attn.hip", "sage_common.h")]
+                for f in ("sage_attn.hip", "sage_common.h", "sage_device.h")]
 
 
 def attn_source_hash():

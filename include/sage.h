@@ -203,6 +203,50 @@ int sage_attn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, cons
                   void* stream);
 
 /*
+ * sage_attn_fwd that also returns each query row's log-sum-exp, the forward
+ * half of 8-bit training (reportify.cn SageAttention3 summary, bullet
+ * 8比特训练: the backward recomputes P from it):
+ *   lse[b][h][i] = fp32(fp32(m_i - log2 448) + log2(l_i))
+ * with m_i, l_i the row's final running max and row sum above, so that
+ * 2^(S_ij c - lse_i) is the softmax probability P_ij in the exp2 domain (log2
+ * on the GPU's own log2; differs from a correctly rounded one by about an
+ * ulp).  lse: fp32 [B][H][N], 16-byte aligned, written for every row; the
+ * rest as sage_attn_fwd (the same kernel; at d = 64 the pipelined one).
+ */
+int sage_attn_fwd_lse(const int8_t* q8, const float* q_scale, const int8_t* k8,
+                      const float* k_scale, const void* vq, const float* v_scale, int B, int H,
+                      int N, int d, int layout, int causal, float sm_scale, int pv_dtype,
+                      void* out, int out_dtype, float* lse, void* stream);
+
+/*
+ * The backward pass of 8-bit trainable attention (reportify.cn SageAttention3
+ * summary, bullet 8比特训练: per-block INT8 Q/K/V, per-token P with no
+ * quantization overhead, dO V^T kept in FP16, the other four backward products
+ * quantized).  Per tile pair of 128 queries x 128 keys, in the exp2 domain:
+ *   S = q8 . k8 (the forward's INT8 codes, K smoothed -- the rows of dS sum to
+ *       zero, so smoothing leaves dQ unchanged in exact arithmetic)
+ *   P = exp2(fma(S, c, -lse_i)), c = fp32(fp32(q_scale * lambda) * k_scale)
+ *   dP = f16(dO) . f16(V)^T (FP16 matrix cores, FP32 accumulation)
+ *   D_i = dO_i . O_i;  dS = fp32(P * fp32(dP - D_i))
+ *   dV += (dO8^T . e4m3(448 P)) * fp32(s_do / 448): dO in FP8 e4m3 per block
+ *         of 128 rows (absmax / 448 scale), P at the forward's static scale
+ *   dS8 = INT8 of dS per tile pair (absmax / 127 scale s_ds)
+ *   dK += (Q8^T . dS8) * fp32(fp32(s_ds * q_scale) * sm_scale)
+ *   dQ += (K8^T . dS8^T) * fp32(fp32(s_ds * k_scale) * sm_scale)
+ * (causal: keys j > i masked).  Inputs: q8 / q_scale / k8 / k_scale from
+ * sage_quant_qk (per-block Q), v the bf16 V, o the forward's bf16 output,
+ * dO the upstream gradient (bf16), all in `layout`; lse from
+ * sage_attn_fwd_lse.  Outputs dq, dk, dv: fp32 in `layout`, overwritten.
+ * workspace: sage_bwd_sizes bytes of device scratch, 256-byte aligned.
+ * d = 128 only in this build (SAGE_ERR_UNSUPPORTED otherwise).
+ */
+int sage_bwd_sizes(int B, int H, int N, int d, size_t* workspace_bytes);
+int sage_attn_bwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                  const void* v, const void* o, const void* dO, const float* lse, int B, int H,
+                  int N, int d, int layout, int causal, float sm_scale, float* dq, float* dk,
+                  float* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * sage_attn_fwd over Q scales of granularity q_gran (sage_q_gran), as
  * produced by sage_quant_qk_ex: sigma above is fp32(q_scale[b][h][i] *
  * lambda) for SAGE_QGRAN_TOKEN (fp32(q_scale[b][h][i / 128] * lambda) for

@@ -43,10 +43,11 @@ class SageConfig(ct.Structure):
 
 
 EXPORTS = ["sage_get_config", "sage_quant_sizes", "sage_quant_sizes_ex", "sage_quant_qk",
-           "sage_quant_qk_ex", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_ex",
+           "sage_quant_qk_ex", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse", "sage_attn_fwd_ex",
            "sage_attn_fwd_sparse", "sage_attn_fwd_debug", "sage_qsmooth_sizes",
            "sage_quant_qk_smooth", "sage_q_smooth_bias", "sage_attn_fwd_smooth",
-           "sage_quant_qk_mx", "sage_quant_v_mx", "sage_attn_fwd_mx", "sage_status_string"]
+           "sage_quant_qk_mx", "sage_quant_v_mx", "sage_attn_fwd_mx", "sage_bwd_sizes",
+           "sage_attn_bwd", "sage_status_string"]
 
 _lib = None
 
@@ -68,6 +69,7 @@ def lib():
     L.sage_quant_qk_ex.argtypes = [P, P, I, I, I, I, I, I, P, P, P, P, P, P, S, P]
     L.sage_quant_v.argtypes = [P, I, I, I, I, I, I, P, P, P, S, P]
     L.sage_attn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
+    L.sage_attn_fwd_lse.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P, P]
     L.sage_attn_fwd_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, I, P]
     L.sage_attn_fwd_sparse.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, I, P]
     L.sage_attn_fwd_debug.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, I, I, I,
@@ -79,6 +81,8 @@ def lib():
     L.sage_quant_qk_mx.argtypes = [P, P, I, I, I, I, I, P, P, P, P, S, P]
     L.sage_quant_v_mx.argtypes = [P, I, I, I, I, I, P, P]
     L.sage_attn_fwd_mx.argtypes = [P, P, P, I, I, I, I, I, I, F, P, I, P]
+    L.sage_bwd_sizes.argtypes = [I, I, I, I, ct.POINTER(ct.c_size_t)]
+    L.sage_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, P, S, P]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = I
     L.sage_status_string.argtypes = [I]
@@ -269,6 +273,57 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
     vq, vs = quant_v(v, pv, layout)
     return attn_fwd(qz, vq, vs, causal=causal, sm_scale=sm_scale, pv=pv, out_dtype=out_dtype,
                     tile_mask=tile_mask)
+
+
+def attn_fwd_lse(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
+                 sm_scale: float | None = None, pv: str = "fp8", out_dtype=torch.bfloat16):
+    """The training forward (sage_attn_fwd_lse): the attention output and each
+    row's log-sum-exp in the exp2 domain, fp32 [B, H, N]."""
+    if qz.get("q_gran", "block") != "block" or "bias" in qz:
+        raise ValueError("the training forward takes per-block Q without smoothing")
+    B, H, N, d, layout = qz["B"], qz["H"], qz["N"], qz["d"], qz["layout"]
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    dev = qz["q8"].device
+    out = torch.empty((B, H, N, d) if layout == "HND" else (B, N, H, d), dtype=out_dtype, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check(lib().sage_attn_fwd_lse(_ptr(qz["q8"]), _ptr(qz["q_scale"]), _ptr(qz["k8"]),
+                                   _ptr(qz["k_scale"]), _ptr(vq), _ptr(vs), B, H, N, d,
+                                   LAYOUTS[layout], int(bool(causal)), sm, PV[pv], _ptr(out),
+                                   OUT[out.dtype], _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+def bwd_sizes(B: int, H: int, N: int, d: int) -> int:
+    """Workspace bytes of sage_attn_bwd."""
+    n = ct.c_size_t(0)
+    _check(lib().sage_bwd_sizes(B, H, N, d, ct.byref(n)))
+    return n.value
+
+
+def attn_bwd(qz: dict, v: torch.Tensor, o: torch.Tensor, do: torch.Tensor, lse: torch.Tensor,
+             causal: bool = False, sm_scale: float | None = None):
+    """The 8-bit backward (sage_attn_bwd): dq, dk, dv fp32 in qz's layout, from
+    the forward's quantized Q/K (qz of quant_qk), V, its bf16 output o, the
+    upstream gradient do (bf16) and lse from attn_fwd_lse."""
+    B, H, N, d, layout = qz["B"], qz["H"], qz["N"], qz["d"], qz["layout"]
+    if qz.get("q_gran", "block") != "block" or "bias" in qz:
+        raise ValueError("the backward takes per-block Q without smoothing")
+    shape = (B, H, N, d) if layout == "HND" else (B, N, H, d)
+    for name, t in (("v", v), ("o", o), ("do", do)):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous bfloat16 {shape}")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError(f"lse must be contiguous float32 [{B}, {H}, {N}]")
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    dev = v.device
+    dq, dk, dv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
+    nbytes = bwd_sizes(B, H, N, d)
+    ws = torch.empty(nbytes // 8 + 32, dtype=torch.int64, device=dev)
+    _check(lib().sage_attn_bwd(_ptr(qz["q8"]), _ptr(qz["q_scale"]), _ptr(qz["k8"]),
+                               _ptr(qz["k_scale"]), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), B, H, N,
+                               d, LAYOUTS[layout], int(bool(causal)), sm, _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(ws), nbytes, _stream(dev)))
+    return dq, dk, dv
 
 
 # ------------------------------------------------------------- MXFP6 path

@@ -15,8 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libsage.so")
-SOURCES = ["sage_api.hip", "sage_quant.hip", "sage_attn.hip"]
-HEADERS = ["sage_common.h"]
+SOURCES = ["sage_api.hip", "sage_quant.hip", "sage_attn.hip", "sage_bwd.hip"]
+HEADERS = ["sage_common.h", "sage_device.h"]
 
 # -ffp-contract=off: no implicit fused multiply-adds, so the quantization pass
 # rounds exactly as documented (fused operations are written out explicitly).

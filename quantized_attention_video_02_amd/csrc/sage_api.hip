@@ -67,7 +67,8 @@ int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const 
                 const void* vq, const float* v_scale, int B, int H, int N, int d, int layout,
                 int causal, float sm_scale, int pv_dtype, int q_gran, const uint8_t* tmask,
                 int sparse, const float* bias, int smooth, void* out, int out_dtype, int dump,
-                int db, int dh, int row0, int nrows, int32_t* s_out, void* stream) {
+                int db, int dh, int row0, int nrows, int32_t* s_out, void* stream,
+                float* lse = nullptr) {
     if (!q8 || !q_scale || !k8 || !k_scale || !vq || !v_scale || !out) return SAGE_ERR_NULL;
     if (smooth && !bias) return SAGE_ERR_NULL;
     if (sparse && !tmask) return SAGE_ERR_NULL;
@@ -89,7 +90,7 @@ int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const 
         return SAGE_ERR_SIZE;
     if (!aligned16(q8) || !aligned16(q_scale) || !aligned16(k8) || !aligned16(k_scale) ||
         !aligned16(vq) || !aligned16(v_scale) || !aligned16(out) || (dump && !aligned16(s_out)) ||
-        (sparse && !aligned16(tmask)) || (smooth && !aligned16(bias)))
+        (sparse && !aligned16(tmask)) || (smooth && !aligned16(bias)) || (lse && !aligned16(lse)))
         return SAGE_ERR_ALIGN;
     sage::AttnArgs a;
     a.q8 = q8;
@@ -115,6 +116,7 @@ int attn_common(const int8_t* q8, const float* q_scale, const int8_t* k8, const 
     a.dbh = dump ? db * H + dh : -1;
     a.drow0 = row0;
     a.dnrows = nrows;
+    a.lse = lse;
     const hipError_t e = sage::launch_attn(a, B, d, pv_dtype == SAGE_PV_FP16, causal, dump,
                                            (hipStream_t)stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
@@ -273,6 +275,93 @@ __attribute__((visibility("default"))) int sage_attn_fwd(
     return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
                        pv_dtype, SAGE_QGRAN_BLOCK, nullptr, 0, nullptr, 0, out, out_dtype, 0, 0, 0,
                        0, 1, nullptr, stream);
+}
+
+__attribute__((visibility("default"))) int sage_attn_fwd_lse(
+    const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+    const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,
+    float sm_scale, int pv_dtype, void* out, int out_dtype, float* lse, void* stream) {
+    if (!lse) return SAGE_ERR_NULL;
+    return attn_common(q8, q_scale, k8, k_scale, vq, v_scale, B, H, N, d, layout, causal, sm_scale,
+                       pv_dtype, SAGE_QGRAN_BLOCK, nullptr, 0, nullptr, 0, out, out_dtype, 0, 0, 0,
+                       0, 1, nullptr, stream, lse);
+}
+
+// Workspace of the 8-bit backward, carved in this order, each part 256-byte
+// aligned: D [bh][N_pad] f32, s_do [bh][nblk] f32, dO and V in fp16
+// [bh][N_pad][d], dO in FP8 and Q, K codes transposed [bh][nblk][d][128].
+static size_t bwd_parts(int B, int H, int N, int d, size_t* off) {
+    const size_t bh = (size_t)B * H, nblk = ((size_t)N + sage::kBlk - 1) / sage::kBlk;
+    const size_t np = nblk * sage::kBlk;
+    const size_t sz[7] = {bh * np * 4, bh * nblk * 4, bh * np * d * 2, bh * np * d * 2,
+                          bh * np * d, bh * np * d, bh * np * d};
+    size_t o = 0;
+    for (int i = 0; i < 7; ++i) {
+        if (off) off[i] = o;
+        o += (sz[i] + 255) / 256 * 256;
+    }
+    return o;
+}
+
+__attribute__((visibility("default"))) int sage_bwd_sizes(int B, int H, int N, int d,
+                                                          size_t* workspace_bytes) {
+    if (!workspace_bytes) return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    if (d != 128) return SAGE_ERR_UNSUPPORTED;
+    *workspace_bytes = bwd_parts(B, H, N, d, nullptr);
+    return SAGE_OK;
+}
+
+__attribute__((visibility("default"))) int sage_attn_bwd(
+    const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale, const void* v,
+    const void* o, const void* dO, const float* lse, int B, int H, int N, int d, int layout,
+    int causal, float sm_scale, float* dq, float* dk, float* dv, void* workspace,
+    size_t workspace_bytes, void* stream) {
+    if (!q8 || !q_scale || !k8 || !k_scale || !v || !o || !dO || !lse || !dq || !dk || !dv ||
+        !workspace)
+        return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    if (d != 128) return SAGE_ERR_UNSUPPORTED;
+    SAGE_TRY(check_layout(layout));
+    if (causal != 0 && causal != 1) return SAGE_ERR_INVALID;
+    if (!(isfinite(sm_scale) && sm_scale > 0.0f)) return SAGE_ERR_INVALID;
+    if (!aligned16(q8) || !aligned16(q_scale) || !aligned16(k8) || !aligned16(k_scale) ||
+        !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(lse) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || ((uintptr_t)workspace & 255u))
+        return SAGE_ERR_ALIGN;
+    size_t off[7];
+    if (workspace_bytes < bwd_parts(B, H, N, d, off)) return SAGE_ERR_WORKSPACE;
+    uint8_t* ws = (uint8_t*)workspace;
+    sage::BwdPrep pp;
+    pp.o = (const sage::u16*)o;
+    pp.dO = (const sage::u16*)dO;
+    pp.v = (const sage::u16*)v;
+    sage::BwdArgs a;
+    a.q8 = q8;
+    a.q_scale = q_scale;
+    a.k8 = k8;
+    a.k_scale = k_scale;
+    a.lse = lse;
+    a.Dq = (float*)(ws + off[0]);
+    a.s_do = (float*)(ws + off[1]);
+    a.do16 = (_Float16*)(ws + off[2]);
+    a.v16 = (_Float16*)(ws + off[3]);
+    a.do8 = ws + off[4];
+    a.qT8 = (int8_t*)(ws + off[5]);
+    a.kT8 = (int8_t*)(ws + off[6]);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.H = H;
+    a.N = N;
+    a.nblk = (N + sage::kBlk - 1) / sage::kBlk;
+    a.N_pad = a.nblk * sage::kBlk;
+    a.total = 0;  // set by the launcher
+    a.layout = layout;
+    a.lambda = (float)((double)sm_scale * 1.4426950408889634);
+    a.sm_scale = sm_scale;
+    const hipError_t e = sage::launch_attn_bwd(pp, a, B, d, causal, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
 __attribute__((visibility("default"))) int sage_attn_fwd_ex(

@@ -1,0 +1,537 @@
+// 8-bit attention backward of libsage for gfx950 (CDNA4).
+//
+// Method (reportify.cn SageAttention tag page, SageAttention3 summary, bullet
+// 8比特训练): per-block INT8 Q/K/V and per-token P with no quantization
+// overhead; in the backward pass dO V^T stays FP16 and the other four products
+// are quantized.  Per tile pair (query block of 128 x key block of 128), in the
+// exp2 domain with the forward's log-sum-exp lse:
+//   S  = q8 . k8 (INT8 MFMA, the forward's codes, K smoothed)
+//   P  = exp2(fma(S, c, -lse_i)),  c = fp32(fp32(q_scale * lambda) * k_scale)
+//   dP = f16(dO) . f16(V)^T (FP16 MFMA, FP32 accumulation)
+//   dS = P (dP - D_i),  D_i = dO_i . O_i
+//   dV += dO8^T . e4m3(448 P) * s_do / 448        (FP8 MFMA; dO8 per 128-row block)
+//   dK += Q8^T . dS8 * s_ds * q_scale * sm_scale   (INT8 MFMA; dS8 per tile pair)
+//   dQ += K8^T . dS8^T * s_ds * k_scale * sm_scale (INT8 MFMA)
+// Two sweeps, each mirroring the forward's register layout: the dQ sweep keeps
+// a wave's 32 queries (S^T, dP^T with queries on lanes; dS^T is directly the B
+// operand of dQ^T = K^T dS^T) and sweeps key tiles; the dK/dV sweep keeps a
+// wave's 32 keys (S, dP with keys on lanes; P and dS are directly the B
+// operands of dV^T = dO8^T P~ and dK^T = Q8^T dS8) and sweeps query tiles.
+// The operands that meet an accumulator-shaped operand along the reduction
+// are stored transposed with the matching order of the reduction index (the
+// forward's V order for FP8, a 32-element order for INT8), written once by
+// the preparation kernels.  The tile's dS absmax is reduced over the
+// workgroup's 4 waves through LDS.  Four waves per workgroup, one workgroup
+// per CU: the sweeps hold about 300-450 registers per lane.
+#include <limits.h>
+
+#include "sage_common.h"
+#include "sage_device.h"
+
+namespace sage {
+
+constexpr int kBwdThreads = 256;  // 4 waves: 128 rows per workgroup, 32 per wave
+constexpr int kKstr = 128 + 16;   // LDS stride of a 128-byte row (INT8 / FP8 tiles), 16-byte pad
+constexpr int kHstr = 256 + 16;   // LDS stride of a 128-channel fp16 row
+
+// Order of a run of 128 elements along a reduction (element e = 32 kb + 8 b +
+// 4 g + q, kb and b in 0..3, g in 0..1, q in 0..3):
+//   pi32: e at 32 kb + 16 g + 4 b + q -- the 16 bytes a lane half g reads per
+//         32-element block are the 16 accumulator registers of that block
+//         (INT8 32x32x32 operands);
+//   pi64: e at 64 g + 16 kb + 4 b + q -- the 32 bytes per 64-element step
+//         (FP8 32x32x64 operands; the forward's V order).
+__device__ inline int pi32_elem(int p) {
+    return 32 * (p >> 5) + 8 * ((p >> 2) & 3) + 4 * ((p >> 4) & 1) + (p & 3);
+}
+__device__ inline int pi64_elem(int p) {
+    return 32 * ((p >> 4) & 3) + 8 * ((p >> 2) & 3) + 4 * (p >> 6) + (p & 3);
+}
+
+__device__ inline float wave_fmax(float x) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+    return x;
+}
+
+__device__ inline _Float16 f16_sat(float x) {
+    return (_Float16)fminf(fmaxf(x, -65504.0f), 65504.0f);
+}
+
+// One block of 128 rows of a head: D_i = dO_i . O_i (fp32), fp16 copies of dO
+// and V (row-major, padded rows 0), and dO in FP8 e4m3 for the block's absmax
+// scale s_do = fp32(a / 448) (codes of fp32(dO * fp32(448 / a))), written
+// channel-major [D][128] with the rows in pi64 order.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(
+    const u16* __restrict__ o, const u16* __restrict__ dO, const u16* __restrict__ v, int H, int N,
+    int nblk, int layout, float* __restrict__ Dq, _Float16* __restrict__ do16,
+    _Float16* __restrict__ v16, uint8_t* __restrict__ do8, float* __restrict__ s_do) {
+    constexpr int CPR = D / 8, RPI = kBwdThreads / CPR;
+    constexpr int LSTR = kBlk + 4;  // floats per channel row of the fp32 dO tile
+    __shared__ float tile[D * LSTR];
+    __shared__ float red[kBwdThreads / 64];
+    const int blk = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
+    const int64_t N_pad = (int64_t)nblk * kBlk;
+    float amax = 0.0f;
+    for (int r = tr; r < kBlk; r += RPI) {
+        const int row = blk * kBlk + r;
+        float xo[8], xd[8], xv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xo[e] = xd[e] = xv[e] = 0.0f;
+        if (row < N) {
+            const int64_t off = row_offset(layout, b, h, row, H, N, D) + cg * 8;
+            const uint4 wo = *(const uint4*)(o + off), wd = *(const uint4*)(dO + off),
+                        wv = *(const uint4*)(v + off);
+            const uint32_t so[4] = {wo.x, wo.y, wo.z, wo.w}, sd[4] = {wd.x, wd.y, wd.z, wd.w},
+                           sv[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xo[2 * e] = bf16_bits_to_f32(so[e] & 0xffffu);
+                xo[2 * e + 1] = bf16_bits_to_f32(so[e] >> 16);
+                xd[2 * e] = bf16_bits_to_f32(sd[e] & 0xffffu);
+                xd[2 * e + 1] = bf16_bits_to_f32(sd[e] >> 16);
+                xv[2 * e] = bf16_bits_to_f32(sv[e] & 0xffffu);
+                xv[2 * e + 1] = bf16_bits_to_f32(sv[e] >> 16);
+            }
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = part + xd[e] * xo[e];
+        // the row's CPR threads are consecutive lanes
+#pragma unroll
+        for (int s = CPR / 2; s >= 1; s >>= 1) part += __shfl_xor(part, s);
+        if (cg == 0) Dq[bh * N_pad + row] = part;
+        v8h hd, hv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            hd[e] = f16_sat(xd[e]);
+            hv[e] = f16_sat(xv[e]);
+            tile[(cg * 8 + e) * LSTR + r] = xd[e];
+            amax = fmaxf(amax, fabsf(xd[e]));
+        }
+        *(v8h*)(do16 + (bh * N_pad + row) * D + cg * 8) = hd;
+        *(v8h*)(v16 + (bh * N_pad + row) * D + cg * 8) = hv;
+    }
+    amax = wave_fmax(amax);
+    if ((t & 63) == 0) red[t >> 6] = amax;
+    __syncthreads();
+    float a = red[0];
+#pragma unroll
+    for (int w = 1; w < kBwdThreads / 64; ++w) a = fmaxf(a, red[w]);
+    const float inv = a > 0.0f ? (float)(448.0 / (double)a) : 0.0f;
+    if (t == 0) s_do[bh * nblk + blk] = (float)((double)a / 448.0);
+    uint8_t* dst = do8 + ((int64_t)bh * nblk + blk) * D * kBlk;
+    for (int i = t; i < D * kBlk / 4; i += kBwdThreads) {
+        const int c = i / (kBlk / 4), w = i % (kBlk / 4);
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = tile[c * LSTR + pi64_elem(4 * w + j)] * inv;
+        int o4 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+        o4 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], o4, true);
+        *(int*)(dst + c * kBlk + 4 * w) = o4;
+    }
+}
+
+// INT8 codes [bh][N_pad][D] -> per block of 128 rows [D][128] with the rows in
+// pi32 order (the Q and K codes as reduction-ordered operands).
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_t8_kernel(const int8_t* __restrict__ x8,
+                                                            int nblk, int8_t* __restrict__ xt) {
+    constexpr int LSTR = D + 4;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kBlk * LSTR];
+    const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    const uint8_t* src = (const uint8_t*)x8 + ((int64_t)bh * nblk + blk) * kBlk * D;
+    for (int i = t; i < kBlk * D / 4; i += kBwdThreads) {
+        const int r = i / (D / 4), c4 = i % (D / 4);
+        *(uint32_t*)&tile[r * LSTR + 4 * c4] = *(const uint32_t*)(src + (int64_t)r * D + 4 * c4);
+    }
+    __syncthreads();
+    uint8_t* dst = (uint8_t*)xt + ((int64_t)bh * nblk + blk) * D * kBlk;
+    for (int i = t; i < D * kBlk / 4; i += kBwdThreads) {
+        const int c = i / (kBlk / 4), w = i % (kBlk / 4);
+        uint32_t o4 = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o4 |= (uint32_t)tile[pi32_elem(4 * w + j) * LSTR + c] << (8 * j);
+        *(uint32_t*)(dst + c * kBlk + 4 * w) = o4;
+    }
+}
+
+// Code of x in INT8 at inv = fp32(127 / a): rne, clamped to +-127.
+__device__ inline int i8_code(float x, float inv) {
+    return (int)fminf(fmaxf(rintf(x * inv), -127.0f), 127.0f);
+}
+
+// 16 accumulator registers of one 32-row block as INT8 codes: the B operand
+// of a 32x32x32 INT8 MFMA whose reduction runs over that block.
+__device__ inline v4i pack_i8(const float* x, float inv) {
+    v4i r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t u = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u |= ((uint32_t)i8_code(x[4 * w + j], inv) & 0xffu) << (8 * j);
+        r[w] = (int)u;
+    }
+    return r;
+}
+
+// The tile's dS absmax over the workgroup's 4 waves (red: 4 floats of LDS)
+// and its INT8 scale s = fp32(a / 127), inv = fp32(127 / a) (0 for a = 0).
+__device__ inline void tile_scale(float amax, float* red, int wave, int lane, float& s, float& inv) {
+    amax = wave_fmax(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    s = (float)((double)a / 127.0);
+    inv = a > 0.0f ? (float)(127.0 / (double)a) : 0.0f;
+}
+
+// Store of a 32x32 accumulator row set: the lane's row `row` of [.., D] fp32
+// output, channels 32 cb + 8 r4 + 4 hh + j.
+template <int D>
+__device__ inline void store_f32_row(float* out, int64_t off, const v16f* X, int hh) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            *(float4*)(out + off + 32 * cb + 8 * r4 + 4 * hh) =
+                make_float4(X[cb][4 * r4], X[cb][4 * r4 + 1], X[cb][4 * r4 + 2], X[cb][4 * r4 + 3]);
+}
+
+// ---------------------------------------------------------------- dQ sweep
+// Workgroup = one query block of 128 (wave w: queries 32 w .. 32 w + 31), key
+// tiles swept in ascending order, double-buffered in LDS: K codes [128 keys]
+// [kKstr], V fp16 [128 keys][kHstr], K codes transposed [D channels][kKstr].
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+    constexpr int NW = 4, KK = D / 32, CB = D / 32, HK = D / 16;
+    constexpr int K8B = kBc * kKstr, V16B = kBc * kHstr, KTB = D * kKstr;
+    constexpr int SLOT = K8B + V16B + KTB;
+    constexpr int KP = K8B / 1024, VP = V16B / 1024, TP = KTB / 1024;
+    constexpr int KMAXP = (KP + NW - 1) / NW, VMAXP = (VP + NW - 1) / NW, TMAXP = (TP + NW - 1) / NW;
+    static_assert(K8B % 1024 == 0 && V16B % 1024 == 0 && KTB % 1024 == 0, "1 KB copy pieces");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOT];
+    __shared__ float red[NW];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hh = lane >> 5;
+    const int wg = xcd_remap(blockIdx.x, a.total);
+    const int bh = wg / a.nblk, qb = wg - bh * a.nblk;
+    const int H = a.H, N = a.N, b = bh / H, h = bh - b * H;
+    const int qi = qb * kBlk + wave * 32 + n;
+    const bool valid = qi < N;
+    const int64_t rowp = (int64_t)bh * a.N_pad + qi;
+
+    v4i qf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const v4i*)(a.q8 + rowp * D + 32 * kk + 16 * hh);
+    v8h dof[HK];
+#pragma unroll
+    for (int kk = 0; kk < HK; ++kk) dof[kk] = *(const v8h*)(a.do16 + rowp * D + 16 * kk + 8 * hh);
+    const float sigma = a.q_scale[bh * a.nblk + qb] * a.lambda;
+    const float lse = valid ? a.lse[(int64_t)bh * N + qi] : 0.0f;
+    const float Di = a.Dq[rowp];
+
+    int koff[KMAXP], voff[VMAXP], toff[TMAXP];
+#pragma unroll
+    for (int j = 0; j < KMAXP; ++j) koff[j] = slot_src<D, kKstr>(64 * (wave + NW * j) + lane);
+#pragma unroll
+    for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<2 * D, kHstr>(64 * (wave + NW * j) + lane);
+#pragma unroll
+    for (int j = 0; j < TMAXP; ++j) toff[j] = slot_src<kBc, kKstr>(64 * (wave + NW * j) + lane);
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const uint8_t* kg = (const uint8_t*)a.k8 + (int64_t)bh * a.N_pad * D;
+    const uint8_t* vg = (const uint8_t*)a.v16 + (int64_t)bh * a.N_pad * D * 2;
+    const uint8_t* tg = (const uint8_t*)a.kT8 + (int64_t)bh * a.nblk * D * kBc;
+    auto load = [&](int t) {
+        const uint32_t l = lbase + (t & 1) * SLOT;
+        tile_to_lds<KP, KMAXP, NW>(kg + (int64_t)t * kBc * D, l, wv, koff);
+        tile_to_lds<VP, VMAXP, NW>(vg + (int64_t)t * kBc * D * 2, l + K8B, wv, voff);
+        tile_to_lds<TP, TMAXP, NW>(tg + (int64_t)t * D * kBc, l + K8B + V16B, wv, toff);
+    };
+
+    v16f dq[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) dq[cb] = v16f{};
+    const int ntiles = CAUSAL ? qb + 1 : a.nblk;
+    const float* ksrow = a.k_scale + bh * a.nblk;
+    float ks_next = ksrow[0];
+    load(0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        // tile t's K scale (loaded one tile earlier; taken before this tile's
+        // copies are issued, so its wait does not cover them)
+        float ks = ks_next;
+        asm volatile("" : "+v"(ks));
+        if (t + 1 < ntiles) {
+            ks_next = ksrow[t + 1];
+            load(t + 1);
+        }
+        const uint8_t* kbuf = smem + (t & 1) * SLOT;
+        const uint8_t* vbuf = kbuf + K8B;
+        const uint8_t* tbuf = vbuf + V16B;
+        const float c = sigma * ks;
+        // S^T (keys x queries) and dP^T = V dO^T, 32-key block k4
+        v16i S[4];
+        v16f dP[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const uint8_t* krow = kbuf + (32 * k4 + n) * kKstr + 16 * hh;
+            v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)krow, qf[0], v16i{}, 0, 0, 0);
+#pragma unroll
+            for (int kk = 1; kk < KK; ++kk)
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)(krow + 32 * kk), qf[kk], acc, 0, 0, 0);
+            S[k4] = acc;
+            const uint8_t* vrow = vbuf + (32 * k4 + n) * kHstr + 16 * hh;
+            v16f pacc = v16f{};
+#pragma unroll
+            for (int kk = 0; kk < HK; ++kk)
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const v8h*)(vrow + 32 * kk), dof[kk], pacc, 0, 0, 0);
+            dP[k4] = pacc;
+        }
+        // P^T and dS^T; masked entries (key >= N, causal key > query, padding
+        // queries) are 0
+        const int key_t = t * kBc;
+        float ds[4][16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = key_t + 32 * k4 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const bool ok = valid && key < N && (!CAUSAL || key <= qi);
+                const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[k4][r], c, -lse)) : 0.0f;
+                ds[k4][r] = p * (dP[k4][r] - Di);
+                amax = fmaxf(amax, fabsf(ds[k4][r]));
+            }
+        float s_ds, inv;
+        tile_scale(amax, red, wave, lane, s_ds, inv);
+        v4i dsb[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) dsb[k4] = pack_i8(ds[k4], inv);
+        // dQ^T (channels x queries) += K8^T dS8^T for this tile, scaled
+        const float fq = (s_ds * ks) * a.sm_scale;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const uint8_t* trow = tbuf + (32 * cb + n) * kKstr + 16 * hh;
+            v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)trow, dsb[0], v16i{}, 0, 0, 0);
+#pragma unroll
+            for (int k4 = 1; k4 < 4; ++k4)
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)(trow + 32 * k4), dsb[k4], acc, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dq[cb][e] = dq[cb][e] + (float)acc[e] * fq;
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) consume(dq[cb]);
+    if (!valid) return;
+    store_f32_row<D>(a.dq, row_offset(a.layout, b, h, qi, H, N, D), dq, hh);
+}
+
+// ------------------------------------------------------------- dK / dV sweep
+// Workgroup = one key block of 128 (wave w: keys 32 w .. 32 w + 31), query
+// tiles swept in ascending order through one LDS slot: Q codes [128 queries]
+// [kKstr], dO fp16 [128][kHstr], dO FP8 transposed [D][kKstr], Q codes
+// transposed [D][kKstr], and the tile's lse / D rows.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+    constexpr int NW = 4, KK = D / 32, CB = D / 32, HK = D / 16;
+    constexpr int Q8B = kBlk * kKstr, DO16B = kBlk * kHstr, DO8B = D * kKstr, QTB = D * kKstr;
+    constexpr int QP = Q8B / 1024, HP = DO16B / 1024, FP = DO8B / 1024, TP = QTB / 1024;
+    constexpr int QMAXP = (QP + NW - 1) / NW, HMAXP = (HP + NW - 1) / NW, FMAXP = (FP + NW - 1) / NW,
+                  TMAXP = (TP + NW - 1) / NW;
+    static_assert(Q8B % 1024 == 0 && DO16B % 1024 == 0 && DO8B % 1024 == 0, "1 KB copy pieces");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Q8B + DO16B + DO8B + QTB];
+    __shared__ __attribute__((aligned(16))) float lseL[kBlk];
+    __shared__ __attribute__((aligned(16))) float dL[kBlk];
+    __shared__ float red[NW];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hh = lane >> 5;
+    const int wg = xcd_remap(blockIdx.x, a.total);
+    const int bh = wg / a.nblk, kb = wg - bh * a.nblk;
+    const int H = a.H, N = a.N, b = bh / H, h = bh - b * H;
+    const int kj = kb * kBc + wave * 32 + n;
+    const bool kvalid = kj < N;
+    const int64_t rowk = (int64_t)bh * a.N_pad + kj;
+
+    v4i kf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kf[kk] = *(const v4i*)(a.k8 + rowk * D + 32 * kk + 16 * hh);
+    v8h vf[HK];
+#pragma unroll
+    for (int kk = 0; kk < HK; ++kk) vf[kk] = *(const v8h*)(a.v16 + rowk * D + 16 * kk + 8 * hh);
+    const float ks = a.k_scale[bh * a.nblk + kb];
+
+    int qoff[QMAXP], hoff[HMAXP], foff[FMAXP], toff[TMAXP];
+#pragma unroll
+    for (int j = 0; j < QMAXP; ++j) qoff[j] = slot_src<D, kKstr>(64 * (wave + NW * j) + lane);
+#pragma unroll
+    for (int j = 0; j < HMAXP; ++j) hoff[j] = slot_src<2 * D, kHstr>(64 * (wave + NW * j) + lane);
+#pragma unroll
+    for (int j = 0; j < FMAXP; ++j) foff[j] = slot_src<kBlk, kKstr>(64 * (wave + NW * j) + lane);
+#pragma unroll
+    for (int j = 0; j < TMAXP; ++j) toff[j] = slot_src<kBlk, kKstr>(64 * (wave + NW * j) + lane);
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const uint8_t* qg = (const uint8_t*)a.q8 + (int64_t)bh * a.N_pad * D;
+    const uint8_t* hg = (const uint8_t*)a.do16 + (int64_t)bh * a.N_pad * D * 2;
+    const uint8_t* fg = (const uint8_t*)a.do8 + (int64_t)bh * a.nblk * D * kBlk;
+    const uint8_t* tg = (const uint8_t*)a.qT8 + (int64_t)bh * a.nblk * D * kBlk;
+
+    v16f dk[CB], dv[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) dk[cb] = dv[cb] = v16f{};
+    for (int qt = CAUSAL ? kb : 0; qt < a.nblk; ++qt) {
+        tile_to_lds<QP, QMAXP, NW>(qg + (int64_t)qt * kBlk * D, lbase, wv, qoff);
+        tile_to_lds<HP, HMAXP, NW>(hg + (int64_t)qt * kBlk * D * 2, lbase + Q8B, wv, hoff);
+        tile_to_lds<FP, FMAXP, NW>(fg + (int64_t)qt * D * kBlk, lbase + Q8B + DO16B, wv, foff);
+        tile_to_lds<TP, TMAXP, NW>(tg + (int64_t)qt * D * kBlk, lbase + Q8B + DO16B + DO8B, wv, toff);
+        if (tid < kBlk) {
+            const int q = qt * kBlk + tid;
+            lseL[tid] = q < N ? a.lse[(int64_t)bh * N + q] : 0.0f;
+            dL[tid] = a.Dq[(int64_t)bh * a.N_pad + q];
+        }
+        const float qsc = a.q_scale[bh * a.nblk + qt];
+        const float sdo = a.s_do[bh * a.nblk + qt];
+        wait_vmem();
+        __syncthreads();
+        const uint8_t* qbuf = smem;
+        const uint8_t* hbuf = smem + Q8B;
+        const uint8_t* fbuf = hbuf + DO16B;
+        const uint8_t* tbuf = fbuf + DO8B;
+        const float c = (qsc * a.lambda) * ks;
+        // S = Q K^T and dP = dO V^T (queries x keys), 32-query block q4
+        v16i S[4];
+        v16f dP[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const uint8_t* qrow = qbuf + (32 * q4 + n) * kKstr + 16 * hh;
+            v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)qrow, kf[0], v16i{}, 0, 0, 0);
+#pragma unroll
+            for (int kk = 1; kk < KK; ++kk)
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)(qrow + 32 * kk), kf[kk], acc, 0, 0, 0);
+            S[q4] = acc;
+            const uint8_t* hrow = hbuf + (32 * q4 + n) * kHstr + 16 * hh;
+            v16f pacc = v16f{};
+#pragma unroll
+            for (int kk = 0; kk < HK; ++kk)
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const v8h*)(hrow + 32 * kk), vf[kk], pacc, 0, 0, 0);
+            dP[q4] = pacc;
+        }
+        // P and dS (masked entries 0), and P in FP8 at the static scale 448
+        float p[4][16], ds[4][16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 L4 = *(const float4*)&lseL[32 * q4 + 8 * i + 4 * hh];
+                const float4 D4 = *(const float4*)&dL[32 * q4 + 8 * i + 4 * hh];
+                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * i + j;
+                    const int q = qt * kBlk + 32 * q4 + 8 * i + 4 * hh + j;
+                    const bool ok = kvalid && q < N && (!CAUSAL || kj <= q);
+                    const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[q4][r], c, -Lv[j])) : 0.0f;
+                    p[q4][r] = pv;
+                    ds[q4][r] = pv * (dP[q4][r] - Dv[j]);
+                    amax = fmaxf(amax, fabsf(ds[q4][r]));
+                }
+            }
+        v8i P8[2];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float x0 = p[q4][4 * u] * 448.0f, x1 = p[q4][4 * u + 1] * 448.0f;
+                const float x2 = p[q4][4 * u + 2] * 448.0f, x3 = p[q4][4 * u + 3] * 448.0f;
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+                P8[q4 >> 1][(q4 & 1) * 4 + u] = w;
+            }
+        // dV^T (channels x keys) += dO8^T P~ over this tile, scaled by s_do / 448
+        const float fv = (float)((double)sdo / 448.0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const uint8_t* frow = fbuf + (32 * cb + n) * kKstr + 64 * hh;
+            v16f T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(*(const v8i*)frow, P8[0], v16f{}, 0, 0,
+                                                                     0, 0, 0, 0);
+            T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(*(const v8i*)(frow + 32), P8[1], T, 0, 0, 0,
+                                                                0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dv[cb][e] = dv[cb][e] + T[e] * fv;
+        }
+        float s_ds, inv;
+        tile_scale(amax, red, wave, lane, s_ds, inv);
+        v4i dsb[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) dsb[q4] = pack_i8(ds[q4], inv);
+        // dK^T (channels x keys) += Q8^T dS8 over this tile, scaled
+        const float fk = (s_ds * qsc) * a.sm_scale;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const uint8_t* trow = tbuf + (32 * cb + n) * kKstr + 16 * hh;
+            v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)trow, dsb[0], v16i{}, 0, 0, 0);
+#pragma unroll
+            for (int q4 = 1; q4 < 4; ++q4)
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)(trow + 32 * q4), dsb[q4], acc, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dk[cb][e] = dk[cb][e] + (float)acc[e] * fk;
+        }
+        // every read of this tile's slot is done before the next tile's copies
+        __syncthreads();
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        consume(dk[cb]);
+        consume(dv[cb]);
+    }
+    if (!kvalid) return;
+    const int64_t off = row_offset(a.layout, b, h, kj, H, N, D);
+    store_f32_row<D>(a.dk, off, dk, hh);
+    store_f32_row<D>(a.dv, off, dv, hh);
+}
+
+hipError_t launch_attn_bwd(const BwdPrep& pp, const BwdArgs& args, int B, int d, int causal,
+                           hipStream_t s) {
+    if (d != 128) return hipErrorInvalidValue;
+    const int BH = B * args.H;
+    hipError_t e;
+    {
+        void* kargs[] = {(void*)&pp.o, (void*)&pp.dO, (void*)&pp.v, (void*)&args.H, (void*)&args.N,
+                         (void*)&args.nblk, (void*)&args.layout, (void*)&args.Dq, (void*)&args.do16,
+                         (void*)&args.v16, (void*)&args.do8, (void*)&args.s_do};
+        if ((e = hipLaunchKernel((const void*)bwd_prep_kernel<128>, dim3(args.nblk, BH),
+                                 dim3(kBwdThreads), kargs, 0, s)) != hipSuccess)
+            return e;
+    }
+    {
+        void* kargs[] = {(void*)&args.q8, (void*)&args.nblk, (void*)&args.qT8};
+        if ((e = hipLaunchKernel((const void*)bwd_t8_kernel<128>, dim3(args.nblk, BH),
+                                 dim3(kBwdThreads), kargs, 0, s)) != hipSuccess)
+            return e;
+    }
+    {
+        void* kargs[] = {(void*)&args.k8, (void*)&args.nblk, (void*)&args.kT8};
+        if ((e = hipLaunchKernel((const void*)bwd_t8_kernel<128>, dim3(args.nblk, BH),
+                                 dim3(kBwdThreads), kargs, 0, s)) != hipSuccess)
+            return e;
+    }
+    BwdArgs a = args;
+    a.total = BH * a.nblk;
+    void* kargs[] = {(void*)&a};
+    const void* fq = causal ? (const void*)bwd_dq_kernel<128, true> : (const void*)bwd_dq_kernel<128, false>;
+    if ((e = hipLaunchKernel(fq, dim3(a.total), dim3(kBwdThreads), kargs, 0, s)) != hipSuccess) return e;
+    const void* fk = causal ? (const void*)bwd_dkdv_kernel<128, true> : (const void*)bwd_dkdv_kernel<128, false>;
+    return hipLaunchKernel(fk, dim3(a.total), dim3(kBwdThreads), kargs, 0, s);
+}
+
+}  // namespace sage

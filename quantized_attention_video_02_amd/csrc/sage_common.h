@@ -71,6 +71,34 @@ struct AttnArgs {
     const float* bias;     // NULL, or the Q-smoothing correction [B*H][nblk][N_pad] (exp2 units)
     float lambda;    // fp32(sm_scale * log2 e)
     int dbh, drow0, dnrows;
+    float* lse = nullptr;  // NULL, or [B*H][N]: each row's log-sum-exp in the exp2 domain
+};
+
+// The 8-bit backward: the operands prepared once per call (workspace) and
+// the two sweeps' arguments.
+struct BwdPrep {
+    const u16* o;   // forward output, bf16, layout
+    const u16* dO;  // upstream gradient, bf16, layout
+    const u16* v;   // V, bf16, layout
+};
+struct BwdArgs {
+    const int8_t* q8;
+    const float* q_scale;  // per block of kBlk queries [bh][nblk]
+    const int8_t* k8;
+    const float* k_scale;
+    const float* lse;      // [bh][N]
+    float* Dq;             // [bh][N_pad]: dO_i . O_i
+    float* s_do;           // [bh][nblk]: FP8 scale of dO per block
+    _Float16* do16;        // [bh][N_pad][d]
+    _Float16* v16;         // [bh][N_pad][d]
+    uint8_t* do8;          // [bh][nblk][d][128], rows in the FP8 reduction order
+    int8_t* qT8;           // [bh][nblk][d][128], rows in the INT8 reduction order
+    int8_t* kT8;
+    float* dq;             // outputs, fp32, layout
+    float* dk;
+    float* dv;
+    int H, N, N_pad, nblk, total, layout;
+    float lambda, sm_scale;
 };
 
 hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
@@ -88,5 +116,7 @@ hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, 
                           void* vq, float* vscale, float* ws, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal, int dump,
                        hipStream_t s);
+hipError_t launch_attn_bwd(const BwdPrep& pp, const BwdArgs& args, int B, int d, int causal,
+                           hipStream_t s);
 
 }  // namespace sage
