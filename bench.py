@@ -9,6 +9,9 @@ of a 14B video DiT: B=1, H=40, N=75600 (21 x 45 x 80 latent tokens), d=128.
 
 --mx runs the microscaled path instead: sage_quant_qk_mx, sage_quant_v_mx and
 sage_attn_fwd_mx (Q, K, P and V in MXFP6), priced against the dense FP6 peak.
+--bwd times the 8-bit backward (sage_attn_bwd) over the training forward's
+outputs: 10 B H N^2 d ops per step (the five backward products), priced
+against the blend of their peaks (four INT8/FP8 products, dP in FP16).
 
 Prints ONE JSON line:
   value       = 4 B H N^2 d * steps / wall time of the timed steps (TOPS),
@@ -33,7 +36,9 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TOPS (4·B·H·N²·d/s) & % MFMA peak at N=32760/75600, d=128"
 PEAK_TOPS = {"fp8": 5000.0,                       # dense INT8 (QK) = dense FP8 (PV) = 5.0 POPS
              "fp16": 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0),  # INT8 QK half + FP16 PV half
-             "mxfp6": 10100.0}                    # dense FP6 (= FP4) MFMA, both products
+             "mxfp6": 10100.0,                    # dense FP6 (= FP4) MFMA, both products
+             # backward: 2d ops each for S, dV, dK, dQ at 5.0 POPS and dP at 2.5
+             "bwd": 10.0 / (8.0 / 5000.0 + 2.0 / 2500.0)}
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 ATTN_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
@@ -124,6 +129,70 @@ def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None, q_smoo
     quant_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     return wall, quant_ms, attn_ms
+
+
+def time_bwd(sage, wl, steps, warmup):
+    """The backward alone, inputs resident: the training forward runs once,
+    then each step is one sage_attn_bwd call (events around each)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    do = si_grad(wl)
+    qz = sage.quant_qk(wl.q, wl.k)
+    vq, vs = sage.quant_v(wl.v, "fp8")
+    out, lse = sage.attn_fwd_lse(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale)
+    for _ in range(warmup):
+        sage.attn_bwd(qz, wl.v, out, do, lse, causal=wl.causal, sm_scale=wl.sm_scale)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        sage.attn_bwd(qz, wl.v, out, do, lse, causal=wl.causal, sm_scale=wl.sm_scale)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [e[0].elapsed_time(e[1]) for e in evs]
+
+
+def si_grad(wl):
+    import synthetic_inputs as si
+
+    return si.output_grad(wl)
+
+
+def cpu_baseline_bwd(wl, target_rows=128):
+    """The oracle on query block 0 of head (0, 0): its forward rows (output
+    and log-sum-exp) and its dQ over all N keys; ops counted 4 d per pair for
+    the forward rows and 6 d per pair (S, dP, dQ) for the dQ sweep."""
+    import numpy as np
+
+    import oracle
+    import synthetic_inputs as si
+
+    q, k, v = (si.bf16_codes(t[0:1, 0:1]) for t in (wl.q, wl.k, wl.v))
+    dO = si.bf16_codes(si.output_grad(wl)[0:1, 0:1])
+    rows = np.arange(min(target_rows, wl.N), dtype=np.int32)
+    t0 = time.perf_counter()
+    oz = oracle.quant_qk(q, k)
+    ovq, ovs = oracle.quant_v(v, "fp8")
+    t_quant = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    o_rows, lse_rows = oracle.train_forward_head(oz, ovq, ovs, 0, 0, rows, wl.causal, wl.sm_scale)
+    o = np.zeros((wl.N, wl.d), np.uint16)
+    o[rows] = o_rows
+    lse = np.zeros(wl.N, np.float32)
+    lse[rows] = lse_rows
+    oracle.bwd_head(oz, v[0, 0], o, dO[0, 0], lse, 0, 0, wl.causal, wl.sm_scale, qblocks=[0], kblocks=[])
+    t = time.perf_counter() - t0 + t_quant * len(rows) / wl.N
+    keys = (rows + 1).sum() if wl.causal else len(rows) * wl.N
+    ops = 10.0 * float(keys) * wl.d
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": (f"head (b=0,h=0) of {wl.name}: the forward rows of query block 0 "
+                       f"({len(rows)} queries, output and log-sum-exp) and their dQ over "
+                       f"{'their causal keys' if wl.causal else f'all {wl.N} keys'} "
+                       f"({t:.2f} s incl. the head's quantization pro rata); single-threaded C "
+                       f"oracle")}
 
 
 def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False, mx=False):
@@ -262,6 +331,8 @@ def main():
     ap.add_argument("--mx", action="store_true",
                     help="the microscaled path: Q, K, P and V in MXFP6 (sage_quant_qk_mx, "
                          "sage_quant_v_mx, sage_attn_fwd_mx)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="the 8-bit backward (sage_attn_bwd) over the training forward's outputs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -274,6 +345,11 @@ def main():
     if args.record_traffic:
         record_traffic(args.workload, args.pv, *args.record_traffic, q_gran=args.q_gran, mx=args.mx)
         return
+    if args.bwd and (args.mx or args.q_smooth or args.tile_keep is not None or
+                     args.q_gran != "block" or args.pv != "fp8"):
+        print("bench.py: --bwd runs the 8-bit backward alone (no --mx, --q-smooth, "
+              "--tile-keep, --q-gran token or --pv fp16)", file=sys.stderr)
+        sys.exit(2)
     if args.mx and (args.q_smooth or args.tile_keep is not None or args.q_gran != "block"
                     or args.pv != "fp8"):
         print("bench.py: --mx runs the MXFP6 path alone (no --q-smooth, --tile-keep, "
@@ -304,6 +380,32 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.bwd:
+        wall, bwd_ms = time_bwd(sage, wl, args.steps, args.warmup)
+        ops = 10.0 * wl.B * wl.H * wl.N * wl.N * wl.d
+        mean = sum(bwd_ms) / len(bwd_ms)
+        srt = sorted(bwd_ms)
+        achieved = ops / (mean * 1e-3) / 1e12
+        res = {
+            "metric": "attention backward TOPS (10·B·H·N²·d/s, the five backward products)",
+            "value": ops * args.steps / wall / 1e12, "unit": "TOPS", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "int8+fp8+fp16", "data": "synthetic",
+            "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
+                       "causal": wl.causal, "pass": "backward", "seed": wl.seed,
+                       "parallelism": "none"},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS["bwd"],
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_TOPS["bwd"], "traffic": None,
+                         "kernel": "sage_attn_bwd (preparation + dQ sweep + dK/dV sweep)",
+                         "ops_per_launch": ops, "mean_launch_ms": mean,
+                         "median_launch_ms": srt[len(srt) // 2]},
+        }
+        if not args.no_cpu_baseline:
+            print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+            res["cpu_baseline"] = cpu_baseline_bwd(wl)
+        print(json.dumps(res), flush=True)
+        return
     tmask = None
     if args.tile_keep is not None:
         mask_np = tile_mask_for(wl, args.tile_keep)

@@ -85,6 +85,18 @@ def test_mx_refuses_the_other_variants():
     assert r.returncode == 2 and "MXFP6" in r.stderr
 
 
+def test_bwd_refuses_the_other_variants_and_samples_the_oracle():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--bwd", "--mx"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "backward" in r.stderr
+    import synthetic_inputs as si
+
+    res = bench.cpu_baseline_bwd(si.make("tiny", N=300, H=1))
+    assert res["value"] > 0 and res["kind"] == "oracle" and "dQ" in res["sample"]
+    # the blended backward peak: 2d ops each at 5.0 POPS for four products, dP at 2.5
+    assert bench.PEAK_TOPS["bwd"] == pytest.approx(10.0 / (8.0 / 5000.0 + 2.0 / 2500.0))
+
+
 def test_algorithmic_ops_count():
     # 4 d ops per (query, key) pair: 2d for Q K^T, 2d for P V
     assert bench.attn_ops(1, 40, 75600, 128) == pytest.approx(1.1705e14, rel=1e-4)
@@ -154,3 +166,16 @@ def test_mx_bench_line():
     assert line["dtype"] == "mxfp6" and rf["kernel"] == "attn_mx_kernel"
     assert rf["peak"] == 10100.0 and rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
     assert "MXFP6" in line["cpu_baseline"]["sample"]
+
+
+@pytest.mark.gpu
+def test_bwd_bench_line():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--bwd",
+                        "--steps", "3", "--warmup", "1"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    rf = line["roofline"]
+    assert line["config"]["pass"] == "backward" and line["value"] > 0
+    assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
+    assert line["cpu_baseline"]["kind"] == "oracle"
