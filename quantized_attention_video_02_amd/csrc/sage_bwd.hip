@@ -158,21 +158,27 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_t8_kernel(const int8_t* __res
     }
 }
 
-// Code of x in INT8 at inv = fp32(127 / a): rne, clamped to +-127.
-__device__ inline int i8_code(float x, float inv) {
-    return (int)fminf(fmaxf(rintf(x * inv), -127.0f), 127.0f);
-}
+// Empty uses: the loads that produce x complete here (a kernel's one-time
+// loads are waited for before its sweep, not inside it, where the wait
+// would also cover the tile copies in flight).
+__device__ inline void settle(const v4i& x) { asm volatile("" ::"v"(x)); }
+__device__ inline void settle(const v8h& x) { asm volatile("" ::"v"(x)); }
+__device__ inline void settle(float x) { asm volatile("" ::"v"(x)); }
 
-// 16 accumulator registers of one 32-row block as INT8 codes: the B operand
-// of a 32x32x32 INT8 MFMA whose reduction runs over that block.
+// 16 accumulator registers of one 32-row block as INT8 codes (rne of
+// fp32(x * inv), inv = fp32(127 / a) with a >= |x|, so the codes stay within
+// +-127): the B operand of a 32x32x32 INT8 MFMA whose reduction runs over
+// that block.  Each code is converted as the unsigned byte of y + 128
+// (v_cvt_pk_u8_f32, round to nearest even; 128 is even, so ties fall the
+// same way), and the bias is removed by flipping the top bit of every byte.
 __device__ inline v4i pack_i8(const float* x, float inv) {
     v4i r;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         uint32_t u = 0u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u |= ((uint32_t)i8_code(x[4 * w + j], inv) & 0xffu) << (8 * j);
-        r[w] = (int)u;
+        for (int j = 0; j < 4; ++j) u = __builtin_amdgcn_cvt_pk_u8_f32(x[4 * w + j] * inv + 128.0f, j, u);
+        r[w] = (int)(u ^ 0x80808080u);
     }
     return r;
 }
@@ -233,6 +239,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     const float sigma = a.q_scale[bh * a.nblk + qb] * a.lambda;
     const float lse = valid ? a.lse[(int64_t)bh * N + qi] : 0.0f;
     const float Di = a.Dq[rowp];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) settle(qf[kk]);
+#pragma unroll
+    for (int kk = 0; kk < HK; ++kk) settle(dof[kk]);
+    settle(sigma);
+    settle(lse);
+    settle(Di);
 
     int koff[KMAXP], voff[VMAXP], toff[TMAXP];
 #pragma unroll
@@ -275,39 +288,84 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         const uint8_t* vbuf = kbuf + K8B;
         const uint8_t* tbuf = vbuf + V16B;
         const float c = sigma * ks;
-        // S^T (keys x queries) and dP^T = V dO^T, 32-key block k4
+        // S^T (keys x queries) and dP^T = V dO^T: every operand of the two
+        // products read first (the LDS latency is paid once), then the MFMAs
+        // with the four 32-key blocks' chains interleaved
         v16i S[4];
         v16f dP[4];
+        {
+            v4i ka[4][KK];
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-            const uint8_t* krow = kbuf + (32 * k4 + n) * kKstr + 16 * hh;
-            v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)krow, qf[0], v16i{}, 0, 0, 0);
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const uint8_t* krow = kbuf + (32 * k4 + n) * kKstr + 16 * hh;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) ka[k4][kk] = *(const v4i*)(krow + 32 * kk);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) S[k4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[k4][0], qf[0], v16i{}, 0, 0, 0);
 #pragma unroll
             for (int kk = 1; kk < KK; ++kk)
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)(krow + 32 * kk), qf[kk], acc, 0, 0, 0);
-            S[k4] = acc;
-            const uint8_t* vrow = vbuf + (32 * k4 + n) * kHstr + 16 * hh;
-            v16f pacc = v16f{};
 #pragma unroll
-            for (int kk = 0; kk < HK; ++kk)
-                pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const v8h*)(vrow + 32 * kk), dof[kk], pacc, 0, 0, 0);
-            dP[k4] = pacc;
+                for (int k4 = 0; k4 < 4; ++k4)
+                    S[k4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[k4][kk], qf[kk], S[k4], 0, 0, 0);
+        }
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) dP[k4] = v16f{};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            v8h va[4][HK / 2];
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const uint8_t* vrow = vbuf + (32 * k4 + n) * kHstr + 16 * hh + 32 * (HK / 2) * half;
+#pragma unroll
+                for (int kk = 0; kk < HK / 2; ++kk) va[k4][kk] = *(const v8h*)(vrow + 32 * kk);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < HK / 2; ++kk)
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4)
+                    dP[k4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[k4][kk], dof[(HK / 2) * half + kk], dP[k4], 0, 0, 0);
+        }
+        // the transposed K operands of dQ^T, read while the vector work below runs
+        v4i ta[CB][4];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const uint8_t* trow = tbuf + (32 * cb + n) * kKstr + 16 * hh;
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) ta[cb][k4] = *(const v4i*)(trow + 32 * k4);
         }
         // P^T and dS^T; masked entries (key >= N, causal key > query, padding
         // queries) are 0
+        // (padding queries give dS = 0 by themselves: their dO, D and codes
+        // are 0; keys past N and, causal, keys after the query are masked on
+        // the tiles that hold any)
         const int key_t = t * kBc;
+        const bool needmask = key_t + kBc > N || (CAUSAL && t == qb);
         float ds[4][16];
         float amax = 0.0f;
+        if (needmask) {
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4)
+            for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = key_t + 32 * k4 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const bool ok = valid && key < N && (!CAUSAL || key <= qi);
-                const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[k4][r], c, -lse)) : 0.0f;
-                ds[k4][r] = p * (dP[k4][r] - Di);
-                amax = fmaxf(amax, fabsf(ds[k4][r]));
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const int key = key_t + 32 * k4 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    const bool ok = key < N && (!CAUSAL || key <= qi);
+                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[k4][r], c, -lse)) : 0.0f;
+                    ds[k4][r] = p * (dP[k4][r] - Di);
+                    amax = fmaxf(amax, fabsf(ds[k4][r]));
+                }
+        } else {
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[k4][r], c, -lse));
+                    ds[k4][r] = p * (dP[k4][r] - Di);
+                    amax = fmaxf(amax, fabsf(ds[k4][r]));
+                }
+        }
         float s_ds, inv;
         tile_scale(amax, red, wave, lane, s_ds, inv);
         v4i dsb[4];
@@ -315,16 +373,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         for (int k4 = 0; k4 < 4; ++k4) dsb[k4] = pack_i8(ds[k4], inv);
         // dQ^T (channels x queries) += K8^T dS8^T for this tile, scaled
         const float fq = (s_ds * ks) * a.sm_scale;
+        v16i qacc[CB];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const uint8_t* trow = tbuf + (32 * cb + n) * kKstr + 16 * hh;
-            v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)trow, dsb[0], v16i{}, 0, 0, 0);
+        for (int cb = 0; cb < CB; ++cb) qacc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ta[cb][0], dsb[0], v16i{}, 0, 0, 0);
 #pragma unroll
-            for (int k4 = 1; k4 < 4; ++k4)
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)(trow + 32 * k4), dsb[k4], acc, 0, 0, 0);
+        for (int k4 = 1; k4 < 4; ++k4)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dq[cb][e] = dq[cb][e] + (float)acc[e] * fq;
-        }
+            for (int cb = 0; cb < CB; ++cb)
+                qacc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ta[cb][k4], dsb[k4], qacc[cb], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dq[cb][e] = dq[cb][e] + (float)qacc[cb][e] * fq;
         wait_vmem();
         __syncthreads();
     }
@@ -368,6 +428,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < HK; ++kk) vf[kk] = *(const v8h*)(a.v16 + rowk * D + 16 * kk + 8 * hh);
     const float ks = a.k_scale[bh * a.nblk + kb];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) settle(kf[kk]);
+#pragma unroll
+    for (int kk = 0; kk < HK; ++kk) settle(vf[kk]);
+    settle(ks);
 
     int qoff[QMAXP], hoff[HMAXP], foff[FMAXP], toff[TMAXP];
 #pragma unroll
@@ -410,23 +475,52 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // S = Q K^T and dP = dO V^T (queries x keys), 32-query block q4
         v16i S[4];
         v16f dP[4];
+        {
+            v4i qa[4][KK];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const uint8_t* qrow = qbuf + (32 * q4 + n) * kKstr + 16 * hh;
-            v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)qrow, kf[0], v16i{}, 0, 0, 0);
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const uint8_t* qrow = qbuf + (32 * q4 + n) * kKstr + 16 * hh;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) qa[q4][kk] = *(const v4i*)(qrow + 32 * kk);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) S[q4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[q4][0], kf[0], v16i{}, 0, 0, 0);
 #pragma unroll
             for (int kk = 1; kk < KK; ++kk)
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)(qrow + 32 * kk), kf[kk], acc, 0, 0, 0);
-            S[q4] = acc;
-            const uint8_t* hrow = hbuf + (32 * q4 + n) * kHstr + 16 * hh;
-            v16f pacc = v16f{};
 #pragma unroll
-            for (int kk = 0; kk < HK; ++kk)
-                pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const v8h*)(hrow + 32 * kk), vf[kk], pacc, 0, 0, 0);
-            dP[q4] = pacc;
+                for (int q4 = 0; q4 < 4; ++q4)
+                    S[q4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[q4][kk], kf[kk], S[q4], 0, 0, 0);
         }
-        // P and dS (masked entries 0), and P in FP8 at the static scale 448
-        float p[4][16], ds[4][16];
+        {
+            // dP in two halves of the channels (the operands of one half held at once)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) dP[q4] = v16f{};
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                v8h ha[4][HK / 2];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const uint8_t* hrow = hbuf + (32 * q4 + n) * kHstr + 16 * hh + 32 * (HK / 2) * half;
+#pragma unroll
+                    for (int kk = 0; kk < HK / 2; ++kk) ha[q4][kk] = *(const v8h*)(hrow + 32 * kk);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kk = 0; kk < HK / 2; ++kk)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        dP[q4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[q4][kk], vf[(HK / 2) * half + kk], dP[q4], 0, 0, 0);
+            }
+        }
+        // P and dS (masked entries 0); each group of 4 probabilities goes
+        // straight into the FP8 operand at the static scale 448.  Padding
+        // queries give dS = 0 by themselves (dO, D and codes 0) and add
+        // nothing to dV; padding keys and, causal, keys after the query are
+        // masked on the tiles that hold any.
+        const bool needmask = kb * kBc + kBc > N || (CAUSAL && qt == kb);
+        float ds[4][16];
+        v8i P8[2];
         float amax = 0.0f;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
@@ -435,27 +529,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 const float4 L4 = *(const float4*)&lseL[32 * q4 + 8 * i + 4 * hh];
                 const float4 D4 = *(const float4*)&dL[32 * q4 + 8 * i + 4 * hh];
                 const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+                float pv[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 4 * i + j;
                     const int q = qt * kBlk + 32 * q4 + 8 * i + 4 * hh + j;
-                    const bool ok = kvalid && q < N && (!CAUSAL || kj <= q);
-                    const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[q4][r], c, -Lv[j])) : 0.0f;
-                    p[q4][r] = pv;
-                    ds[q4][r] = pv * (dP[q4][r] - Dv[j]);
+                    const bool ok = !needmask || (kvalid && (!CAUSAL || kj <= q));
+                    pv[j] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[q4][r], c, -Lv[j])) : 0.0f;
+                    ds[q4][r] = pv[j] * (dP[q4][r] - Dv[j]);
                     amax = fmaxf(amax, fabsf(ds[q4][r]));
                 }
-            }
-        v8i P8[2];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float x0 = p[q4][4 * u] * 448.0f, x1 = p[q4][4 * u + 1] * 448.0f;
-                const float x2 = p[q4][4 * u + 2] * 448.0f, x3 = p[q4][4 * u + 3] * 448.0f;
-                int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-                w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
-                P8[q4 >> 1][(q4 & 1) * 4 + u] = w;
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0] * 448.0f, pv[1] * 448.0f, 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2] * 448.0f, pv[3] * 448.0f, w, true);
+                P8[q4 >> 1][(q4 & 1) * 4 + i] = w;
             }
         // dV^T (channels x keys) += dO8^T P~ over this tile, scaled by s_do / 448
         const float fv = (float)((double)sdo / 448.0);
