@@ -289,14 +289,15 @@ __attribute__((visibility("default"))) int sage_attn_fwd_lse(
 
 // Workspace of the 8-bit backward, carved in this order, each part 256-byte
 // aligned: D [bh][N_pad] f32, s_do [bh][nblk] f32, dO and V in fp16
-// [bh][N_pad][d], dO in FP8 and Q, K codes transposed [bh][nblk][d][128].
+// [bh][N_pad][d], dO in FP8 and Q, K codes transposed [bh][nblk][d][128],
+// the per-tile records of the dK/dV sweep [bh][nblk][512] f32.
 static size_t bwd_parts(int B, int H, int N, int d, size_t* off) {
     const size_t bh = (size_t)B * H, nblk = ((size_t)N + sage::kBlk - 1) / sage::kBlk;
     const size_t np = nblk * sage::kBlk;
-    const size_t sz[7] = {bh * np * 4, bh * nblk * 4, bh * np * d * 2, bh * np * d * 2,
-                          bh * np * d, bh * np * d, bh * np * d};
+    const size_t sz[8] = {bh * np * 4, bh * nblk * 4, bh * np * d * 2, bh * np * d * 2,
+                          bh * np * d, bh * np * d, bh * np * d, bh * nblk * sage::kRecFloats * 4};
     size_t o = 0;
-    for (int i = 0; i < 7; ++i) {
+    for (int i = 0; i < 8; ++i) {
         if (off) off[i] = o;
         o += (sz[i] + 255) / 256 * 256;
     }
@@ -329,7 +330,7 @@ __attribute__((visibility("default"))) int sage_attn_bwd(
         !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(lse) || !aligned16(dq) ||
         !aligned16(dk) || !aligned16(dv) || ((uintptr_t)workspace & 255u))
         return SAGE_ERR_ALIGN;
-    size_t off[7];
+    size_t off[8];
     if (workspace_bytes < bwd_parts(B, H, N, d, off)) return SAGE_ERR_WORKSPACE;
     uint8_t* ws = (uint8_t*)workspace;
     sage::BwdPrep pp;
@@ -349,6 +350,7 @@ __attribute__((visibility("default"))) int sage_attn_bwd(
     a.do8 = ws + off[4];
     a.qT8 = (int8_t*)(ws + off[5]);
     a.kT8 = (int8_t*)(ws + off[6]);
+    a.rec = (float*)(ws + off[7]);
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;

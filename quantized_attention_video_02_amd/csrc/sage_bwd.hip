@@ -65,8 +65,9 @@ __device__ inline _Float16 f16_sat(float x) {
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(
     const u16* __restrict__ o, const u16* __restrict__ dO, const u16* __restrict__ v, int H, int N,
-    int nblk, int layout, float* __restrict__ Dq, _Float16* __restrict__ do16,
-    _Float16* __restrict__ v16, uint8_t* __restrict__ do8, float* __restrict__ s_do) {
+    int nblk, int layout, const float* __restrict__ lse, const float* __restrict__ q_scale,
+    float* __restrict__ Dq, _Float16* __restrict__ do16, _Float16* __restrict__ v16,
+    uint8_t* __restrict__ do8, float* __restrict__ s_do, float* __restrict__ rec) {
     constexpr int CPR = D / 8, RPI = kBwdThreads / CPR;
     constexpr int LSTR = kBlk + 4;  // floats per channel row of the fp32 dO tile
     __shared__ float tile[D * LSTR];
@@ -102,7 +103,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(
         // the row's CPR threads are consecutive lanes
 #pragma unroll
         for (int s = CPR / 2; s >= 1; s >>= 1) part += __shfl_xor(part, s);
-        if (cg == 0) Dq[bh * N_pad + row] = part;
+        float* rc = rec + ((int64_t)bh * nblk + blk) * kRecFloats;
+        if (cg == 0) {
+            Dq[bh * N_pad + row] = part;
+            rc[kBlk + r] = part;
+            rc[r] = row < N ? lse[(int64_t)bh * N + row] : 0.0f;
+        }
         v8h hd, hv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -121,7 +127,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(
 #pragma unroll
     for (int w = 1; w < kBwdThreads / 64; ++w) a = fmaxf(a, red[w]);
     const float inv = a > 0.0f ? (float)(448.0 / (double)a) : 0.0f;
-    if (t == 0) s_do[bh * nblk + blk] = (float)((double)a / 448.0);
+    if (t == 0) {
+        const float sd = (float)((double)a / 448.0);
+        s_do[bh * nblk + blk] = sd;
+        float* rc = rec + ((int64_t)bh * nblk + blk) * kRecFloats;
+        rc[2 * kBlk] = q_scale[bh * nblk + blk];
+        rc[2 * kBlk + 1] = sd;
+    }
     uint8_t* dst = do8 + ((int64_t)bh * nblk + blk) * D * kBlk;
     for (int i = t; i < D * kBlk / 4; i += kBwdThreads) {
         const int c = i / (kBlk / 4), w = i % (kBlk / 4);
@@ -395,21 +407,44 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------- dK / dV sweep
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (they complete in issue order).
+template <int N>
+__device__ inline void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Copy pieces wave w issues for a tile of P pieces (piece J = w + 4 j).
+constexpr int pieces_of(int P, int w) { return P > w ? (P - w + 3) / 4 : 0; }
+
 // Workgroup = one key block of 128 (wave w: keys 32 w .. 32 w + 31), query
-// tiles swept in ascending order through one LDS slot: Q codes [128 queries]
-// [kKstr], dO fp16 [128][kHstr], dO FP8 transposed [D][kKstr], Q codes
-// transposed [D][kKstr], and the tile's lse / D rows.
+// tiles swept in ascending order.  LDS: slot A, double-buffered: Q codes
+// [128 queries][kKstr], dO fp16 [128][kHstr] and the tile's record (lse, D,
+// q_scale, s_do); slot B, single: dO FP8 transposed [D][kKstr] and Q codes
+// transposed [D][kKstr].  A(t + 1) is copied while tile t computes; B(t + 1)
+// after tile t's dV / dK, awaited only before tile t + 1's dV / dK.  Every
+// vector-memory load of the sweep is a tile copy, so the waits count them.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int NW = 4, KK = D / 32, CB = D / 32, HK = D / 16;
-    constexpr int Q8B = kBlk * kKstr, DO16B = kBlk * kHstr, DO8B = D * kKstr, QTB = D * kKstr;
-    constexpr int QP = Q8B / 1024, HP = DO16B / 1024, FP = DO8B / 1024, TP = QTB / 1024;
-    constexpr int QMAXP = (QP + NW - 1) / NW, HMAXP = (HP + NW - 1) / NW, FMAXP = (FP + NW - 1) / NW,
-                  TMAXP = (TP + NW - 1) / NW;
-    static_assert(Q8B % 1024 == 0 && DO16B % 1024 == 0 && DO8B % 1024 == 0, "1 KB copy pieces");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[Q8B + DO16B + DO8B + QTB];
-    __shared__ __attribute__((aligned(16))) float lseL[kBlk];
-    __shared__ __attribute__((aligned(16))) float dL[kBlk];
+    constexpr int Q8B = kBlk * kKstr, DO16B = kBlk * kHstr, RECB = kRecFloats * 4;
+    constexpr int SLOTA = Q8B + DO16B + RECB;
+    constexpr int DO8B = D * kKstr, QTB = D * kKstr;
+    constexpr int QP = Q8B / 1024, HP = DO16B / 1024, LP = RECB / 1024, FP = DO8B / 1024, TP = QTB / 1024;
+    constexpr int QMAXP = (QP + NW - 1) / NW, HMAXP = (HP + NW - 1) / NW, LMAXP = (LP + NW - 1) / NW,
+                  FMAXP = (FP + NW - 1) / NW, TMAXP = (TP + NW - 1) / NW;
+    static_assert(Q8B % 1024 == 0 && DO16B % 1024 == 0 && RECB % 1024 == 0 && DO8B % 1024 == 0,
+                  "1 KB copy pieces");
+    // loads per wave of the A and B copies (waves 0, 1 and 2, 3 issue alike)
+    constexpr int NA01 = pieces_of(QP, 0) + pieces_of(HP, 0) + pieces_of(LP, 0);
+    constexpr int NA23 = pieces_of(QP, 2) + pieces_of(HP, 2) + pieces_of(LP, 2);
+    constexpr int NB01 = pieces_of(FP, 0) + pieces_of(TP, 0);
+    constexpr int NB23 = pieces_of(FP, 2) + pieces_of(TP, 2);
+    static_assert(NA01 == pieces_of(QP, 1) + pieces_of(HP, 1) + pieces_of(LP, 1) &&
+                  NA23 == pieces_of(QP, 3) + pieces_of(HP, 3) + pieces_of(LP, 3) &&
+                  NB01 == pieces_of(FP, 1) + pieces_of(TP, 1) &&
+                  NB23 == pieces_of(FP, 3) + pieces_of(TP, 3), "wave pairs issue alike");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOTA + DO8B + QTB];
     __shared__ float red[NW];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -434,11 +469,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int kk = 0; kk < HK; ++kk) settle(vf[kk]);
     settle(ks);
 
-    int qoff[QMAXP], hoff[HMAXP], foff[FMAXP], toff[TMAXP];
+    int qoff[QMAXP], hoff[HMAXP], loff[LMAXP], foff[FMAXP], toff[TMAXP];
 #pragma unroll
     for (int j = 0; j < QMAXP; ++j) qoff[j] = slot_src<D, kKstr>(64 * (wave + NW * j) + lane);
 #pragma unroll
     for (int j = 0; j < HMAXP; ++j) hoff[j] = slot_src<2 * D, kHstr>(64 * (wave + NW * j) + lane);
+#pragma unroll
+    for (int j = 0; j < LMAXP; ++j) loff[j] = 16 * (64 * (wave + NW * j) + lane);
 #pragma unroll
     for (int j = 0; j < FMAXP; ++j) foff[j] = slot_src<kBlk, kKstr>(64 * (wave + NW * j) + lane);
 #pragma unroll
@@ -447,30 +484,40 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const uint8_t* qg = (const uint8_t*)a.q8 + (int64_t)bh * a.N_pad * D;
     const uint8_t* hg = (const uint8_t*)a.do16 + (int64_t)bh * a.N_pad * D * 2;
+    const uint8_t* lg = (const uint8_t*)a.rec + (int64_t)bh * a.nblk * RECB;
     const uint8_t* fg = (const uint8_t*)a.do8 + (int64_t)bh * a.nblk * D * kBlk;
     const uint8_t* tg = (const uint8_t*)a.qT8 + (int64_t)bh * a.nblk * D * kBlk;
+    const uint32_t lB = lbase + 2 * SLOTA;
+    auto copy_a = [&](int qt) {
+        const uint32_t l = lbase + (qt & 1) * SLOTA;
+        tile_to_lds<QP, QMAXP, NW>(qg + (int64_t)qt * kBlk * D, l, wv, qoff);
+        tile_to_lds<HP, HMAXP, NW>(hg + (int64_t)qt * kBlk * D * 2, l + Q8B, wv, hoff);
+        tile_to_lds<LP, LMAXP, NW>(lg + (int64_t)qt * RECB, l + Q8B + DO16B, wv, loff);
+    };
+    auto copy_b = [&](int qt) {
+        tile_to_lds<FP, FMAXP, NW>(fg + (int64_t)qt * D * kBlk, lB, wv, foff);
+        tile_to_lds<TP, TMAXP, NW>(tg + (int64_t)qt * D * kBlk, lB + DO8B, wv, toff);
+    };
 
     v16f dk[CB], dv[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) dk[cb] = dv[cb] = v16f{};
-    for (int qt = CAUSAL ? kb : 0; qt < a.nblk; ++qt) {
-        tile_to_lds<QP, QMAXP, NW>(qg + (int64_t)qt * kBlk * D, lbase, wv, qoff);
-        tile_to_lds<HP, HMAXP, NW>(hg + (int64_t)qt * kBlk * D * 2, lbase + Q8B, wv, hoff);
-        tile_to_lds<FP, FMAXP, NW>(fg + (int64_t)qt * D * kBlk, lbase + Q8B + DO16B, wv, foff);
-        tile_to_lds<TP, TMAXP, NW>(tg + (int64_t)qt * D * kBlk, lbase + Q8B + DO16B + DO8B, wv, toff);
-        if (tid < kBlk) {
-            const int q = qt * kBlk + tid;
-            lseL[tid] = q < N ? a.lse[(int64_t)bh * N + q] : 0.0f;
-            dL[tid] = a.Dq[(int64_t)bh * a.N_pad + q];
-        }
-        const float qsc = a.q_scale[bh * a.nblk + qt];
-        const float sdo = a.s_do[bh * a.nblk + qt];
-        wait_vmem();
+    const int t0 = CAUSAL ? kb : 0;
+    copy_a(t0);
+    copy_b(t0);
+    for (int qt = t0; qt < a.nblk; ++qt) {
+        // A(qt) complete (only B(qt) may still be in flight), for every wave
+        if (wv < 2) wait_vm<NB01>();
+        else wait_vm<NB23>();
         __syncthreads();
-        const uint8_t* qbuf = smem;
-        const uint8_t* hbuf = smem + Q8B;
-        const uint8_t* fbuf = hbuf + DO16B;
+        const bool more = qt + 1 < a.nblk;
+        if (more) copy_a(qt + 1);
+        const uint8_t* qbuf = smem + (qt & 1) * SLOTA;
+        const uint8_t* hbuf = qbuf + Q8B;
+        const float* recL = (const float*)(hbuf + DO16B);
+        const uint8_t* fbuf = smem + 2 * SLOTA;
         const uint8_t* tbuf = fbuf + DO8B;
+        const float qsc = recL[2 * kBlk], sdo = recL[2 * kBlk + 1];
         const float c = (qsc * a.lambda) * ks;
         // S = Q K^T and dP = dO V^T (queries x keys), 32-query block q4
         v16i S[4];
@@ -526,8 +573,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float4 L4 = *(const float4*)&lseL[32 * q4 + 8 * i + 4 * hh];
-                const float4 D4 = *(const float4*)&dL[32 * q4 + 8 * i + 4 * hh];
+                const float4 L4 = *(const float4*)&recL[32 * q4 + 8 * i + 4 * hh];
+                const float4 D4 = *(const float4*)&recL[kBlk + 32 * q4 + 8 * i + 4 * hh];
                 const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
                 float pv[4];
 #pragma unroll
@@ -543,6 +590,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2] * 448.0f, pv[3] * 448.0f, w, true);
                 P8[q4 >> 1][(q4 & 1) * 4 + i] = w;
             }
+        // B(qt) complete for this wave (A(qt + 1), issued after it, may still
+        // be in flight); the barrier in tile_scale makes it so for all waves
+        if (more) {
+            if (wv < 2) wait_vm<NA01>();
+            else wait_vm<NA23>();
+        } else {
+            wait_vmem();
+        }
+        float s_ds, inv;
+        tile_scale(amax, red, wave, lane, s_ds, inv);
         // dV^T (channels x keys) += dO8^T P~ over this tile, scaled by s_do / 448
         const float fv = (float)((double)sdo / 448.0);
 #pragma unroll
@@ -555,8 +612,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) dv[cb][e] = dv[cb][e] + T[e] * fv;
         }
-        float s_ds, inv;
-        tile_scale(amax, red, wave, lane, s_ds, inv);
         v4i dsb[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) dsb[q4] = pack_i8(ds[q4], inv);
@@ -572,8 +627,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) dk[cb][e] = dk[cb][e] + (float)acc[e] * fk;
         }
-        // every read of this tile's slot is done before the next tile's copies
+        // every wave is done with slot B (and this tile's slot A) before
+        // B(qt + 1) is copied
         __syncthreads();
+        if (more) copy_b(qt + 1);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -593,8 +650,9 @@ hipError_t launch_attn_bwd(const BwdPrep& pp, const BwdArgs& args, int B, int d,
     hipError_t e;
     {
         void* kargs[] = {(void*)&pp.o, (void*)&pp.dO, (void*)&pp.v, (void*)&args.H, (void*)&args.N,
-                         (void*)&args.nblk, (void*)&args.layout, (void*)&args.Dq, (void*)&args.do16,
-                         (void*)&args.v16, (void*)&args.do8, (void*)&args.s_do};
+                         (void*)&args.nblk, (void*)&args.layout, (void*)&args.lse, (void*)&args.q_scale,
+                         (void*)&args.Dq, (void*)&args.do16, (void*)&args.v16, (void*)&args.do8,
+                         (void*)&args.s_do, (void*)&args.rec};
         if ((e = hipLaunchKernel((const void*)bwd_prep_kernel<128>, dim3(args.nblk, BH),
                                  dim3(kBwdThreads), kargs, 0, s)) != hipSuccess)
             return e;

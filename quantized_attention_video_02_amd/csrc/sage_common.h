@@ -81,6 +81,9 @@ struct BwdPrep {
     const u16* dO;  // upstream gradient, bf16, layout
     const u16* v;   // V, bf16, layout
 };
+// Per-tile record of the dK/dV sweep, one per (bh, query block), copied into
+// LDS with the tile: lse and D of the block's rows, its Q scale and dO scale.
+constexpr int kRecFloats = 512;  // 2 KB: [0, 128) lse, [128, 256) D, 256 q_scale, 257 s_do
 struct BwdArgs {
     const int8_t* q8;
     const float* q_scale;  // per block of kBlk queries [bh][nblk]
@@ -94,6 +97,7 @@ struct BwdArgs {
     uint8_t* do8;          // [bh][nblk][d][128], rows in the FP8 reduction order
     int8_t* qT8;           // [bh][nblk][d][128], rows in the INT8 reduction order
     int8_t* kT8;
+    float* rec;            // [bh][nblk][kRecFloats]
     float* dq;             // outputs, fp32, layout
     float* dk;
     float* dv;
