@@ -178,19 +178,22 @@ __device__ inline void settle(const v8h& x) { asm volatile("" ::"v"(x)); }
 __device__ inline void settle(float x) { asm volatile("" ::"v"(x)); }
 
 // 16 accumulator registers of one 32-row block as INT8 codes (rne of
-// fp32(x * inv), inv = fp32(127 / a) with a >= |x|, so the codes stay within
-// +-127): the B operand of a 32x32x32 INT8 MFMA whose reduction runs over
-// that block.  Each code is converted as the unsigned byte of y + 128
-// (v_cvt_pk_u8_f32, round to nearest even; 128 is even, so ties fall the
-// same way), and the bias is removed by flipping the top bit of every byte.
+// y = fp32(x * inv), inv = fp32(127 / a) with a >= |x|, so the codes stay
+// within +-127): the B operand of a 32x32x32 INT8 MFMA whose reduction runs
+// over that block.  fp32(y + 1.5 * 2^23) is 1.5 * 2^23 + rne(y) exactly (for
+// |y| < 2^22 the sum's ulp is 1), so the low byte of its bit pattern is the
+// two's-complement code; v_perm_b32 gathers the low bytes of two sums.
 __device__ inline v4i pack_i8(const float* x, float inv) {
     v4i r;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        uint32_t u = 0u;
+        uint32_t z[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u = __builtin_amdgcn_cvt_pk_u8_f32(x[4 * w + j] * inv + 128.0f, j, u);
-        r[w] = (int)(u ^ 0x80808080u);
+        for (int j = 0; j < 4; ++j) z[j] = __float_as_uint(x[4 * w + j] * inv + 12582912.0f);
+        // bytes (z0.b0, z1.b0, 0, 0) and (0, 0, z2.b0, z3.b0)
+        const uint32_t lo = __builtin_amdgcn_perm(z[1], z[0], 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(z[3], z[2], 0x04000c0cu);
+        r[w] = (int)(lo | hi);
     }
     return r;
 }
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dq[cb][e] = dq[cb][e] + (float)qacc[cb][e] * fq;
+            for (int e = 0; e < 16; ++e) dq[cb][e] = __builtin_fmaf((float)qacc[cb][e], fq, dq[cb][e]);
         wait_vmem();
         __syncthreads();
     }
@@ -610,7 +613,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(*(const v8i*)(frow + 32), P8[1], T, 0, 0, 0,
                                                                 0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dv[cb][e] = dv[cb][e] + T[e] * fv;
+            for (int e = 0; e < 16; ++e) dv[cb][e] = __builtin_fmaf(T[e], fv, dv[cb][e]);
         }
         v4i dsb[4];
 #pragma unroll
@@ -625,7 +628,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             for (int q4 = 1; q4 < 4; ++q4)
                 acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)(trow + 32 * q4), dsb[q4], acc, 0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dk[cb][e] = dk[cb][e] + (float)acc[e] * fk;
+            for (int e = 0; e < 16; ++e) dk[cb][e] = __builtin_fmaf((float)acc[e], fk, dk[cb][e]);
         }
         // every wave is done with slot B (and this tile's slot A) before
         // B(qt + 1) is copied
