@@ -63,11 +63,11 @@ enum sage_status {
     SAGE_OK = 0,
     SAGE_ERR_NULL = -1,        /* a required pointer is NULL */
     SAGE_ERR_INVALID = -2,     /* bad size, enum, flag, sm_scale or dump window */
-    SAGE_ERR_UNSUPPORTED = -3, /* d not in {64, 128} */
+    SAGE_ERR_UNSUPPORTED = -3, /* d not in {64, 128} (the backward: d != 128) */
     SAGE_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
     SAGE_ERR_SIZE = -5,        /* the problem exceeds the supported size */
     SAGE_ERR_HIP = -6,         /* a HIP launch failed */
-    SAGE_ERR_WORKSPACE = -7    /* workspace smaller than sage_quant_sizes asks */
+    SAGE_ERR_WORKSPACE = -7    /* workspace smaller than the matching *_sizes call asks */
 };
 
 enum sage_layout { SAGE_LAYOUT_HND = 0, SAGE_LAYOUT_NHD = 1 };
@@ -237,7 +237,13 @@ int sage_attn_fwd_lse(const int8_t* q8, const float* q_scale, const int8_t* k8,
  * sage_quant_qk (per-block Q), v the bf16 V, o the forward's bf16 output,
  * dO the upstream gradient (bf16), all in `layout`; lse from
  * sage_attn_fwd_lse.  Outputs dq, dk, dv: fp32 in `layout`, overwritten.
- * workspace: sage_bwd_sizes bytes of device scratch, 256-byte aligned.
+ * workspace: sage_bwd_sizes bytes of device scratch, 256-byte aligned, owned by
+ * the caller and free again when the call's stream work has finished.  With
+ * nblk = ceil(N / 128) and N_pad = 128 nblk it holds, in this order and each
+ * part rounded up to 256 bytes: D [B*H][N_pad] f32, s_do [B*H][nblk] f32, dO
+ * and V in fp16 [B*H][N_pad][d] (two parts), dO in FP8 and the Q and K codes
+ * transposed [B*H][nblk][d][128] bytes (three parts), and the per-tile
+ * records of the dK/dV sweep [B*H][nblk][512] f32.
  * d = 128 only in this build (SAGE_ERR_UNSUPPORTED otherwise).
  */
 int sage_bwd_sizes(int B, int H, int N, int d, size_t* workspace_bytes);

@@ -181,6 +181,48 @@ def test_invalid_arguments_rejected_before_launch(sage):
     assert dbg(s=A + 4) == -4
 
 
+def test_backward_arguments_rejected_before_launch(sage):
+    L = sage.lib()
+    ws = ct.c_size_t()
+    assert L.sage_bwd_sizes(1, 1, 256, 128, None) == -1
+    assert L.sage_bwd_sizes(1, 1, 0, 128, ct.byref(ws)) == -2
+    assert L.sage_bwd_sizes(1, 1, 256, 64, ct.byref(ws)) == -3
+    assert L.sage_bwd_sizes(1, 1, 256, 96, ct.byref(ws)) == -3
+    assert L.sage_bwd_sizes(70000, 1, 256, 128, ct.byref(ws)) == -5
+    # the documented parts, each rounded up to 256 bytes
+    B, H, N, d = 2, 3, 300, 128
+    assert L.sage_bwd_sizes(B, H, N, d, ct.byref(ws)) == 0
+    bh, nblk = B * H, -(-N // 128)
+    parts = [bh * 128 * nblk * 4, bh * nblk * 4] + [bh * 128 * nblk * d * 2] * 2 + \
+        [bh * nblk * d * 128] * 3 + [bh * nblk * 512 * 4]
+    need = sum(-(-p // 256) * 256 for p in parts)
+    assert ws.value == need
+    bwd = lambda q8=A, lse=A, dq=A, wsp=A, wsb=need, N=N, d=d, lay=0, causal=0, sm=0.1: \
+        L.sage_attn_bwd(q8, A, A, A, A, A, A, lse, B, H, N, d, lay, causal, sm, dq, A, A, wsp, wsb,
+                        None)
+    assert bwd(q8=None) == -1
+    assert bwd(lse=None) == -1
+    assert bwd(dq=None) == -1
+    assert bwd(wsp=None) == -1
+    assert bwd(N=0) == -2
+    assert bwd(d=64) == -3
+    assert bwd(lay=2) == -2
+    assert bwd(causal=2) == -2
+    for sm in (float("nan"), float("inf"), 0.0, -1.0):
+        assert bwd(sm=sm) == -2
+    assert bwd(dq=A + 4) == -4
+    assert bwd(wsp=A + 16) == -4      # the workspace must be 256-byte aligned
+    assert bwd(wsb=need - 1) == -7
+    lse = lambda out=A, ls=A, causal=0, sm=0.1, pv=0: L.sage_attn_fwd_lse(
+        A, A, A, A, A, A, 1, 2, 256, 128, 0, causal, sm, pv, out, 0, ls, None)
+    assert lse(ls=None) == -1
+    assert lse(out=None) == -1
+    assert lse(causal=2) == -2
+    assert lse(sm=0.0) == -2
+    assert lse(pv=7) == -2
+    assert lse(ls=A + 4) == -4
+
+
 def test_status_strings(sage):
     L = sage.lib()
     names = [L.sage_status_string(c).decode() for c in range(0, -8, -1)]
