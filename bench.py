@@ -43,13 +43,16 @@ HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 ATTN_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
                 for f in ("sage_attn.hip", "sage_common.h", "sage_device.h")]
+BWD_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
+               for f in ("sage_bwd.hip", "sage_api.hip", "sage_common.h", "sage_device.h")]
 
 
-def attn_source_hash():
-    """sha256 of the attention kernel's sources: HBM byte counts measured on
-    another version of the kernel are not reported."""
+def attn_source_hash(bwd=False):
+    """sha256 of the measured kernels' sources (the attention kernel, or the
+    backward's kernels and the workspace carving): HBM byte counts measured
+    on another version of the code are not reported."""
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
+    for f in (BWD_SOURCES if bwd else ATTN_SOURCES):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -268,11 +271,13 @@ def attn_kernel_name(mx):
     return "attn_mx_kernel" if mx else "attn_fwd_kernel"
 
 
-def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False):
+def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False, bwd=False):
     """Write profiles/traffic.json from two rocprofv3 --pmc runs of
     `bench.py --steps 1 --warmup 0 --no-cpu-baseline --calibrate-copy` (one with
-    FETCH_SIZE, one with WRITE_SIZE; KiB per dispatch).  Each counter is scaled
-    so that the plain 1 GiB device copy in the same run reads (writes) 1 GiB."""
+    FETCH_SIZE, one with WRITE_SIZE; KiB per dispatch; with --bwd for the
+    backward).  Each counter is scaled so that the plain 1 GiB device copy in
+    the same run reads (writes) 1 GiB.  The backward's entry is per call: the
+    bytes of all its kernels (names with "bwd_") over the number of calls."""
     import csv
     import glob
 
@@ -284,7 +289,7 @@ def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False)
         return rows
 
     res = {}
-    kname = attn_kernel_name(mx)
+    kname = "bwd_" if bwd else attn_kernel_name(mx)
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = per_kernel(d, counter)
         attn = [float(r["Counter_Value"]) * 1024 for r in rows if kname in r["Kernel_Name"]]
@@ -293,8 +298,13 @@ def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False)
         if not attn or not copy:
             raise SystemExit(f"no {kname} or copy dispatch with {counter} under {d}")
         scale = float(1 << 30) / max(copy)
-        res[counter] = (sum(attn) / len(attn) * scale, scale)
-    entry = {"kernel": kname, "source_hash": attn_source_hash(),
+        # one launch of the attention kernel, or one backward call (one dK/dV sweep each)
+        n = sum(1 for r in rows if "bwd_dkdv_kernel" in r["Kernel_Name"]) if bwd else len(attn)
+        if n == 0:
+            raise SystemExit(f"no bwd_dkdv_kernel dispatch with {counter} under {d}")
+        res[counter] = (sum(attn) / n * scale, scale)
+    entry = {"kernel": "sage_attn_bwd (all its kernels)" if bwd else kname,
+             "source_hash": attn_source_hash(bwd),
              "fetch_bytes": res["FETCH_SIZE"][0], "write_bytes": res["WRITE_SIZE"][0],
              "bytes_per_launch": res["FETCH_SIZE"][0] + res["WRITE_SIZE"][0],
              "fetch_scale": res["FETCH_SIZE"][1], "write_scale": res["WRITE_SIZE"][1],
@@ -304,7 +314,7 @@ def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False)
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
-    data[traffic_key(workload, "mxfp6" if mx else pv, q_gran)] = entry
+    data[traffic_key(workload, "bwd" if bwd else ("mxfp6" if mx else pv), q_gran)] = entry
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(data, f, indent=1)
     print(json.dumps(entry))
@@ -343,7 +353,8 @@ def main():
                          "--pmc output folders (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.record_traffic:
-        record_traffic(args.workload, args.pv, *args.record_traffic, q_gran=args.q_gran, mx=args.mx)
+        record_traffic(args.workload, args.pv, *args.record_traffic, q_gran=args.q_gran, mx=args.mx,
+                       bwd=args.bwd)
         return
     if args.bwd and (args.mx or args.q_smooth or args.tile_keep is not None or
                      args.q_gran != "block" or args.pv != "fp8"):
@@ -386,6 +397,12 @@ def main():
         mean = sum(bwd_ms) / len(bwd_ms)
         srt = sorted(bwd_ms)
         achieved = ops / (mean * 1e-3) / 1e12
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                t = json.load(f).get(traffic_key(wl.name, "bwd"))
+            if t and t.get("source_hash") == attn_source_hash(bwd=True):
+                traffic = t.get("bytes_per_launch")
         res = {
             "metric": "attention backward TOPS (10·B·H·N²·d/s, the five backward products)",
             "value": ops * args.steps / wall / 1e12, "unit": "TOPS", "n_gpus": 1,
@@ -396,7 +413,7 @@ def main():
                        "causal": wl.causal, "pass": "backward", "seed": wl.seed,
                        "parallelism": "none"},
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS["bwd"],
-                         "unit": "TFLOP/s", "frac": achieved / PEAK_TOPS["bwd"], "traffic": None,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_TOPS["bwd"], "traffic": traffic,
                          "kernel": "sage_attn_bwd (preparation + dQ sweep + dK/dV sweep)",
                          "ops_per_launch": ops, "mean_launch_ms": mean,
                          "median_launch_ms": srt[len(srt) // 2]},

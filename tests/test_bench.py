@@ -70,6 +70,31 @@ def test_record_traffic_of_the_mx_kernel(tmp_path, monkeypatch):
     assert e["kernel"] == "attn_mx_kernel" and e["fetch_bytes"] == pytest.approx(700.0 * 1024)
 
 
+def test_record_traffic_of_the_backward_sums_its_kernels_per_call(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    gib_kib = (1 << 30) / 1024
+    call = [("_ZN4sage15bwd_prep_kernelILi128EEEvPKt", 10.0),
+            ("void sage::bwd_t8_kernel<128>(signed char const*, int, signed char*)", 2.0),
+            ("void sage::bwd_t8_kernel<128>(signed char const*, int, signed char*)", 3.0),
+            ("void sage::bwd_dq_kernel<128, false>(sage::BwdArgs)", 100.0),
+            ("void sage::bwd_dkdv_kernel<128, false>(sage::BwdArgs)", 200.0)]
+    # the training forward and the copy are not part of a backward call; two calls
+    rows = [("__amd_rocclr_copyBuffer", gib_kib),
+            ("void sage::attn_fwd_kernel<128, false, false, 0, false>(sage::AttnArgs)", 50.0)]
+    _write_counters(tmp_path / "f", "FETCH_SIZE", rows + call + call)
+    _write_counters(tmp_path / "w", "WRITE_SIZE", rows + call + call)
+    bench.record_traffic("video_14b_720p", "fp8", str(tmp_path / "f"), str(tmp_path / "w"), bwd=True)
+    e = json.load(open(tmp_path / "traffic.json"))["video_14b_720p/bwd"]
+    assert e["fetch_bytes"] == pytest.approx(315.0 * 1024)
+    assert e["write_bytes"] == pytest.approx(315.0 * 1024)
+    assert e["source_hash"] == bench.attn_source_hash(bwd=True) != bench.attn_source_hash()
+    # counters without a dK/dV sweep say nothing per call
+    _write_counters(tmp_path / "w2", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", gib_kib)] + call[:1])
+    with pytest.raises(SystemExit):
+        bench.record_traffic("video_14b_720p", "fp8", str(tmp_path / "f"), str(tmp_path / "w2"),
+                             bwd=True)
+
+
 def test_cpu_baseline_of_the_mx_path():
     import synthetic_inputs as si
 
