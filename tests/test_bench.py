@@ -153,6 +153,8 @@ def test_source_hash_covers_the_kernel_sources():
     h = bench.attn_source_hash()
     assert len(h) == 16 and all(os.path.exists(f) for f in bench.ATTN_SOURCES)
     assert h == bench.attn_source_hash()
+    assert all(os.path.exists(f) for f in bench.BWD_SOURCES)
+    assert any(f.endswith("sage_bwd.hip") for f in bench.BWD_SOURCES)
 
 
 def test_more_than_one_gpu_is_refused():
