@@ -104,6 +104,22 @@ def _stream(device):
     return ct.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _one_gpu(*ts):
+    """The one GPU every given tensor lives on.  The C ABI takes raw device
+    pointers, so a host tensor (or one on another GPU) is refused here rather
+    than handed to a kernel."""
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1 or next(iter(devs)).type != "cuda":
+        raise ValueError("all tensors must be on one GPU, got " + ", ".join(sorted(map(str, devs))))
+    return next(iter(devs))
+
+
+def _check_out(out, shape, dev):
+    if tuple(out.shape) != shape or out.dtype not in OUT or not out.is_contiguous() or \
+            out.device != dev:
+        raise ValueError(f"out must be contiguous {shape} (bfloat16 or float32) on {dev}")
+
+
 def get_config(d: int = 128) -> dict:
     c = SageConfig()
     _check(lib().sage_get_config(d, ct.byref(c)))
@@ -158,8 +174,8 @@ def quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", q_gran: str 
     if q_gran not in QGRAN:
         raise ValueError(f"q_gran must be one of {list(QGRAN)}, not {q_gran!r}")
     B, H, N, d = _dims(q, layout)
+    dev = _one_gpu(q, k)
     sz = quant_sizes(B, H, N, d, q_gran=q_gran)
-    dev = q.device
     nblk = -(-N // 128)
     r = dict(q8=torch.empty((B, H, nblk * 128, d), dtype=torch.int8, device=dev),
              q_scale=torch.empty((B, H, nblk * 128 if q_gran == "token" else nblk),
@@ -195,8 +211,8 @@ def quant_v(v: torch.Tensor, pv: str = "fp8", layout: str = "HND"):
     if v.dtype != torch.bfloat16 or not v.is_contiguous():
         raise TypeError("v must be a contiguous bfloat16 tensor")
     B, H, N, d = _dims(v, layout)
+    dev = _one_gpu(v)
     sz = quant_sizes(B, H, N, d, pv)
-    dev = v.device
     nblk = -(-N // 128)
     vq = torch.empty((B, H, nblk, d, 128), dtype=torch.uint8 if pv == "fp8" else torch.float16,
                      device=dev)
@@ -220,9 +236,20 @@ def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
     B, H, N, d, layout = qz["B"], qz["H"], qz["N"], qz["d"], qz["layout"]
     sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
     shape = (B, H, N, d) if layout == "HND" else (B, N, H, d)
-    dev = qz["q8"].device
+    dev = _one_gpu(qz["q8"], qz["q_scale"], qz["k8"], qz["k_scale"], vq, vs, out, qz.get("bias"))
+    nblk = -(-N // 128)
+    if pv not in PV:
+        raise ValueError(f"pv must be one of {list(PV)}, not {pv!r}")
+    if vq.dtype != (torch.uint8 if pv == "fp8" else torch.float16) or \
+            tuple(vq.shape) != (B, H, nblk, d, 128) or not vq.is_contiguous():
+        raise ValueError(f"vq must be quant_v's contiguous [{B}, {H}, {nblk}, {d}, 128] "
+                         f"({'uint8' if pv == 'fp8' else 'float16'} for pv={pv})")
+    if vs.dtype != torch.float32 or tuple(vs.shape) != (B, H, d) or not vs.is_contiguous():
+        raise ValueError(f"vs must be contiguous float32 [{B}, {H}, {d}]")
     if out is None:
         out = torch.empty(shape, dtype=out_dtype, device=dev)
+    else:
+        _check_out(out, shape, dev)
     args = (_ptr(qz["q8"]), _ptr(qz["q_scale"]), _ptr(qz["k8"]), _ptr(qz["k_scale"]), _ptr(vq),
             _ptr(vs), B, H, N, d, LAYOUTS[layout], int(bool(causal)), sm, PV[pv], _ptr(out),
             OUT[out.dtype])
@@ -231,7 +258,6 @@ def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,
     if tile_mask is not None:
         if debug is not None:
             raise ValueError("the debug dump runs dense")
-        nblk = -(-N // 128)
         if tuple(tile_mask.shape) != (B, H, nblk, nblk) or tile_mask.device != dev:
             raise ValueError(f"tile_mask must be [B, H, {nblk}, {nblk}] on {dev}")
         tm = tile_mask.to(torch.uint8).contiguous()
@@ -283,7 +309,15 @@ def attn_fwd_lse(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = Fa
         raise ValueError("the training forward takes per-block Q without smoothing")
     B, H, N, d, layout = qz["B"], qz["H"], qz["N"], qz["d"], qz["layout"]
     sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
-    dev = qz["q8"].device
+    dev = _one_gpu(qz["q8"], qz["q_scale"], qz["k8"], qz["k_scale"], vq, vs)
+    nblk = -(-N // 128)
+    if pv not in PV:
+        raise ValueError(f"pv must be one of {list(PV)}, not {pv!r}")
+    if vq.dtype != (torch.uint8 if pv == "fp8" else torch.float16) or \
+            tuple(vq.shape) != (B, H, nblk, d, 128) or not vq.is_contiguous():
+        raise ValueError(f"vq must be quant_v's contiguous [{B}, {H}, {nblk}, {d}, 128] for pv={pv}")
+    if vs.dtype != torch.float32 or tuple(vs.shape) != (B, H, d) or not vs.is_contiguous():
+        raise ValueError(f"vs must be contiguous float32 [{B}, {H}, {d}]")
     out = torch.empty((B, H, N, d) if layout == "HND" else (B, N, H, d), dtype=out_dtype, device=dev)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     _check(lib().sage_attn_fwd_lse(_ptr(qz["q8"]), _ptr(qz["q_scale"]), _ptr(qz["k8"]),
@@ -315,7 +349,7 @@ def attn_bwd(qz: dict, v: torch.Tensor, o: torch.Tensor, do: torch.Tensor, lse: 
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise ValueError(f"lse must be contiguous float32 [{B}, {H}, {N}]")
     sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
-    dev = v.device
+    dev = _one_gpu(qz["q8"], qz["q_scale"], qz["k8"], qz["k_scale"], v, o, do, lse)
     dq, dk, dv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
     nbytes = bwd_sizes(B, H, N, d)
     ws = torch.empty(nbytes // 8 + 32, dtype=torch.int64, device=dev)
@@ -335,8 +369,8 @@ def quant_qk_mx(q: torch.Tensor, k: torch.Tensor, layout: str = "HND") -> dict:
     if q.shape != k.shape or not q.is_contiguous() or not k.is_contiguous():
         raise ValueError("q and k must be contiguous and of the same shape")
     B, H, N, d = _dims(q, layout)
+    dev = _one_gpu(q, k)
     sz = quant_sizes(B, H, N, d)
-    dev = q.device
     nblk = -(-N // 128)
     r = dict(q6=torch.empty((B, H, nblk * 128, d), dtype=torch.uint8, device=dev),
              k6=torch.empty((B, H, nblk * 128, d), dtype=torch.uint8, device=dev),
@@ -354,9 +388,10 @@ def quant_v_mx(v: torch.Tensor, layout: str = "HND") -> torch.Tensor:
     if v.dtype != torch.bfloat16 or not v.is_contiguous():
         raise TypeError("v must be a contiguous bfloat16 tensor")
     B, H, N, d = _dims(v, layout)
+    dev = _one_gpu(v)
     nblk = -(-N // 128)
-    v6 = torch.empty((B, H, nblk, d, 128), dtype=torch.uint8, device=v.device)
-    _check(lib().sage_quant_v_mx(_ptr(v), B, H, N, d, LAYOUTS[layout], _ptr(v6), _stream(v.device)))
+    v6 = torch.empty((B, H, nblk, d, 128), dtype=torch.uint8, device=dev)
+    _check(lib().sage_quant_v_mx(_ptr(v), B, H, N, d, LAYOUTS[layout], _ptr(v6), _stream(dev)))
     return v6
 
 
@@ -366,16 +401,15 @@ def attn_fwd_mx(mz: dict, v6: torch.Tensor, causal: bool = False, sm_scale: floa
     B, H, N, d, layout = mz["B"], mz["H"], mz["N"], mz["d"], mz["layout"]
     sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
     shape = (B, H, N, d) if layout == "HND" else (B, N, H, d)
-    dev = mz["q6"].device
+    dev = _one_gpu(mz["q6"], mz["k6"], v6, out)
     nblk = -(-N // 128)
     if v6.dtype != torch.uint8 or tuple(v6.shape) != (B, H, nblk, d, 128) or \
-            not v6.is_contiguous() or v6.device != dev:
+            not v6.is_contiguous():
         raise ValueError(f"v6 must be contiguous uint8 [{B}, {H}, {nblk}, {d}, 128] on {dev}")
     if out is None:
         out = torch.empty(shape, dtype=out_dtype, device=dev)
-    elif tuple(out.shape) != shape or out.dtype not in OUT or not out.is_contiguous() or \
-            out.device != dev:
-        raise ValueError(f"out must be contiguous {shape} (bfloat16 or float32) on {dev}")
+    else:
+        _check_out(out, shape, dev)
     _check(lib().sage_attn_fwd_mx(_ptr(mz["q6"]), _ptr(mz["k6"]), _ptr(v6), B, H, N, d,
                                   LAYOUTS[layout], int(bool(causal)), sm, _ptr(out),
                                   OUT[out.dtype], _stream(dev)))

@@ -223,6 +223,41 @@ def test_backward_arguments_rejected_before_launch(sage):
     assert lse(ls=A + 4) == -4
 
 
+def test_binding_refuses_host_tensors_and_wrong_operands(sage):
+    """The binding passes raw pointers: a host tensor, or an operand of the
+    wrong size, is refused before the library is called."""
+    import torch
+
+    B, H, N, d = 1, 2, 200, 128
+    x = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+    for call in (lambda: sage.quant_qk(x, x), lambda: sage.quant_v(x),
+                 lambda: sage.quant_qk_mx(x, x), lambda: sage.quant_v_mx(x)):
+        with pytest.raises(ValueError, match="one GPU"):
+            call()
+    nblk = -(-N // 128)
+    qz = dict(B=B, H=H, N=N, d=d, layout="HND", q_gran="block",
+              q8=torch.zeros((B, H, nblk * 128, d), dtype=torch.int8),
+              q_scale=torch.zeros((B, H, nblk)), k8=torch.zeros((B, H, nblk * 128, d), dtype=torch.int8),
+              k_scale=torch.zeros((B, H, nblk)))
+    vq = torch.zeros((B, H, nblk, d, 128), dtype=torch.uint8)
+    vs = torch.zeros((B, H, d))
+    lse = torch.zeros((B, H, N))
+    with pytest.raises(ValueError, match="one GPU"):
+        sage.attn_fwd(qz, vq, vs)
+    with pytest.raises(ValueError, match="one GPU"):
+        sage.attn_fwd_lse(qz, vq, vs)
+    with pytest.raises(ValueError, match="one GPU"):
+        sage.attn_bwd(qz, x, x, x, lse)
+    mz = dict(B=B, H=H, N=N, d=d, layout="HND", q6=torch.zeros((B, H, nblk * 128, d), dtype=torch.uint8),
+              k6=torch.zeros((B, H, nblk * 128, d), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="one GPU"):
+        sage.attn_fwd_mx(mz, vq)
+    # the operand sizes are checked after the device (on GPU tensors, in the
+    # GPU parity tests); the output check on its own:
+    with pytest.raises(ValueError):
+        sage._check_out(torch.zeros((B, H, N, d)), (B, H, N, 64), torch.device("cpu"))
+
+
 def test_status_strings(sage):
     L = sage.lib()
     names = [L.sage_status_string(c).decode() for c in range(0, -8, -1)]

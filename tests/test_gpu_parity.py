@@ -197,6 +197,34 @@ def test_attention_matches_oracle(sage, orc, name, kw, pv, layout):
             assert c_gpu >= COS_FP64, c_gpu
 
 
+def test_binding_refuses_operands_of_the_wrong_size(sage):
+    """Operands that would make a kernel read or write outside them are
+    refused before anything is launched."""
+    wl = si.make("tiny", N=300, H=2, device="cuda")
+    qz = sage.quant_qk(wl.q, wl.k)
+    vq, vs = sage.quant_v(wl.v, "fp8")
+    vq16, _ = sage.quant_v(wl.v, "fp16")
+    with pytest.raises(ValueError, match="vq"):
+        sage.attn_fwd(qz, vq[:, :, :-1].contiguous(), vs)
+    with pytest.raises(ValueError, match="vq"):
+        sage.attn_fwd(qz, vq16, vs, pv="fp8")
+    with pytest.raises(ValueError, match="vs"):
+        sage.attn_fwd(qz, vq, vs.double())
+    with pytest.raises(ValueError, match="out"):
+        sage.attn_fwd(qz, vq, vs, out=torch.empty((1, 2, 299, 128), dtype=torch.bfloat16,
+                                                  device="cuda"))
+    with pytest.raises(ValueError, match="one GPU"):
+        sage.attn_fwd(qz, vq, vs.cpu())
+    with pytest.raises(ValueError, match="vq"):
+        sage.attn_fwd_lse(qz, vq16, vs)
+    o, lse = sage.attn_fwd_lse(qz, vq, vs)
+    with pytest.raises(ValueError, match="lse"):
+        sage.attn_bwd(qz, wl.v, o, o, lse[:, :, :-1].contiguous())
+    with pytest.raises(ValueError, match="one GPU"):
+        sage.attn_bwd(qz, wl.v, o, o.cpu(), lse)
+    torch.cuda.synchronize()
+
+
 def test_bf16_output_is_rounded_fp32_output(sage, orc):
     wl = si.make("tiny", N=400, H=2)
     *_, o32 = run_gpu(sage, wl, "fp8", out_dtype=torch.float32)
