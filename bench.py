@@ -51,10 +51,16 @@ def attn_source_hash(bwd=False):
     """sha256 of the measured kernels' sources (the attention kernel, or the
     backward's kernels and the workspace carving): HBM byte counts measured
     on another version of the code are not reported."""
+    from quantized_attention_video_02_amd import build as sage_build
+
     h = hashlib.sha256()
     for f in (BWD_SOURCES if bwd else ATTN_SOURCES):
         with open(f, "rb") as fh:
             h.update(fh.read())
+        # a source compiled with extra flags is a different kernel
+        extra = sage_build.SOURCE_FLAGS.get(os.path.basename(f))
+        if extra:
+            h.update(" ".join(extra).encode())
     return h.hexdigest()[:16]
 
 
