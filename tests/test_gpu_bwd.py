@@ -129,3 +129,49 @@ def test_bwd_full_size_sampled(sage, orc):
     err, c = np.abs(g - ref).max() / np.abs(ref).max(), _cos(g, ref)
     print(f"  dq sampled blocks: max-abs/max {err:.2e} cos(oracle) {c:.7f}")
     assert err <= 2e-2 and c >= 0.9999, (err, c)
+
+
+def _run_bwd(sage, wl, do, causal):
+    qd, kd, vd, dod = (t.contiguous().cuda() for t in (wl.q, wl.k, wl.v, do))
+    qz = sage.quant_qk(qd, kd)
+    vq, vs = sage.quant_v(vd, "fp8")
+    out, lse = sage.attn_fwd_lse(qz, vq, vs, causal=causal, sm_scale=wl.sm_scale)
+    g = sage.attn_bwd(qz, vd, out, dod, lse, causal=causal, sm_scale=wl.sm_scale)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in g]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_zero_output_gradient(sage, causal):
+    """dO = 0: D = 0 and dP = 0, so dS = 0 on every tile (its INT8 scale is 0
+    and so are its codes) and every dO FP8 code is 0: dq, dk and dv are
+    exactly zero, with the ragged last tile and the causal diagonal masked."""
+    print(f"[bwd degenerate] dO = 0, causal={causal}", flush=True)
+    wl = si.make("tiny", N=300, H=2)
+    for name, x in zip(("dq", "dk", "dv"), _run_bwd(sage, wl, torch.zeros_like(si.output_grad(wl)), causal)):
+        assert not x.any(), name
+
+
+def test_bwd_single_key(sage, orc):
+    """N = 1: the one probability is 1, so dv is dO through its FP8 block code
+    (within e4m3's half-step: 1/16 relative, or half the subnormal step
+    max|dO| / 448 / 2^10 below the normal range).  Smoothing subtracts the
+    one key from itself, so the K codes and dq are exactly 0.  V's per-channel
+    scale is its own magnitude, so the FP8 path reproduces V and O = V: the
+    one score's gradient dS = dO . f16(V) - dO . O is 0 up to the two sums'
+    fp32 rounding (exactly 0 in the oracle, whose sums run in one order), and
+    so is dk."""
+    print("[bwd degenerate] N = 1", flush=True)
+    wl = si.make("tiny", N=1, H=1)
+    do = si.output_grad(wl)
+    dq, dk, dv = _run_bwd(sage, wl, do, False)
+    q, k, v, dO = codes(wl.q), codes(wl.k), codes(wl.v), codes(do)
+    oz = orc.quant_qk(q, k)
+    ovq, ovs = orc.quant_v(v, "fp8")
+    o_or, lse_or = orc.train_forward_head(oz, ovq, ovs, 0, 0, np.arange(1), False, wl.sm_scale)
+    dq_o, dk_o, dv_o = orc.bwd_head(oz, v[0, 0], o_or, dO[0, 0], lse_or, 0, 0, False, wl.sm_scale)
+    assert not oz["k8"].any() and not dq_o[0].any() and not dq.any()
+    assert not dk_o[0].any() and np.abs(dk).max() <= 1e-3
+    assert np.allclose(dv[0, 0], dv_o[0], rtol=1e-6, atol=1e-7)
+    dof = orc.bf16_to_f32(dO[0, 0]).astype(np.float64)
+    assert np.all(np.abs(dv[0, 0] - dof) <= np.abs(dof) / 16 + 2.2e-6 * np.abs(dof).max())
