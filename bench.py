@@ -204,13 +204,27 @@ def cpu_baseline_bwd(wl, target_rows=128):
                        f"oracle")}
 
 
-def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False, mx=False):
+def host_cores():
+    """Threads for the all-core oracle run: the CPUs this process may use,
+    at most 16 (a one-GPU machine's share of its host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False, mx=False, cores=None,
+                 all_core_s=None):
     """The oracle as it stands (single-threaded C) on one head of the workload:
     quantization of the whole head, then attention for R query rows against
     all N keys; the head's quantization time is charged pro rata (R / N).
     With Q smoothing the correction rows of the blocks the R rows use are
     computed too (charged to the quantization at the rate per block).  With
-    mx the oracle's MXFP6 quantization and attention."""
+    mx the oracle's MXFP6 quantization and attention.
+
+    Then the all-core run: `cores` threads (default host_cores()) each run the
+    same single-threaded oracle on disjoint query rows of the head, wall-clocked
+    (the C calls release the interpreter lock); the quantization is charged
+    pro rata over the threads.  `value` is that run's rate, `cores` its thread
+    count, `single_core_value` the one-thread rate."""
+    from concurrent.futures import ThreadPoolExecutor
     import numpy as np
 
     import oracle
@@ -260,13 +274,42 @@ def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False, mx=False
     t_equiv = t_attn + t_quant * R / wl.N
     if q_smooth:
         t_equiv += t_bias * R / (len(used) * 128)
-    return {"value": ops / t_equiv / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "sample": (f"head (b=0,h=0) of {wl.name}: quantization of all {wl.N} tokens "
-                       f"({t_quant:.2f} s, charged pro rata) + attention for {R} queries x "
-                       f"{'their causal keys' if wl.causal else f'{wl.N} keys'} ({t_attn:.2f} s)"
-                       + (f"; Q-smoothing correction of their blocks ({t_bias:.2f} s, pro rata)"
-                          if q_smooth else "") + ("; MXFP6 path" if mx else "")
-                       + "; single-threaded C oracle")}
+    single = ops / t_equiv / 1e12
+    sample = (f"head (b=0,h=0) of {wl.name}: quantization of all {wl.N} tokens "
+              f"({t_quant:.2f} s, charged pro rata) + attention for {R} queries x "
+              f"{'their causal keys' if wl.causal else f'{wl.N} keys'} ({t_attn:.2f} s)"
+              + (f"; Q-smoothing correction of their blocks ({t_bias:.2f} s, pro rata)"
+                 if q_smooth else "") + ("; MXFP6 path" if mx else "") + "; C oracle")
+    P = host_cores() if cores is None else int(cores)
+    if P <= 1:
+        return {"value": single, "unit": "TOPS", "cores": 1, "kind": "oracle",
+                "single_core_value": single, "sample": sample + ", one thread"}
+    # all-core run: P threads, Rt rows each (disjoint; causal: the longest rows)
+    per_row = t_attn / R
+    budget = 0.6 * target_s if all_core_s is None else all_core_s
+    Rt = int(max(1, min(wl.N // P, budget / max(per_row, 1e-9))))
+    if wl.causal:
+        slices = [np.arange(wl.N - (i + 1) * Rt, wl.N - i * Rt, dtype=np.int32) for i in range(P)]
+    else:
+        slices = [np.arange(i * Rt, (i + 1) * Rt, dtype=np.int32) for i in range(P)]
+    t_bias_all = 0.0
+    if q_smooth:
+        used_all = sorted(set(np.concatenate(slices) // 128))
+        t0 = time.perf_counter()
+        bias = oracle.smooth_bias(oz, k, wl.sm_scale, blocks=used_all)
+        t_bias_all = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=P) as ex:
+        list(ex.map(lambda r: attn_rows(r, bias), slices))
+    wall = time.perf_counter() - t0
+    rows_all = P * Rt
+    keys_all = sum(int((r + 1).sum()) for r in slices) if wl.causal else rows_all * wl.N
+    t_all = wall + (t_quant * rows_all / wl.N + t_bias_all) / P
+    return {"value": 4.0 * keys_all * wl.d / t_all / 1e12, "unit": "TOPS", "cores": P,
+            "kind": "oracle", "single_core_value": single,
+            "sample": (f"{sample}; then {P} threads, each the single-threaded oracle on "
+                       f"{Rt} disjoint query rows of the same head ({wall:.2f} s wall), the "
+                       f"quantization charged pro rata over the threads")}
 
 
 def traffic_key(workload, pv, q_gran="block"):

@@ -95,12 +95,26 @@ def test_record_traffic_of_the_backward_sums_its_kernels_per_call(tmp_path, monk
                              bwd=True)
 
 
+@pytest.mark.parametrize("causal_name", ["tiny", "causal_prefill"])
+def test_cpu_baseline_all_core_run(causal_name):
+    """The all-core run: the same oracle on disjoint rows in threads; one
+    thread reports the single-thread rate itself."""
+    import synthetic_inputs as si
+
+    wl = si.make(causal_name, B=1, H=1, N=600)
+    one = bench.cpu_baseline(wl, "fp8", target_s=0.2, cores=1)
+    assert one["cores"] == 1 and one["value"] == one["single_core_value"] > 0
+    two = bench.cpu_baseline(wl, "fp8", target_s=0.2, cores=2, all_core_s=0.2)
+    assert two["cores"] == 2 and two["value"] > 0 and two["single_core_value"] > 0
+    assert "2 threads" in two["sample"]
+
+
 def test_cpu_baseline_of_the_mx_path():
     import synthetic_inputs as si
 
     wl = si.make("tiny", N=300, H=1)
     r = bench.cpu_baseline(wl, "fp8", target_s=0.2, mx=True)
-    assert r["value"] > 0 and r["kind"] == "oracle" and r["cores"] == 1
+    assert r["value"] > 0 and r["kind"] == "oracle" and r["cores"] == bench.host_cores()
     assert "MXFP6" in r["sample"]
 
 
@@ -178,7 +192,8 @@ def test_bench_line_keeps_the_contract():
     rf = line["roofline"]
     assert rf["bound"] == "mfma" and rf["peak"] == 5000.0 and rf["unit"] == "TFLOP/s"
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
-    assert line["cpu_baseline"]["kind"] == "oracle" and line["cpu_baseline"]["cores"] == 1
+    cb = line["cpu_baseline"]
+    assert cb["kind"] == "oracle" and 1 <= cb["cores"] <= 16 and cb["single_core_value"] > 0
     assert line["config"]["workload"] == "tiny"
 
 
