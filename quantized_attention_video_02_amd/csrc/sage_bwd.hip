@@ -22,7 +22,7 @@
 // forward's V order for FP8, a 32-element order for INT8), written once by
 // the preparation kernels.  The tile's dS absmax is reduced over the
 // workgroup's 4 waves through LDS.  Four waves per workgroup, one workgroup
-// per CU: the sweeps hold about 300-450 registers per lane.
+// per CU: the sweeps hold about 400-500 registers per lane.
 #include <limits.h>
 
 #include "sage_common.h"
