@@ -467,6 +467,11 @@ def main():
                          "ops_per_launch": ops, "mean_launch_ms": mean,
                          "median_launch_ms": srt[len(srt) // 2]},
         }
+        if wl.causal:
+            # the formula counts every (query, key) pair; the causal mask keeps N(N+1)/2
+            useful = 10.0 * wl.B * wl.H * wl.d * wl.N * (wl.N + 1) / 2
+            res["roofline"]["useful_causal_ops_per_launch"] = useful
+            res["roofline"]["useful_causal_tops"] = useful / (mean * 1e-3) / 1e12
         if not args.no_cpu_baseline:
             print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
             res["cpu_baseline"] = cpu_baseline_bwd(wl)
