@@ -63,7 +63,7 @@ enum sage_status {
     SAGE_OK = 0,
     SAGE_ERR_NULL = -1,        /* a required pointer is NULL */
     SAGE_ERR_INVALID = -2,     /* bad size, enum, flag, sm_scale or dump window */
-    SAGE_ERR_UNSUPPORTED = -3, /* d not in {64, 128} (the backward: d != 128) */
+    SAGE_ERR_UNSUPPORTED = -3, /* d not in {64, 128} */
     SAGE_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
     SAGE_ERR_SIZE = -5,        /* the problem exceeds the supported size */
     SAGE_ERR_HIP = -6,         /* a HIP launch failed */
@@ -243,8 +243,7 @@ int sage_attn_fwd_lse(const int8_t* q8, const float* q_scale, const int8_t* k8,
  * part rounded up to 256 bytes: D [B*H][N_pad] f32, s_do [B*H][nblk] f32, dO
  * and V in fp16 [B*H][N_pad][d] (two parts), dO in FP8 and the Q and K codes
  * transposed [B*H][nblk][d][128] bytes (three parts), and the per-tile
- * records of the dK/dV sweep [B*H][nblk][512] f32.
- * d = 128 only in this build (SAGE_ERR_UNSUPPORTED otherwise).
+ * records of the dK/dV sweep [B*H][nblk][512] f32.  d in {64, 128}.
  */
 int sage_bwd_sizes(int B, int H, int N, int d, size_t* workspace_bytes);
 int sage_attn_bwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,

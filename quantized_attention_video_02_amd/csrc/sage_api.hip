@@ -308,7 +308,6 @@ __attribute__((visibility("default"))) int sage_bwd_sizes(int B, int H, int N, i
                                                           size_t* workspace_bytes) {
     if (!workspace_bytes) return SAGE_ERR_NULL;
     SAGE_TRY(check_dims(B, H, N, d));
-    if (d != 128) return SAGE_ERR_UNSUPPORTED;
     *workspace_bytes = bwd_parts(B, H, N, d, nullptr);
     return SAGE_OK;
 }
@@ -322,7 +321,6 @@ __attribute__((visibility("default"))) int sage_attn_bwd(
         !workspace)
         return SAGE_ERR_NULL;
     SAGE_TRY(check_dims(B, H, N, d));
-    if (d != 128) return SAGE_ERR_UNSUPPORTED;
     SAGE_TRY(check_layout(layout));
     if (causal != 0 && causal != 1) return SAGE_ERR_INVALID;
     if (!(isfinite(sm_scale) && sm_scale > 0.0f)) return SAGE_ERR_INVALID;

@@ -31,8 +31,16 @@
 namespace sage {
 
 constexpr int kBwdThreads = 256;  // 4 waves: 128 rows per workgroup, 32 per wave
-constexpr int kKstr = 128 + 16;   // LDS stride of a 128-byte row (INT8 / FP8 tiles), 16-byte pad
-constexpr int kHstr = 256 + 16;   // LDS stride of a 128-channel fp16 row
+// LDS row strides, each with a 16-byte pad (16 consecutive rows then start in
+// distinct 16-byte bank groups: the strides are odd multiples of 16 bytes):
+// the transposed tiles have rows of 128 elements (queries or keys, 1 byte);
+// the row tiles have rows of D channels (INT8 codes, 1 byte, or fp16).
+constexpr int kKstr = 128 + 16;
+template <int D>
+struct BwdRow {
+    static constexpr int I8 = D + 16;       // a row of D INT8 codes
+    static constexpr int F16 = 2 * D + 16;  // a row of D fp16 values
+};
 
 // Order of a run of 128 elements along a reduction (element e = 32 kb + 8 b +
 // 4 g + q, kb and b in 0..3, g in 0..1, q in 0..3):
@@ -224,11 +232,12 @@ __device__ inline void store_f32_row(float* out, int64_t off, const v16f* X, int
 // ---------------------------------------------------------------- dQ sweep
 // Workgroup = one query block of 128 (wave w: queries 32 w .. 32 w + 31), key
 // tiles swept in ascending order, double-buffered in LDS: K codes [128 keys]
-// [kKstr], V fp16 [128 keys][kHstr], K codes transposed [D channels][kKstr].
+// [BwdRow::I8], V fp16 [128 keys][BwdRow::F16], K codes transposed [D channels][kKstr].
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     constexpr int NW = 4, KK = D / 32, CB = D / 32, HK = D / 16;
-    constexpr int K8B = kBc * kKstr, V16B = kBc * kHstr, KTB = D * kKstr;
+    constexpr int R8 = BwdRow<D>::I8, R16 = BwdRow<D>::F16;
+    constexpr int K8B = kBc * R8, V16B = kBc * R16, KTB = D * kKstr;
     constexpr int SLOT = K8B + V16B + KTB;
     constexpr int KP = K8B / 1024, VP = V16B / 1024, TP = KTB / 1024;
     constexpr int KMAXP = (KP + NW - 1) / NW, VMAXP = (VP + NW - 1) / NW, TMAXP = (TP + NW - 1) / NW;
@@ -264,9 +273,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
     int koff[KMAXP], voff[VMAXP], toff[TMAXP];
 #pragma unroll
-    for (int j = 0; j < KMAXP; ++j) koff[j] = slot_src<D, kKstr>(64 * (wave + NW * j) + lane);
+    for (int j = 0; j < KMAXP; ++j) koff[j] = slot_src<D, R8>(64 * (wave + NW * j) + lane);
 #pragma unroll
-    for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<2 * D, kHstr>(64 * (wave + NW * j) + lane);
+    for (int j = 0; j < VMAXP; ++j) voff[j] = slot_src<2 * D, R16>(64 * (wave + NW * j) + lane);
 #pragma unroll
     for (int j = 0; j < TMAXP; ++j) toff[j] = slot_src<kBc, kKstr>(64 * (wave + NW * j) + lane);
     const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
@@ -312,7 +321,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
             v4i ka[4][KK];
 #pragma unroll
             for (int k4 = 0; k4 < 4; ++k4) {
-                const uint8_t* krow = kbuf + (32 * k4 + n) * kKstr + 16 * hh;
+                const uint8_t* krow = kbuf + (32 * k4 + n) * R8 + 16 * hh;
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) ka[k4][kk] = *(const v4i*)(krow + 32 * kk);
             }
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
             v8h va[4][HK / 2];
 #pragma unroll
             for (int k4 = 0; k4 < 4; ++k4) {
-                const uint8_t* vrow = vbuf + (32 * k4 + n) * kHstr + 16 * hh + 32 * (HK / 2) * half;
+                const uint8_t* vrow = vbuf + (32 * k4 + n) * R16 + 16 * hh + 32 * (HK / 2) * half;
 #pragma unroll
                 for (int kk = 0; kk < HK / 2; ++kk) va[k4][kk] = *(const v8h*)(vrow + 32 * kk);
             }
@@ -420,9 +429,18 @@ __device__ inline void wait_vm() {
 // Copy pieces wave w issues for a tile of P pieces (piece J = w + 4 j).
 constexpr int pieces_of(int P, int w) { return P > w ? (P - w + 3) / 4 : 0; }
 
+// wait_vm with this wave's own count (w uniform)
+template <int N0, int N1, int N2, int N3>
+__device__ inline void wait_vm_wave(int w) {
+    if (w == 0) wait_vm<N0>();
+    else if (w == 1) wait_vm<N1>();
+    else if (w == 2) wait_vm<N2>();
+    else wait_vm<N3>();
+}
+
 // Workgroup = one key block of 128 (wave w: keys 32 w .. 32 w + 31), query
 // tiles swept in ascending order.  LDS: slot A, double-buffered: Q codes
-// [128 queries][kKstr], dO fp16 [128][kHstr] and the tile's record (lse, D,
+// [128 queries][BwdRow::I8], dO fp16 [128][BwdRow::F16] and the tile's record (lse, D,
 // q_scale, s_do); slot B, single: dO FP8 transposed [D][kKstr] and Q codes
 // transposed [D][kKstr].  A(t + 1) is copied while tile t computes; B(t + 1)
 // after tile t's dV / dK, awaited only before tile t + 1's dV / dK.  Every
@@ -430,7 +448,8 @@ constexpr int pieces_of(int P, int w) { return P > w ? (P - w + 3) / 4 : 0; }
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int NW = 4, KK = D / 32, CB = D / 32, HK = D / 16;
-    constexpr int Q8B = kBlk * kKstr, DO16B = kBlk * kHstr, RECB = kRecFloats * 4;
+    constexpr int R8 = BwdRow<D>::I8, R16 = BwdRow<D>::F16;
+    constexpr int Q8B = kBlk * R8, DO16B = kBlk * R16, RECB = kRecFloats * 4;
     constexpr int SLOTA = Q8B + DO16B + RECB;
     constexpr int DO8B = D * kKstr, QTB = D * kKstr;
     constexpr int QP = Q8B / 1024, HP = DO16B / 1024, LP = RECB / 1024, FP = DO8B / 1024, TP = QTB / 1024;
@@ -438,15 +457,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                   FMAXP = (FP + NW - 1) / NW, TMAXP = (TP + NW - 1) / NW;
     static_assert(Q8B % 1024 == 0 && DO16B % 1024 == 0 && RECB % 1024 == 0 && DO8B % 1024 == 0,
                   "1 KB copy pieces");
-    // loads per wave of the A and B copies (waves 0, 1 and 2, 3 issue alike)
-    constexpr int NA01 = pieces_of(QP, 0) + pieces_of(HP, 0) + pieces_of(LP, 0);
-    constexpr int NA23 = pieces_of(QP, 2) + pieces_of(HP, 2) + pieces_of(LP, 2);
-    constexpr int NB01 = pieces_of(FP, 0) + pieces_of(TP, 0);
-    constexpr int NB23 = pieces_of(FP, 2) + pieces_of(TP, 2);
-    static_assert(NA01 == pieces_of(QP, 1) + pieces_of(HP, 1) + pieces_of(LP, 1) &&
-                  NA23 == pieces_of(QP, 3) + pieces_of(HP, 3) + pieces_of(LP, 3) &&
-                  NB01 == pieces_of(FP, 1) + pieces_of(TP, 1) &&
-                  NB23 == pieces_of(FP, 3) + pieces_of(TP, 3), "wave pairs issue alike");
+    // loads per wave w of the A and B copies
+    constexpr int NA0 = pieces_of(QP, 0) + pieces_of(HP, 0) + pieces_of(LP, 0);
+    constexpr int NA1 = pieces_of(QP, 1) + pieces_of(HP, 1) + pieces_of(LP, 1);
+    constexpr int NA2 = pieces_of(QP, 2) + pieces_of(HP, 2) + pieces_of(LP, 2);
+    constexpr int NA3 = pieces_of(QP, 3) + pieces_of(HP, 3) + pieces_of(LP, 3);
+    constexpr int NB0 = pieces_of(FP, 0) + pieces_of(TP, 0), NB1 = pieces_of(FP, 1) + pieces_of(TP, 1);
+    constexpr int NB2 = pieces_of(FP, 2) + pieces_of(TP, 2), NB3 = pieces_of(FP, 3) + pieces_of(TP, 3);
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOTA + DO8B + QTB];
     __shared__ float red[NW];
 
@@ -474,9 +491,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
     int qoff[QMAXP], hoff[HMAXP], loff[LMAXP], foff[FMAXP], toff[TMAXP];
 #pragma unroll
-    for (int j = 0; j < QMAXP; ++j) qoff[j] = slot_src<D, kKstr>(64 * (wave + NW * j) + lane);
+    for (int j = 0; j < QMAXP; ++j) qoff[j] = slot_src<D, R8>(64 * (wave + NW * j) + lane);
 #pragma unroll
-    for (int j = 0; j < HMAXP; ++j) hoff[j] = slot_src<2 * D, kHstr>(64 * (wave + NW * j) + lane);
+    for (int j = 0; j < HMAXP; ++j) hoff[j] = slot_src<2 * D, R16>(64 * (wave + NW * j) + lane);
 #pragma unroll
     for (int j = 0; j < LMAXP; ++j) loff[j] = 16 * (64 * (wave + NW * j) + lane);
 #pragma unroll
@@ -510,8 +527,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     copy_b(t0);
     for (int qt = t0; qt < a.nblk; ++qt) {
         // A(qt) complete (only B(qt) may still be in flight), for every wave
-        if (wv < 2) wait_vm<NB01>();
-        else wait_vm<NB23>();
+        wait_vm_wave<NB0, NB1, NB2, NB3>(wv);
         __syncthreads();
         const bool more = qt + 1 < a.nblk;
         if (more) copy_a(qt + 1);
@@ -529,7 +545,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             v4i qa[4][KK];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const uint8_t* qrow = qbuf + (32 * q4 + n) * kKstr + 16 * hh;
+                const uint8_t* qrow = qbuf + (32 * q4 + n) * R8 + 16 * hh;
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) qa[q4][kk] = *(const v4i*)(qrow + 32 * kk);
             }
@@ -551,7 +567,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 v8h ha[4][HK / 2];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const uint8_t* hrow = hbuf + (32 * q4 + n) * kHstr + 16 * hh + 32 * (HK / 2) * half;
+                    const uint8_t* hrow = hbuf + (32 * q4 + n) * R16 + 16 * hh + 32 * (HK / 2) * half;
 #pragma unroll
                     for (int kk = 0; kk < HK / 2; ++kk) ha[q4][kk] = *(const v8h*)(hrow + 32 * kk);
                 }
@@ -596,8 +612,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // B(qt) complete for this wave (A(qt + 1), issued after it, may still
         // be in flight); the barrier in tile_scale makes it so for all waves
         if (more) {
-            if (wv < 2) wait_vm<NA01>();
-            else wait_vm<NA23>();
+            wait_vm_wave<NA0, NA1, NA2, NA3>(wv);
         } else {
             wait_vmem();
         }
@@ -646,9 +661,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     store_f32_row<D>(a.dv, off, dv, hh);
 }
 
-hipError_t launch_attn_bwd(const BwdPrep& pp, const BwdArgs& args, int B, int d, int causal,
-                           hipStream_t s) {
-    if (d != 128) return hipErrorInvalidValue;
+template <int D>
+static hipError_t launch_attn_bwd_d(const BwdPrep& pp, const BwdArgs& args, int B, int causal,
+                                    hipStream_t s) {
     const int BH = B * args.H;
     hipError_t e;
     {
@@ -656,29 +671,36 @@ hipError_t launch_attn_bwd(const BwdPrep& pp, const BwdArgs& args, int B, int d,
                          (void*)&args.nblk, (void*)&args.layout, (void*)&args.lse, (void*)&args.q_scale,
                          (void*)&args.Dq, (void*)&args.do16, (void*)&args.v16, (void*)&args.do8,
                          (void*)&args.s_do, (void*)&args.rec};
-        if ((e = hipLaunchKernel((const void*)bwd_prep_kernel<128>, dim3(args.nblk, BH),
+        if ((e = hipLaunchKernel((const void*)bwd_prep_kernel<D>, dim3(args.nblk, BH),
                                  dim3(kBwdThreads), kargs, 0, s)) != hipSuccess)
             return e;
     }
     {
         void* kargs[] = {(void*)&args.q8, (void*)&args.nblk, (void*)&args.qT8};
-        if ((e = hipLaunchKernel((const void*)bwd_t8_kernel<128>, dim3(args.nblk, BH),
+        if ((e = hipLaunchKernel((const void*)bwd_t8_kernel<D>, dim3(args.nblk, BH),
                                  dim3(kBwdThreads), kargs, 0, s)) != hipSuccess)
             return e;
     }
     {
         void* kargs[] = {(void*)&args.k8, (void*)&args.nblk, (void*)&args.kT8};
-        if ((e = hipLaunchKernel((const void*)bwd_t8_kernel<128>, dim3(args.nblk, BH),
+        if ((e = hipLaunchKernel((const void*)bwd_t8_kernel<D>, dim3(args.nblk, BH),
                                  dim3(kBwdThreads), kargs, 0, s)) != hipSuccess)
             return e;
     }
     BwdArgs a = args;
     a.total = BH * a.nblk;
     void* kargs[] = {(void*)&a};
-    const void* fq = causal ? (const void*)bwd_dq_kernel<128, true> : (const void*)bwd_dq_kernel<128, false>;
+    const void* fq = causal ? (const void*)bwd_dq_kernel<D, true> : (const void*)bwd_dq_kernel<D, false>;
     if ((e = hipLaunchKernel(fq, dim3(a.total), dim3(kBwdThreads), kargs, 0, s)) != hipSuccess) return e;
-    const void* fk = causal ? (const void*)bwd_dkdv_kernel<128, true> : (const void*)bwd_dkdv_kernel<128, false>;
+    const void* fk = causal ? (const void*)bwd_dkdv_kernel<D, true> : (const void*)bwd_dkdv_kernel<D, false>;
     return hipLaunchKernel(fk, dim3(a.total), dim3(kBwdThreads), kargs, 0, s);
+}
+
+hipError_t launch_attn_bwd(const BwdPrep& pp, const BwdArgs& args, int B, int d, int causal,
+                           hipStream_t s) {
+    if (d == 128) return launch_attn_bwd_d<128>(pp, args, B, causal, s);
+    if (d == 64) return launch_attn_bwd_d<64>(pp, args, B, causal, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace sage

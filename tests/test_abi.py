@@ -186,8 +186,8 @@ def test_backward_arguments_rejected_before_launch(sage):
     ws = ct.c_size_t()
     assert L.sage_bwd_sizes(1, 1, 256, 128, None) == -1
     assert L.sage_bwd_sizes(1, 1, 0, 128, ct.byref(ws)) == -2
-    assert L.sage_bwd_sizes(1, 1, 256, 64, ct.byref(ws)) == -3
     assert L.sage_bwd_sizes(1, 1, 256, 96, ct.byref(ws)) == -3
+    assert L.sage_bwd_sizes(1, 1, 256, 64, ct.byref(ws)) == 0
     assert L.sage_bwd_sizes(70000, 1, 256, 128, ct.byref(ws)) == -5
     # the documented parts, each rounded up to 256 bytes
     B, H, N, d = 2, 3, 300, 128
@@ -205,7 +205,7 @@ def test_backward_arguments_rejected_before_launch(sage):
     assert bwd(dq=None) == -1
     assert bwd(wsp=None) == -1
     assert bwd(N=0) == -2
-    assert bwd(d=64) == -3
+    assert bwd(d=96) == -3
     assert bwd(lay=2) == -2
     assert bwd(causal=2) == -2
     for sm in (float("nan"), float("inf"), 0.0, -1.0):

@@ -40,6 +40,8 @@ BWD_CASES = [
     ("causal_prefill", dict(B=2, H=1, N=260), "HND", True),
     ("tiny", dict(N=1000, H=1), "HND", False),
     ("tiny", dict(N=17, H=1), "HND", False),
+    ("outlier", dict(B=1, H=2, N=300), "HND", False),     # d = 64, outlier keys and queries
+    ("outlier", dict(B=1, H=1, N=270), "NHD", True),
 ]
 
 
