@@ -1,6 +1,6 @@
 /*
- * sage.h -- C ABI of libsage: SageAttention-style low-bit attention forward on
- * AMD Instinct MI355X (gfx950).
+ * sage.h -- C ABI of libsage: SageAttention-style low-bit attention (the
+ * forward and the 8-bit backward) on AMD Instinct MI355X (gfx950).
  *
  *   O = softmax(Q K^T * sm_scale) V, computed as
  *     1. smooth K by subtracting its per-head token mean,
@@ -29,8 +29,8 @@
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer allocated by the caller
- *     (e.g. by PyTorch), except `out` of sage_get_config / sage_quant_sizes
- *     (host).  libsage never allocates, frees, synchronises, or changes the
+ *     (e.g. by PyTorch), except the outputs of sage_get_config and of the
+ *     *_sizes calls (host memory).  libsage never allocates, frees, synchronises, or changes the
  *     current device.  All work is enqueued asynchronously on `stream`
  *     (a hipStream_t; NULL means the null stream) on the current device.
  *   - Device buffers must be 16-byte aligned.
