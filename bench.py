@@ -170,10 +170,15 @@ def si_grad(wl):
     return si.output_grad(wl)
 
 
-def cpu_baseline_bwd(wl, target_rows=128):
-    """The oracle on query block 0 of head (0, 0): its forward rows (output
-    and log-sum-exp) and its dQ over all N keys; ops counted 4 d per pair for
-    the forward rows and 6 d per pair (S, dP, dQ) for the dQ sweep."""
+def cpu_baseline_bwd(wl, cores=None):
+    """The oracle on head (0, 0): for a query block, its forward rows (output
+    and log-sum-exp) and its dQ over all N keys; ops counted 10 d per pair
+    (the forward rows' 4 d and the dQ sweep's 6 d: S, dP, dQ).  First block 0
+    on one thread (`single_core_value`), then `cores` threads (default
+    host_cores()) on blocks 0 .. cores - 1 at once, wall-clocked; the head's
+    quantization is charged pro rata."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
@@ -181,27 +186,47 @@ def cpu_baseline_bwd(wl, target_rows=128):
 
     q, k, v = (si.bf16_codes(t[0:1, 0:1]) for t in (wl.q, wl.k, wl.v))
     dO = si.bf16_codes(si.output_grad(wl)[0:1, 0:1])
-    rows = np.arange(min(target_rows, wl.N), dtype=np.int32)
     t0 = time.perf_counter()
     oz = oracle.quant_qk(q, k)
     ovq, ovs = oracle.quant_v(v, "fp8")
     t_quant = time.perf_counter() - t0
+    nblk = -(-wl.N // 128)
+
+    def block(qb):
+        rows = np.arange(128 * qb, min(wl.N, 128 * qb + 128), dtype=np.int32)
+        o_rows, lse_rows = oracle.train_forward_head(oz, ovq, ovs, 0, 0, rows, wl.causal, wl.sm_scale)
+        o = np.zeros((wl.N, wl.d), np.uint16)
+        o[rows] = o_rows
+        lse = np.zeros(wl.N, np.float32)
+        lse[rows] = lse_rows
+        oracle.bwd_head(oz, v[0, 0], o, dO[0, 0], lse, 0, 0, wl.causal, wl.sm_scale,
+                        qblocks=[qb], kblocks=[])
+        keys = (rows + 1).sum() if wl.causal else len(rows) * wl.N
+        return 10.0 * float(keys) * wl.d, len(rows)
+
     t0 = time.perf_counter()
-    o_rows, lse_rows = oracle.train_forward_head(oz, ovq, ovs, 0, 0, rows, wl.causal, wl.sm_scale)
-    o = np.zeros((wl.N, wl.d), np.uint16)
-    o[rows] = o_rows
-    lse = np.zeros(wl.N, np.float32)
-    lse[rows] = lse_rows
-    oracle.bwd_head(oz, v[0, 0], o, dO[0, 0], lse, 0, 0, wl.causal, wl.sm_scale, qblocks=[0], kblocks=[])
-    t = time.perf_counter() - t0 + t_quant * len(rows) / wl.N
-    keys = (rows + 1).sum() if wl.causal else len(rows) * wl.N
-    ops = 10.0 * float(keys) * wl.d
-    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "sample": (f"head (b=0,h=0) of {wl.name}: the forward rows of query block 0 "
-                       f"({len(rows)} queries, output and log-sum-exp) and their dQ over "
-                       f"{'their causal keys' if wl.causal else f'all {wl.N} keys'} "
-                       f"({t:.2f} s incl. the head's quantization pro rata); single-threaded C "
-                       f"oracle")}
+    ops, nrows = block(0)
+    t1 = time.perf_counter() - t0 + t_quant * nrows / wl.N
+    single = ops / t1 / 1e12
+    P = min(host_cores() if cores is None else int(cores), nblk)
+    sample = (f"head (b=0,h=0) of {wl.name}: for a block of 128 queries, the forward rows (output "
+              f"and log-sum-exp) and their dQ over "
+              f"{'their causal keys' if wl.causal else f'all {wl.N} keys'}; block 0 on one thread "
+              f"({t1:.2f} s incl. the head's quantization pro rata)")
+    if P <= 1:
+        return {"value": single, "unit": "TOPS", "cores": 1, "kind": "oracle",
+                "single_core_value": single, "sample": sample + "; C oracle"}
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=P) as ex:
+        done = list(ex.map(block, range(P)))
+    wall = time.perf_counter() - t0
+    ops_all = sum(x[0] for x in done)
+    rows_all = sum(x[1] for x in done)
+    t_all = wall + t_quant * rows_all / wl.N / P
+    return {"value": ops_all / t_all / 1e12, "unit": "TOPS", "cores": P, "kind": "oracle",
+            "single_core_value": single,
+            "sample": (f"{sample}; then {P} threads on blocks 0-{P - 1} at once ({wall:.2f} s "
+                       f"wall), the quantization pro rata over the threads; C oracle")}
 
 
 def host_cores():

@@ -130,8 +130,12 @@ def test_bwd_refuses_the_other_variants_and_samples_the_oracle():
     assert r.returncode == 2 and "backward" in r.stderr
     import synthetic_inputs as si
 
-    res = bench.cpu_baseline_bwd(si.make("tiny", N=300, H=1))
+    wl = si.make("tiny", N=300, H=1)
+    res = bench.cpu_baseline_bwd(wl)
     assert res["value"] > 0 and res["kind"] == "oracle" and "dQ" in res["sample"]
+    assert res["cores"] == min(bench.host_cores(), 3)     # at most one thread per query block
+    one = bench.cpu_baseline_bwd(wl, cores=1)
+    assert one["cores"] == 1 and one["value"] == one["single_core_value"] > 0
     # the blended backward peak: 2d ops each at 5.0 POPS for four products, dP at 2.5
     assert bench.PEAK_TOPS["bwd"] == pytest.approx(10.0 / (8.0 / 5000.0 + 2.0 / 2500.0))
 
