@@ -121,8 +121,9 @@ def test_one_hot_output_gradient(orc):
     assert _cos(P, p64) >= 0.9999
 
 
-def test_doubling_dO_doubles_every_gradient_exactly(orc):
-    wl, q, k, v, dO = _inputs(N=260, H=1)
+@pytest.mark.parametrize("name,kw", [("tiny", dict(N=260, H=1)), ("outlier", dict(B=1, H=1, N=260))])
+def test_doubling_dO_doubles_every_gradient_exactly(orc, name, kw):
+    wl, q, k, v, dO = _inputs(name, **kw)
     g1 = orc.train_step_head(q, k, v, dO, 0, 0, False, wl.sm_scale)
     d2 = orc.f32_to_bf16(2.0 * orc.bf16_to_f32(dO))
     assert np.array_equal(orc.bf16_to_f32(d2), 2.0 * orc.bf16_to_f32(dO))
