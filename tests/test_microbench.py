@@ -1,0 +1,36 @@
+"""The microbenchmark library (quantized_attention_video_02_amd/microbench):
+builds, exports its two entry points, counts the operations of a launch as
+documented and refuses bad arguments before launching (no GPU needed)."""
+import ctypes as ct
+import os
+
+import pytest
+
+
+@pytest.fixture(scope="module")
+def mb():
+    from quantized_attention_video_02_amd.microbench import __main__ as m
+
+    if not os.path.exists(m.LIB):
+        m.build()
+    L = ct.CDLL(m.LIB)
+    L.mb_ops.argtypes = [ct.c_int, ct.c_int, ct.c_int]
+    L.mb_ops.restype = ct.c_double
+    L.mb_run.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_void_p]
+    return L
+
+
+def test_operation_counts(mb):
+    waves = 4 * 256 // 64                                  # 4 workgroups of 256 threads
+    assert mb.mb_ops(0, 4, 10) == waves * 10 * 8 * 2 * 32 * 32 * 32
+    assert mb.mb_ops(1, 4, 10) == waves * 10 * 8 * 2 * 32 * 32 * 64
+    assert mb.mb_ops(2, 4, 10) == waves * 10 * 8 * 2 * 32 * 32 * 16
+    assert mb.mb_ops(3, 4, 10) == waves * 10 * 16 * 64
+    assert mb.mb_ops(4, 4, 10) == 0
+
+
+def test_bad_arguments_rejected(mb):
+    assert mb.mb_run(0, 4, 10, None, None) == -1
+    assert mb.mb_run(0, 0, 10, ct.c_void_p(0x10000), None) == -1
+    assert mb.mb_run(0, 4, 0, ct.c_void_p(0x10000), None) == -1
+    assert mb.mb_run(5, 4, 10, ct.c_void_p(0x10000), None) == -1
