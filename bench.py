@@ -337,6 +337,42 @@ def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False, mx=False
                        f"quantization charged pro rata over the threads")}
 
 
+def measured_mfma_tops():
+    """This board's INT8 and FP8 MFMA rates (TOPS) from the register-only
+    microbenchmarks (quantized_attention_video_02_amd/microbench), or None
+    when that library is not built."""
+    import ctypes as ct
+    import statistics
+
+    import torch
+
+    from quantized_attention_video_02_amd.microbench import __main__ as mb
+
+    if not os.path.exists(mb.LIB):
+        return None
+    L = ct.CDLL(mb.LIB)
+    L.mb_run.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_void_p]
+    L.mb_ops.argtypes = [ct.c_int, ct.c_int, ct.c_int]
+    L.mb_ops.restype = ct.c_double
+    stream = torch.cuda.current_stream()
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count * 12
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    rates = {}
+    for kind, name in ((0, "int8"), (1, "fp8")):
+        ts = []
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if L.mb_run(kind, blocks, 1000, ct.c_void_p(out.data_ptr()), ct.c_void_p(stream.cuda_stream)):
+                return None
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep:
+                ts.append(e0.elapsed_time(e1))
+        rates[name] = L.mb_ops(kind, blocks, 1000) / (statistics.median(ts) * 1e-3) / 1e12
+    return rates
+
+
 def traffic_key(workload, pv, q_gran="block"):
     return f"{workload}/{pv}" + ("" if q_gran == "block" else f"/{q_gran}")
 
@@ -577,6 +613,14 @@ def main():
         useful = 4.0 * wl.B * wl.H * wl.d * wl.N * (wl.N + 1) / 2
         res["roofline"]["useful_causal_ops_per_launch"] = useful
         res["roofline"]["useful_causal_tops"] = useful / (attn_mean * 1e-3) / 1e12
+    if not args.mx and args.pv == "fp8":
+        # this board's own matrix-core rates, measured after the timed steps:
+        # the kernel does half its work on each, so the blend is its peak here
+        m = measured_mfma_tops()
+        if m:
+            blend = 1.0 / (0.5 / m["int8"] + 0.5 / m["fp8"])
+            res["roofline"]["measured_peak"] = {"int8": m["int8"], "fp8": m["fp8"], "blend": blend,
+                                                "frac": achieved / blend}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.pv, args.cpu_seconds, args.q_gran,

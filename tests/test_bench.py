@@ -175,6 +175,13 @@ def test_source_hash_covers_the_kernel_sources():
     assert any(f.endswith("sage_bwd.hip") for f in bench.BWD_SOURCES)
 
 
+def test_measured_peak_is_absent_without_the_microbenchmarks(monkeypatch):
+    from quantized_attention_video_02_amd.microbench import __main__ as mb
+
+    monkeypatch.setattr(mb, "LIB", os.path.join(ROOT, "no_such_libmb.so"))
+    assert bench.measured_mfma_tops() is None
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
@@ -196,6 +203,13 @@ def test_bench_line_keeps_the_contract():
     rf = line["roofline"]
     assert rf["bound"] == "mfma" and rf["peak"] == 5000.0 and rf["unit"] == "TFLOP/s"
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
+    from quantized_attention_video_02_amd.microbench import __main__ as mb
+
+    if os.path.exists(mb.LIB):
+        mp = rf["measured_peak"]
+        assert 0 < mp["int8"] <= 5000 * 1.05 and 0 < mp["fp8"] <= 5000 * 1.05
+        assert min(mp["int8"], mp["fp8"]) <= mp["blend"] <= max(mp["int8"], mp["fp8"])
+        assert mp["frac"] == pytest.approx(rf["achieved"] / mp["blend"])
     cb = line["cpu_baseline"]
     assert cb["kind"] == "oracle" and 1 <= cb["cores"] <= 16 and cb["single_core_value"] > 0
     assert line["config"]["workload"] == "tiny"
