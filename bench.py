@@ -23,6 +23,7 @@ Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -453,6 +454,11 @@ def main():
                          "sage_quant_v_mx, sage_attn_fwd_mx)")
     ap.add_argument("--bwd", action="store_true",
                     help="the 8-bit backward (sage_attn_bwd) over the training forward's outputs")
+    ap.add_argument("--shape", default=None, metavar="B,H,N",
+                    help="override the workload's batch, heads and sequence length (its value "
+                         "recipe and head dim stay); the line then carries no traffic figure")
+    ap.add_argument("--no-causal", action="store_true",
+                    help="run a causal workload without the causal mask")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -489,7 +495,14 @@ def main():
 
     sage.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    wl = si.make(args.workload, device="cuda", q_sigma=args.q_sigma)
+    dims = {}
+    if args.shape:
+        dims = dict(zip(("B", "H", "N"), (int(x) for x in args.shape.split(","))))
+    wl = si.make(args.workload, device="cuda", q_sigma=args.q_sigma, **dims)
+    if args.no_causal:
+        wl = dataclasses.replace(wl, causal=False)
+    # traffic.json holds counter runs of the named workloads as they are defined
+    stock = not dims and not args.no_causal
     torch.cuda.synchronize()
     fmt = "mxfp6" if args.mx else args.pv
     print(f"[bench] {wl.name}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} causal={wl.causal} path={fmt}",
@@ -508,7 +521,7 @@ def main():
         srt = sorted(bwd_ms)
         achieved = ops / (mean * 1e-3) / 1e12
         traffic = None
-        if os.path.exists(TRAFFIC_FILE):
+        if stock and os.path.exists(TRAFFIC_FILE):
             with open(TRAFFIC_FILE) as f:
                 t = json.load(f).get(traffic_key(wl.name, "bwd"))
             if t and t.get("source_hash") == attn_source_hash(bwd=True):
@@ -561,7 +574,7 @@ def main():
     # also reads V twice (per-channel scale first): 13 BHNd, MX: 11 BHNd
     qbytes = (11 if args.mx else 13) * bhnd
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if stock and os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f).get(traffic_key(wl.name, fmt, args.q_gran))
         if t and t.get("source_hash") == attn_source_hash() and not args.q_smooth:

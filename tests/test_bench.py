@@ -239,3 +239,16 @@ def test_bwd_bench_line():
     assert line["config"]["pass"] == "backward" and line["value"] > 0
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
     assert line["cpu_baseline"]["kind"] == "oracle"
+
+
+@pytest.mark.gpu
+def test_bench_shape_override_and_no_causal():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "causal_prefill",
+                        "--shape", "1,2,1000", "--no-causal", "--steps", "2", "--warmup", "1",
+                        "--no-cpu-baseline"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    cfg = line["config"]
+    assert (cfg["B"], cfg["H"], cfg["N"], cfg["causal"]) == (1, 2, 1000, False)
+    assert line["roofline"]["traffic"] is None
+    assert "useful_causal_tops" not in line["roofline"]
