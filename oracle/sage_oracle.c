@@ -176,8 +176,11 @@ OR_API void or_k_mean(const uint16_t* k, int N, int d, float* mean) {
  * Reading: symmetric range +-127 (-128 unused), absmax scale per block,
  * quotients formed in fp64 and rounded once to fp32 (= the correctly
  * rounded fp32 quotient), round to nearest even.
- * Pinned by invariants: |code| <= 127, the absmax element maps to +-127,
- * |code * scale - x| <= scale / 2 (1 + 2^-20), sign preserved, zero block. */
+ * Pinned by hand-written codes on blocks whose scaled values sit exactly on
+ * k + 1/2 (ties to even, both signs) and on a block where x * inv and
+ * x / scale round to different codes; and by invariants: |code| <= 127, the
+ * absmax element maps to +-127, |code * scale - x| <= scale / 2 (1 + 2^-20),
+ * sign preserved, zero block. */
 OR_API void or_quant_block(const float* x, int rows, int d, int8_t* out, float* scale) {
     float a = 0.0f;
     for (int i = 0; i < rows * d; ++i) {

@@ -114,6 +114,33 @@ def test_quantization_bitexact(sage, orc, name, kw, pv, layout):
     assert not pad[:, :, -1][..., vperm_positions()[tail:]].any()  # padded keys are 0
 
 
+def test_int8_rounding_ties(sage, orc):
+    """Q and K blocks whose scaled values sit exactly on k + 1/2: the codes are
+    round-half-to-even of the value (absmax 127, so the inverse scale is 1),
+    per block and per token, on the GPU and in the oracle alike."""
+    ties = np.array([0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, -3.5, 126.5, -126.5, 62.5, -63.5,
+                     4.5, -5.5, 100.5, -101.5], np.float32)
+    d, N = 128, 128
+    x = np.resize(ties, (N, d)).astype(np.float32)
+    x[:, 0] = 127.0  # every row's (and the block's) absmax
+    # K: the second half is the negated first half, so each channel's mean is 0
+    # exactly and the smoothed K equals K
+    k = np.concatenate([x[: N // 2], -x[: N // 2]])
+    want_q = np.rint(x).astype(np.int8)  # ties to even: 0.5 -> 0, 2.5 -> 2, -3.5 -> -4 ...
+    want_k = np.rint(k).astype(np.int8)
+    assert want_q[0, 1:5].tolist() == [0, 2, 2, 4]
+    tb = lambda a: torch.from_numpy(a).to(torch.bfloat16).reshape(1, 1, N, d).cuda()
+    for gran in ("block", "token"):
+        qz = sage.quant_qk(tb(x), tb(k), "HND", q_gran=gran)
+        torch.cuda.synchronize()
+        assert np.all(qz["q_scale"].cpu().numpy().ravel()[: (N if gran == "token" else 1)] == 1.0)
+        assert np.array_equal(qz["q8"][0, 0, :N].cpu().numpy(), want_q), gran
+        assert np.array_equal(qz["k8"][0, 0, :N].cpu().numpy(), want_k), gran
+        assert not qz["k_mean"].cpu().numpy().any()
+    oz = orc.quant_qk(codes(tb(x).cpu()), codes(tb(k).cpu()), q_gran="token")
+    assert np.array_equal(oz["q8"][0, 0], want_q) and np.array_equal(oz["k8"][0, 0], want_k)
+
+
 def test_fp8_encoder_ties_and_boundaries(sage, orc):
     """Every bf16 value in [-448, 448] through V quantization with inv = 1
     (each channel's absmax is 448): codes equal the oracle's RNE encoder."""

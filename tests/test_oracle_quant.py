@@ -97,6 +97,63 @@ def test_quant_block_invariants(orc):
     assert s == 0.0 and not q.any()
 
 
+def test_quant_block_rounding_rule_hand_codes(orc):
+    """The INT8 rounding rule itself: code = rne(fp32(x * fp32(127 / a))).
+
+    Expected codes are written out by hand, on blocks whose scaled values land
+    exactly on k + 1/2 (for even and odd k, both signs), where round half to
+    even, round half away from zero and truncation all differ; and on a block
+    where x * fp32(127 / a) and x / fp32(a / 127) fall on opposite sides of a
+    half step, so dividing by the scale instead of multiplying by the inverse
+    gives another code."""
+    # absmax 127: inv = fp32(127 / 127) = 1 exactly, the values are their own
+    # scaled values
+    x = np.array([[0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, -3.5, 126.5, -126.5, 62.5, -63.5, 127.0]],
+                 np.float32)
+    q, s = orc.quant_block(x)
+    assert s == np.float32(1.0)
+    assert q.tolist() == [[0, 2, 2, 4, 0, -2, -2, -4, 126, -126, 62, -64, 127]]
+    # absmax 254: inv = 0.5 exactly; 5 -> 2.5 -> 2, 7 -> 3.5 -> 4, -9 -> -4.5 -> -4
+    x = np.array([[5.0, 7.0, -9.0, 1.0, 254.0]], np.float32)
+    q, s = orc.quant_block(x)
+    assert s == np.float32(2.0)
+    assert q.tolist() == [[2, 4, -4, 0, 127]]
+    # absmax 63.5, one row (the per-token case): inv = 2 exactly
+    x = np.array([[1.25, 0.75, -0.25, -1.75, 63.5]], np.float32)
+    q, s = orc.quant_block(x)
+    assert q.tolist() == [[2, 2, 0, -4, 127]]
+    # absmax 5.9375: fp32(127 / 5.9375) is below 127 / 5.9375, so -2.96875 (exactly
+    # half of the absmax, -63.5 in real arithmetic) scales to -63.499996 -> -63,
+    # while -2.96875 / fp32(5.9375 / 127) gives -63.5 -> -64.
+    x = np.array([[5.9375, -2.96875]], np.float32)
+    inv = np.float32(127.0 / 5.9375)
+    assert np.float32(x[0, 1] * inv) > np.float32(-63.5)
+    assert np.float32(x[0, 1] / np.float32(5.9375 / 127.0)) == np.float32(-63.5)
+    q, s = orc.quant_block(x)
+    assert q.tolist() == [[127, -63]]
+    # absmax 4.5: the other way round, the product lands on -63.5 exactly -> -64
+    x = np.array([[4.5, -2.25]], np.float32)
+    assert np.float32(x[0, 1] * np.float32(127.0 / 4.5)) == np.float32(-63.5)
+    q, s = orc.quant_block(x)
+    assert q.tolist() == [[127, -64]]
+
+
+def test_quant_block_matches_numpy_rule(orc):
+    """Every code of random blocks (Gaussian and bf16-grid values, one-row and
+    many-row) equals numpy's rint(fp32(x) * fp32(127 / fp64(a))), clamped."""
+    rng = np.random.default_rng(12)
+    for trial in range(40):
+        rows = 1 if trial % 2 else 128
+        x = (rng.standard_normal((rows, 64)) * rng.uniform(0.01, 50)).astype(np.float32)
+        if trial % 4 == 1:  # coarse grid: many exact half steps
+            x = (np.round(x * 4) / 4).astype(np.float32)
+        q, _ = orc.quant_block(x)
+        a = np.float64(np.abs(x).max())
+        inv = np.float32(127.0 / a)
+        ref = np.clip(np.rint(x * inv), -127, 127).astype(np.int8)
+        assert np.array_equal(q, ref), trial
+
+
 def test_quant_qk_blocks_and_tail(orc):
     wl = si.make("tiny", N=300, H=1)  # blocks of 128, 128, 44 rows
     q, k = si.bf16_codes(wl.q), si.bf16_codes(wl.k)
