@@ -133,6 +133,78 @@ def test_bwd_full_size_sampled(sage, orc):
     assert err <= 2e-2 and c >= 0.9999, (err, c)
 
 
+def _fp64_forward(wl, chunk=4096):
+    """Plain FP64 attention of the bf16 inputs (torch, on the inputs' device):
+    the output rounded to bf16 and the exp2-domain log-sum-exp of the scores
+    against the smoothed keys (the backward's S is taken on K minus its token
+    mean, which shifts each row's scores, and so its lse, by q_i . mean):
+    lse2_i = log2 sum_j 2^(q_i . (k_j - kbar) sm_scale log2 e), every head."""
+    lam = wl.sm_scale / np.log(2.0)
+    o = torch.empty_like(wl.q)
+    lse = torch.empty(wl.q.shape[:3], dtype=torch.float32, device=wl.q.device)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            kh, vh = wl.k[b, h].double(), wl.v[b, h].double()
+            kt = (kh - kh.mean(dim=0, keepdim=True)).t().contiguous()
+            for r0 in range(0, wl.N, chunk):
+                s = torch.mm(wl.q[b, h, r0:r0 + chunk].double(), kt) * lam
+                m = s.max(dim=1, keepdim=True).values
+                p = torch.exp2(s - m)
+                l = p.sum(dim=1)
+                o[b, h, r0:r0 + chunk] = (torch.mm(p, vh) / l[:, None]).to(torch.bfloat16)
+                lse[b, h, r0:r0 + chunk] = (m[:, 0] + torch.log2(l)).float()
+    return o, lse
+
+
+def test_bwd_full_size_dkdv_elementwise(sage, orc):
+    """video_14b_720p at full size in the benchmark's launch configuration: dK
+    and dV of four key blocks (the first, one in the middle and the second of
+    head 0; the ragged last block of head 39) element by element against the
+    oracle's dK/dV sweep over all 75600 queries, to the bars of the small
+    cases.  The backward takes the forward's output O and its log-sum-exp as
+    inputs.  The oracle's own forward over 75600 rows of a head would take
+    hours on one core, so both sides get the same inputs from plain FP64
+    attention of the bf16 Q, K, V (torch): O rounded to bf16 and the
+    log-sum-exp of the smoothed scores, which differs from the quantized
+    forward's by the quantization error of the scores only."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    print("[bwd full-size parity] video_14b_720p dK/dV blocks", flush=True)
+    wl = si.make("video_14b_720p", device="cuda")
+    do = si.output_grad(wl)
+    o, lse = _fp64_forward(wl)
+    qz = sage.quant_qk(wl.q, wl.k)
+    dq, dk, dv = sage.attn_bwd(qz, wl.v, o, do, lse, sm_scale=wl.sm_scale)
+    torch.cuda.synchronize()
+    print("  GPU backward done", flush=True)
+    N, nblk = wl.N, -(-wl.N // 128)
+    picks = [(0, 0, 0), (0, 0, nblk // 2), (0, 0, 1), (0, wl.H - 1, nblk - 1)]
+    heads = {}
+    for b, h, _ in picks:
+        if (b, h) not in heads:
+            q, k, v, dO, oh = (codes(t[b:b + 1, h:h + 1]) for t in (wl.q, wl.k, wl.v, do, o))
+            heads[(b, h)] = (orc.quant_qk(q, k), v[0, 0], oh[0, 0], dO[0, 0],
+                             lse[b, h].cpu().numpy())
+
+    def run(pick):
+        b, h, kb = pick
+        oz, v, oh, dO, lh = heads[(b, h)]
+        _, dk_o, dv_o = orc.bwd_head(oz, v, oh, dO, lh, 0, 0, False, wl.sm_scale, qblocks=[],
+                                     kblocks=[kb])
+        return dk_o[kb], dv_o[kb]
+
+    with ThreadPoolExecutor(max_workers=len(picks)) as ex:  # ctypes releases the GIL
+        refs = list(ex.map(run, picks))
+    for name, g_t, idx in (("dk", dk, 0), ("dv", dv, 1)):
+        g = np.concatenate([g_t[b, h, kb * 128:min(N, kb * 128 + 128)].cpu().numpy()
+                            for b, h, kb in picks])
+        ref = np.concatenate([r[idx] for r in refs])
+        assert np.isfinite(g).all()
+        err, c = np.abs(g - ref).max() / np.abs(ref).max(), _cos(g, ref)
+        print(f"  {name} sampled key blocks: max-abs/max {err:.2e} cos(oracle) {c:.7f}", flush=True)
+        assert err <= 2e-2 and c >= 0.9999, (name, err, c)
+
+
 def _run_bwd(sage, wl, do, causal):
     qd, kd, vd, dod = (t.contiguous().cuda() for t in (wl.q, wl.k, wl.v, do))
     qz = sage.quant_qk(qd, kd)

@@ -281,3 +281,25 @@ def test_per_token_q_is_closer_to_fp64_on_outlier_tokens(orc, pv):
     cb = _cos(orc.attention(q, k, v, False, wl.sm_scale, pv)[0][0], ref)
     ct = _cos(orc.attention(q, k, v, False, wl.sm_scale, pv, q_gran="token")[0][0], ref)
     assert ct > cb + 1e-3, (cb, ct)
+
+
+@pytest.mark.xfail(strict=True, reason=(
+    "unmet bar, kept visible: on the outlier recipe at full length the quantized "
+    "method itself stays near cosine 0.996-0.998 against FP64 attention (INT8 K "
+    "resolution times the x30 query tokens); the GPU path matches this oracle's FP64 "
+    "cosine to 2e-4 on the same rows"))
+@pytest.mark.parametrize("pv", ["fp8", "fp16"])
+def test_outlier_full_length_meets_fp64_bar(orc, pv):
+    """The FP64 bar (cosine >= 0.999 against plain attention) on the outlier
+    workload at its full length N = 17550, one head, rows of the first and the
+    last (ragged) query block and the head's outlier tokens."""
+    wl = si.make("outlier", B=1, H=1)
+    q, k, v = (si.bf16_codes(t) for t in (wl.q, wl.k, wl.v))
+    rows = sorted(set(range(0, 64)) | set(range(wl.N - 14, wl.N))
+                  | set(wl.outlier_tokens[0, 0, :32].tolist()))
+    rows = np.array(rows, np.int32)
+    out, *_ = orc.attention(q, k, v, False, wl.sm_scale, pv, rows=rows)
+    ref = orc.ref64_rows_head(q, k, v, 0, 0, rows, False, wl.sm_scale)
+    c = _cos(out[0, 0], ref)
+    print(f"outlier N={wl.N} pv={pv}: cosine vs FP64 {c:.6f} on {len(rows)} rows")
+    assert c >= 0.999, c
