@@ -186,7 +186,9 @@ int sage_quant_v(const void* v, int B, int H, int N, int d, int layout, int pv_d
  *   c = fp32(sigma * k_scale[t]);  S_j = exact int32 dot(q8_i, k8_j)
  *   m_t = max_j fp32(S_j c);  m' = max(m, m_t);  alpha = exp2(m - m') (0 at start)
  *   p_j = exp2(fma(S_j, c, -fp32(m' - log2 448)))     (about 448 * P_ij)
- *   l = alpha l + sum_j p_j
+ *   l = alpha l + sum_j e4m3(p_j)         (the quantized P the product uses; fp16
+ *                                         path: binary16(p_j)), so the weights
+ *                                         applied to V sum to one
  *   O = alpha O + sum_j e4m3(p_j) * v_j   (fp16 path: binary16(p_j)), FP32 MFMA
  *                                         accumulation (the two-level form, a fresh
  *                                         FP32 sum per tile added to O, differs only
@@ -206,8 +208,9 @@ int sage_attn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, cons
  * sage_attn_fwd that also returns each query row's log-sum-exp, the forward
  * half of 8-bit training (reportify.cn SageAttention3 summary, bullet
  * 8比特训练: the backward recomputes P from it):
- *   lse[b][h][i] = fp32(fp32(m_i - log2 448) + log2(l_i))
- * with m_i, l_i the row's final running max and row sum above, so that
+ *   lse[b][h][i] = fp32(fp32(m_i - log2 448) + log2(lx_i))
+ * with m_i the row's final running max and lx_i = alpha lx + sum_j p_j its row
+ * sum of the unquantized p (the log-sum-exp of the scores), so that
  * 2^(S_ij c - lse_i) is the softmax probability P_ij in the exp2 domain (log2
  * on the GPU's own log2; differs from a correctly rounded one by about an
  * ulp).  lse: fp32 [B][H][N], 16-byte aligned, written for every row; the

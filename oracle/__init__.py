@@ -70,7 +70,7 @@ def lib():
             "or_quant_v": [P, i32, i32, i32, P, P],
             "or_dump_s": [P, P, i32, i32, i32, i32, i32, P],
             "or_attn_rows": [P, P, P, P, P, P, i32, i32, P, i32, i32, f32, i32, i32, i32, i32, P, P,
-                             P, P, P, P],
+                             P, P, P, P, P],
             "or_ref64_rows": [P, P, P, i32, i32, P, i32, i32, f64, P, P],
             "or_f32_to_mx_n": [i32, P, i64, P], "or_mx_to_f32_n": [i32, P, i64, P],
             "or_mx_blocks_n": [i32, P, i64, P, P],
@@ -259,11 +259,13 @@ def dump_s(q8h: np.ndarray, k8h: np.ndarray, row0: int, nrows: int, causal: bool
 
 def attn_rows_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scale: float,
                    pv: str = "fp8", blk: int = BLK, bc: int = BC, return_ml: bool = False,
-                   tile_mask=None, bias=None):
+                   tile_mask=None, bias=None, return_lx: bool = False):
     """Quantized attention for query rows ``rows`` of head (b, h): fp32 [len(rows), d].
     tile_mask: None (dense) or uint8 [B, H, ceil(N/128), ceil(N/bc)], nonzero =
     the query block visits the key tile.  bias: None, or the Q-smoothing
-    correction fp32 [B, H, ceil(N/128), N] of smooth_bias."""
+    correction fp32 [B, H, ceil(N/128), N] of smooth_bias.  return_ml: also the
+    final running max m and row sum l (of the quantized P) per row; return_lx:
+    also lx, the row sum of the unquantized p (the log-sum-exp's)."""
     q8h = np.ascontiguousarray(qz["q8"][b, h])
     k8h = np.ascontiguousarray(qz["k8"][b, h])
     qsh = np.ascontiguousarray(qz["q_scale"][b, h])
@@ -275,6 +277,7 @@ def attn_rows_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scal
     out = np.empty((len(rows), d), np.float32)
     m = np.empty(len(rows), np.float32)
     l = np.empty(len(rows), np.float32)
+    lx = np.empty(len(rows), np.float32)
     scratch = np.empty(4 * bc + 3 * d, np.float32)
     qblk = int(qz.get("qblk", blk))
     tm = None
@@ -288,7 +291,9 @@ def attn_rows_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scal
     lib().or_attn_rows(_p(q8h), _p(qsh), _p(k8h), _p(ksh), _p(vqh), _p(vsh), N, d, _p(rows),
                        len(rows), int(causal), float(sm_scale), int(pv == "fp16"), qblk, blk, bc,
                        None if tm is None else _p(tm), None if bs is None else _p(bs), _p(out),
-                       _p(m), _p(l), _p(scratch))
+                       _p(m), _p(l), _p(lx), _p(scratch))
+    if return_lx:
+        return out, m, l, lx
     if return_ml:
         return out, m, l
     return out
@@ -443,7 +448,8 @@ def mx_attention(q, k, v, causal: bool, sm_scale: float, rows=None, fmt="mxfp6")
 # ------------------------------------------------------------- 8-bit backward
 def lse2_from_ml(m, l):
     """The forward's log-sum-exp in the exp2 domain: lse2 = fp32(mu + log2(l))
-    with mu = fp32(m - log2 448) (log2 rounded once to fp32)."""
+    with mu = fp32(m - log2 448) (log2 rounded once to fp32), l the row sum of
+    the unquantized p."""
     mu = (np.asarray(m, np.float32) - np.float32(np.log2(P_SCALE))).astype(np.float32)
     return (mu + np.log2(np.asarray(l, np.float64)).astype(np.float32)).astype(np.float32)
 
@@ -451,8 +457,8 @@ def lse2_from_ml(m, l):
 def train_forward_head(qz: dict, vq, vs, b: int, h: int, rows, causal: bool, sm_scale: float):
     """The training forward for ``rows`` of head (b, h): the bf16 output (uint16
     codes, as a training step keeps it) and lse2 per row."""
-    out, m, l = attn_rows_head(qz, vq, vs, b, h, rows, causal, sm_scale, "fp8", return_ml=True)
-    return f32_to_bf16(out), lse2_from_ml(m, l)
+    out, m, _, lx = attn_rows_head(qz, vq, vs, b, h, rows, causal, sm_scale, "fp8", return_lx=True)
+    return f32_to_bf16(out), lse2_from_ml(m, lx)
 
 
 def bwd_prep_head(o, dO):

@@ -345,8 +345,10 @@ OR_API void or_q_smooth_bias(const float* qmean, const uint16_t* k, const float*
  *   alpha = m == -inf ? 0 : exp2(fp32(m - m'))
  *   mu    = fp32(m' - log2 448)
  *   p_j   = exp2(fma(S_j, c, -mu))           (= 448 * 2^(S_j c - m') up to rounding)
- *   l     = fp32(fp32(alpha * l) + sum_j p_j) (sum in ascending j)
  *   pq_j  = e4m3(p_j)   (FP16 path: f16(p_j))           -- static scale 448
+ *   l     = fp32(fp32(alpha * l) + sum_j dec(pq_j))  (sum in ascending j)
+ *   lx    = fp32(fp32(alpha * lx) + sum_j p_j)       (the unquantized sum: the
+ *           log-sum-exp of the scores, mu + log2 lx, for the backward)
  *   T_c   = sum_j dec(pq_j) * dec(v_jc)      level 1: a fresh fp32 sum per tile
  *   O_c   = fp32(fp32(alpha * O_c) + T_c)    level 2: the running fp32 accumulator
  * Epilogue: out_c = fp32( fp32(O_c * v_scale_c) / l ).
@@ -358,8 +360,10 @@ OR_API void or_q_smooth_bias(const float* qmean, const uint16_t* k, const float*
  * Readings: the static P scale is 448 (the e4m3fn maximum: the running max
  * makes every p <= 1, so 448 p fills the FP8 range with no per-token
  * statistics -- the "no quantization overhead" of the reportify summary);
- * the 448 is folded into the exp2 argument through mu; l sums the
- * unquantized p; key tiles of bc = 128 keys in ascending order, no split;
+ * the 448 is folded into the exp2 argument through mu; l sums the P values
+ * the P V product uses (after their FP8 / FP16 rounding), so that the
+ * weights applied to V sum to exactly one (a constant V comes out unchanged);
+ * key tiles of bc = 128 keys in ascending order, no split;
  * the two accumulation levels are one key tile and the whole row.
  * qs is indexed by query block of qblk rows: qblk = 128 is the per-block
  * quantization (reportify SageAttention3 summary, bullet 8比特训练), qblk = 1
@@ -380,13 +384,13 @@ static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, con
                         const void* vq, const float* vs, int N, int d, int i, int causal,
                         float lambda, int pv_fp16, int qblk, int kblk, int bc,
                         const uint8_t* tmask, const float* bias, float* out, float* m_out,
-                        float* l_out, int32_t* S, float* T, float* O, float* P) {
+                        float* l_out, float* lx_out, int32_t* S, float* T, float* O, float* P) {
     const uint8_t* v8 = (const uint8_t*)vq;
     const uint16_t* v16 = (const uint16_t*)vq;
     const float L = or_log2_pscale();
     const float sigma = qs[i / qblk] * lambda;
     const int8_t* qi = q8 + (int64_t)i * d;
-    float m = -INFINITY, l = 0.0f;
+    float m = -INFINITY, l = 0.0f, lx = 0.0f;
     for (int c = 0; c < d; ++c) O[c] = 0.0f;
     int ntiles = (N + bc - 1) / bc;
     for (int t = 0; t < ntiles; ++t) {
@@ -406,14 +410,16 @@ static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, con
         float mn = m > mt ? m : mt;
         float alpha = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
         float mu = mn - L;
-        float psum = 0.0f;
+        float psum = 0.0f, xsum = 0.0f;
         for (int j = 0; j < n; ++j) {
             float p = bias ? exp2f(fmaf((float)S[j], c, bias[j0 + j]) - mu)
                            : exp2f(fmaf((float)S[j], c, -mu));
-            psum += p;
             P[j] = pv_fp16 ? or_f16_to_f32(or_f32_to_f16(p)) : or_e4m3_to_f32(or_f32_to_e4m3(p));
+            psum += P[j];
+            xsum += p;
         }
         l = alpha * l + psum;
+        lx = alpha * lx + xsum;
         for (int cc = 0; cc < d; ++cc) T[cc] = 0.0f;
         for (int j = 0; j < n; ++j) {
             int64_t row = (int64_t)(j0 + j) * d;
@@ -428,6 +434,7 @@ static void or_attn_row(const int8_t* q8, const float* qs, const int8_t* k8, con
     for (int cc = 0; cc < d; ++cc) out[cc] = l > 0.0f ? (O[cc] * vs[cc]) / l : 0.0f;
     if (m_out) *m_out = m;
     if (l_out) *l_out = l;
+    if (lx_out) *lx_out = lx;
 }
 
 /* Rows rows[0..nrows) of one head; out [nrows][d]; m_out/l_out optional.
@@ -440,7 +447,8 @@ OR_API void or_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, co
                          const void* vq, const float* vs, int N, int d, const int32_t* rows,
                          int nrows, int causal, float sm_scale, int pv_fp16, int qblk,
                          int kblk, int bc, const uint8_t* tmask, const float* bias,
-                         float* out, float* m_out, float* l_out, float* scratch) {
+                         float* out, float* m_out, float* l_out, float* lx_out,
+                         float* scratch) {
     float lambda = or_lambda(sm_scale);
     int32_t* S = (int32_t*)scratch;
     float* P = scratch + bc;
@@ -449,8 +457,9 @@ OR_API void or_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, co
     for (int r = 0; r < nrows; ++r)
         or_attn_row(q8, qs, k8, ks, vq, vs, N, d, rows[r], causal, lambda, pv_fp16, qblk, kblk, bc,
                     tmask ? tmask + (int64_t)(rows[r] / 128) * ((N + bc - 1) / bc) : 0,
-                    bias ? bias + (int64_t)(rows[r] / 128) * N : 0, out + (int64_t)r * d, m_out ? m_out + r : 0, l_out ? l_out + r : 0, S, T, O,
-                    P);
+                    bias ? bias + (int64_t)(rows[r] / 128) * N : 0, out + (int64_t)r * d,
+                    m_out ? m_out + r : 0, l_out ? l_out + r : 0, lx_out ? lx_out + r : 0, S, T,
+                    O, P);
 }
 
 /* ------------------------------------------------------------------------ */

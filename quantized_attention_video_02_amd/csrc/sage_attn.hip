@@ -25,12 +25,17 @@
 //     8 x v_mfma_f32_32x32x64_f8f6f4 (d = 128) -- O^T keeps queries on lanes,
 //     so the per-query rescale alpha is a per-lane scalar.
 // Schedule: a per-wave software pipeline with one workgroup barrier per tile.
-// Iteration t runs A = P V of tile t-1 (MFMA) and the max / alpha / float(S)
-// of tile t (VALU), then B = the Q K^T of tile t+1 (MFMA) interleaved with the
-// exp2 / row sum / FP8 packing of tile t (VALU), so every wave always holds
-// independent MFMA and VALU work.  The kernel is bound by VALU issue (about
-// 350 VALU instructions per wave and tile against 24 MFMAs), not by the
-// matrix cores.
+// Iteration t runs A = P V of tile t-1 (MFMA) with the max / alpha / float(S)
+// and exponent arguments of tile t (VALU), then B = the Q K^T of tile t+1
+// (MFMA) with the exp2 / FP8 packing of tile t (VALU).  Each phase is written
+// as chunks of one MFMA (its LDS operand read one chunk ahead) followed by a
+// share of the phase's vector work, kept in that order by scheduling barriers,
+// so the vector instructions issue in the MFMAs' shadow.  The row sum of the
+// FP8 P is two more MFMAs (a 0/1 pattern times P).  The second wave of each
+// SIMD passes each step's barrier between its A and B, so the two waves of a
+// SIMD run opposite phases.  Per wave and tile: 26 MFMAs and about 300
+// vector instructions (65 of them v_exp_f32); the vector issue of one wave and
+// the arbitration of the two waves for the matrix core bound the kernel.
 // K and V tiles go straight from global memory into LDS (global_load_lds_dwordx4
 // issued from asm, no register staging), double-buffered: K(t+2) and V(t) are
 // loaded during iteration t and awaited before its closing barrier.  LDS rows
@@ -45,6 +50,17 @@
 
 #include "sage_common.h"
 #include "sage_device.h"
+
+// Build switches for timing the schedules against each other (every setting
+// computes the same result): SAGE_FWD_SCHED=0 builds the FP8 sweep with the
+// unchunked per-tile code the FP16 and Q-smoothing sweeps use;
+// SAGE_PINGPONG=0 keeps both waves of a SIMD on the same step order.
+#ifndef SAGE_FWD_SCHED
+#define SAGE_FWD_SCHED 1
+#endif
+#ifndef SAGE_PINGPONG
+#define SAGE_PINGPONG 1
+#endif
 
 namespace sage {
 
@@ -115,6 +131,12 @@ struct MaskTile {
         if constexpr (R + 1 < 16) MaskTile<K4, R + 1>::apply_float(F, lim);
         else if constexpr (K4 + 1 < 4) MaskTile<K4 + 1, 0>::apply_float(F, lim);
     }
+    // INT32 scores held as fp32 bit patterns: masked keys get INT_MIN
+    __device__ static void apply_intbits(v16f* S, int lim) {
+        S[K4][R] = __uint_as_float(mask_key<OFF>(__float_as_uint(S[K4][R]), lim, 0x80000000u));
+        if constexpr (R + 1 < 16) MaskTile<K4, R + 1>::apply_intbits(S, lim);
+        else if constexpr (K4 + 1 < 4) MaskTile<K4 + 1, 0>::apply_intbits(S, lim);
+    }
 };
 
 // First half of the online-softmax step of one tile for this lane's query:
@@ -179,13 +201,17 @@ __device__ inline void softmax_prep(v16i* S, v16f* F, float c, const uint8_t* br
 }
 
 // Second half, one 32-key block k4: p = exp2(fma(F, c, -mu)) (= 448 * 2^(s - m')),
-// P (FP8 e4m3 or FP16) into the P V operand, and the partial row sum.
+// P (FP8 e4m3 or FP16) into the P V operand, and the partial row sum of the
+// quantized P (the values the P V product weights V with, decoded from the
+// operand).  XS: also the partial sum of the unquantized p into xs (the
+// log-sum-exp of the scores).
 // c == 0 only when the whole tile's S is 0; any positive factor then gives
 // the same argument, and a positive one keeps -inf * factor = -inf.
 // With Q smoothing F already holds s: p = exp2(fp32(s - mu)).
-template <bool QSM, typename PT>
-__device__ inline float softmax_block(const v16f& Fk, PT* P, int k4, float cf, float mu) {
-    float part[4];
+template <bool QSM, bool XS, typename PT>
+__device__ inline float softmax_block(const v16f& Fk, PT* P, int k4, float cf, float mu,
+                                      float& xs) {
+    float part[4], xpart[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         float p[4];
@@ -193,18 +219,27 @@ __device__ inline float softmax_block(const v16f& Fk, PT* P, int k4, float cf, f
         for (int j = 0; j < 4; ++j)
             p[j] = __builtin_amdgcn_exp2f(QSM ? Fk[4 * u + j] - mu
                                               : __builtin_fmaf(Fk[4 * u + j], cf, -mu));
-        part[u] = (p[0] + p[1]) + (p[2] + p[3]);
+        if constexpr (XS) xpart[u] = (p[0] + p[1]) + (p[2] + p[3]);
         if constexpr (__is_same(PT, v8i)) {
             // the first half-word write keeps the other half of its old operand;
             // p[0]'s own register (dead after this) serves, so no zeroing move
             int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
             w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
             P[k4 >> 1][(k4 & 1) * 4 + u] = w;
+            const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+            const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+            part[u] = (lo.x + lo.y) + (hi.x + hi.y);
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) P[2 * k4 + (u >> 1)][4 * (u & 1) + j] = (_Float16)p[j];
+            const v2h h01 = v2h{(_Float16)p[0], (_Float16)p[1]};
+            const v2h h23 = v2h{(_Float16)p[2], (_Float16)p[3]};
+            const v2h one = v2h{(_Float16)1.0f, (_Float16)1.0f};
+            part[u] = __builtin_amdgcn_fdot2(h01, one, 0.0f, false) +
+                      __builtin_amdgcn_fdot2(h23, one, 0.0f, false);
         }
     }
+    if constexpr (XS) xs = (xpart[0] + xpart[1]) + (xpart[2] + xpart[3]);
     return (part[0] + part[1]) + (part[2] + part[3]);
 }
 
@@ -243,6 +278,44 @@ __device__ inline void pv_tile(const uint8_t* vb, const v8h* P, v16f* O, float a
 #pragma unroll
             for (int e = 0; e < 16; ++e) O[cb][e] *= alpha;
     }
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const v8h av = *(const v8h*)(vrow + 32 * cb * L::VSTR + 16 * u);
+            O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, P[u], O[cb], 0, 0, 0);
+        }
+}
+
+// O = alpha O when some lane's alpha differs from 1 (a wave-uniform branch).
+template <int D>
+__device__ inline void rescale_o(v16f* O, float alpha) {
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) O[cb][e] *= alpha;
+    }
+}
+
+// The P V MFMAs of pv_tile alone (O already rescaled).
+template <int D>
+__device__ inline void pv_mfma(const uint8_t* vb, const v8i* P, v16f* O, int n, int hh) {
+    using L = Lds<D, false>;
+    const uint8_t* vrow = vb + n * L::VSTR + 64 * hh;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+        const v8i a0 = *(const v8i*)(vrow + 32 * cb * L::VSTR);
+        const v8i a1 = *(const v8i*)(vrow + 32 * cb * L::VSTR + 32);
+        O[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, P[0], O[cb], 0, 0, 0, 0, 0, 0);
+        O[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, P[1], O[cb], 0, 0, 0, 0, 0, 0);
+    }
+}
+
+template <int D>
+__device__ inline void pv_mfma(const uint8_t* vb, const v8h* P, v16f* O, int n, int hh) {
+    using L = Lds<D, true>;
+    const uint8_t* vrow = vb + n * L::VSTR + 128 * hh;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -311,10 +384,193 @@ __device__ inline void store_row(const AttnArgs& a, const v16f* O, float lt, int
         }
 }
 
+// The two halves of one key tile's step in the pipelined sweep, written as
+// chunks that __builtin_amdgcn_sched_barrier keeps in program order: each
+// chunk issues one MFMA (its LDS operand read one chunk ahead) and then a
+// share of the tile's vector work, so the vector instructions issue while the
+// MFMAs run instead of before or after all of them.
+// An empty asm that takes x and gives it back: x is computed at this point of
+// the program and not moved by the compiler's code motion (sinking towards its
+// uses would pull a chunk's vector work out of the MFMA shadow it was placed
+// in).
+__device__ inline float pinned(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ inline int pinned(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+__device__ inline v16f mfma_pv(const v8i& a, const v8i& b, const v16f& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ inline v16f mfma_pv(const v8h& a, const v8h& b, const v16f& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Row sum of the FP8 P operand on the matrix core: one 16x16x128 MFMA per
+// 64-key half of the tile, A = a 0/1 pattern in FP8 (e4m3, 1.0 = 0x38),
+// B = the P V operand (32 keys of one query per lane).  Lane l of the
+// B operand holds column l % 16 of key group l / 16 (query l % 32); the
+// pattern row r takes key groups g with g % 2 == (r / 4) % 2, so output row
+// r, column c sums both key halves of query c + 16 ((r / 4) % 2), which is
+// what lane c + 16 (r / 4) holds in its 4 accumulator registers: each lane
+// gets its own query's sum over all 128 keys (both lane halves).
+__device__ inline v4f rowsum_p(const v8i& ones, const v8i* P, const v4f& acc, int half) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, P[half], acc, 0, 0, 0, 0, 0, 0);
+}
+__device__ inline v4f rowsum_p(const v8i&, const v8h*, const v4f& acc, int) { return acc; }
+__device__ inline v8i rowsum_pattern(int lane) {
+    const int on = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1)) ? 0x38383838 : 0;
+    return v8i{on, on, on, on, on, on, on, on};
+}
+
+// Phase A: P V of the previous tile (O already rescaled by its alpha) with, in
+// the MFMAs' shadow, this tile's integer row max and float(S) (one 32-key
+// block per unit), then the running max m, alpha and mu, then the exponent
+// arguments F = fma(float(S), c, -mu) (one block per unit).  Same arithmetic
+// as pv_tile + softmax_prep + the argument of softmax_block.
+template <int D, bool PV16, bool SPARSE, bool RS, typename PT>
+__device__ inline void phase_a(const uint8_t* vb, const PT* P, v16f* O, const v16f* S, v16f* F,
+                               float c, float& m, float& alpha, float& l, const v8i& ones, int n,
+                               int hh) {
+    using L = Lds<D, PV16>;
+    constexpr int NPV = (PV16 ? 8 : 2) * (D / 32);
+    // MFMA i: fp8 -> channel block i / 2, 32 key bytes at 32 (i % 2);
+    //         fp16 -> channel block i / 8, 8 keys at 16 (i % 8) bytes
+    const uint8_t* vrow = vb + n * L::VSTR + (PV16 ? 128 : 64) * hh;
+    auto vop = [&](int i) -> PT {
+        return PV16 ? *(const PT*)(vrow + 32 * (i / 8) * L::VSTR + 16 * (i % 8))
+                    : *(const PT*)(vrow + 32 * (i / 2) * L::VSTR + 32 * (i % 2));
+    };
+    constexpr int PER = PV16 ? 8 : 2;
+    int mk[4];
+    float cf = 1.0f, mu = 0.0f;
+    PT op[2];
+    op[0] = vop(0);
+    v4f rs = v4f{};
+    const float alpha_prev = alpha;  // the previous tile's, which its P was formed with
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+        if (i + 1 < NPV) op[(i + 1) & 1] = vop(i + 1);
+        O[i / PER] = mfma_pv(op[i & 1], P[i % PER], O[i / PER]);
+        if constexpr (RS) {
+            // the previous tile's row sum of P on the matrix core (see rowsum_p)
+            if (i == 0) rs = rowsum_p(ones, P, rs, 0);
+            if (i == 1) rs = rowsum_p(ones, P, rs, 1);
+            if (i == NPV - 1) l = alpha_prev * l + rs[0];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (u * NPV / 8 != i) continue;
+            if (u < 4) {
+                const v16i Si = __builtin_bit_cast(v16i, S[u]);
+                int x = max(Si[0], Si[1]);
+#pragma unroll
+                for (int r = 2; r < 16; r += 2) x = max(max(x, Si[r]), Si[r + 1]);
+                mk[u] = pinned(x);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) F[u][r] = pinned((float)Si[r]);
+            } else {
+                if (u == 4) {
+                    const int mx = pair_max(max(max(mk[0], mk[1]), max(mk[2], mk[3])));
+                    const float mt = mx == INT_MIN ? -INFINITY : (float)mx * c;
+                    const float mn = fmaxf(m, mt);
+                    alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+                    m = mn;
+                    mu = mn - kLog2PScale;
+                    // no key seen yet (m = -inf): any finite mu keeps p = exp2(-inf) = 0
+                    if (SPARSE && m == -INFINITY) mu = 0.0f;
+                    cf = c == 0.0f ? 1.0f : c;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    F[u - 4][r] = pinned(__builtin_fmaf(F[u - 4][r], cf, -mu));
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// P (FP8 or FP16) of 4 consecutive values of block k4 (registers 4u .. 4u+3)
+// into the P V operand, and their partial sum (p0 + p1) + (p2 + p3).
+// The sum is formed first and pinned in place (an empty asm that takes it),
+// so the compiler neither sinks the adds to the end of the sweep step nor
+// keeps p0 alive past the pack (whose first write reuses p0's register for
+// the dword's other half).
+template <bool SUM>
+__device__ inline float pack_group(const v16f& Fk, v8i* P, int k4, int u) {
+    const float p0 = Fk[4 * u], p1 = Fk[4 * u + 1], p2 = Fk[4 * u + 2], p3 = Fk[4 * u + 3];
+    float sum = 0.0f;
+    if constexpr (SUM) {
+        sum = (p0 + p1) + (p2 + p3);
+        asm volatile("" : "+v"(sum));
+    }
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
+    w = pinned(__builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true));
+    P[k4 >> 1][(k4 & 1) * 4 + u] = w;
+    return sum;
+}
+template <bool SUM>
+__device__ inline float pack_group(const v16f& Fk, v8h* P, int k4, int u) {
+    float sum = (Fk[4 * u] + Fk[4 * u + 1]) + (Fk[4 * u + 2] + Fk[4 * u + 3]);
+    asm volatile("" : "+v"(sum));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) P[2 * k4 + (u >> 1)][4 * (u & 1) + j] = (_Float16)Fk[4 * u + j];
+    return sum;
+}
+
+// Phase B: Q K^T of the next tile (16 INT8 MFMAs at d = 128) with, in their
+// shadow, p = exp2(F) of this tile in groups of 4 values, each group packed
+// into P and summed one chunk after its exponentials (so no exp2 result is
+// read right after it is written).  part[k4] = the row sum of block k4, in
+// softmax_block's association.
+template <int D, int KSTR, bool SUM, typename PT>
+__device__ inline void phase_b(const uint8_t* kb, const v4i* qf, v16f* S, v16f* F, PT* P,
+                               float* part, int n, int hh) {
+    constexpr int KK = D / 32, NQK = 4 * KK;
+    // MFMA j: key block j / KK, channel chunk j % KK
+    auto kop = [&](int j) -> v4i {
+        return *(const v4i*)(kb + (32 * (j / KK) + n) * KSTR + 16 * hh + 32 * (j % KK));
+    };
+    float gs[16];
+    v4i op[2];
+    op[0] = kop(0);
+#pragma unroll
+    for (int j = 0; j <= NQK; ++j) {
+        if (j < NQK) {
+            if (j + 1 < NQK) op[(j + 1) & 1] = kop(j + 1);
+            S[j / KK] = __builtin_bit_cast(
+                v16f, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                          op[j & 1], qf[j % KK],
+                          (j % KK) ? __builtin_bit_cast(v16i, S[j / KK]) : v16i{}, 0, 0, 0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            const int cj = g * NQK / 16;  // chunk of this group's exponentials
+            if (cj == j && j < NQK)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    F[g >> 2][4 * (g & 3) + q] = __builtin_amdgcn_exp2f(F[g >> 2][4 * (g & 3) + q]);
+                    F[g >> 2][4 * (g & 3) + q] = pinned(F[g >> 2][4 * (g & 3) + q]);
+                }
+            if (cj + 1 == j) gs[g] = pack_group<SUM>(F[g >> 2], P, g >> 2, g & 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+        part[k4] = (gs[4 * k4] + gs[4 * k4 + 1]) + (gs[4 * k4 + 2] + gs[4 * k4 + 3]);
+}
+
 // MODE: kDense, kDump (also writes the int32 Q K^T of one head), kSparse
-// (visits only the key tiles a tile mask selects).  QSM: Q smoothing, the
-// scores carry the per-(query block, key) correction a.bias.
-enum { kDense = 0, kDump = 1, kSparse = 2 };
+// (visits only the key tiles a tile mask selects), kLse (dense, and writes
+// each row's log-sum-exp: the forward of 8-bit training).  QSM: Q smoothing,
+// the scores carry the per-(query block, key) correction a.bias.
+enum { kDense = 0, kDump = 1, kSparse = 2, kLse = 3 };
 
 // Waves per workgroup: 8 (256 queries, one workgroup per CU), or 4 (128
 // queries = one query block, two workgroups per CU) for the sparse sweep, so
@@ -332,7 +588,7 @@ constexpr int kBiasSlot = 1024;
 template <int D, bool PV16, bool CAUSAL, int MODE, bool QSM>
 __global__ __launch_bounds__((64 * attn_waves<D, PV16, MODE>()), (8 / attn_waves<D, PV16, MODE>()))
 void attn_fwd_kernel(AttnArgs a) {
-    constexpr bool DUMP = MODE == kDump, SPARSE = MODE == kSparse;
+    constexpr bool DUMP = MODE == kDump, SPARSE = MODE == kSparse, LSE = MODE == kLse;
     static_assert(!(QSM && DUMP), "the dump runs without Q smoothing");
     constexpr int NW = attn_waves<D, PV16, MODE>(), NT = 64 * NW, BR = 32 * NW;
     using L = Lds<D, PV16>;
@@ -341,7 +597,11 @@ void attn_fwd_kernel(AttnArgs a) {
     constexpr int KK = D / 32;
     constexpr int CB = D / 32;
     constexpr int BBASE = L::TOTAL;  // correction tiles (Q smoothing), two slots
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::TOTAL + (QSM ? 2 * kBiasSlot : 0)];
+    // PP: the two waves of a SIMD run the halves of a sweep step in opposite
+    // order (see the loop), which needs a third K slot, after the V slots
+    constexpr bool PP = MODE != kSparse && !QSM && !PV16 && SAGE_FWD_SCHED && SAGE_PINGPONG;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::TOTAL + (QSM ? 2 * kBiasSlot : 0) +
+                                                          (PP ? L::KBYTES : 0)];
     // sparse: the key tiles this workgroup visits, ascending; bits 14 / 15 say
     // whether the first / second 128-query block of the workgroup visits it
     __shared__ uint16_t vlist[SPARSE ? kMaxSparseTiles : 1];
@@ -378,9 +638,16 @@ void attn_fwd_kernel(AttnArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     // step t of the sweep works on key tile T (every tile when dense: T = t);
     // the tile goes to LDS slot t & 1
+    // K slot of step t: t & 1, or t % 3 with PP (slot 2 after the V slots)
+    auto kslot = [&](int t) -> uint32_t {
+        if constexpr (PP) {
+            const int s3 = t % 3;
+            return s3 == 2 ? (uint32_t)L::TOTAL : (uint32_t)(s3 * L::KBYTES);
+        }
+        return (uint32_t)((t & 1) * L::KBYTES);
+    };
     auto load_k = [&](int t, int T) {
-        tile_to_lds<L::KPIECES, KMAXP, NW>(kg + (int64_t)T * L::KHBM, lbase + (t & 1) * L::KBYTES,
-                                           wv, koff);
+        tile_to_lds<L::KPIECES, KMAXP, NW>(kg + (int64_t)T * L::KHBM, lbase + kslot(t), wv, koff);
     };
     auto load_v = [&](int t, int T) {
         tile_to_lds<L::VPIECES, VMAXP, NW>(vg + (int64_t)T * L::VHBM,
@@ -434,10 +701,24 @@ void attn_fwd_kernel(AttnArgs a) {
 
     float m = -INFINITY, l = 0.0f;
     float alpha = 1.0f;  // alpha of the tile whose P is held (tile -1: P = 0, alpha = 1)
+    // RS: the row sum l of the quantized P is taken on the matrix core (the
+    // chunked schedule, FP8 P); otherwise each lane adds its half of the
+    // decoded P values.  LSE also keeps lx, the row sum of the unquantized p,
+    // for the log-sum-exp of the scores.
+    constexpr bool RS = !QSM && !PV16 && SAGE_FWD_SCHED;
+    float lx = 0.0f;
+    const v8i ones = rowsum_pattern(lane);
     v16f O[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) O[cb] = v16f{};
-    v16i S[4];
+    // NEW: the chunked schedule (phase_a / phase_b).  X holds S(t) (INT32
+    // scores as fp32 bit patterns) at the start of step t; phase A turns it
+    // into the exponent arguments F(t) in Y, phase B forms S(t+1) in X.
+    constexpr bool NEW = !QSM && !PV16 && SAGE_FWD_SCHED;
+    v16i S[4];  // the older path's INT32 scores
+    v16f F[4];  // the older path's exponent arguments
+    v16f X[4], Y[4];
+    float part[4];  // row sums by 32-key block (when not taken on the matrix core)
     PT P[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) P[i] = PT{};
@@ -449,6 +730,15 @@ void attn_fwd_kernel(AttnArgs a) {
     //   B: per 32-key block, Q K^T of tile t+1 (MFMA) || exp / sum / FP8 of tile t (VALU)
     // so each wave always has independent MFMA and VALU work for the SIMD to
     // overlap with the other wave's.  V buffer 1 is zero-filled for tile -1.
+    // PP: the second wave of each SIMD (waves 4-7) reaches each step's
+    // barrier between A and B.  Between two barriers the first waves then run
+    // A and B of step t while the second waves run B of step t-1 and A of
+    // step t, so the two waves of a SIMD work on opposite halves at once, one
+    // on P V + max + exponent arguments, the other on Q K^T + exp2 + P, and
+    // the matrix core and the vector ALU both have a wave's work at all times.
+    // Same code and arithmetic per wave; a K tile is read half a step longer,
+    // hence the third K slot.
+    const bool second = PP && wv >= 4;
     {
         uint4* vz = (uint4*)(smem + L::VBASE + L::VBYTES);
         for (int i = tid; i < L::VBYTES / 16; i += NT) vz[i] = make_uint4(0, 0, 0, 0);
@@ -458,8 +748,14 @@ void attn_fwd_kernel(AttnArgs a) {
     if (!SPARSE || ntiles > 0) load_bias(0, SPARSE ? (e0 & 0x3fff) : 0);
     wait_vmem();
     __syncthreads();
+    if constexpr (NEW) {
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) S[k4] = qk_block<D, L::KSTR>(smem, qf, k4, n, hh);
+        for (int k4 = 0; k4 < 4; ++k4)
+            X[k4] = __builtin_bit_cast(v16f, qk_block<D, L::KSTR>(smem, qf, k4, n, hh));
+    } else {
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) S[k4] = qk_block<D, L::KSTR>(smem, qf, k4, n, hh);
+    }
     __syncthreads();
 
     const float* ksrow = a.k_scale + bh * a.nblk;
@@ -477,50 +773,87 @@ void attn_fwd_kernel(AttnArgs a) {
         load_v(t, T);
         if (t + 1 < ntiles) load_bias(t + 1, SPARSE ? (e1 & 0x3fff) : t + 1);
         const int key_t = T * kBc;
-        if (DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows)
-            dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
-        // A
-        pv_tile<D>(smem + L::VBASE + ((t + 1) & 1) * L::VBYTES, P, O, alpha, n, hh);
         // a tile this wave's query block does not visit is masked whole: with
         // p = 0 and alpha = 1 it changes nothing, as if never seen
         const bool visits = !SPARSE || ((e0 >> vbit) & 1);
         const bool needmask = (tail && T == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase) ||
                               !visits;
-        v16f F[4];
-        float mu;
-        softmax_prep<QSM>(S, F, c, smem + BBASE + (t & 1) * kBiasSlot + (wave >> 2) * 512, m, alpha,
-                          mu, needmask, visits ? kmax - key_t - 4 * hh : -1, hh);
-        // no key seen yet (m = -inf): any finite mu keeps p = exp2(-inf) = 0
-        if (SPARSE && m == -INFINITY) mu = 0.0f;
-        const float cf = c == 0.0f ? 1.0f : c;
-        // B (the Q K^T of "tile ntiles" reads a stale buffer; its result is unused)
-        const uint8_t* kb = smem + ((t + 1) & 1) * L::KBYTES;
-        float part[4];
+        const int lim = visits ? kmax - key_t - 4 * hh : -1;
+        const uint8_t* vbuf = smem + L::VBASE + ((t + 1) & 1) * L::VBYTES;
+        const bool dumps = DUMP && bh == a.dbh && qi >= a.drow0 && qi < a.drow0 + a.dnrows;
+        if constexpr (NEW) {
+            // A: P V of tile t-1 || max, float(S) and exponent arguments of tile t
+            if (dumps) {
+                v16i Sd[4];
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-            S[k4] = qk_block<D, L::KSTR>(kb, qf, k4, n, hh);
-            part[k4] = softmax_block<QSM>(F[k4], P, k4, cf, mu);
+                for (int k4 = 0; k4 < 4; ++k4) Sd[k4] = __builtin_bit_cast(v16i, X[k4]);
+                dump_tile(Sd, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
+            }
+            rescale_o<D>(O, alpha);
+            if (needmask) MaskTile<0, 0>::apply_intbits(X, lim);
+            phase_a<D, PV16, SPARSE, RS>(vbuf, P, O, X, Y, c, m, alpha, l, ones, n, hh);
+            if (needmask) MaskTile<0, 0>::apply_float(Y, lim);
+            // PP: the second waves reach this step's barrier between A and B,
+            // so their B of this tile runs after it, beside the first waves' A
+            // of the next tile
+            if (second) {
+                wait_vmem();
+                __syncthreads();
+            }
+            // B: Q K^T of tile t+1 || exp2, P (and row sums) of tile t
+            phase_b<D, L::KSTR, LSE>(smem + kslot(t + 1), qf, X, Y, P, part, n, hh);
+            if constexpr (LSE) lx = alpha * lx + ((part[0] + part[1]) + (part[2] + part[3]));
+        } else {
+            if (dumps) dump_tile(S, a.s_out + (int64_t)(qi - a.drow0) * N, key_t, N, CAUSAL, qi, hh);
+            // A
+            pv_tile<D>(vbuf, P, O, alpha, n, hh);
+            float mu;
+            softmax_prep<QSM>(S, F, c, smem + BBASE + (t & 1) * kBiasSlot + (wave >> 2) * 512, m,
+                              alpha, mu, needmask, lim, hh);
+            // no key seen yet (m = -inf): any finite mu keeps p = exp2(-inf) = 0
+            if (SPARSE && m == -INFINITY) mu = 0.0f;
+            const float cf = c == 0.0f ? 1.0f : c;
+            // B (the Q K^T of "tile ntiles" reads a stale buffer; its result is unused)
+            const uint8_t* kb = smem + kslot(t + 1);
+            float xpart[4];
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                S[k4] = qk_block<D, L::KSTR>(kb, qf, k4, n, hh);
+                part[k4] = softmax_block<QSM, LSE>(F[k4], P, k4, cf, mu, xpart[k4]);
+            }
+            l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
+            if constexpr (LSE) lx = alpha * lx + ((xpart[0] + xpart[1]) + (xpart[2] + xpart[3]));
         }
-        l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
         if (SPARSE) {
             e0 = e1;
             e1 = e2;
             e2 = __builtin_amdgcn_readfirstlane((int)e3raw);
         }
-        wait_vmem();
-        __syncthreads();
+        if (!second) {
+            wait_vmem();
+            __syncthreads();
+        }
     }
     pv_tile<D>(smem + L::VBASE + ((ntiles + 1) & 1) * L::VBYTES, P, O, alpha, n, hh);
+    if constexpr (RS) {
+        v4f rs = rowsum_p(ones, P, v4f{}, 0);
+        rs = rowsum_p(ones, P, rs, 1);
+        l = alpha * l + rs[0];
+    }
     // the final P V completes while every lane is active (see attn_mx_kernel)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) consume(O[cb]);
 
     // ---- epilogue: out = O * v_scale / l (l summed over both lane halves)
-    const float lt = pair_sum(l);
+    const float lt = RS ? l : pair_sum(l);
     if (!active || qi >= N) return;
     // the row's log-sum-exp in the exp2 domain: p = 448 * 2^(s - m) makes
-    // 2^(s - lse) = p / l the softmax probability with lse = (m - log2 448) + log2 l
-    if (a.lse && hh == 0) a.lse[(int64_t)bh * N + qi] = (m - kLog2PScale) + log2f(lt);
+    // 2^(s - lse) = p / lx the softmax probability with lse = (m - log2 448) + log2 lx,
+    // lx the row sum of the unquantized p
+    if constexpr (LSE) {
+        const float lxt = pair_sum(lx);
+        if (hh == 0) a.lse[(int64_t)bh * N + qi] = (m - kLog2PScale) + log2f(lxt);
+    }
     store_row<D, SPARSE>(a, O, lt, b, h, bh, qi, hh);
 }
 
@@ -596,8 +929,9 @@ __global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
         softmax_prep<false>(S, F, c, nullptr, m, alpha, mu, needmask, kmax - key_t - 4 * hh, hh);
         const float cf = c == 0.0f ? 1.0f : c;
         float part[4];
+        float xs;
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) part[k4] = softmax_block<false>(F[k4], P, k4, cf, mu);
+        for (int k4 = 0; k4 < 4; ++k4) part[k4] = softmax_block<false, false>(F[k4], P, k4, cf, mu, xs);
         l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
         pv_tile<D>(smem + VB + (t & 1) * L::VBYTES, P, O, alpha, n, hh);
         wait_vmem();
@@ -896,6 +1230,7 @@ static const void* attn_fn_rt(bool causal) {
 template <int D, bool PV16>
 static const void* attn_fn_rt(bool causal, int mode, bool qsm) {
     if (mode == kDump) return attn_fn_rt<D, PV16, kDump, false>(causal);
+    if (mode == kLse) return attn_fn_rt<D, PV16, kLse, false>(causal);
     if (mode == kSparse)
         return qsm ? attn_fn_rt<D, PV16, kSparse, true>(causal) : attn_fn_rt<D, PV16, kSparse, false>(causal);
     return qsm ? attn_fn_rt<D, PV16, kDense, true>(causal) : attn_fn_rt<D, PV16, kDense, false>(causal);
@@ -926,7 +1261,7 @@ static int sparse_waves(int d, int pv16) {
 
 hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal, int dump,
                        hipStream_t s) {
-    const int mode = dump ? kDump : (args.tmask ? kSparse : kDense);
+    const int mode = dump ? kDump : (args.tmask ? kSparse : (args.lse ? kLse : kDense));
     const bool qsm = args.bias != nullptr && !dump;
     const void* fn;
     if (d == 128)
@@ -946,3 +1281,4 @@ hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal,
 }
 
 }  // namespace sage
+

@@ -128,7 +128,7 @@ def test_int8_rounding_ties(sage, orc):
     k = np.concatenate([x[: N // 2], -x[: N // 2]])
     want_q = np.rint(x).astype(np.int8)  # ties to even: 0.5 -> 0, 2.5 -> 2, -3.5 -> -4 ...
     want_k = np.rint(k).astype(np.int8)
-    assert want_q[0, 1:5].tolist() == [0, 2, 2, 4]
+    assert want_q[0, 1:5].tolist() == [2, 2, 4, 0]  # 1.5, 2.5, 3.5, -0.5
     tb = lambda a: torch.from_numpy(a).to(torch.bfloat16).reshape(1, 1, N, d).cuda()
     for gran in ("block", "token"):
         qz = sage.quant_qk(tb(x), tb(k), "HND", q_gran=gran)

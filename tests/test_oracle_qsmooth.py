@@ -159,8 +159,9 @@ def _non_online_bias(orc, z, bias, vq, vs, i, causal, sm_scale, pv):
         mu = np.float32(M - L8)
         p = np.exp2((s - mu).astype(np.float32).astype(np.float64)).astype(np.float32)
         Ms.append(M)
-        Ls.append(p.astype(np.float64).sum())
-        Ts.append(dec(enc(p)).astype(np.float64) @ vdec[t0:t0 + len(St)])
+        pq = dec(enc(p)).astype(np.float64)
+        Ls.append(pq.sum())  # the row sum adds the quantized P the P V product uses
+        Ts.append(pq @ vdec[t0:t0 + len(St)])
     w = np.exp2(np.array(Ms, np.float64) - np.float64(M))
     num = sum(wt * Tt for wt, Tt in zip(w, Ts))
     return num * vs[0, 0] / (w @ np.array(Ls)), M, w @ np.array(Ls)
