@@ -46,16 +46,21 @@ ATTN_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f
                 for f in ("sage_attn.hip", "sage_common.h", "sage_device.h")]
 BWD_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
                for f in ("sage_bwd.hip", "sage_api.hip", "sage_common.h", "sage_device.h")]
+QUANT_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
+                 for f in ("sage_quant.hip", "sage_api.hip", "sage_common.h")]
+# the kernels of one quantization pass (sage_quant_qk + sage_quant_v, FP8 V)
+QUANT_KERNELS = ("kv_stats_kernel", "k_stats_kernel", "k_mean_kernel", "v_stats_kernel",
+                 "v_scale_kernel", "quant_qk_kernel", "quant_v_fp8_kernel", "quant_v_fp16_kernel")
 
 
-def attn_source_hash(bwd=False):
-    """sha256 of the measured kernels' sources (the attention kernel, or the
-    backward's kernels and the workspace carving): HBM byte counts measured
-    on another version of the code are not reported."""
+def attn_source_hash(bwd=False, quant=False):
+    """sha256 of the measured kernels' sources (the attention kernel, the
+    backward's kernels and the workspace carving, or the quantization pass):
+    HBM byte counts measured on another version of the code are not reported."""
     from quantized_attention_video_02_amd import build as sage_build
 
     h = hashlib.sha256()
-    for f in (BWD_SOURCES if bwd else ATTN_SOURCES):
+    for f in (QUANT_SOURCES if quant else BWD_SOURCES if bwd else ATTN_SOURCES):
         with open(f, "rb") as fh:
             h.update(fh.read())
         # a source compiled with extra flags is a different kernel
@@ -426,6 +431,27 @@ def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False,
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     data[traffic_key(workload, "bwd" if bwd else ("mxfp6" if mx else pv), q_gran)] = entry
+    if not bwd and not mx:
+        # the quantization pass of the same runs: all its kernels, per step
+        # (a step launches sage_quant_qk's and sage_quant_v's kernels once)
+        qres = {}
+        for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            rows = per_kernel(d, counter)
+            copy = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]]
+            scale = float(1 << 30) / max(copy)
+            qk = [float(r["Counter_Value"]) * 1024 for r in rows
+                  if any(k in r["Kernel_Name"] for k in QUANT_KERNELS)]
+            steps = sum(1 for r in rows if "quant_qk_kernel" in r["Kernel_Name"])
+            if qk and steps:
+                qres[counter] = (sum(qk) / steps * scale, scale)
+    if not bwd and not mx and len(qres) == 2:
+        qentry = {"kernel": "quantization pass (sage_quant_qk + sage_quant_v: all their kernels)",
+                  "source_hash": attn_source_hash(quant=True),
+                  "fetch_bytes": qres["FETCH_SIZE"][0], "write_bytes": qres["WRITE_SIZE"][0],
+                  "bytes_per_step": qres["FETCH_SIZE"][0] + qres["WRITE_SIZE"][0],
+                  "note": entry["note"]}
+        data[traffic_key(workload, pv, q_gran) + "/quant"] = qentry
+        print(json.dumps(qentry))
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(data, f, indent=1)
     print(json.dumps(entry))
@@ -573,12 +599,16 @@ def main():
     # codes), Q and V once as bf16, the codes written once; the INT8/FP8 path
     # also reads V twice (per-channel scale first): 13 BHNd, MX: 11 BHNd
     qbytes = (11 if args.mx else 13) * bhnd
-    traffic = None
+    traffic, qtraffic = None, None
     if stock and os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f).get(traffic_key(wl.name, fmt, args.q_gran))
+            tdata = json.load(f)
+        t = tdata.get(traffic_key(wl.name, fmt, args.q_gran))
         if t and t.get("source_hash") == attn_source_hash() and not args.q_smooth:
             traffic = t.get("bytes_per_launch")
+        t = tdata.get(traffic_key(wl.name, fmt, args.q_gran) + "/quant")
+        if t and t.get("source_hash") == attn_source_hash(quant=True) and not args.q_smooth:
+            qtraffic = t.get("bytes_per_step")
     res = {
         "metric": METRIC,
         "value": ops * args.steps / wall / 1e12,
@@ -604,7 +634,9 @@ def main():
                      "median_tops": work / (attn_med * 1e-3) / 1e12},
         "quant": {"ms": quant_mean, "bytes_two_pass": qbytes,
                   "gbps_two_pass": qbytes / (quant_mean * 1e-3) / 1e9,
-                  "frac_hbm": qbytes / (quant_mean * 1e-3) / 1e9 / HBM_GBPS},
+                  "frac_hbm": qbytes / (quant_mean * 1e-3) / 1e9 / HBM_GBPS,
+                  "bytes_measured": qtraffic,
+                  "gbps_measured": (qtraffic / (quant_mean * 1e-3) / 1e9) if qtraffic else None},
     }
     if args.q_smooth or args.q_sigma is not None:
         res["config"]["q_smooth"] = bool(args.q_smooth)
@@ -622,10 +654,16 @@ def main():
         res["config"]["value_is"] = "dense-equivalent (4 B H N^2 d / s) of a block-sparse run"
         res["roofline"]["traffic"] = None
     if wl.causal and tmask is None:
-        # the formula above counts every (query, key) pair; the causal mask keeps N(N+1)/2
+        # `value` keeps the metric's formula over every (query, key) pair; the
+        # kernel computes only the N(N+1)/2 pairs the causal mask keeps (and
+        # skips the tiles above the diagonal), so the roofline counts those
         useful = 4.0 * wl.B * wl.H * wl.d * wl.N * (wl.N + 1) / 2
-        res["roofline"]["useful_causal_ops_per_launch"] = useful
-        res["roofline"]["useful_causal_tops"] = useful / (attn_mean * 1e-3) / 1e12
+        res["roofline"]["all_pairs_tops"] = achieved
+        achieved = useful / (attn_mean * 1e-3) / 1e12
+        res["roofline"].update({"achieved": achieved, "frac": achieved / peak,
+                                "ops_per_launch": useful,
+                                "median_tops": useful / (attn_med * 1e-3) / 1e12,
+                                "ops_counted": "causal pairs (key <= query)"})
     if not args.mx and args.pv == "fp8":
         # this board's own matrix-core rates, measured after the timed steps:
         # the kernel does half its work on each, so the blend is its peak here

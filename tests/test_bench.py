@@ -47,6 +47,27 @@ def test_record_traffic_scales_by_the_copy_and_tags_the_source(tmp_path, monkeyp
     assert e["source_hash"] == bench.attn_source_hash()
 
 
+def test_record_traffic_of_the_quantization_pass_per_step(tmp_path, monkeypatch):
+    """The quantization kernels of the same counter runs: their bytes summed
+    per step (one quant_qk_kernel launch per step), scaled by the copy."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    gib_kib = (1 << 30) / 1024
+    attn = "void sage::attn_fwd_kernel<128, false, false, 0, false>(sage::AttnArgs)"
+    quant = [("void sage::kv_stats_kernel<128>(...)", 100.0), ("sage::k_mean_kernel", 1.0),
+             ("void sage::quant_qk_kernel<128, false>(...)", 200.0),
+             ("void sage::quant_v_fp8_kernel<128>(...)", 50.0)]
+    _write_counters(tmp_path / "f", "FETCH_SIZE",
+                    [("__amd_rocclr_copyBuffer", gib_kib / 2), (attn, 10.0)] + quant + quant)
+    _write_counters(tmp_path / "w", "WRITE_SIZE",
+                    [("__amd_rocclr_copyBuffer", gib_kib), (attn, 5.0)] + quant)
+    bench.record_traffic("video_14b_720p", "fp8", str(tmp_path / "f"), str(tmp_path / "w"))
+    e = json.load(open(tmp_path / "traffic.json"))["video_14b_720p/fp8/quant"]
+    assert e["fetch_bytes"] == pytest.approx(351.0 * 1024 * 2.0)  # two steps, mean
+    assert e["write_bytes"] == pytest.approx(351.0 * 1024)
+    assert e["bytes_per_step"] == pytest.approx(e["fetch_bytes"] + e["write_bytes"])
+    assert e["source_hash"] == bench.attn_source_hash(quant=True)
+
+
 def test_record_traffic_refuses_runs_without_the_copy(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     _write_counters(tmp_path / "f", "FETCH_SIZE", [("void sage::attn_fwd_kernel<128>", 1.0)])
@@ -251,4 +272,4 @@ def test_bench_shape_override_and_no_causal():
     cfg = line["config"]
     assert (cfg["B"], cfg["H"], cfg["N"], cfg["causal"]) == (1, 2, 1000, False)
     assert line["roofline"]["traffic"] is None
-    assert "useful_causal_tops" not in line["roofline"]
+    assert "ops_counted" not in line["roofline"]
