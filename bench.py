@@ -2,9 +2,10 @@
 """Benchmark of libsage on one MI355X.
 
 One step = the whole hot path over one batch of synthetic input already
-resident in HBM: sage_quant_qk (K smoothing + per-block INT8 Q/K),
-sage_quant_v (per-channel FP8 V) and sage_attn_fwd (fused INT8-QK / FP8-PV
-attention), enqueued on one stream.  The headline workload is the 720p clip
+resident in HBM: sage_quant_qkv (K smoothing + per-block INT8 Q/K and
+per-channel FP8 V, the K and V statistics in one launch) and sage_attn_fwd
+(fused INT8-QK / FP8-PV attention), enqueued on one stream.  Per-token Q
+scales and Q smoothing go through sage_quant_qk(_ex/_smooth) + sage_quant_v.  The headline workload is the 720p clip
 of a 14B video DiT: B=1, H=40, N=75600 (21 x 45 x 80 latent tokens), d=128.
 
 --mx runs the microscaled path instead: sage_quant_qk_mx, sage_quant_v_mx and
@@ -48,9 +49,10 @@ BWD_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
                for f in ("sage_bwd.hip", "sage_api.hip", "sage_common.h", "sage_device.h")]
 QUANT_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
                  for f in ("sage_quant.hip", "sage_api.hip", "sage_common.h")]
-# the kernels of one quantization pass (sage_quant_qk + sage_quant_v, FP8 V)
-QUANT_KERNELS = ("kv_stats_kernel", "k_stats_kernel", "k_mean_kernel", "v_stats_kernel",
-                 "v_scale_kernel", "quant_qk_kernel", "quant_v_fp8_kernel", "quant_v_fp16_kernel")
+# the kernels of one quantization pass (sage_quant_qkv, or sage_quant_qk + sage_quant_v)
+QUANT_KERNELS = ("kv_stats_kernel", "kv_combine_kernel", "k_stats_kernel", "k_mean_kernel",
+                 "v_stats_kernel", "v_scale_kernel", "quant_qk_kernel", "quant_v_fp8_kernel",
+                 "quant_v_fp16_kernel")
 
 
 def attn_source_hash(bwd=False, quant=False):
@@ -117,6 +119,8 @@ def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None, q_smoo
             evs[0].record(stream)
         if mx:
             mz, v6 = sage.quant_qk_mx(q, k), sage.quant_v_mx(v)
+        elif q_gran == "block" and not q_smooth:
+            qz, vq, vs = sage.quant_qkv(q, k, v, pv)
         else:
             qz = sage.quant_qk(q, k, q_gran=q_gran, q_smooth=q_smooth, sm_scale=wl.sm_scale)
             vq, vs = sage.quant_v(v, pv)
@@ -433,7 +437,7 @@ def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False,
     data[traffic_key(workload, "bwd" if bwd else ("mxfp6" if mx else pv), q_gran)] = entry
     if not bwd and not mx:
         # the quantization pass of the same runs: all its kernels, per step
-        # (a step launches sage_quant_qk's and sage_quant_v's kernels once)
+        # (a step launches the quantization kernels once: one quant_qk_kernel)
         qres = {}
         for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
             rows = per_kernel(d, counter)
@@ -445,7 +449,7 @@ def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False,
             if qk and steps:
                 qres[counter] = (sum(qk) / steps * scale, scale)
     if not bwd and not mx and len(qres) == 2:
-        qentry = {"kernel": "quantization pass (sage_quant_qk + sage_quant_v: all their kernels)",
+        qentry = {"kernel": "quantization pass (sage_quant_qkv: all its kernels)",
                   "source_hash": attn_source_hash(quant=True),
                   "fetch_bytes": qres["FETCH_SIZE"][0], "write_bytes": qres["WRITE_SIZE"][0],
                   "bytes_per_step": qres["FETCH_SIZE"][0] + qres["WRITE_SIZE"][0],

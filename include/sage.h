@@ -178,6 +178,22 @@ int sage_quant_v(const void* v, int B, int H, int N, int d, int layout, int pv_d
                  void* stream);
 
 /*
+ * One quantization pass over Q, K and V: exactly sage_quant_qk followed by
+ * sage_quant_v (the same codes, scales and k_mean, bit for bit), with the K
+ * and V column statistics taken in one launch and combined in one more
+ * (wxsanhe §三.1: Q K to INT8 with K smoothing, P V in FP8 or FP16).
+ * Buffers and layouts as in those two calls (sizes from sage_quant_sizes with
+ * pv_dtype).  workspace: sizes[SAGE_BUF_WS_QK] + sizes[SAGE_BUF_WS_V] bytes
+ * of device scratch (no initialisation needed; contents undefined on return).
+ * Errors as sage_quant_qk and sage_quant_v; SAGE_ERR_WORKSPACE if workspace
+ * is smaller than that sum.
+ */
+int sage_quant_qkv(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                   int layout, int pv_dtype, int8_t* q8, float* q_scale, int8_t* k8,
+                   float* k_scale, float* k_mean, void* vq, float* v_scale, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
  * Fused attention over the quantized operands (hunxia glossary, FlashAttention:
  * tiled, online softmax; wxsanhe §三.1: FP8 P V with FP32 accumulation).
  * For each query i (with sigma = fp32(q_scale * lambda), lambda =

@@ -43,7 +43,7 @@ class SageConfig(ct.Structure):
 
 
 EXPORTS = ["sage_get_config", "sage_quant_sizes", "sage_quant_sizes_ex", "sage_quant_qk",
-           "sage_quant_qk_ex", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse", "sage_attn_fwd_ex",
+           "sage_quant_qk_ex", "sage_quant_v", "sage_quant_qkv", "sage_attn_fwd", "sage_attn_fwd_lse", "sage_attn_fwd_ex",
            "sage_attn_fwd_sparse", "sage_attn_fwd_debug", "sage_qsmooth_sizes",
            "sage_quant_qk_smooth", "sage_q_smooth_bias", "sage_attn_fwd_smooth",
            "sage_quant_qk_mx", "sage_quant_v_mx", "sage_attn_fwd_mx", "sage_bwd_sizes",
@@ -68,6 +68,7 @@ def lib():
     L.sage_quant_qk.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, S, P]
     L.sage_quant_qk_ex.argtypes = [P, P, I, I, I, I, I, I, P, P, P, P, P, P, S, P]
     L.sage_quant_v.argtypes = [P, I, I, I, I, I, I, P, P, P, S, P]
+    L.sage_quant_qkv.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, S, P]
     L.sage_attn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
     L.sage_attn_fwd_lse.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P, P]
     L.sage_attn_fwd_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, I, P]
@@ -221,6 +222,36 @@ def quant_v(v: torch.Tensor, pv: str = "fp8", layout: str = "HND"):
     _check(lib().sage_quant_v(_ptr(v), B, H, N, d, LAYOUTS[layout], PV[pv], _ptr(vq), _ptr(vs),
                               _ptr(ws), sz[BUF_WS_V], _stream(dev)))
     return vq, vs
+
+
+def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pv: str = "fp8",
+              layout: str = "HND") -> tuple[dict, torch.Tensor, torch.Tensor]:
+    """One quantization pass over Q, K and V (sage_quant_qkv): returns
+    (qz, vq, v_scale), the same results as quant_qk(q, k) and quant_v(v, pv),
+    with the K and V statistics taken in one launch."""
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
+        raise TypeError("q, k and v must be bfloat16")
+    if not (q.shape == k.shape == v.shape) or not all(t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k and v must be contiguous and of the same shape")
+    B, H, N, d = _dims(q, layout)
+    dev = _one_gpu(q, k, v)
+    sz = quant_sizes(B, H, N, d, pv)
+    nblk = -(-N // 128)
+    r = dict(q8=torch.empty((B, H, nblk * 128, d), dtype=torch.int8, device=dev),
+             q_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+             k8=torch.empty((B, H, nblk * 128, d), dtype=torch.int8, device=dev),
+             k_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+             k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev),
+             workspace=_empty(sz[BUF_WS_QK] + sz[BUF_WS_V], dev, torch.int64))
+    vq = torch.empty((B, H, nblk, d, 128), dtype=torch.uint8 if pv == "fp8" else torch.float16,
+                     device=dev)
+    vs = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    _check(lib().sage_quant_qkv(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, LAYOUTS[layout], PV[pv],
+                                _ptr(r["q8"]), _ptr(r["q_scale"]), _ptr(r["k8"]),
+                                _ptr(r["k_scale"]), _ptr(r["k_mean"]), _ptr(vq), _ptr(vs),
+                                _ptr(r["workspace"]), sz[BUF_WS_QK] + sz[BUF_WS_V], _stream(dev)))
+    r.update(B=B, H=H, N=N, d=d, layout=layout, q_gran="block")
+    return r, vq, vs
 
 
 def attn_fwd(qz: dict, vq: torch.Tensor, vs: torch.Tensor, causal: bool = False,

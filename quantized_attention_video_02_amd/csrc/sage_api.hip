@@ -268,6 +268,31 @@ __attribute__((visibility("default"))) int sage_quant_v(const void* v, int B, in
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
+__attribute__((visibility("default"))) int sage_quant_qkv(
+    const void* q, const void* k, const void* v, int B, int H, int N, int d, int layout,
+    int pv_dtype, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, float* k_mean, void* vq,
+    float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !q8 || !q_scale || !k8 || !k_scale || !k_mean || !vq || !v_scale ||
+        !workspace)
+        return SAGE_ERR_NULL;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_layout(layout));
+    SAGE_TRY(check_pv(pv_dtype));
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(q_scale) ||
+        !aligned16(k8) || !aligned16(k_scale) || !aligned16(k_mean) || !aligned16(vq) ||
+        !aligned16(v_scale) || !aligned16(workspace))
+        return SAGE_ERR_ALIGN;
+    const Sizes s = sizes_of(B, H, N, d, pv_dtype);
+    if (workspace_bytes < s.v[SAGE_BUF_WS_QK] + s.v[SAGE_BUF_WS_V]) return SAGE_ERR_WORKSPACE;
+    uint64_t* kws = (uint64_t*)workspace;
+    float* vws = (float*)((char*)workspace + s.v[SAGE_BUF_WS_QK]);
+    const hipError_t e = sage::launch_quant_qkv(
+        (const sage::u16*)q, (const sage::u16*)k, (const sage::u16*)v, B, H, N, d, layout,
+        pv_dtype == SAGE_PV_FP16, q8, q_scale, k8, k_scale, k_mean, vq, v_scale, kws, vws,
+        (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
 __attribute__((visibility("default"))) int sage_attn_fwd(
     const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
     const void* vq, const float* v_scale, int B, int H, int N, int d, int layout, int causal,

@@ -120,6 +120,10 @@ hipError_t launch_quant_v_mx(const u16* v, int B, int H, int N, int d, int layou
 hipError_t launch_attn_mx(const AttnArgs& args, int B, int d, int causal, hipStream_t s);
 hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, int pv16,
                           void* vq, float* vscale, float* ws, hipStream_t s);
+hipError_t launch_quant_qkv(const u16* q, const u16* k, const u16* v, int B, int H, int N, int d,
+                            int layout, int pv16, int8_t* q8, float* qs, int8_t* k8, float* ks,
+                            float* kmean, void* vq, float* vscale, uint64_t* kws, float* vws,
+                            hipStream_t s);
 hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal, int dump,
                        hipStream_t s);
 hipError_t launch_attn_bwd(const BwdPrep& pp, const BwdArgs& args, int B, int d, int causal,

@@ -39,13 +39,14 @@ __device__ inline uint64_t fix30_bf16(uint32_t u) {
     return neg ? (0ull - mag) : mag;
 }
 
+// Workgroup body of the K statistics: chunk blockIdx.x of head blockIdx.y;
+// red is the workgroup's LDS reduction buffer.
 template <int D>
-__global__ __launch_bounds__(kQuantThreads) void k_stats_kernel(const u16* __restrict__ k, int H,
-                                                                int N, int layout, int nchunk,
-                                                                uint64_t* __restrict__ part) {
+__device__ inline void k_stats_body(const u16* __restrict__ k, int H, int N, int layout,
+                                    int nchunk, uint64_t* __restrict__ part,
+                                    uint64_t (*red)[D]) {
     constexpr int CPR = D / 8;                  // 16-byte chunks per row
     constexpr int RPI = kQuantThreads / CPR;    // rows per pass
-    __shared__ uint64_t red[RPI][D];
     const int chunk = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
     const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
     const int n0 = chunk * kStatsChunk, n1 = min(N, n0 + kStatsChunk);
@@ -96,15 +97,21 @@ __global__ __launch_bounds__(kQuantThreads) void k_stats_kernel(const u16* __res
     }
 }
 
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void k_stats_kernel(const u16* __restrict__ k, int H,
+                                                                int N, int layout, int nchunk,
+                                                                uint64_t* __restrict__ part) {
+    __shared__ uint64_t red[kQuantThreads / (D / 8)][D];
+    k_stats_body<D>(k, H, N, layout, nchunk, part, red);
+}
+
 // Combination kernels: workgroup (b*h, group of 32 channels), 256 threads =
 // 32 channels x 8 chunk lanes; lane j adds chunks j, j + 8, ... (coalesced
 // across the 32 channels), then the 8 lane results are combined in LDS.
 constexpr int kCombCh = 32, kCombLanes = kQuantThreads / kCombCh;
 
-__global__ __launch_bounds__(kQuantThreads) void k_mean_kernel(const uint64_t* __restrict__ part,
-                                                               int nchunk, int D, int N,
-                                                               float* __restrict__ mean) {
-    __shared__ uint64_t red[kCombLanes][kCombCh];
+__device__ inline void k_mean_body(const uint64_t* __restrict__ part, int nchunk, int D, int N,
+                                   float* __restrict__ mean, uint64_t (*red)[kCombCh]) {
     const int bh = blockIdx.x, c = blockIdx.y * kCombCh + threadIdx.x % kCombCh;
     const int j = threadIdx.x / kCombCh;
     uint64_t s = 0;
@@ -118,13 +125,18 @@ __global__ __launch_bounds__(kQuantThreads) void k_mean_kernel(const uint64_t* _
     }
 }
 
+__global__ __launch_bounds__(kQuantThreads) void k_mean_kernel(const uint64_t* __restrict__ part,
+                                                               int nchunk, int D, int N,
+                                                               float* __restrict__ mean) {
+    __shared__ uint64_t red[kCombLanes][kCombCh];
+    k_mean_body(part, nchunk, D, N, mean, red);
+}
+
 template <int D>
-__global__ __launch_bounds__(kQuantThreads) void v_stats_kernel(const u16* __restrict__ v, int H,
-                                                                int N, int layout, int nchunk,
-                                                                float* __restrict__ part) {
+__device__ inline void v_stats_body(const u16* __restrict__ v, int H, int N, int layout,
+                                    int nchunk, float* __restrict__ part, float (*red)[D]) {
     constexpr int CPR = D / 8;
     constexpr int RPI = kQuantThreads / CPR;
-    __shared__ float red[RPI][D];
     const int chunk = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
     const int t = threadIdx.x, cg = t % CPR, tr = t / CPR;
     const int n0 = chunk * kStatsChunk, n1 = min(N, n0 + kStatsChunk);
@@ -151,12 +163,18 @@ __global__ __launch_bounds__(kQuantThreads) void v_stats_kernel(const u16* __res
     }
 }
 
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void v_stats_kernel(const u16* __restrict__ v, int H,
+                                                                int N, int layout, int nchunk,
+                                                                float* __restrict__ part) {
+    __shared__ float red[kQuantThreads / (D / 8)][D];
+    v_stats_body<D>(v, H, N, layout, nchunk, part, red);
+}
+
 // v_scale = fp32(a / 448); inv = fp32(448 / a) (0 for a == 0), both via fp64.
-__global__ __launch_bounds__(kQuantThreads) void v_scale_kernel(const float* __restrict__ part,
-                                                                int nchunk, int D,
-                                                                float* __restrict__ v_scale,
-                                                                float* __restrict__ v_inv) {
-    __shared__ float red[kCombLanes][kCombCh];
+__device__ inline void v_scale_body(const float* __restrict__ part, int nchunk, int D,
+                                    float* __restrict__ v_scale, float* __restrict__ v_inv,
+                                    float (*red)[kCombCh]) {
     const int bh = blockIdx.x, c = blockIdx.y * kCombCh + threadIdx.x % kCombCh;
     const int j = threadIdx.x / kCombCh;
     float a = 0.0f;
@@ -171,6 +189,41 @@ __global__ __launch_bounds__(kQuantThreads) void v_scale_kernel(const float* __r
         v_scale[i] = (float)((double)a / 448.0);
         v_inv[i] = a > 0.0f ? (float)(448.0 / (double)a) : 0.0f;
     }
+}
+
+__global__ __launch_bounds__(kQuantThreads) void v_scale_kernel(const float* __restrict__ part,
+                                                                int nchunk, int D,
+                                                                float* __restrict__ v_scale,
+                                                                float* __restrict__ v_inv) {
+    __shared__ float red[kCombLanes][kCombCh];
+    v_scale_body(part, nchunk, D, v_scale, v_inv, red);
+}
+
+// The K and V statistics of one quantization pass in one launch: grid
+// (nchunk, B*H, 2), blockIdx.z 0 the K sums, 1 the V absmax.  The two share
+// one LDS buffer (a workgroup runs only one of them).
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void kv_stats_kernel(
+    const u16* __restrict__ k, const u16* __restrict__ v, int H, int N, int layout, int nchunk,
+    uint64_t* __restrict__ kpart, float* __restrict__ vpart) {
+    constexpr int RPI = kQuantThreads / (D / 8);
+    __shared__ uint64_t red[RPI][D];
+    if (blockIdx.z == 0)
+        k_stats_body<D>(k, H, N, layout, nchunk, kpart, red);
+    else
+        v_stats_body<D>(v, H, N, layout, nchunk, vpart, reinterpret_cast<float(*)[D]>(&red[0][0]));
+}
+
+// k_mean (blockIdx.z 0) and v_scale (1) in one launch: grid (B*H, D/32, 2).
+__global__ __launch_bounds__(kQuantThreads) void kv_combine_kernel(
+    const uint64_t* __restrict__ kpart, const float* __restrict__ vpart, int nchunk, int D, int N,
+    float* __restrict__ kmean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
+    __shared__ uint64_t red[kCombLanes][kCombCh];
+    if (blockIdx.z == 0)
+        k_mean_body(kpart, nchunk, D, N, kmean, red);
+    else
+        v_scale_body(vpart, nchunk, D, v_scale, v_inv,
+                     reinterpret_cast<float(*)[kCombCh]>(&red[0][0]));
 }
 
 // trunc(x * 2^30) saturated at +-2^62, NaN -> 0 (the grid of the K mean), for
@@ -634,6 +687,40 @@ static inline hipError_t launch(const void* fn, dim3 grid, dim3 block, void** ar
     return hipLaunchKernel(fn, grid, block, args, 0, s);
 }
 
+// INT8 codes and scales of Q and smoothed K, once k_mean is in place.
+static hipError_t launch_qk_codes(const u16* q, const u16* k, int B, int H, int N, int d,
+                                  int layout, int qtok, int8_t* q8, float* qs, int8_t* k8,
+                                  float* ks, const float* kmean, float* qmean, hipStream_t s) {
+    int nblk = (N + kBlk - 1) / kBlk, N_pad = nblk * kBlk;
+    void* args[] = {(void*)&q,      (void*)&k,    (void*)&H,     (void*)&N,
+                    (void*)&N_pad,  (void*)&nblk, (void*)&layout, (void*)&qtok,
+                    (void*)&kmean,  (void*)&q8,   (void*)&qs,     (void*)&k8,
+                    (void*)&ks,     (void*)&qmean};
+    const void* fn = qmean ? (d == 128 ? (const void*)quant_qk_kernel<128, true>
+                                       : (const void*)quant_qk_kernel<64, true>)
+                           : (d == 128 ? (const void*)quant_qk_kernel<128, false>
+                                       : (const void*)quant_qk_kernel<64, false>);
+    return launch(fn, dim3(nblk, B * H, 2), dim3(kQuantThreads), args, s);
+}
+
+// FP8 (or FP16) codes of V, once v_inv is in place (FP8 only).
+static hipError_t launch_v_codes(const u16* v, int B, int H, int N, int d, int layout, int pv16,
+                                 const float* vinv, void* vq, float* vscale, hipStream_t s) {
+    int nblk = (N + kBc - 1) / kBc;
+    if (pv16) {
+        void* args[] = {(void*)&v, (void*)&H, (void*)&N, (void*)&nblk, (void*)&layout, (void*)&vq,
+                        (void*)&vscale};
+        const void* fn = d == 128 ? (const void*)quant_v_fp16_kernel<128>
+                                  : (const void*)quant_v_fp16_kernel<64>;
+        return launch(fn, dim3(nblk, B * H), dim3(kQuantThreads), args, s);
+    }
+    void* args[] = {(void*)&v, (void*)&H, (void*)&N, (void*)&nblk, (void*)&layout, (void*)&vinv,
+                    (void*)&vq};
+    const void* fn = d == 128 ? (const void*)quant_v_fp8_kernel<128>
+                              : (const void*)quant_v_fp8_kernel<64>;
+    return launch(fn, dim3(nblk, B * H), dim3(kQuantThreads), args, s);
+}
+
 hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
                            int qtok, int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean,
                            float* qmean, uint64_t* ws, hipStream_t s) {
@@ -652,18 +739,7 @@ hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int 
                         s)) != hipSuccess)
             return e;
     }
-    {
-        void* args[] = {(void*)&q,      (void*)&k,    (void*)&H,     (void*)&N,
-                        (void*)&N_pad,  (void*)&nblk, (void*)&layout, (void*)&qtok,
-                        (void*)&kmean,  (void*)&q8,   (void*)&qs,     (void*)&k8,
-                        (void*)&ks,     (void*)&qmean};
-        const void* fn = qmean ? (d == 128 ? (const void*)quant_qk_kernel<128, true>
-                                           : (const void*)quant_qk_kernel<64, true>)
-                               : (d == 128 ? (const void*)quant_qk_kernel<128, false>
-                                           : (const void*)quant_qk_kernel<64, false>);
-        if ((e = launch(fn, dim3(nblk, BH, 2), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return launch_qk_codes(q, k, B, H, N, d, layout, qtok, q8, qs, k8, ks, kmean, qmean, s);
 }
 
 hipError_t launch_q_bias(const float* qmean, const u16* k, const float* kmean, int B, int H, int N,
@@ -717,13 +793,7 @@ hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, 
     const int nchunk = (N + kStatsChunk - 1) / kStatsChunk;
     const int BH = B * H;
     hipError_t e;
-    if (pv16) {
-        void* args[] = {(void*)&v, (void*)&H, (void*)&N, (void*)&nblk, (void*)&layout, (void*)&vq,
-                        (void*)&vscale};
-        const void* fn = d == 128 ? (const void*)quant_v_fp16_kernel<128>
-                                  : (const void*)quant_v_fp16_kernel<64>;
-        return launch(fn, dim3(nblk, BH), dim3(kQuantThreads), args, s);
-    }
+    if (pv16) return launch_v_codes(v, B, H, N, d, layout, 1, nullptr, vq, vscale, s);
     float* part = ws;
     float* vinv = ws + (size_t)BH * nchunk * d;
     {
@@ -737,14 +807,40 @@ hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, 
                         s)) != hipSuccess)
             return e;
     }
+    return launch_v_codes(v, B, H, N, d, layout, 0, vinv, vq, vscale, s);
+}
+
+// One quantization pass over Q, K and V: the K and V statistics in one launch
+// and their combinations in one more (FP8 V; FP16 V needs no statistics),
+// then the Q/K and V codes.  kws: B*H*nchunk*d uint64 K partials; vws:
+// B*H*nchunk*d float V partials followed by B*H*d floats of v_inv (FP8 only).
+hipError_t launch_quant_qkv(const u16* q, const u16* k, const u16* v, int B, int H, int N, int d,
+                            int layout, int pv16, int8_t* q8, float* qs, int8_t* k8, float* ks,
+                            float* kmean, void* vq, float* vscale, uint64_t* kws, float* vws,
+                            hipStream_t s) {
+    int nchunk = (N + kStatsChunk - 1) / kStatsChunk;
+    const int BH = B * H;
+    float* vinv = vws + (size_t)BH * nchunk * d;
+    hipError_t e;
     {
-        void* args[] = {(void*)&v, (void*)&H, (void*)&N, (void*)&nblk, (void*)&layout, (void*)&vinv,
-                        (void*)&vq};
-        const void* fn = d == 128 ? (const void*)quant_v_fp8_kernel<128>
-                                  : (const void*)quant_v_fp8_kernel<64>;
-        if ((e = launch(fn, dim3(nblk, BH), dim3(kQuantThreads), args, s)) != hipSuccess) return e;
+        void* args[] = {(void*)&k,      (void*)&v,      (void*)&H,   (void*)&N,
+                        (void*)&layout, (void*)&nchunk, (void*)&kws, (void*)&vws};
+        const void* fn = d == 128 ? (const void*)kv_stats_kernel<128> : (const void*)kv_stats_kernel<64>;
+        if ((e = launch(fn, dim3(nchunk, BH, pv16 ? 1 : 2), dim3(kQuantThreads), args, s)) !=
+            hipSuccess)
+            return e;
     }
-    return hipSuccess;
+    {
+        void* args[] = {(void*)&kws, (void*)&vws,    (void*)&nchunk, (void*)&d,
+                        (void*)&N,   (void*)&kmean, (void*)&vscale, (void*)&vinv};
+        if ((e = launch((const void*)kv_combine_kernel, dim3(BH, d / kCombCh, pv16 ? 1 : 2),
+                        dim3(kQuantThreads), args, s)) != hipSuccess)
+            return e;
+    }
+    if ((e = launch_qk_codes(q, k, B, H, N, d, layout, 0, q8, qs, k8, ks, kmean, nullptr, s)) !=
+        hipSuccess)
+        return e;
+    return launch_v_codes(v, B, H, N, d, layout, pv16, vinv, vq, vscale, s);
 }
 
 }  // namespace sage

@@ -115,6 +115,18 @@ def test_invalid_arguments_rejected_before_launch(sage):
     assert qv(ws=None) == -1
     assert qv(wsb=8) == -7
     assert qv(v=A + 4) == -4
+    sz1 = (ct.c_size_t * 9)()
+    assert L.sage_quant_sizes(1, 1, 256, 128, 0, sz1) == 0
+    need = sz1[7] + sz1[8]
+    qkv = lambda v=A, pv=0, ws=A, wsb=need, N=256, vq=A: L.sage_quant_qkv(
+        A, A, v, 1, 1, N, 128, 0, pv, A, A, A, A, A, vq, A, ws, wsb, None)
+    assert qkv(v=None) == -1
+    assert qkv(ws=None) == -1
+    assert qkv(pv=2) == -2
+    assert qkv(N=0) == -2
+    assert qkv(vq=A + 2) == -4
+    assert qkv(wsb=need - 1) == -7
+    assert qkv(wsb=sz1[7]) == -7  # the V partials need room too
     fwd = lambda causal=0, sm=0.1, pv=0, od=0, out=A, N=256, lay=0: L.sage_attn_fwd(
         A, A, A, A, A, A, 1, 2, N, 128, lay, causal, sm, pv, out, od, None)
     assert fwd(out=None) == -1

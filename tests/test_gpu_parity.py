@@ -114,6 +114,31 @@ def test_quantization_bitexact(sage, orc, name, kw, pv, layout):
     assert not pad[:, :, -1][..., vperm_positions()[tail:]].any()  # padded keys are 0
 
 
+FUSED_CASES = QUANT_CASES + [("outlier", dict(N=700, B=1, H=3), "fp8", "HND"),  # d = 64
+                             ("outlier", dict(N=700, B=1, H=3), "fp16", "NHD")]
+
+
+@pytest.mark.parametrize("name,kw,pv,layout", FUSED_CASES)
+def test_fused_quantization_pass_bitexact(sage, orc, name, kw, pv, layout):
+    """sage_quant_qkv (K and V statistics in one launch) gives the oracle's
+    codes, scales and K mean bit for bit, and the same bytes as
+    sage_quant_qk + sage_quant_v, padding included."""
+    wl = si.make(name, **kw)
+    qd, kd, vd = (_to_layout(t, layout).cuda() for t in (wl.q, wl.k, wl.v))
+    qz, vq, vs = sage.quant_qkv(qd, kd, vd, pv, layout)
+    torch.cuda.synchronize()
+    g = gpu_quant_np(qz, vq, vs, wl.N, pv)
+    _, _, _, oz, ovq, ovs = oracle_quant(orc, wl, pv)
+    assert_quant_bitexact(g, oz, ovq, ovs, wl.N)
+    qz2 = sage.quant_qk(qd, kd, layout)
+    vq2, vs2 = sage.quant_v(vd, pv, layout)
+    torch.cuda.synchronize()
+    for key in ("q8", "q_scale", "k8", "k_scale", "k_mean"):
+        assert torch.equal(qz[key].view(torch.uint8), qz2[key].view(torch.uint8)), key
+    assert torch.equal(vq.view(torch.uint8), vq2.view(torch.uint8))
+    assert torch.equal(vs.view(torch.int32), vs2.view(torch.int32))
+
+
 def test_int8_rounding_ties(sage, orc):
     """Q and K blocks whose scaled values sit exactly on k + 1/2: the codes are
     round-half-to-even of the value (absmax 127, so the inverse scale is 1),
@@ -565,10 +590,12 @@ def test_k_mean_exact_with_large_and_special_values(sage, orc):
         k[0, i % 2, r, rng.integers(0, 128, 3)] = specials[i % len(specials)]
     kt = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).cuda()
     qz = sage.quant_qk(wl.q.cuda(), kt)
+    fz, _, _ = sage.quant_qkv(wl.q.cuda(), kt, wl.v.cuda())
     torch.cuda.synchronize()
-    got = qz["k_mean"].cpu().numpy()
     ref = np.stack([orc.k_mean_head(k[0, h]) for h in range(2)])[None]
-    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    for z in (qz, fz):
+        got = z["k_mean"].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
 @pytest.mark.parametrize("pv", ["fp8", "fp16"])
