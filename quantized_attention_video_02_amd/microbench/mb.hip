@@ -1,6 +1,8 @@
 // Microbenchmarks of the MI355X (gfx950) units the attention kernels are
 // bound by: the dense matrix-core rate for INT8, FP8 and FP16 MFMAs, and the
-// v_exp_f32 rate.  Register-only kernels: each wave runs eight independent
+// v_exp_f32 rate; and two premise checks of the hardware behaviour the
+// attention kernels rely on (FP8 matrix-core accumulation, the fp32 -> e4m3
+// convert).  The timing kernels are register-only: each wave runs eight independent
 // accumulation chains (so the matrix core never waits on a result), and one
 // float per thread is stored at the end so nothing is optimised away.
 #include <hip/hip_runtime.h>
@@ -12,6 +14,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kChains = 8;
@@ -87,9 +90,84 @@ __global__ __launch_bounds__(256) void mb_exp(int iters, float* out) {
     out[blockIdx.x * blockDim.x + t] = s;
 }
 
+// Premise checks (not timings).  One wave per problem: D = A B + C on the FP8
+// matrix core with the attention kernels' call form (e4m3 operands, no block
+// scales), shape 0 the 32x32x64 instruction, 1 the 16x16x128 one.  Operands
+// are register images: A and B 8 dwords per lane, C and D 16 (shape 0) or 4
+// (shape 1) floats per lane, lane-major, one image per problem.
+__global__ __launch_bounds__(64) void mb_f8_mfma_k(int shape, const int* __restrict__ A,
+                                                   const int* __restrict__ B,
+                                                   const float* __restrict__ C,
+                                                   float* __restrict__ D) {
+    const int l = threadIdx.x, pb = blockIdx.x;
+    v8i a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = A[(pb * 64 + l) * 8 + e];
+        b[e] = B[(pb * 64 + l) * 8 + e];
+    }
+    if (shape == 0) {
+        v16f c;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[r] = C[(pb * 64 + l) * 16 + r];
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) D[(pb * 64 + l) * 16 + r] = c[r];
+    } else {
+        v4f c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c[r] = C[(pb * 64 + l) * 4 + r];
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) D[(pb * 64 + l) * 4 + r] = c[r];
+    }
+}
+
+// The packed fp32 -> e4m3 convert in the attention kernels' call form (no
+// clamp; two calls fill the low then the high half of a dword): thread i
+// converts the fp32 bit patterns first + 4i .. first + 4i + 3.
+__global__ __launch_bounds__(256) void mb_cvt_e4m3_k(uint32_t first, uint32_t nquad,
+                                                     uint32_t* __restrict__ out) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= nquad) return;
+    const uint32_t u = first + 4u * i;
+    const float x0 = __uint_as_float(u), x1 = __uint_as_float(u + 1), x2 = __uint_as_float(u + 2),
+                x3 = __uint_as_float(u + 3);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+    out[i] = (uint32_t)w;
+}
+
 }  // namespace
 
 extern "C" {
+
+// D = A B + C for nprob independent problems on the FP8 matrix core (see
+// mb_f8_mfma_k for the operand images; all device pointers).  Returns 0, or
+// -1 for a bad argument / launch failure.
+__attribute__((visibility("default"))) int mb_f8_mfma(int shape, int nprob, const int* A,
+                                                      const int* B, const float* C, float* D,
+                                                      void* stream) {
+    if (!A || !B || !C || !D || (shape != 0 && shape != 1) || nprob < 1 || nprob > 65535)
+        return -1;
+    hipLaunchKernelGGL(mb_f8_mfma_k, dim3(nprob), dim3(64), 0, (hipStream_t)stream, shape, A, B,
+                       C, D);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// out[j] = e4m3 code of the fp32 bit pattern first + j, j < count (device
+// uint8 buffer of count bytes, 4-byte aligned).  count: a multiple of 4 with
+// first + count <= 2^32.  Returns 0 or -1.
+__attribute__((visibility("default"))) int mb_cvt_e4m3(uint32_t first, uint64_t count, void* out,
+                                                       void* stream) {
+    if (!out || ((uintptr_t)out & 3u) || count == 0 || (count & 3u) ||
+        (uint64_t)first + count > (1ull << 32))
+        return -1;
+    const uint32_t nquad = (uint32_t)(count / 4);
+    hipLaunchKernelGGL(mb_cvt_e4m3_k, dim3((nquad + 255u) / 256u), dim3(256), 0,
+                       (hipStream_t)stream, first, nquad, (uint32_t*)out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 // Operations one launch performs: (blocks * 256 threads) / 64 waves x iters x
 // chains x the instruction's ops (INT8 32x32x32: 65536, FP8 32x32x64: 131072,

@@ -17,6 +17,9 @@ def mb():
     L.mb_ops.argtypes = [ct.c_int, ct.c_int, ct.c_int]
     L.mb_ops.restype = ct.c_double
     L.mb_run.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_void_p]
+    P = ct.c_void_p
+    L.mb_f8_mfma.argtypes = [ct.c_int, ct.c_int, P, P, P, P, P]
+    L.mb_cvt_e4m3.argtypes = [ct.c_uint32, ct.c_uint64, P, P]
     return L
 
 
@@ -34,3 +37,16 @@ def test_bad_arguments_rejected(mb):
     assert mb.mb_run(0, 0, 10, ct.c_void_p(0x10000), None) == -1
     assert mb.mb_run(0, 4, 0, ct.c_void_p(0x10000), None) == -1
     assert mb.mb_run(5, 4, 10, ct.c_void_p(0x10000), None) == -1
+
+
+def test_premise_entry_points_refuse_bad_arguments(mb):
+    A = ct.c_void_p(0x10000)
+    assert mb.mb_f8_mfma(0, 4, None, A, A, A, None) == -1
+    assert mb.mb_f8_mfma(2, 4, A, A, A, A, None) == -1
+    assert mb.mb_f8_mfma(0, 0, A, A, A, A, None) == -1
+    assert mb.mb_f8_mfma(1, 70000, A, A, A, A, None) == -1
+    assert mb.mb_cvt_e4m3(0, 16, None, None) == -1
+    assert mb.mb_cvt_e4m3(0, 16, ct.c_void_p(0x10002), None) == -1   # not 4-byte aligned
+    assert mb.mb_cvt_e4m3(0, 6, A, None) == -1                       # not whole quads
+    assert mb.mb_cvt_e4m3(0, 0, A, None) == -1
+    assert mb.mb_cvt_e4m3(0xFFFFFFF0, 32, A, None) == -1             # past 2^32 patterns
