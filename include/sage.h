@@ -67,7 +67,8 @@ enum sage_status {
     SAGE_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
     SAGE_ERR_SIZE = -5,        /* the problem exceeds the supported size */
     SAGE_ERR_HIP = -6,         /* a HIP launch failed */
-    SAGE_ERR_WORKSPACE = -7    /* workspace smaller than the matching *_sizes call asks */
+    SAGE_ERR_WORKSPACE = -7,   /* workspace smaller than the matching *_sizes call asks */
+    SAGE_ERR_SCRATCH = -8      /* sage_quant_qkv_noalloc: more than its fixed scratch needed */
 };
 
 enum sage_layout { SAGE_LAYOUT_HND = 0, SAGE_LAYOUT_NHD = 1 };
@@ -192,6 +193,26 @@ int sage_quant_qkv(const void* q, const void* k, const void* v, int B, int H, in
                    int layout, int pv_dtype, int8_t* q8, float* q_scale, int8_t* k8,
                    float* k_scale, float* k_mean, void* vq, float* v_scale, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * sage_quant_qkv without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * results, buffers and errors as sage_quant_qkv; the K and V partial
+ * statistics live in a fixed 32 MiB device array of the library instead
+ * (one per GPU, held until the process ends).  The problem must need at most
+ * that much: sizes[SAGE_BUF_WS_QK] + sizes[SAGE_BUF_WS_V] <= 32 MiB (FP8 V:
+ * 12 B H d ceil(N / 512) + 4 B H d bytes, so B = 1, H = 40, d = 128 allows
+ * N <= 279040), else SAGE_ERR_SCRATCH before any launch.
+ * stream must belong to the current device (else SAGE_ERR_HIP); the
+ * library looks the array up once per device on the first call there.
+ * Every call on one GPU shares the array: calls that overlap on one GPU
+ * (other streams or host threads) race and must be serialised by the caller.
+ */
+int sage_quant_qkv_noalloc(const void* q, const void* k, const void* v, int B, int H, int N,
+                           int d, int layout, int pv_dtype, int8_t* q8, float* q_scale,
+                           int8_t* k8, float* k_scale, float* k_mean, void* vq, float* v_scale,
+                           void* stream);
 
 /*
  * Fused attention over the quantized operands (hunxia glossary, FlashAttention:

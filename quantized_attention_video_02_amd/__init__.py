@@ -43,7 +43,7 @@ class SageConfig(ct.Structure):
 
 
 EXPORTS = ["sage_get_config", "sage_quant_sizes", "sage_quant_sizes_ex", "sage_quant_qk",
-           "sage_quant_qk_ex", "sage_quant_v", "sage_quant_qkv", "sage_attn_fwd", "sage_attn_fwd_lse", "sage_attn_fwd_ex",
+           "sage_quant_qk_ex", "sage_quant_v", "sage_quant_qkv", "sage_quant_qkv_noalloc", "sage_attn_fwd", "sage_attn_fwd_lse", "sage_attn_fwd_ex",
            "sage_attn_fwd_sparse", "sage_attn_fwd_debug", "sage_qsmooth_sizes",
            "sage_quant_qk_smooth", "sage_q_smooth_bias", "sage_attn_fwd_smooth",
            "sage_quant_qk_mx", "sage_quant_v_mx", "sage_attn_fwd_mx", "sage_bwd_sizes",
@@ -69,6 +69,7 @@ def lib():
     L.sage_quant_qk_ex.argtypes = [P, P, I, I, I, I, I, I, P, P, P, P, P, P, S, P]
     L.sage_quant_v.argtypes = [P, I, I, I, I, I, I, P, P, P, S, P]
     L.sage_quant_qkv.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, S, P]
+    L.sage_quant_qkv_noalloc.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P]
     L.sage_attn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
     L.sage_attn_fwd_lse.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P, P]
     L.sage_attn_fwd_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, I, P]
@@ -225,10 +226,11 @@ def quant_v(v: torch.Tensor, pv: str = "fp8", layout: str = "HND"):
 
 
 def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pv: str = "fp8",
-              layout: str = "HND") -> tuple[dict, torch.Tensor, torch.Tensor]:
+              layout: str = "HND", noalloc: bool = False) -> tuple[dict, torch.Tensor, torch.Tensor]:
     """One quantization pass over Q, K and V (sage_quant_qkv): returns
     (qz, vq, v_scale), the same results as quant_qk(q, k) and quant_v(v, pv),
-    with the K and V statistics taken in one launch."""
+    with the K and V statistics taken in one launch.  noalloc: through
+    sage_quant_qkv_noalloc (the library's fixed scratch, no workspace)."""
     if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
         raise TypeError("q, k and v must be bfloat16")
     if not (q.shape == k.shape == v.shape) or not all(t.is_contiguous() for t in (q, k, v)):
@@ -241,15 +243,20 @@ def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pv: str = "fp8"
              q_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
              k8=torch.empty((B, H, nblk * 128, d), dtype=torch.int8, device=dev),
              k_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
-             k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev),
-             workspace=_empty(sz[BUF_WS_QK] + sz[BUF_WS_V], dev, torch.int64))
+             k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev))
     vq = torch.empty((B, H, nblk, d, 128), dtype=torch.uint8 if pv == "fp8" else torch.float16,
                      device=dev)
     vs = torch.empty((B, H, d), dtype=torch.float32, device=dev)
-    _check(lib().sage_quant_qkv(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, LAYOUTS[layout], PV[pv],
-                                _ptr(r["q8"]), _ptr(r["q_scale"]), _ptr(r["k8"]),
-                                _ptr(r["k_scale"]), _ptr(r["k_mean"]), _ptr(vq), _ptr(vs),
-                                _ptr(r["workspace"]), sz[BUF_WS_QK] + sz[BUF_WS_V], _stream(dev)))
+    args = (_ptr(q), _ptr(k), _ptr(v), B, H, N, d, LAYOUTS[layout], PV[pv], _ptr(r["q8"]),
+            _ptr(r["q_scale"]), _ptr(r["k8"]), _ptr(r["k_scale"]), _ptr(r["k_mean"]), _ptr(vq),
+            _ptr(vs))
+    if noalloc:
+        with torch.cuda.device(dev):
+            _check(lib().sage_quant_qkv_noalloc(*args, _stream(dev)))
+    else:
+        ws_bytes = sz[BUF_WS_QK] + sz[BUF_WS_V]
+        r["workspace"] = _empty(ws_bytes, dev, torch.int64)
+        _check(lib().sage_quant_qkv(*args, _ptr(r["workspace"]), ws_bytes, _stream(dev)))
     r.update(B=B, H=H, N=N, d=d, layout=layout, q_gran="block")
     return r, vq, vs
 

@@ -268,22 +268,33 @@ __attribute__((visibility("default"))) int sage_quant_v(const void* v, int B, in
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
-__attribute__((visibility("default"))) int sage_quant_qkv(
-    const void* q, const void* k, const void* v, int B, int H, int N, int d, int layout,
-    int pv_dtype, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, float* k_mean, void* vq,
-    float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Validation and launch of one quantization pass; workspace == NULL with
+// noalloc: the library's fixed scratch instead.
+int quant_qkv_common(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                     int layout, int pv_dtype, int8_t* q8, float* q_scale, int8_t* k8,
+                     float* k_scale, float* k_mean, void* vq, float* v_scale, void* workspace,
+                     size_t workspace_bytes, int noalloc, void* stream) {
     if (!q || !k || !v || !q8 || !q_scale || !k8 || !k_scale || !k_mean || !vq || !v_scale ||
-        !workspace)
+        (!noalloc && !workspace))
         return SAGE_ERR_NULL;
     SAGE_TRY(check_dims(B, H, N, d));
     SAGE_TRY(check_layout(layout));
     SAGE_TRY(check_pv(pv_dtype));
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(q_scale) ||
         !aligned16(k8) || !aligned16(k_scale) || !aligned16(k_mean) || !aligned16(vq) ||
-        !aligned16(v_scale) || !aligned16(workspace))
+        !aligned16(v_scale) || (!noalloc && !aligned16(workspace)))
         return SAGE_ERR_ALIGN;
     const Sizes s = sizes_of(B, H, N, d, pv_dtype);
-    if (workspace_bytes < s.v[SAGE_BUF_WS_QK] + s.v[SAGE_BUF_WS_V]) return SAGE_ERR_WORKSPACE;
+    const size_t need = s.v[SAGE_BUF_WS_QK] + s.v[SAGE_BUF_WS_V];
+    if (noalloc) {
+        if (need > sage::kNoAllocScratchBytes) return SAGE_ERR_SCRATCH;
+        if (sage::noalloc_scratch((hipStream_t)stream, &workspace) != hipSuccess)
+            return SAGE_ERR_HIP;
+    } else if (workspace_bytes < need) {
+        return SAGE_ERR_WORKSPACE;
+    }
     uint64_t* kws = (uint64_t*)workspace;
     float* vws = (float*)((char*)workspace + s.v[SAGE_BUF_WS_QK]);
     const hipError_t e = sage::launch_quant_qkv(
@@ -291,6 +302,24 @@ __attribute__((visibility("default"))) int sage_quant_qkv(
         pv_dtype == SAGE_PV_FP16, q8, q_scale, k8, k_scale, k_mean, vq, v_scale, kws, vws,
         (hipStream_t)stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+}  // namespace
+
+__attribute__((visibility("default"))) int sage_quant_qkv(
+    const void* q, const void* k, const void* v, int B, int H, int N, int d, int layout,
+    int pv_dtype, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, float* k_mean, void* vq,
+    float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    return quant_qkv_common(q, k, v, B, H, N, d, layout, pv_dtype, q8, q_scale, k8, k_scale,
+                            k_mean, vq, v_scale, workspace, workspace_bytes, 0, stream);
+}
+
+__attribute__((visibility("default"))) int sage_quant_qkv_noalloc(
+    const void* q, const void* k, const void* v, int B, int H, int N, int d, int layout,
+    int pv_dtype, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, float* k_mean, void* vq,
+    float* v_scale, void* stream) {
+    return quant_qkv_common(q, k, v, B, H, N, d, layout, pv_dtype, q8, q_scale, k8, k_scale,
+                            k_mean, vq, v_scale, nullptr, 0, 1, stream);
 }
 
 __attribute__((visibility("default"))) int sage_attn_fwd(
@@ -497,6 +526,9 @@ __attribute__((visibility("default"))) const char* sage_status_string(int status
         case SAGE_ERR_SIZE: return "SAGE_ERR_SIZE: problem exceeds the supported size";
         case SAGE_ERR_HIP: return "SAGE_ERR_HIP: a HIP launch failed";
         case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace too small";
+        case SAGE_ERR_SCRATCH:
+            return "SAGE_ERR_SCRATCH: the problem needs more than the library's fixed 32 MiB "
+                   "scratch (use sage_quant_qkv with a workspace)";
         default: return "SAGE_ERR_UNKNOWN";
     }
 }

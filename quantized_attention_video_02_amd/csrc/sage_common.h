@@ -124,6 +124,10 @@ hipError_t launch_quant_qkv(const u16* q, const u16* k, const u16* v, int B, int
                             int layout, int pv16, int8_t* q8, float* qs, int8_t* k8, float* ks,
                             float* kmean, void* vq, float* vscale, uint64_t* kws, float* vws,
                             hipStream_t s);
+// Bytes of the fixed scratch behind sage_quant_qkv_noalloc, and its device
+// address for the stream's (current) device.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(hipStream_t s, void** out);
 hipError_t launch_attn(const AttnArgs& args, int B, int d, int pv16, int causal, int dump,
                        hipStream_t s);
 hipError_t launch_attn_bwd(const BwdPrep& pp, const BwdArgs& args, int B, int d, int causal,

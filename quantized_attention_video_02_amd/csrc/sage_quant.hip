@@ -16,6 +16,8 @@
 // chunk; consecutive lanes read consecutive chunks of a row, so each wave
 // reads whole rows.  The partial-sum layout makes every reduction order-free
 // (wrapping int64 adds, max), so results are bitwise deterministic.
+#include <mutex>
+
 #include "sage_common.h"
 
 namespace sage {
@@ -841,6 +843,40 @@ hipError_t launch_quant_qkv(const u16* q, const u16* k, const u16* v, int B, int
         hipSuccess)
         return e;
     return launch_v_codes(v, B, H, N, d, layout, pv16, vinv, vq, vscale, s);
+}
+
+// Fixed device scratch of the allocation-free quantization pass
+// (sage_quant_qkv_noalloc): the K and V partial statistics of one call, laid
+// out as the workspace of sage_quant_qkv.  Each GPU holds its own copy for
+// the life of the process; every call on a GPU reuses it, so calls that
+// overlap on one GPU (other streams or threads) race.  Nothing in it needs
+// clearing: each call writes every partial before reading it.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_at[kMaxDevices];  // device address of `scratch` per device, once looked up
+}  // namespace
+
+// The device address of `scratch` on the stream's device, which must be the
+// current device (the symbol is looked up with that device current, once per
+// device).  hipErrorInvalidDevice if the stream belongs to another device.
+hipError_t noalloc_scratch(hipStream_t s, void** out) {
+    int dev = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if ((e = hipStreamGetDevice(s, &sdev)) != hipSuccess) return e;
+    if (sdev != dev || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_at[dev]) {
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_at[dev] = p;
+    }
+    *out = scratch_at[dev];
+    return hipSuccess;
 }
 
 }  // namespace sage
