@@ -42,6 +42,7 @@ PEAK_TOPS = {"fp8": 5000.0,                       # dense INT8 (QK) = dense FP8 
              # backward: 2d ops each for S, dV, dK, dQ at 5.0 POPS and dP at 2.5
              "bwd": 10.0 / (8.0 / 5000.0 + 2.0 / 2500.0)}
 HBM_GBPS = 8000.0
+FWD_TARGET_FRAC = 0.50  # the forward's throughput target (fraction of the dense MFMA peak)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 ATTN_SOURCES = [os.path.join(ROOT, "quantized_attention_video_02_amd", "csrc", f)
                 for f in ("sage_attn.hip", "sage_common.h", "sage_device.h")]
@@ -676,6 +677,10 @@ def main():
             blend = 1.0 / (0.5 / m["int8"] + 0.5 / m["fp8"])
             res["roofline"]["measured_peak"] = {"int8": m["int8"], "fp8": m["fp8"], "blend": blend,
                                                 "frac": achieved / blend}
+    if not args.mx:
+        # the forward's throughput target: half of the dense INT8/FP8 peak
+        res["roofline"]["target_frac"] = FWD_TARGET_FRAC
+        res["roofline"]["target_met"] = bool(res["roofline"]["frac"] >= FWD_TARGET_FRAC)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.pv, args.cpu_seconds, args.q_gran,

@@ -224,6 +224,7 @@ def test_bench_line_keeps_the_contract():
     rf = line["roofline"]
     assert rf["bound"] == "mfma" and rf["peak"] == 5000.0 and rf["unit"] == "TFLOP/s"
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
+    assert rf["target_frac"] == 0.5 and rf["target_met"] == (rf["frac"] >= 0.5)
     from quantized_attention_video_02_amd.microbench import __main__ as mb
 
     if os.path.exists(mb.LIB):
