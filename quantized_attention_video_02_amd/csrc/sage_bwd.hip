@@ -12,17 +12,19 @@
 //   dV += dO8^T . e4m3(448 P) * s_do / 448        (FP8 MFMA; dO8 per 128-row block)
 //   dK += Q8^T . dS8 * s_ds * q_scale * sm_scale   (INT8 MFMA; dS8 per tile pair)
 //   dQ += K8^T . dS8^T * s_ds * k_scale * sm_scale (INT8 MFMA)
-// Two sweeps, each mirroring the forward's register layout: the dQ sweep keeps
-// a wave's 32 queries (S^T, dP^T with queries on lanes; dS^T is directly the B
-// operand of dQ^T = K^T dS^T) and sweeps key tiles; the dK/dV sweep keeps a
-// wave's 32 keys (S, dP with keys on lanes; P and dS are directly the B
-// operands of dV^T = dO8^T P~ and dK^T = Q8^T dS8) and sweeps query tiles.
-// The operands that meet an accumulator-shaped operand along the reduction
-// are stored transposed with the matching order of the reduction index (the
-// forward's V order for FP8, a 32-element order for INT8), written once by
-// the preparation kernels.  The tile's dS absmax is reduced over the
-// workgroup's 4 waves through LDS.  Four waves per workgroup, one workgroup
-// per CU: the sweeps hold about 400-500 registers per lane.
+// Three sweeps, each mirroring the forward's register layout: the dQ sweep
+// keeps a wave's 32 queries (S^T, dP^T with queries on lanes; dS^T is directly
+// the B operand of dQ^T = K^T dS^T) and sweeps key tiles; the dV and dK sweeps
+// keep a wave's 32 keys (S, dP with keys on lanes; P and dS are directly the B
+// operands of dV^T = dO8^T P~ and dK^T = Q8^T dS8) and sweep query tiles, one
+// sum each.  The operands that meet an accumulator-shaped operand along the
+// reduction are stored transposed with the matching order of the reduction
+// index (the forward's V order for FP8, a 32-element order for INT8), written
+// once by the preparation kernels.  A tile's dS absmax is reduced over the 4
+// waves of its 128-row block through LDS.  Every sweep runs two waves per SIMD:
+// the dQ and dK sweeps form S, dP and dS one 32-row block at a time and keep
+// two row blocks per workgroup (8 waves), the dV sweep needs no dP or dS and
+// runs two 4-wave workgroups per CU.
 #include <limits.h>
 
 #include "sage_common.h"
@@ -206,13 +208,15 @@ __device__ inline v4i pack_i8(const float* x, float inv) {
     return r;
 }
 
-// The tile's dS absmax over the workgroup's 4 waves (red: 4 floats of LDS)
-// and its INT8 scale s = fp32(a / 127), inv = fp32(127 / a) (0 for a = 0).
-__device__ inline void tile_scale(float amax, float* red, int wave, int lane, float& s, float& inv) {
+// The tile's dS absmax over the 4 waves red[base .. base + 3] of one 128-row
+// block (red: a float of LDS per wave of the workgroup) and its INT8 scale
+// s = fp32(a / 127), inv = fp32(127 / a) (0 for a = 0).
+__device__ inline void tile_scale(float amax, float* red, int wave, int lane, float& s, float& inv,
+                                  int base = 0) {
     amax = wave_fmax(amax);
     if (lane == 0) red[wave] = amax;
     __syncthreads();
-    const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float a = fmaxf(fmaxf(red[base], red[base + 1]), fmaxf(red[base + 2], red[base + 3]));
     s = (float)((double)a / 127.0);
     inv = a > 0.0f ? (float)(127.0 / (double)a) : 0.0f;
 }
@@ -230,12 +234,23 @@ __device__ inline void store_f32_row(float* out, int64_t off, const v16f* X, int
 }
 
 // ---------------------------------------------------------------- dQ sweep
-// Workgroup = one query block of 128 (wave w: queries 32 w .. 32 w + 31), key
-// tiles swept in ascending order, double-buffered in LDS: K codes [128 keys]
-// [BwdRow::I8], V fp16 [128 keys][BwdRow::F16], K codes transposed [D channels][kKstr].
+// Workgroup = two query blocks of 128 (8 waves, two per SIMD), key tiles swept
+// in ascending order, double-buffered in LDS: K codes [128 keys][BwdRow::I8],
+// V fp16 [128 keys][BwdRow::F16], K codes transposed [D channels][kKstr].
+// wave w keeps queries 128 (2 qg + w / 4) + 32 (w % 4) .. + 31, and both
+// blocks share each key tile in LDS.  Per tile, S^T, dP^T, P^T and dS^T are
+// formed one 32-key block at a time (one block's products live beside the
+// tile's dS), the masked entries are zeroed after the blocks (a branch inside
+// them would let the compiler hoist every block's products above it), and
+// the transposed K operands of each channel block are read just before its
+// dQ MFMAs; the dS scale is each query block's own (its 4 waves).  Causal:
+// the sweep runs to the second block's diagonal tile; for the first block
+// the tile after its own diagonal is masked whole.  (One wave keeps dQ, its
+// Q codes and fp16 dO rows and one block's products in about 232 registers,
+// so two waves share a SIMD.)
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-    constexpr int NW = 4, KK = D / 32, CB = D / 32, HK = D / 16;
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
+    constexpr int NW = 8, KK = D / 32, CB = D / 32, HK = D / 16;
     constexpr int R8 = BwdRow<D>::I8, R16 = BwdRow<D>::F16;
     constexpr int K8B = kBc * R8, V16B = kBc * R16, KTB = D * kKstr;
     constexpr int SLOT = K8B + V16B + KTB;
@@ -248,21 +263,26 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const int wg = xcd_remap(blockIdx.x, a.total);
-    const int bh = wg / a.nblk, qb = wg - bh * a.nblk;
+    const int nqg = (a.nblk + 1) / 2;  // workgroups per head
+    const int bh = wg / nqg, qg = wg - bh * nqg;
     const int H = a.H, N = a.N, b = bh / H, h = bh - b * H;
-    const int qi = qb * kBlk + wave * 32 + n;
+    const int qb = 2 * qg + (wave >> 2);  // this wave's query block
+    const bool qbvalid = qb < a.nblk;     // (the second block of the last pair may not exist)
+    const int qi = qb * kBlk + (wave & 3) * 32 + n;
     const bool valid = qi < N;
-    const int64_t rowp = (int64_t)bh * a.N_pad + qi;
+    const int64_t rowp = (int64_t)bh * a.N_pad + (qbvalid ? qi : 0);
 
     v4i qf[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const v4i*)(a.q8 + rowp * D + 32 * kk + 16 * hh);
+    for (int kk = 0; kk < KK; ++kk)
+        qf[kk] = qbvalid ? *(const v4i*)(a.q8 + rowp * D + 32 * kk + 16 * hh) : v4i{};
     v8h dof[HK];
 #pragma unroll
-    for (int kk = 0; kk < HK; ++kk) dof[kk] = *(const v8h*)(a.do16 + rowp * D + 16 * kk + 8 * hh);
-    const float sigma = a.q_scale[bh * a.nblk + qb] * a.lambda;
+    for (int kk = 0; kk < HK; ++kk)
+        dof[kk] = qbvalid ? *(const v8h*)(a.do16 + rowp * D + 16 * kk + 8 * hh) : v8h{};
+    const float sigma = qbvalid ? a.q_scale[bh * a.nblk + qb] * a.lambda : 0.0f;
     const float lse = valid ? a.lse[(int64_t)bh * N + qi] : 0.0f;
-    const float Di = a.Dq[rowp];
+    const float Di = qbvalid ? a.Dq[rowp] : 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) settle(qf[kk]);
 #pragma unroll
@@ -293,7 +313,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     v16f dq[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) dq[cb] = v16f{};
-    const int ntiles = CAUSAL ? qb + 1 : a.nblk;
+    const int ntiles = CAUSAL ? min(2 * qg + 2, a.nblk) : a.nblk;
     const float* ksrow = a.k_scale + bh * a.nblk;
     float ks_next = ksrow[0];
     load(0);
@@ -312,63 +332,44 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         const uint8_t* vbuf = kbuf + K8B;
         const uint8_t* tbuf = vbuf + V16B;
         const float c = sigma * ks;
-        // S^T (keys x queries) and dP^T = V dO^T: every operand of the two
-        // products read first (the LDS latency is paid once), then the MFMAs
-        // with the four 32-key blocks' chains interleaved
-        v16i S[4];
-        v16f dP[4];
-        {
-            v4i ka[4][KK];
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                const uint8_t* krow = kbuf + (32 * k4 + n) * R8 + 16 * hh;
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) ka[k4][kk] = *(const v4i*)(krow + 32 * kk);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) S[k4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[k4][0], qf[0], v16i{}, 0, 0, 0);
-#pragma unroll
-            for (int kk = 1; kk < KK; ++kk)
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4)
-                    S[k4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[k4][kk], qf[kk], S[k4], 0, 0, 0);
-        }
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) dP[k4] = v16f{};
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            v8h va[4][HK / 2];
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                const uint8_t* vrow = vbuf + (32 * k4 + n) * R16 + 16 * hh + 32 * (HK / 2) * half;
-#pragma unroll
-                for (int kk = 0; kk < HK / 2; ++kk) va[k4][kk] = *(const v8h*)(vrow + 32 * kk);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kk = 0; kk < HK / 2; ++kk)
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4)
-                    dP[k4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[k4][kk], dof[(HK / 2) * half + kk], dP[k4], 0, 0, 0);
-        }
-        // the transposed K operands of dQ^T, read while the vector work below runs
-        v4i ta[CB][4];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const uint8_t* trow = tbuf + (32 * cb + n) * kKstr + 16 * hh;
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) ta[cb][k4] = *(const v4i*)(trow + 32 * k4);
-        }
-        // P^T and dS^T; masked entries (key >= N, causal key > query, padding
-        // queries) are 0
-        // (padding queries give dS = 0 by themselves: their dO, D and codes
-        // are 0; keys past N and, causal, keys after the query are masked on
-        // the tiles that hold any)
         const int key_t = t * kBc;
-        const bool needmask = key_t + kBc > N || (CAUSAL && t == qb);
         float ds[4][16];
-        float amax = 0.0f;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            // (the barrier keeps the next block's operand reads from being
+            // hoisted above this block's work, which would hold them all)
+            __builtin_amdgcn_sched_barrier(0);
+            v4i ka[KK];
+            const uint8_t* krow = kbuf + (32 * k4 + n) * R8 + 16 * hh;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) ka[kk] = *(const v4i*)(krow + 32 * kk);
+            const uint8_t* vrow = vbuf + (32 * k4 + n) * R16 + 16 * hh;
+            v16i Sk = v16i{};
+            v16f dPk = v16f{};
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                v8h va[HK / 2];
+#pragma unroll
+                for (int kk = 0; kk < HK / 2; ++kk)
+                    va[kk] = *(const v8h*)(vrow + 32 * ((HK / 2) * half + kk));
+#pragma unroll
+                for (int kk = 0; kk < HK / 2; ++kk) {
+                    const int ks8 = (KK / 2) * half + kk;  // S takes KK steps over both halves
+                    if (kk < KK / 2)
+                        Sk = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[ks8], qf[ks8], Sk, 0, 0, 0);
+                    dPk = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[kk], dof[(HK / 2) * half + kk], dPk,
+                                                                 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)Sk[r], c, -lse));
+                ds[k4][r] = p * (dPk[r] - Di);
+            }
+        }
+        // P^T and dS^T of masked entries (key >= N, causal key > query) to 0;
+        // padding queries give dS = 0 by themselves (their dO, D and codes are 0)
+        const bool needmask = key_t + kBc > N || (CAUSAL && t >= qb);
         if (needmask) {
 #pragma unroll
             for (int k4 = 0; k4 < 4; ++k4)
@@ -376,39 +377,34 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
                 for (int r = 0; r < 16; ++r) {
                     const int key = key_t + 32 * k4 + 8 * (r >> 2) + 4 * hh + (r & 3);
                     const bool ok = key < N && (!CAUSAL || key <= qi);
-                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[k4][r], c, -lse)) : 0.0f;
-                    ds[k4][r] = p * (dP[k4][r] - Di);
-                    amax = fmaxf(amax, fabsf(ds[k4][r]));
-                }
-        } else {
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[k4][r], c, -lse));
-                    ds[k4][r] = p * (dP[k4][r] - Di);
-                    amax = fmaxf(amax, fabsf(ds[k4][r]));
+                    ds[k4][r] = ok ? ds[k4][r] : 0.0f;
                 }
         }
+        float amax = 0.0f;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ds[k4][r]));
         float s_ds, inv;
-        tile_scale(amax, red, wave, lane, s_ds, inv);
+        tile_scale(amax, red, wave, lane, s_ds, inv, wave & ~3);
         v4i dsb[4];
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) dsb[k4] = pack_i8(ds[k4], inv);
         // dQ^T (channels x queries) += K8^T dS8^T for this tile, scaled
         const float fq = (s_ds * ks) * a.sm_scale;
-        v16i qacc[CB];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) qacc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ta[cb][0], dsb[0], v16i{}, 0, 0, 0);
+        for (int cb = 0; cb < CB; ++cb) {
+            v4i ta[4];
+            const uint8_t* trow = tbuf + (32 * cb + n) * kKstr + 16 * hh;
 #pragma unroll
-        for (int k4 = 1; k4 < 4; ++k4)
+            for (int k4 = 0; k4 < 4; ++k4) ta[k4] = *(const v4i*)(trow + 32 * k4);
+            v16i qacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ta[0], dsb[0], v16i{}, 0, 0, 0);
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-                qacc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ta[cb][k4], dsb[k4], qacc[cb], 0, 0, 0);
+            for (int k4 = 1; k4 < 4; ++k4)
+                qacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ta[k4], dsb[k4], qacc, 0, 0, 0);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) dq[cb][e] = __builtin_fmaf((float)qacc[cb][e], fq, dq[cb][e]);
+            for (int e = 0; e < 16; ++e) dq[cb][e] = __builtin_fmaf((float)qacc[e], fq, dq[cb][e]);
+        }
         wait_vmem();
         __syncthreads();
     }
@@ -427,7 +423,7 @@ __device__ inline void wait_vm() {
 }
 
 // Copy pieces wave w issues for a tile of P pieces (piece J = w + 4 j).
-constexpr int pieces_of(int P, int w) { return P > w ? (P - w + 3) / 4 : 0; }
+constexpr int pieces_of(int P, int w, int nw = 4) { return P > w ? (P - w + nw - 1) / nw : 0; }
 
 // wait_vm with this wave's own count (w uniform)
 template <int N0, int N1, int N2, int N3>
@@ -438,58 +434,97 @@ __device__ inline void wait_vm_wave(int w) {
     else wait_vm<N3>();
 }
 
-// Workgroup = one key block of 128 (wave w: keys 32 w .. 32 w + 31), query
+// The vector-memory loads wave w of NW issues for tiles of P1, P2 and P3
+// pieces (piece J = w + NW j): wait until at most that many are in flight.
+template <int NW, int P1, int P2, int P3>
+__device__ inline void wait_own_pieces(int w) {
+#define SAGE_WAIT_W(W)                                                                   \
+    if (w == W) {                                                                        \
+        wait_vm<pieces_of(P1, W, NW) + pieces_of(P2, W, NW) + pieces_of(P3, W, NW)>(); \
+        return;                                                                          \
+    }
+    SAGE_WAIT_W(0)
+    SAGE_WAIT_W(1)
+    SAGE_WAIT_W(2)
+    SAGE_WAIT_W(3)
+    if constexpr (NW > 4) {
+        SAGE_WAIT_W(4)
+        SAGE_WAIT_W(5)
+        SAGE_WAIT_W(6)
+        SAGE_WAIT_W(7)
+    }
+#undef SAGE_WAIT_W
+}
+
+// The key sweeps, one per sum: kDV (the dV sum: S, P and dO8^T P~) and kDK
+// (the dK sum: S, dP, dS and Q8^T dS8).  Workgroup = 4 waves x 32 keys = one
+// key block (kDV, two workgroups per CU) or 8 waves = two key blocks sharing
+// each query tile (kDK, one per CU); either way two waves per SIMD.  Query
 // tiles swept in ascending order.  LDS: slot A, double-buffered: Q codes
-// [128 queries][BwdRow::I8], dO fp16 [128][BwdRow::F16] and the tile's record (lse, D,
-// q_scale, s_do); slot B, single: dO FP8 transposed [D][kKstr] and Q codes
-// transposed [D][kKstr].  A(t + 1) is copied while tile t computes; B(t + 1)
-// after tile t's dV / dK, awaited only before tile t + 1's dV / dK.  Every
-// vector-memory load of the sweep is a tile copy, so the waits count them.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-    constexpr int NW = 4, KK = D / 32, CB = D / 32, HK = D / 16;
+// [128 queries][BwdRow::I8], dO fp16 [128][BwdRow::F16] (kDK) and the tile's
+// record (lse, D, q_scale, s_do); slot B, single: dO FP8 transposed [D][kKstr]
+// (kDV) or Q codes transposed [D][kKstr] (kDK).  A(t + 1) is copied while
+// tile t computes; B(t + 1) after tile t's product, awaited only before tile
+// t + 1's.  Every vector-memory load of the sweep is a tile copy, so the
+// waits count them.  Two sweeps instead of one joint one (which kept dK, dV
+// and the tile's S, dP and dS: 400-500 registers, one wave per SIMD and
+// moves out of the accumulation registers) cost one more S product and one
+// more exp2 per score and run 1.5x faster.
+enum { kDV = 1, kDK = 2 };
+
+template <int MODE>
+constexpr int dkdv_waves() { return MODE == kDK ? 8 : 4; }
+
+template <int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(64 * dkdv_waves<MODE>(), MODE == kDV ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
+    constexpr bool WDV = MODE == kDV, WDK = MODE == kDK;  // which sum this sweep keeps
+    constexpr int NW = dkdv_waves<MODE>(), KBW = NW / 4;   // waves, key blocks per workgroup
+    constexpr int KK = D / 32, CB = D / 32, HK = D / 16;
     constexpr int R8 = BwdRow<D>::I8, R16 = BwdRow<D>::F16;
-    constexpr int Q8B = kBlk * R8, DO16B = kBlk * R16, RECB = kRecFloats * 4;
+    constexpr int Q8B = kBlk * R8, DO16B = WDK ? kBlk * R16 : 0, RECB = kRecFloats * 4;
     constexpr int SLOTA = Q8B + DO16B + RECB;
-    constexpr int DO8B = D * kKstr, QTB = D * kKstr;
+    constexpr int DO8B = WDV ? D * kKstr : 0, QTB = WDK ? D * kKstr : 0;
     constexpr int QP = Q8B / 1024, HP = DO16B / 1024, LP = RECB / 1024, FP = DO8B / 1024, TP = QTB / 1024;
     constexpr int QMAXP = (QP + NW - 1) / NW, HMAXP = (HP + NW - 1) / NW, LMAXP = (LP + NW - 1) / NW,
                   FMAXP = (FP + NW - 1) / NW, TMAXP = (TP + NW - 1) / NW;
     static_assert(Q8B % 1024 == 0 && DO16B % 1024 == 0 && RECB % 1024 == 0 && DO8B % 1024 == 0,
                   "1 KB copy pieces");
-    // loads per wave w of the A and B copies
-    constexpr int NA0 = pieces_of(QP, 0) + pieces_of(HP, 0) + pieces_of(LP, 0);
-    constexpr int NA1 = pieces_of(QP, 1) + pieces_of(HP, 1) + pieces_of(LP, 1);
-    constexpr int NA2 = pieces_of(QP, 2) + pieces_of(HP, 2) + pieces_of(LP, 2);
-    constexpr int NA3 = pieces_of(QP, 3) + pieces_of(HP, 3) + pieces_of(LP, 3);
-    constexpr int NB0 = pieces_of(FP, 0) + pieces_of(TP, 0), NB1 = pieces_of(FP, 1) + pieces_of(TP, 1);
-    constexpr int NB2 = pieces_of(FP, 2) + pieces_of(TP, 2), NB3 = pieces_of(FP, 3) + pieces_of(TP, 3);
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOTA + DO8B + QTB];
     __shared__ float red[NW];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const int wg = xcd_remap(blockIdx.x, a.total);
-    const int bh = wg / a.nblk, kb = wg - bh * a.nblk;
+    const int nkg = (a.nblk + KBW - 1) / KBW;  // workgroups per head
+    const int bh = wg / nkg, kg = wg - bh * nkg;
     const int H = a.H, N = a.N, b = bh / H, h = bh - b * H;
-    const int kj = kb * kBc + wave * 32 + n;
+    const int kb = kg * KBW + (wave >> 2);  // this wave's key block
+    const bool kbvalid = kb < a.nblk;       // (the second block of the last pair may not exist)
+    const int kj = kb * kBc + (wave & 3) * 32 + n;
     const bool kvalid = kj < N;
-    const int64_t rowk = (int64_t)bh * a.N_pad + kj;
+    const int64_t rowk = (int64_t)bh * a.N_pad + (kbvalid ? kj : 0);
 
     v4i kf[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kf[kk] = *(const v4i*)(a.k8 + rowk * D + 32 * kk + 16 * hh);
-    v8h vf[HK];
+    for (int kk = 0; kk < KK; ++kk)
+        kf[kk] = kbvalid ? *(const v4i*)(a.k8 + rowk * D + 32 * kk + 16 * hh) : v4i{};
+    v8h vf[WDK ? HK : 1];
+    if constexpr (WDK) {
 #pragma unroll
-    for (int kk = 0; kk < HK; ++kk) vf[kk] = *(const v8h*)(a.v16 + rowk * D + 16 * kk + 8 * hh);
-    const float ks = a.k_scale[bh * a.nblk + kb];
+        for (int kk = 0; kk < HK; ++kk)
+            vf[kk] = kbvalid ? *(const v8h*)(a.v16 + rowk * D + 16 * kk + 8 * hh) : v8h{};
+    }
+    const float ks = kbvalid ? a.k_scale[bh * a.nblk + kb] : 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) settle(kf[kk]);
+    if constexpr (WDK) {
 #pragma unroll
-    for (int kk = 0; kk < HK; ++kk) settle(vf[kk]);
+        for (int kk = 0; kk < HK; ++kk) settle(vf[kk]);
+    }
     settle(ks);
 
-    int qoff[QMAXP], hoff[HMAXP], loff[LMAXP], foff[FMAXP], toff[TMAXP];
+    int qoff[QMAXP], hoff[HMAXP > 0 ? HMAXP : 1], loff[LMAXP], foff[FMAXP > 0 ? FMAXP : 1],
+        toff[TMAXP > 0 ? TMAXP : 1];
 #pragma unroll
     for (int j = 0; j < QMAXP; ++j) qoff[j] = slot_src<D, R8>(64 * (wave + NW * j) + lane);
 #pragma unroll
@@ -519,15 +554,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         tile_to_lds<TP, TMAXP, NW>(tg + (int64_t)qt * D * kBlk, lB + DO8B, wv, toff);
     };
 
-    v16f dk[CB], dv[CB];
+    v16f dk[WDK ? CB : 1], dv[WDV ? CB : 1];
+    if constexpr (WDK) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) dk[cb] = dv[cb] = v16f{};
-    const int t0 = CAUSAL ? kb : 0;
+        for (int cb = 0; cb < CB; ++cb) dk[cb] = v16f{};
+    }
+    if constexpr (WDV) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) dv[cb] = v16f{};
+    }
+    const int t0 = CAUSAL ? kg * KBW : 0;  // the first key block's diagonal tile
     copy_a(t0);
     copy_b(t0);
     for (int qt = t0; qt < a.nblk; ++qt) {
         // A(qt) complete (only B(qt) may still be in flight), for every wave
-        wait_vm_wave<NB0, NB1, NB2, NB3>(wv);
+        wait_own_pieces<NW, FP, TP, 0>(wv);
         __syncthreads();
         const bool more = qt + 1 < a.nblk;
         if (more) copy_a(qt + 1);
@@ -538,9 +579,80 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         const uint8_t* tbuf = fbuf + DO8B;
         const float qsc = recL[2 * kBlk], sdo = recL[2 * kBlk + 1];
         const float c = (qsc * a.lambda) * ks;
-        // S = Q K^T and dP = dO V^T (queries x keys), 32-query block q4
+        // (causal: a tile before this wave's block, possible for the second
+        // block of a pair, is masked whole)
+        const bool needmask = kb * kBc + kBc > N || (CAUSAL && qt <= kb);
+        float ds[WDK ? 4 : 1][16];
+        v8i P8[2];
+        float amax = 0.0f;
+        if constexpr (MODE == kDK) {
+            // dK alone: S, dP, P and dS one 32-query block at a time, so only
+            // one block's scores and products are live beside the tile's dS
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                // (the barrier keeps the next block's operand reads from being
+                // hoisted above this block's work, which would hold them all)
+                __builtin_amdgcn_sched_barrier(0);
+                v4i qa[KK];
+                const uint8_t* qrow = qbuf + (32 * q4 + n) * R8 + 16 * hh;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) qa[kk] = *(const v4i*)(qrow + 32 * kk);
+                const uint8_t* hrow = hbuf + (32 * q4 + n) * R16 + 16 * hh;
+                v16i Sq = v16i{};
+                v16f dPq = v16f{};
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    // dP's operands in two halves of the channels
+                    v8h ha[HK / 2];
+#pragma unroll
+                    for (int kk = 0; kk < HK / 2; ++kk)
+                        ha[kk] = *(const v8h*)(hrow + 32 * ((HK / 2) * half + kk));
+#pragma unroll
+                    for (int kk = 0; kk < HK / 2; ++kk) {
+                        const int ks8 = (KK / 2) * half + kk;  // S takes KK steps over both halves
+                        if (kk < KK / 2)
+                            Sq = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[ks8], kf[ks8], Sq, 0, 0, 0);
+                        dPq = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[kk], vf[(HK / 2) * half + kk], dPq,
+                                                                     0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 L4 = *(const float4*)&recL[32 * q4 + 8 * i + 4 * hh];
+                    const float4 D4 = *(const float4*)&recL[kBlk + 32 * q4 + 8 * i + 4 * hh];
+                    const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * i + j;
+                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf((float)Sq[r], c, -Lv[j]));
+                        ds[q4][r] = pv * (dPq[r] - Dv[j]);
+                    }
+                }
+            }
+            // masked entries to 0 after the blocks (a branch inside them would
+            // let the compiler hoist every block's products above it and keep
+            // them all live), then the tile's absmax
+            if (needmask) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int q = qt * kBlk + 32 * q4 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        const bool ok = kvalid && (!CAUSAL || kj <= q);
+                        ds[q4][r] = ok ? ds[q4][r] : 0.0f;
+                    }
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(ds[q4][r]));
+        } else {
+        // dV alone: S = Q K^T (queries x keys) of the four 32-query blocks,
+        // then P, each group of 4 probabilities straight into the FP8 operand
+        // at the static scale 448.  Padding queries add nothing to dV (their
+        // dO codes are 0); padding keys and, causal, keys after the query are
+        // masked on the tiles that hold any.
         v16i S[4];
-        v16f dP[4];
         {
             v4i qa[4][KK];
 #pragma unroll
@@ -558,43 +670,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 for (int q4 = 0; q4 < 4; ++q4)
                     S[q4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[q4][kk], kf[kk], S[q4], 0, 0, 0);
         }
-        {
-            // dP in two halves of the channels (the operands of one half held at once)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) dP[q4] = v16f{};
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                v8h ha[4][HK / 2];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const uint8_t* hrow = hbuf + (32 * q4 + n) * R16 + 16 * hh + 32 * (HK / 2) * half;
-#pragma unroll
-                    for (int kk = 0; kk < HK / 2; ++kk) ha[q4][kk] = *(const v8h*)(hrow + 32 * kk);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int kk = 0; kk < HK / 2; ++kk)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        dP[q4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[q4][kk], vf[(HK / 2) * half + kk], dP[q4], 0, 0, 0);
-            }
-        }
-        // P and dS (masked entries 0); each group of 4 probabilities goes
-        // straight into the FP8 operand at the static scale 448.  Padding
-        // queries give dS = 0 by themselves (dO, D and codes 0) and add
-        // nothing to dV; padding keys and, causal, keys after the query are
-        // masked on the tiles that hold any.
-        const bool needmask = kb * kBc + kBc > N || (CAUSAL && qt == kb);
-        float ds[4][16];
-        v8i P8[2];
-        float amax = 0.0f;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float4 L4 = *(const float4*)&recL[32 * q4 + 8 * i + 4 * hh];
-                const float4 D4 = *(const float4*)&recL[kBlk + 32 * q4 + 8 * i + 4 * hh];
-                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
                 float pv[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -602,63 +683,73 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                     const int q = qt * kBlk + 32 * q4 + 8 * i + 4 * hh + j;
                     const bool ok = !needmask || (kvalid && (!CAUSAL || kj <= q));
                     pv[j] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[q4][r], c, -Lv[j])) : 0.0f;
-                    ds[q4][r] = pv[j] * (dP[q4][r] - Dv[j]);
-                    amax = fmaxf(amax, fabsf(ds[q4][r]));
                 }
                 int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0] * 448.0f, pv[1] * 448.0f, 0, false);
                 w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2] * 448.0f, pv[3] * 448.0f, w, true);
                 P8[q4 >> 1][(q4 & 1) * 4 + i] = w;
             }
+        }
         // B(qt) complete for this wave (A(qt + 1), issued after it, may still
-        // be in flight); the barrier in tile_scale makes it so for all waves
+        // be in flight); the next barrier (in tile_scale for dK) makes it so
+        // for all waves
         if (more) {
-            wait_vm_wave<NA0, NA1, NA2, NA3>(wv);
+            wait_own_pieces<NW, QP, HP, LP>(wv);
         } else {
             wait_vmem();
         }
-        float s_ds, inv;
-        tile_scale(amax, red, wave, lane, s_ds, inv);
-        // dV^T (channels x keys) += dO8^T P~ over this tile, scaled by s_do / 448
-        const float fv = (float)((double)sdo / 448.0);
+        float s_ds = 0.0f, inv = 0.0f;
+        if constexpr (WDK)
+            tile_scale(amax, red, wave, lane, s_ds, inv, wave & ~3);
+        else
+            __syncthreads();
+        if constexpr (WDV) {
+            // dV^T (channels x keys) += dO8^T P~ over this tile, scaled by s_do / 448
+            const float fv = (float)((double)sdo / 448.0);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const uint8_t* frow = fbuf + (32 * cb + n) * kKstr + 64 * hh;
-            v16f T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(*(const v8i*)frow, P8[0], v16f{}, 0, 0,
-                                                                     0, 0, 0, 0);
-            T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(*(const v8i*)(frow + 32), P8[1], T, 0, 0, 0,
-                                                                0, 0, 0);
+            for (int cb = 0; cb < CB; ++cb) {
+                const uint8_t* frow = fbuf + (32 * cb + n) * kKstr + 64 * hh;
+                v16f T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(*(const v8i*)frow, P8[0], v16f{}, 0, 0,
+                                                                         0, 0, 0, 0);
+                T = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(*(const v8i*)(frow + 32), P8[1], T, 0, 0, 0,
+                                                                    0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dv[cb][e] = __builtin_fmaf(T[e], fv, dv[cb][e]);
+                for (int e = 0; e < 16; ++e) dv[cb][e] = __builtin_fmaf(T[e], fv, dv[cb][e]);
+            }
         }
-        v4i dsb[4];
+        if constexpr (WDK) {
+            v4i dsb[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) dsb[q4] = pack_i8(ds[q4], inv);
-        // dK^T (channels x keys) += Q8^T dS8 over this tile, scaled
-        const float fk = (s_ds * qsc) * a.sm_scale;
+            for (int q4 = 0; q4 < 4; ++q4) dsb[q4] = pack_i8(ds[q4], inv);
+            // dK^T (channels x keys) += Q8^T dS8 over this tile, scaled
+            const float fk = (s_ds * qsc) * a.sm_scale;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const uint8_t* trow = tbuf + (32 * cb + n) * kKstr + 16 * hh;
-            v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)trow, dsb[0], v16i{}, 0, 0, 0);
+            for (int cb = 0; cb < CB; ++cb) {
+                const uint8_t* trow = tbuf + (32 * cb + n) * kKstr + 16 * hh;
+                v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)trow, dsb[0], v16i{}, 0, 0, 0);
 #pragma unroll
-            for (int q4 = 1; q4 < 4; ++q4)
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)(trow + 32 * q4), dsb[q4], acc, 0, 0, 0);
+                for (int q4 = 1; q4 < 4; ++q4)
+                    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const v4i*)(trow + 32 * q4), dsb[q4], acc, 0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dk[cb][e] = __builtin_fmaf((float)acc[e], fk, dk[cb][e]);
+                for (int e = 0; e < 16; ++e) dk[cb][e] = __builtin_fmaf((float)acc[e], fk, dk[cb][e]);
+            }
         }
         // every wave is done with slot B (and this tile's slot A) before
         // B(qt + 1) is copied
         __syncthreads();
         if (more) copy_b(qt + 1);
     }
+    if constexpr (WDK) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        consume(dk[cb]);
-        consume(dv[cb]);
+        for (int cb = 0; cb < CB; ++cb) consume(dk[cb]);
+    }
+    if constexpr (WDV) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) consume(dv[cb]);
     }
     if (!kvalid) return;
     const int64_t off = row_offset(a.layout, b, h, kj, H, N, D);
-    store_f32_row<D>(a.dk, off, dk, hh);
-    store_f32_row<D>(a.dv, off, dv, hh);
+    if constexpr (WDK) store_f32_row<D>(a.dk, off, dk, hh);
+    if constexpr (WDV) store_f32_row<D>(a.dv, off, dv, hh);
 }
 
 template <int D>
@@ -687,13 +778,28 @@ static hipError_t launch_attn_bwd_d(const BwdPrep& pp, const BwdArgs& args, int 
                                  dim3(kBwdThreads), kargs, 0, s)) != hipSuccess)
             return e;
     }
-    BwdArgs a = args;
-    a.total = BH * a.nblk;
-    void* kargs[] = {(void*)&a};
+    // dQ sweep: one workgroup per pair of query blocks
+    BwdArgs aq = args;
+    aq.total = BH * ((args.nblk + 1) / 2);
+    void* kq[] = {(void*)&aq};
     const void* fq = causal ? (const void*)bwd_dq_kernel<D, true> : (const void*)bwd_dq_kernel<D, false>;
-    if ((e = hipLaunchKernel(fq, dim3(a.total), dim3(kBwdThreads), kargs, 0, s)) != hipSuccess) return e;
-    const void* fk = causal ? (const void*)bwd_dkdv_kernel<D, true> : (const void*)bwd_dkdv_kernel<D, false>;
-    return hipLaunchKernel(fk, dim3(a.total), dim3(kBwdThreads), kargs, 0, s);
+    if ((e = hipLaunchKernel(fq, dim3(aq.total), dim3(512), kq, 0, s)) != hipSuccess) return e;
+    // dV sweep: one workgroup per key block
+    BwdArgs av = args;
+    av.total = BH * args.nblk;
+    void* kv[] = {(void*)&av};
+    const void* fv = causal ? (const void*)bwd_dkdv_kernel<D, true, kDV>
+                            : (const void*)bwd_dkdv_kernel<D, false, kDV>;
+    if ((e = hipLaunchKernel(fv, dim3(av.total), dim3(64 * dkdv_waves<kDV>()), kv, 0, s)) !=
+        hipSuccess)
+        return e;
+    // dK sweep: one workgroup per pair of key blocks
+    BwdArgs ak = args;
+    ak.total = BH * ((args.nblk + 1) / 2);
+    void* kk[] = {(void*)&ak};
+    const void* fk = causal ? (const void*)bwd_dkdv_kernel<D, true, kDK>
+                            : (const void*)bwd_dkdv_kernel<D, false, kDK>;
+    return hipLaunchKernel(fk, dim3(ak.total), dim3(64 * dkdv_waves<kDK>()), kk, 0, s);
 }
 
 hipError_t launch_attn_bwd(const BwdPrep& pp, const BwdArgs& args, int B, int d, int causal,

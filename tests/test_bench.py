@@ -98,7 +98,8 @@ def test_record_traffic_of_the_backward_sums_its_kernels_per_call(tmp_path, monk
             ("void sage::bwd_t8_kernel<128>(signed char const*, int, signed char*)", 2.0),
             ("void sage::bwd_t8_kernel<128>(signed char const*, int, signed char*)", 3.0),
             ("void sage::bwd_dq_kernel<128, false>(sage::BwdArgs)", 100.0),
-            ("void sage::bwd_dkdv_kernel<128, false>(sage::BwdArgs)", 200.0)]
+            ("void sage::bwd_dkdv_kernel<128, false, 1>(sage::BwdArgs)", 80.0),
+            ("void sage::bwd_dkdv_kernel<128, false, 2>(sage::BwdArgs)", 120.0)]
     # the training forward and the copy are not part of a backward call; two calls
     rows = [("__amd_rocclr_copyBuffer", gib_kib),
             ("void sage::attn_fwd_kernel<128, false, false, 0, false>(sage::AttnArgs)", 50.0)]
@@ -109,8 +110,8 @@ def test_record_traffic_of_the_backward_sums_its_kernels_per_call(tmp_path, monk
     assert e["fetch_bytes"] == pytest.approx(315.0 * 1024)
     assert e["write_bytes"] == pytest.approx(315.0 * 1024)
     assert e["source_hash"] == bench.attn_source_hash(bwd=True) != bench.attn_source_hash()
-    # counters without a dK/dV sweep say nothing per call
-    _write_counters(tmp_path / "w2", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", gib_kib)] + call[:1])
+    # counters without a dQ sweep say nothing per call
+    _write_counters(tmp_path / "w2", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", gib_kib)] + call[:3])
     with pytest.raises(SystemExit):
         bench.record_traffic("video_14b_720p", "fp8", str(tmp_path / "f"), str(tmp_path / "w2"),
                              bwd=True)
