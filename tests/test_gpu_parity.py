@@ -384,6 +384,32 @@ def test_full_size_sampled(sage, orc, name, pv):
         assert c_gpu >= COS_FP64, c_gpu
 
 
+@pytest.mark.xfail(strict=True, reason=(
+    "unmet bar, kept visible: the outlier workload (d = 64, x30 query tokens) reaches "
+    "about 0.9968 against FP64 attention at full size, as the oracle does (the INT8 "
+    "resolution of K times the large queries); test_full_size_sampled holds the GPU "
+    "to the oracle's own FP64 cosine within 2e-4"))
+@pytest.mark.parametrize("pv", ["fp8", "fp16"])
+def test_outlier_full_size_gpu_meets_fp64_bar(sage, orc, pv):
+    """The FP64 bar (cosine >= 0.999 against plain attention) on the GPU output
+    of the outlier workload at full size, on the first head's sampled rows (the
+    outlier tokens included)."""
+    print(f"[outlier FP64 bar] pv={pv}", flush=True)
+    wl = si.make("outlier", device="cuda")
+    qz = sage.quant_qk(wl.q, wl.k)
+    vq, vs = sage.quant_v(wl.v, pv)
+    out = sage.attn_fwd(qz, vq, vs, causal=wl.causal, sm_scale=wl.sm_scale, pv=pv,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl, 0, 0, np.random.default_rng(2))
+    q, k, v = (codes(x[:1, :1]) for x in (wl.q, wl.k, wl.v))
+    ref = orc.ref64_rows_head(q, k, v, 0, 0, rows, wl.causal, wl.sm_scale)
+    o_gpu = out[0, 0, torch.from_numpy(rows).long().cuda()].cpu().numpy()
+    c = _cos(o_gpu, ref)
+    print(f"  cos64 gpu {c:.6f}")
+    assert c >= COS_FP64, c
+
+
 # ------------------------------------------------------- per-token Q scales
 def run_gpu_token(sage, wl, pv, layout="HND"):
     qd, kd, vd = (_to_layout(t, layout).cuda() for t in (wl.q, wl.k, wl.v))
