@@ -208,7 +208,7 @@ __device__ inline void softmax_prep(v16i* S, v16f* F, float c, const uint8_t* br
 // c == 0 only when the whole tile's S is 0; any positive factor then gives
 // the same argument, and a positive one keeps -inf * factor = -inf.
 // With Q smoothing F already holds s: p = exp2(fp32(s - mu)).
-template <bool QSM, bool XS, typename PT>
+template <bool QSM, bool XS, typename PT, bool SUM = true>
 __device__ inline float softmax_block(const v16f& Fk, PT* P, int k4, float cf, float mu,
                                       float& xs) {
     float part[4], xpart[4];
@@ -226,9 +226,13 @@ __device__ inline float softmax_block(const v16f& Fk, PT* P, int k4, float cf, f
             int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
             w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
             P[k4 >> 1][(k4 & 1) * 4 + u] = w;
-            const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-            const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-            part[u] = (lo.x + lo.y) + (hi.x + hi.y);
+            if constexpr (SUM) {
+                const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+                const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+                part[u] = (lo.x + lo.y) + (hi.x + hi.y);
+            } else {
+                part[u] = 0.0f;
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) P[2 * k4 + (u >> 1)][4 * (u & 1) + j] = (_Float16)p[j];
@@ -909,6 +913,10 @@ __global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
     PT P[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) P[i] = PT{};
+    // FP8 P: the row sum of the quantized P on the matrix core (two 16x16x128
+    // MFMAs per tile, see rowsum_p); FP16 P: each lane adds its half
+    constexpr bool RSN = !PV16;
+    const v8i ones = rowsum_pattern(lane);
     const int kmax = N - 1;
     load_kv(0);
     wait_vmem();
@@ -931,8 +939,15 @@ __global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
         float part[4];
         float xs;
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) part[k4] = softmax_block<false, false>(F[k4], P, k4, cf, mu, xs);
-        l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
+        for (int k4 = 0; k4 < 4; ++k4)
+            part[k4] = softmax_block<false, false, PT, !RSN>(F[k4], P, k4, cf, mu, xs);
+        if constexpr (RSN) {
+            v4f rs = rowsum_p(ones, P, v4f{}, 0);
+            rs = rowsum_p(ones, P, rs, 1);
+            l = alpha * l + rs[0];
+        } else {
+            l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
+        }
         pv_tile<D>(smem + VB + (t & 1) * L::VBYTES, P, O, alpha, n, hh);
         wait_vmem();
         __syncthreads();
@@ -940,7 +955,7 @@ __global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
     // the last P V completes while every lane is active (see attn_mx_kernel)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) consume(O[cb]);
-    const float lt = pair_sum(l);
+    const float lt = RSN ? l : pair_sum(l);
     if (!active || qi >= N) return;
     store_row<D, false>(a, O, lt, b, h, bh, qi, hh);
 }
