@@ -8,7 +8,7 @@
 //   S  = q8 . k8 (INT8 MFMA, the forward's codes, K smoothed)
 //   P  = exp2(fma(S, c, -lse_i)),  c = fp32(fp32(q_scale * lambda) * k_scale)
 //   dP = f16(dO) . f16(V)^T (FP16 MFMA, FP32 accumulation)
-//   dS = P (dP - D_i),  D_i = dO_i . O_i
+//   dS = P (dP - D_i),  D_i = dO_i . O_i (dP's MFMA chain starts at -D_i)
 //   dV += dO8^T . e4m3(448 P) * s_do / 448        (FP8 MFMA; dO8 per 128-row block)
 //   dK += Q8^T . dS8 * s_ds * q_scale * sm_scale   (INT8 MFMA; dS8 per tile pair)
 //   dQ += K8^T . dS8^T * s_ds * k_scale * sm_scale (INT8 MFMA)
@@ -68,7 +68,8 @@ __device__ inline _Float16 f16_sat(float x) {
     return (_Float16)fminf(fmaxf(x, -65504.0f), 65504.0f);
 }
 
-// One block of 128 rows of a head: D_i = dO_i . O_i (fp32), fp16 copies of dO
+// One block of 128 rows of a head: D_i = dO_i . O_i (fp32; the tile record
+// keeps -D_i, the start of the key sweeps' dP chains), fp16 copies of dO
 // and V (row-major, padded rows 0), and dO in FP8 e4m3 for the block's absmax
 // scale s_do = fp32(a / 448) (codes of fp32(dO * fp32(448 / a))), written
 // channel-major [D][128] with the rows in pi64 order.
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(
         float* rc = rec + ((int64_t)bh * nblk + blk) * kRecFloats;
         if (cg == 0) {
             Dq[bh * N_pad + row] = part;
-            rc[kBlk + r] = part;
+            rc[kBlk + r] = -part;
             rc[r] = row < N ? lse[(int64_t)bh * N + row] : 0.0f;
         }
         v8h hd, hv;
@@ -313,6 +314,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
     v16f dq[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) dq[cb] = v16f{};
+    // dP^T's accumulation starts at -D_i, so the chain yields dP - D directly
+    v16f negD;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negD[r] = -Di;
     const int ntiles = CAUSAL ? min(2 * qg + 2, a.nblk) : a.nblk;
     const float* ksrow = a.k_scale + bh * a.nblk;
     float ks_next = ksrow[0];
@@ -345,7 +350,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
             for (int kk = 0; kk < KK; ++kk) ka[kk] = *(const v4i*)(krow + 32 * kk);
             const uint8_t* vrow = vbuf + (32 * k4 + n) * R16 + 16 * hh;
             v16i Sk = v16i{};
-            v16f dPk = v16f{};
+            v16f dPk = negD;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 v8h va[HK / 2];
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)Sk[r], c, -lse));
-                ds[k4][r] = p * (dPk[r] - Di);
+                ds[k4][r] = p * dPk[r];
             }
         }
         // P^T and dS^T of masked entries (key >= N, causal key > query) to 0;
@@ -599,7 +604,16 @@ __global__ __launch_bounds__(64 * dkdv_waves<MODE>(), MODE == kDV ? 2 : 1) void 
                 for (int kk = 0; kk < KK; ++kk) qa[kk] = *(const v4i*)(qrow + 32 * kk);
                 const uint8_t* hrow = hbuf + (32 * q4 + n) * R16 + 16 * hh;
                 v16i Sq = v16i{};
-                v16f dPq = v16f{};
+                // dP's accumulation starts at the record's -D of each query
+                v16f dPq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 D4 = *(const float4*)&recL[kBlk + 32 * q4 + 8 * i + 4 * hh];
+                    dPq[4 * i] = D4.x;
+                    dPq[4 * i + 1] = D4.y;
+                    dPq[4 * i + 2] = D4.z;
+                    dPq[4 * i + 3] = D4.w;
+                }
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     // dP's operands in two halves of the channels
@@ -619,13 +633,12 @@ __global__ __launch_bounds__(64 * dkdv_waves<MODE>(), MODE == kDV ? 2 : 1) void 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float4 L4 = *(const float4*)&recL[32 * q4 + 8 * i + 4 * hh];
-                    const float4 D4 = *(const float4*)&recL[kBlk + 32 * q4 + 8 * i + 4 * hh];
-                    const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+                    const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int r = 4 * i + j;
                         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf((float)Sq[r], c, -Lv[j]));
-                        ds[q4][r] = pv * (dPq[r] - Dv[j]);
+                        ds[q4][r] = pv * dPq[r];
                     }
                 }
             }

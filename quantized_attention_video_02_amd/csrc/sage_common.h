@@ -85,7 +85,7 @@ struct BwdPrep {
 };
 // Per-tile record of the dK/dV sweep, one per (bh, query block), copied into
 // LDS with the tile: lse and D of the block's rows, its Q scale and dO scale.
-constexpr int kRecFloats = 512;  // 2 KB: [0, 128) lse, [128, 256) D, 256 q_scale, 257 s_do
+constexpr int kRecFloats = 512;  // 2 KB: [0, 128) lse, [128, 256) -D, 256 q_scale, 257 s_do
 struct BwdArgs {
     const int8_t* q8;
     const float* q_scale;  // per block of kBlk queries [bh][nblk]
