@@ -8,8 +8,9 @@ per-channel FP8 V, the K and V statistics in one launch) and sage_attn_fwd
 scales and Q smoothing go through sage_quant_qk(_ex/_smooth) + sage_quant_v.  The headline workload is the 720p clip
 of a 14B video DiT: B=1, H=40, N=75600 (21 x 45 x 80 latent tokens), d=128.
 
---mx runs the microscaled path instead: sage_quant_qk_mx, sage_quant_v_mx and
-sage_attn_fwd_mx (Q, K, P and V in MXFP6), priced against the dense FP6 peak.
+--mx runs the microscaled path instead: sage_quant_qk_mx_fmt, sage_quant_v_mx_fmt
+and sage_attn_fwd_mx_fmt (Q, K, P and V in MXFP6, or MXFP4 with --mx mxfp4),
+priced against the dense FP6 = FP4 peak.
 --bwd times the 8-bit backward (sage_attn_bwd) over the training forward's
 outputs: 10 B H N^2 d ops per step (the five backward products), priced
 against the blend of their peaks (four INT8/FP8 products, dP in FP16).
@@ -39,6 +40,7 @@ METRIC = "attention TOPS (4·B·H·N²·d/s) & % MFMA peak at N=32760/75600, d=1
 PEAK_TOPS = {"fp8": 5000.0,                       # dense INT8 (QK) = dense FP8 (PV) = 5.0 POPS
              "fp16": 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0),  # INT8 QK half + FP16 PV half
              "mxfp6": 10100.0,                    # dense FP6 (= FP4) MFMA, both products
+             "mxfp4": 10100.0,
              # backward: 2d ops each for S, dV, dK, dQ at 5.0 POPS and dP at 2.5
              "bwd": 10.0 / (8.0 / 5000.0 + 2.0 / 2500.0)}
 HBM_GBPS = 8000.0
@@ -108,10 +110,17 @@ def visited_ops(wl, mask):
     return 4.0 * wl.d * float((mask.astype(np.float64) * pairs).sum())
 
 
+def mx_format(mx):
+    """The MX element format an `mx` argument names: False / None (the INT8
+    path), True (MXFP6), or "mxfp6" / "mxfp4"."""
+    return "mxfp6" if mx is True else (mx or None)
+
+
 def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None, q_smooth=False,
              mx=False):
     import torch
 
+    mx = mx_format(mx)
     q, k, v = wl.q, wl.k, wl.v
     stream = torch.cuda.current_stream()
 
@@ -119,7 +128,7 @@ def time_gpu(sage, wl, pv, steps, warmup, q_gran="block", tile_mask=None, q_smoo
         if evs:
             evs[0].record(stream)
         if mx:
-            mz, v6 = sage.quant_qk_mx(q, k), sage.quant_v_mx(v)
+            mz, v6 = sage.quant_qk_mx(q, k, fmt=mx), sage.quant_v_mx(v, fmt=mx)
         elif q_gran == "block" and not q_smooth:
             qz, vq, vs = sage.quant_qkv(q, k, v, pv)
         else:
@@ -253,7 +262,7 @@ def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False, mx=False
     all N keys; the head's quantization time is charged pro rata (R / N).
     With Q smoothing the correction rows of the blocks the R rows use are
     computed too (charged to the quantization at the rate per block).  With
-    mx the oracle's MXFP6 quantization and attention.
+    mx ("mxfp6" or "mxfp4") the oracle's MX quantization and attention.
 
     Then the all-core run: `cores` threads (default host_cores()) each run the
     same single-threaded oracle on disjoint query rows of the head, wall-clocked
@@ -266,12 +275,13 @@ def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False, mx=False
     import oracle
     import synthetic_inputs as si
 
+    mx = mx_format(mx)
     b, h = 0, 0
     q, k, v = (si.bf16_codes(t[b:b + 1, h:h + 1]) for t in (wl.q, wl.k, wl.v))
     t0 = time.perf_counter()
     if mx:
-        mz = oracle.mx_quant_qk(q, k)
-        vc, ve = oracle.mx_quant_v(v)
+        mz = oracle.mx_quant_qk(q, k, mx)
+        vc, ve = oracle.mx_quant_v(v, mx)
     else:
         oz = oracle.quant_qk(q, k, q_gran=q_gran, q_smooth=q_smooth)
         ovq, ovs = oracle.quant_v(v, pv)
@@ -315,7 +325,7 @@ def cpu_baseline(wl, pv, target_s=12.0, q_gran="block", q_smooth=False, mx=False
               f"({t_quant:.2f} s, charged pro rata) + attention for {R} queries x "
               f"{'their causal keys' if wl.causal else f'{wl.N} keys'} ({t_attn:.2f} s)"
               + (f"; Q-smoothing correction of their blocks ({t_bias:.2f} s, pro rata)"
-                 if q_smooth else "") + ("; MXFP6 path" if mx else "") + "; C oracle")
+                 if q_smooth else "") + (f"; {mx.upper()} path" if mx else "") + "; C oracle")
     P = host_cores() if cores is None else int(cores)
     if P <= 1:
         return {"value": single, "unit": "TOPS", "cores": 1, "kind": "oracle",
@@ -402,6 +412,8 @@ def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False,
     import csv
     import glob
 
+    mx = mx_format(mx)
+
     def per_kernel(d, counter):
         rows = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -435,7 +447,7 @@ def record_traffic(workload, pv, fetch_dir, write_dir, q_gran="block", mx=False,
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
-    data[traffic_key(workload, "bwd" if bwd else ("mxfp6" if mx else pv), q_gran)] = entry
+    data[traffic_key(workload, "bwd" if bwd else (mx if mx else pv), q_gran)] = entry
     if not bwd and not mx:
         # the quantization pass of the same runs: all its kernels, per step
         # (a step launches the quantization kernels once: one quant_qk_kernel)
@@ -480,9 +492,9 @@ def main():
     ap.add_argument("--q-sigma", type=float, default=None,
                     help="give the workload's queries a per-channel offset of this sigma "
                          "(the inputs Q smoothing is for)")
-    ap.add_argument("--mx", action="store_true",
-                    help="the microscaled path: Q, K, P and V in MXFP6 (sage_quant_qk_mx, "
-                         "sage_quant_v_mx, sage_attn_fwd_mx)")
+    ap.add_argument("--mx", nargs="?", const="mxfp6", default=None, choices=["mxfp6", "mxfp4"],
+                    help="the microscaled path: Q, K, P and V in MXFP6 (the default) or MXFP4 "
+                         "(sage_quant_qk_mx_fmt, sage_quant_v_mx_fmt, sage_attn_fwd_mx_fmt)")
     ap.add_argument("--bwd", action="store_true",
                     help="the 8-bit backward (sage_attn_bwd) over the training forward's outputs")
     ap.add_argument("--shape", default=None, metavar="B,H,N",
@@ -510,7 +522,7 @@ def main():
         sys.exit(2)
     if args.mx and (args.q_smooth or args.tile_keep is not None or args.q_gran != "block"
                     or args.pv != "fp8"):
-        print("bench.py: --mx runs the MXFP6 path alone (no --q-smooth, --tile-keep, "
+        print("bench.py: --mx runs the MX path alone (no --q-smooth, --tile-keep, "
               "--q-gran token or --pv fp16)", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -535,7 +547,7 @@ def main():
     # traffic.json holds counter runs of the named workloads as they are defined
     stock = not dims and not args.no_causal
     torch.cuda.synchronize()
-    fmt = "mxfp6" if args.mx else args.pv
+    fmt = args.mx if args.mx else args.pv
     print(f"[bench] {wl.name}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} causal={wl.causal} path={fmt}",
           file=sys.stderr, flush=True)
     if args.calibrate_copy:
@@ -630,7 +642,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp8": "int8+fp8", "fp16": "int8+fp16", "mxfp6": "mxfp6"}[fmt],
+        "dtype": {"fp8": "int8+fp8", "fp16": "int8+fp16", "mxfp6": "mxfp6", "mxfp4": "mxfp4"}[fmt],
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
                    "causal": wl.causal, "pv": fmt, "q_gran": "mx32" if args.mx else args.q_gran,

@@ -80,6 +80,8 @@ enum sage_out_dtype { SAGE_OUT_BF16 = 0, SAGE_OUT_FP32 = 1 };
  * QbitAI article, section 四个步骤极限压缩时间); SAGE_QGRAN_TOKEN is the finest
  * Q granularity: one scale per query row.  K stays per block of 128 rows. */
 enum sage_q_gran { SAGE_QGRAN_BLOCK = 0, SAGE_QGRAN_TOKEN = 1 };
+/* Element format of the microscaled path: E2M3 (MXFP6) or E2M1 (MXFP4). */
+enum sage_mx_fmt { SAGE_MX_FP4 = 4, SAGE_MX_FP6 = 6 };
 
 /* Compile-time constants of the method as built. */
 typedef struct {
@@ -368,19 +370,26 @@ int sage_attn_fwd_smooth(const int8_t* q8, const float* q_scale, const int8_t* k
                          int out_dtype, void* stream);
 
 /*
- * Microscaled attention, MXFP6 (reportify.cn SageAttention3 summary, bullet
- * FP4量化创新: microscaling FP4 attention; MXFP4 rated less accurate there).
- * The gfx950 matrix cores take MX operands with E8M0 block scales of 32
- * (OCP Microscaling), FP4 and FP6 at the same rate; this path uses FP6 E2M3
- * elements (3 mantissa bits): with E2M1 (FP4) the cosine against FP64
- * attention drops to ~0.97 on Gaussian inputs, with E2M3 it stays ~0.998.
- * Every MX block of 32 elements is stored as 32 bytes: the 24 bytes of the
- * 32 packed E2M3 codes (element 2i at bits [12i, 12i + 6) is value i of the
- * block, element 2i + 1 is value 16 + i: the packing of
- * v_cvt_scalef32_2xpk16_fp6_f32), the E8M0 scale byte at offset 24, then 7
- * zero bytes.  Block rule: e = floor(log2(amax)) - 2, codes =
- * E2M3(x / 2^e) rounded to nearest even and saturated at 7.5, byte e + 127;
- * a block with amax < 2^-100 is all zero with byte 0.
+ * Microscaled attention, MXFP6 or MXFP4 (reportify.cn SageAttention3
+ * summary, bullet FP4量化创新: microscaling FP4 attention; MXFP4 rated less
+ * accurate there).  The gfx950 matrix cores take MX operands with E8M0
+ * block scales of 32 (OCP Microscaling), FP4 and FP6 at the same rate.  The
+ * default entry points use FP6 E2M3 elements (3 mantissa bits); the _fmt
+ * forms take fmt = SAGE_MX_FP6 or SAGE_MX_FP4 (E2M1, 1 mantissa bit: the
+ * cosine against FP64 attention drops from ~0.998 to ~0.97 on Gaussian
+ * inputs).  The pages' two-stage quantization of P answers the narrow range
+ * of NVFP4's FP8 block scales; an E8M0 scale is any power of two, so P is
+ * quantized in one stage here.
+ * Every MX block of 32 elements is stored as 32 bytes.  E2M3: the 24 bytes
+ * of the 32 packed codes (element 2i at bits [12i, 12i + 6) is value i of
+ * the block, element 2i + 1 is value 16 + i: the packing of
+ * v_cvt_scalef32_2xpk16_fp6_f32).  E2M1: 16 bytes, byte i holding value i
+ * in its low nibble and value 16 + i in its high nibble (the packing of
+ * v_cvt_scalef32_pk_fp4_f32 with those two values), then 8 zero bytes.
+ * Both: the E8M0 scale byte at offset 24, then 7 zero bytes.  Block rule:
+ * e = floor(log2(amax)) - 2, codes = element(x / 2^e) rounded to nearest
+ * even and saturated at the largest magnitude (7.5 for E2M3, 6 for E2M1),
+ * byte e + 127; a block with amax < 2^-100 is all zero with byte 0.
  *   sage_quant_qk_mx: K smoothed as in sage_quant_qk (k_mean, same
  *     workspace), then Q and K' per row and 32 channels:
  *     q6, k6 [B][H][N_pad][d] bytes (d / 32 blocks per row), rows >= N 0.
@@ -408,6 +417,17 @@ int sage_quant_v_mx(const void* v, int B, int H, int N, int d, int layout, uint8
 int sage_attn_fwd_mx(const uint8_t* q6, const uint8_t* k6, const uint8_t* v6, int B, int H, int N,
                      int d, int layout, int causal, float sm_scale, void* out, int out_dtype,
                      void* stream);
+/* The same three calls for element format fmt (SAGE_MX_FP6 or SAGE_MX_FP4;
+ * any other value: SAGE_ERR_INVALID, nothing launched).  The three calls of
+ * one attention take the same fmt; buffers and sizes do not depend on it. */
+int sage_quant_qk_mx_fmt(const void* q, const void* k, int B, int H, int N, int d, int layout,
+                         int fmt, uint8_t* q6, uint8_t* k6, float* k_mean, void* workspace,
+                         size_t workspace_bytes, void* stream);
+int sage_quant_v_mx_fmt(const void* v, int B, int H, int N, int d, int layout, int fmt,
+                        uint8_t* v6, void* stream);
+int sage_attn_fwd_mx_fmt(const uint8_t* q6, const uint8_t* k6, const uint8_t* v6, int B, int H,
+                         int N, int d, int layout, int fmt, int causal, float sm_scale, void* out,
+                         int out_dtype, void* stream);
 
 /*
  * sage_attn_fwd that also writes the raw int32 Q K^T accumulators of head

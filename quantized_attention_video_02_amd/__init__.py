@@ -46,7 +46,8 @@ EXPORTS = ["sage_get_config", "sage_quant_sizes", "sage_quant_sizes_ex", "sage_q
            "sage_quant_qk_ex", "sage_quant_v", "sage_quant_qkv", "sage_quant_qkv_noalloc", "sage_attn_fwd", "sage_attn_fwd_lse", "sage_attn_fwd_ex",
            "sage_attn_fwd_sparse", "sage_attn_fwd_debug", "sage_qsmooth_sizes",
            "sage_quant_qk_smooth", "sage_q_smooth_bias", "sage_attn_fwd_smooth",
-           "sage_quant_qk_mx", "sage_quant_v_mx", "sage_attn_fwd_mx", "sage_bwd_sizes",
+           "sage_quant_qk_mx", "sage_quant_v_mx", "sage_attn_fwd_mx", "sage_quant_qk_mx_fmt",
+           "sage_quant_v_mx_fmt", "sage_attn_fwd_mx_fmt", "sage_bwd_sizes",
            "sage_attn_bwd", "sage_status_string"]
 
 _lib = None
@@ -83,6 +84,9 @@ def lib():
     L.sage_quant_qk_mx.argtypes = [P, P, I, I, I, I, I, P, P, P, P, S, P]
     L.sage_quant_v_mx.argtypes = [P, I, I, I, I, I, P, P]
     L.sage_attn_fwd_mx.argtypes = [P, P, P, I, I, I, I, I, I, F, P, I, P]
+    L.sage_quant_qk_mx_fmt.argtypes = [P, P, I, I, I, I, I, I, P, P, P, P, S, P]
+    L.sage_quant_v_mx_fmt.argtypes = [P, I, I, I, I, I, I, P, P]
+    L.sage_attn_fwd_mx_fmt.argtypes = [P, P, P, I, I, I, I, I, I, I, F, P, I, P]
     L.sage_bwd_sizes.argtypes = [I, I, I, I, ct.POINTER(ct.c_size_t)]
     L.sage_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, P, S, P]
     for name in EXPORTS[:-1]:
@@ -398,10 +402,20 @@ def attn_bwd(qz: dict, v: torch.Tensor, o: torch.Tensor, do: torch.Tensor, lse: 
     return dq, dk, dv
 
 
-# ------------------------------------------------------------- MXFP6 path
-def quant_qk_mx(q: torch.Tensor, k: torch.Tensor, layout: str = "HND") -> dict:
-    """Smooth K, then Q and K to MXFP6 (sage_quant_qk_mx): q6, k6 uint8
-    [B, H, N_pad, d] (32-byte MX blocks, see sage.h), k_mean."""
+# ------------------------------------------------------------- MX path
+MX_FMT = {"mxfp6": 6, "mxfp4": 4}   # sage_mx_fmt: E2M3, E2M1
+
+
+def _mx_fmt(fmt: str) -> int:
+    if fmt not in MX_FMT:
+        raise ValueError(f"fmt must be one of {sorted(MX_FMT)}")
+    return MX_FMT[fmt]
+
+
+def quant_qk_mx(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", fmt: str = "mxfp6") -> dict:
+    """Smooth K, then Q and K to MXFP6 or MXFP4 (sage_quant_qk_mx_fmt): q6, k6
+    uint8 [B, H, N_pad, d] (32-byte MX blocks, see sage.h), k_mean."""
+    f = _mx_fmt(fmt)
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
         raise TypeError("q and k must be bfloat16")
     if q.shape != k.shape or not q.is_contiguous() or not k.is_contiguous():
@@ -414,29 +428,34 @@ def quant_qk_mx(q: torch.Tensor, k: torch.Tensor, layout: str = "HND") -> dict:
              k6=torch.empty((B, H, nblk * 128, d), dtype=torch.uint8, device=dev),
              k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev),
              workspace=_empty(sz[BUF_WS_QK], dev, torch.int64))
-    _check(lib().sage_quant_qk_mx(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout], _ptr(r["q6"]),
-                                  _ptr(r["k6"]), _ptr(r["k_mean"]), _ptr(r["workspace"]),
-                                  sz[BUF_WS_QK], _stream(dev)))
-    r.update(B=B, H=H, N=N, d=d, layout=layout)
+    _check(lib().sage_quant_qk_mx_fmt(_ptr(q), _ptr(k), B, H, N, d, LAYOUTS[layout], f,
+                                      _ptr(r["q6"]), _ptr(r["k6"]), _ptr(r["k_mean"]),
+                                      _ptr(r["workspace"]), sz[BUF_WS_QK], _stream(dev)))
+    r.update(B=B, H=H, N=N, d=d, layout=layout, fmt=fmt)
     return r
 
 
-def quant_v_mx(v: torch.Tensor, layout: str = "HND") -> torch.Tensor:
-    """V to MXFP6 (sage_quant_v_mx): uint8 [B, H, nblk, d, 128]."""
+def quant_v_mx(v: torch.Tensor, layout: str = "HND", fmt: str = "mxfp6") -> torch.Tensor:
+    """V to MXFP6 or MXFP4 (sage_quant_v_mx_fmt): uint8 [B, H, nblk, d, 128]."""
+    f = _mx_fmt(fmt)
     if v.dtype != torch.bfloat16 or not v.is_contiguous():
         raise TypeError("v must be a contiguous bfloat16 tensor")
     B, H, N, d = _dims(v, layout)
     dev = _one_gpu(v)
     nblk = -(-N // 128)
     v6 = torch.empty((B, H, nblk, d, 128), dtype=torch.uint8, device=dev)
-    _check(lib().sage_quant_v_mx(_ptr(v), B, H, N, d, LAYOUTS[layout], _ptr(v6), _stream(dev)))
+    _check(lib().sage_quant_v_mx_fmt(_ptr(v), B, H, N, d, LAYOUTS[layout], f, _ptr(v6),
+                                     _stream(dev)))
     return v6
 
 
 def attn_fwd_mx(mz: dict, v6: torch.Tensor, causal: bool = False, sm_scale: float | None = None,
                 out_dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
-    """MXFP6 attention over quantized operands (sage_attn_fwd_mx)."""
+    """MX attention over quantized operands (sage_attn_fwd_mx_fmt), in the
+    element format Q and K were quantized to (mz["fmt"]; v6 must have been
+    quantized to the same one)."""
     B, H, N, d, layout = mz["B"], mz["H"], mz["N"], mz["d"], mz["layout"]
+    f = _mx_fmt(mz.get("fmt", "mxfp6"))
     sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
     shape = (B, H, N, d) if layout == "HND" else (B, N, H, d)
     dev = _one_gpu(mz["q6"], mz["k6"], v6, out)
@@ -448,16 +467,16 @@ def attn_fwd_mx(mz: dict, v6: torch.Tensor, causal: bool = False, sm_scale: floa
         out = torch.empty(shape, dtype=out_dtype, device=dev)
     else:
         _check_out(out, shape, dev)
-    _check(lib().sage_attn_fwd_mx(_ptr(mz["q6"]), _ptr(mz["k6"]), _ptr(v6), B, H, N, d,
-                                  LAYOUTS[layout], int(bool(causal)), sm, _ptr(out),
-                                  OUT[out.dtype], _stream(dev)))
+    _check(lib().sage_attn_fwd_mx_fmt(_ptr(mz["q6"]), _ptr(mz["k6"]), _ptr(v6), B, H, N, d,
+                                      LAYOUTS[layout], f, int(bool(causal)), sm, _ptr(out),
+                                      OUT[out.dtype], _stream(dev)))
     return out
 
 
 def attn_mx(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
             sm_scale: float | None = None, layout: str = "HND",
-            out_dtype=torch.bfloat16) -> torch.Tensor:
-    """softmax(Q K^T sm_scale) V through the MXFP6 path."""
-    mz = quant_qk_mx(q, k, layout)
-    v6 = quant_v_mx(v, layout)
+            out_dtype=torch.bfloat16, fmt: str = "mxfp6") -> torch.Tensor:
+    """softmax(Q K^T sm_scale) V through the MX path (MXFP6 or MXFP4)."""
+    mz = quant_qk_mx(q, k, layout, fmt)
+    v6 = quant_v_mx(v, layout, fmt)
     return attn_fwd_mx(mz, v6, causal=causal, sm_scale=sm_scale, out_dtype=out_dtype)

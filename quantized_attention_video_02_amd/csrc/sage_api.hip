@@ -457,13 +457,16 @@ __attribute__((visibility("default"))) int sage_attn_fwd_debug(
                        h, row0, nrows, s_out, stream);
 }
 
-__attribute__((visibility("default"))) int sage_quant_qk_mx(const void* q, const void* k, int B,
-                                                            int H, int N, int d, int layout,
-                                                            uint8_t* q6, uint8_t* k6,
-                                                            float* k_mean, void* workspace,
-                                                            size_t workspace_bytes,
-                                                            void* stream) {
+static bool mx_fmt_ok(int fmt) { return fmt == SAGE_MX_FP6 || fmt == SAGE_MX_FP4; }
+
+__attribute__((visibility("default"))) int sage_quant_qk_mx_fmt(const void* q, const void* k, int B,
+                                                                int H, int N, int d, int layout,
+                                                                int fmt, uint8_t* q6, uint8_t* k6,
+                                                                float* k_mean, void* workspace,
+                                                                size_t workspace_bytes,
+                                                                void* stream) {
     if (!q || !k || !q6 || !k6 || !k_mean || !workspace) return SAGE_ERR_NULL;
+    if (!mx_fmt_ok(fmt)) return SAGE_ERR_INVALID;
     SAGE_TRY(check_dims(B, H, N, d));
     SAGE_TRY(check_layout(layout));
     if (!aligned16(q) || !aligned16(k) || !aligned16(q6) || !aligned16(k6) || !aligned16(k_mean) ||
@@ -472,28 +475,47 @@ __attribute__((visibility("default"))) int sage_quant_qk_mx(const void* q, const
     const Sizes s = sizes_of(B, H, N, d, SAGE_PV_FP8);
     if (workspace_bytes < s.v[SAGE_BUF_WS_QK]) return SAGE_ERR_WORKSPACE;
     const hipError_t e = sage::launch_quant_qk_mx((const sage::u16*)q, (const sage::u16*)k, B, H, N,
-                                                  d, layout, q6, k6, k_mean, (uint64_t*)workspace,
-                                                  (hipStream_t)stream);
+                                                  d, layout, fmt, q6, k6, k_mean,
+                                                  (uint64_t*)workspace, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+__attribute__((visibility("default"))) int sage_quant_qk_mx(const void* q, const void* k, int B,
+                                                            int H, int N, int d, int layout,
+                                                            uint8_t* q6, uint8_t* k6,
+                                                            float* k_mean, void* workspace,
+                                                            size_t workspace_bytes,
+                                                            void* stream) {
+    return sage_quant_qk_mx_fmt(q, k, B, H, N, d, layout, SAGE_MX_FP6, q6, k6, k_mean, workspace,
+                                workspace_bytes, stream);
+}
+
+__attribute__((visibility("default"))) int sage_quant_v_mx_fmt(const void* v, int B, int H, int N,
+                                                               int d, int layout, int fmt,
+                                                               uint8_t* v6, void* stream) {
+    if (!v || !v6) return SAGE_ERR_NULL;
+    if (!mx_fmt_ok(fmt)) return SAGE_ERR_INVALID;
+    SAGE_TRY(check_dims(B, H, N, d));
+    SAGE_TRY(check_layout(layout));
+    if (!aligned16(v) || !aligned16(v6)) return SAGE_ERR_ALIGN;
+    const hipError_t e = sage::launch_quant_v_mx((const sage::u16*)v, B, H, N, d, layout, fmt, v6,
+                                                 (hipStream_t)stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
 __attribute__((visibility("default"))) int sage_quant_v_mx(const void* v, int B, int H, int N, int d,
                                                            int layout, uint8_t* v6, void* stream) {
-    if (!v || !v6) return SAGE_ERR_NULL;
-    SAGE_TRY(check_dims(B, H, N, d));
-    SAGE_TRY(check_layout(layout));
-    if (!aligned16(v) || !aligned16(v6)) return SAGE_ERR_ALIGN;
-    const hipError_t e = sage::launch_quant_v_mx((const sage::u16*)v, B, H, N, d, layout, v6,
-                                                 (hipStream_t)stream);
-    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+    return sage_quant_v_mx_fmt(v, B, H, N, d, layout, SAGE_MX_FP6, v6, stream);
 }
 
-__attribute__((visibility("default"))) int sage_attn_fwd_mx(const uint8_t* q6, const uint8_t* k6,
-                                                            const uint8_t* v6, int B, int H, int N,
-                                                            int d, int layout, int causal,
-                                                            float sm_scale, void* out,
-                                                            int out_dtype, void* stream) {
+__attribute__((visibility("default"))) int sage_attn_fwd_mx_fmt(const uint8_t* q6, const uint8_t* k6,
+                                                                const uint8_t* v6, int B, int H,
+                                                                int N, int d, int layout, int fmt,
+                                                                int causal, float sm_scale,
+                                                                void* out, int out_dtype,
+                                                                void* stream) {
     if (!q6 || !k6 || !v6 || !out) return SAGE_ERR_NULL;
+    if (!mx_fmt_ok(fmt)) return SAGE_ERR_INVALID;
     SAGE_TRY(check_dims(B, H, N, d));
     SAGE_TRY(check_layout(layout));
     if (causal != 0 && causal != 1) return SAGE_ERR_INVALID;
@@ -512,8 +534,17 @@ __attribute__((visibility("default"))) int sage_attn_fwd_mx(const uint8_t* q6, c
     a.layout = layout;
     a.out_fp32 = out_dtype == SAGE_OUT_FP32;
     a.lambda = (float)((double)sm_scale * 1.4426950408889634);
-    const hipError_t e = sage::launch_attn_mx(a, B, d, causal, (hipStream_t)stream);
+    const hipError_t e = sage::launch_attn_mx(a, B, d, causal, fmt, (hipStream_t)stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+__attribute__((visibility("default"))) int sage_attn_fwd_mx(const uint8_t* q6, const uint8_t* k6,
+                                                            const uint8_t* v6, int B, int H, int N,
+                                                            int d, int layout, int causal,
+                                                            float sm_scale, void* out,
+                                                            int out_dtype, void* stream) {
+    return sage_attn_fwd_mx_fmt(q6, k6, v6, B, H, N, d, layout, SAGE_MX_FP6, causal, sm_scale, out,
+                                out_dtype, stream);
 }
 
 __attribute__((visibility("default"))) const char* sage_status_string(int status) {

@@ -960,11 +960,12 @@ __global__ __launch_bounds__((64 * NW), 3) void attn_np_kernel(AttnArgs a) {
     store_row<D, false>(a, O, lt, b, h, bh, qi, hh);
 }
 
-// ------------------------------------------------------------ MXFP6 attention
-// Q, K, P and V in MXFP6 (E2M3 elements, one E8M0 scale per 32 along the
-// reduction; each 32-element block stored as 32 bytes: 24 code bytes, the
-// scale byte at offset 24), Q K^T and P V on v_mfma_scale_f32_32x32x64_f8f6f4
-// (FP6 operands, the FP4 rate), the online softmax in FP32 between them.
+// -------------------------------------------------------------- MX attention
+// Q, K, P and V in MXFP6 (E2M3 elements) or MXFP4 (E2M1), one E8M0 scale per
+// 32 along the reduction; each 32-element block stored as 32 bytes: 24 (FP6)
+// or 16 (FP4) code bytes, the scale byte at offset 24.  Q K^T and P V on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (FP6 or FP4 operands, the same rate), the
+// online softmax in FP32 between them.
 // The matrix core applies the block scales, so S arrives as fp32 and the
 // epilogue needs no V scale.
 //
@@ -997,24 +998,30 @@ struct MaskTileMx {
     }
 };
 
+// Operand format code of the scaled matrix instruction for element format
+// FMT: 2 = E2M3 (FP6), 4 = E2M1 (FP4; only the first 4 dwords of an operand
+// are read).
+template <int FMT>
+constexpr int mx_code() { return FMT == 4 ? 4 : 2; }
+
 // 32-key block k4 of S^T = K6 tile . Q6^T (fp32, block scales applied): lane
 // (n, hh) reads LDS row 32 k4 + n, MX block 2 kk + hh of each 64-channel chunk.
-template <int D, int KSTR>
+template <int D, int KSTR, int FMT>
 __device__ inline v16f qk_mx(const uint8_t* kb, const v8i* qv, int k4, int n, int hh) {
     const uint8_t* krow = kb + (32 * k4 + n) * KSTR + 32 * hh;
     v16f acc = v16f{};
 #pragma unroll
     for (int kk = 0; kk < D / 64; ++kk) {
         const v8i av = *(const v8i*)(krow + 64 * kk);
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qv[kk], acc, 2, 2, 0, av[6], 0,
-                                                              qv[kk][6]);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qv[kk], acc, mx_code<FMT>(),
+                                                              mx_code<FMT>(), 0, av[6], 0, qv[kk][6]);
     }
     return acc;
 }
 
 // P V into the running output: O = alpha O + V^T P^T.  Lane (channel n, hh)
 // reads V row 32 cb + n, MX block 2 u + hh (keys 64 u + 32 hh + [0, 32)).
-template <int D>
+template <int D, int FMT>
 __device__ inline void pv_mx(const uint8_t* vb, const v8i* P, const int* pe, v16f* O, float alpha,
                              int n, int hh) {
     using L = Lds<D, false>;
@@ -1030,15 +1037,30 @@ __device__ inline void pv_mx(const uint8_t* vb, const v8i* P, const int* pe, v16
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const v8i av = *(const v8i*)(vrow + 32 * cb * L::VSTR + 64 * u);
-            O[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, P[u], O[cb], 2, 2, 0, av[6], 0,
-                                                                    pe[u]);
+            O[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, P[u], O[cb], mx_code<FMT>(),
+                                                                    mx_code<FMT>(), 0, av[6], 0, pe[u]);
         }
 }
 
 // One MX block of P: 32 probabilities (pa: keys +0..15, pb: +16..31) with
 // the block exponent e (scale 2^e; a zero block comes with scale 2^127, so
-// every code is 0).
+// every code is 0).  E2M1: byte i of the operand holds keys i and 16 + i,
+// the layout the V blocks are stored in.
+template <int FMT>
 __device__ inline v8i pack_p_mx(const v16f& pa, const v16f& pb, float scale) {
+    if constexpr (FMT == 4) {
+        v8i o = v8i{};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t d = 0u;
+            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, pa[4 * w], pb[4 * w], scale, 0);
+            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, pa[4 * w + 1], pb[4 * w + 1], scale, 1);
+            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, pa[4 * w + 2], pb[4 * w + 2], scale, 2);
+            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, pa[4 * w + 3], pb[4 * w + 3], scale, 3);
+            o[w] = (int)d;
+        }
+        return o;
+    }
     v6i r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(pa, pb, scale);
     // multi-pass conversion: its sources stay live past it, so the result
     // registers cannot overlap them.  The result passes through the same
@@ -1051,7 +1073,7 @@ __device__ inline v8i pack_p_mx(const v16f& pa, const v16f& pb, float scale) {
     return o;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int FMT>
 __global__ __launch_bounds__(512, 1) void attn_mx_kernel(AttnArgs a) {
     constexpr int NW = 8, NT = 64 * NW, BR = 32 * NW;
     using L = Lds<D, false>;
@@ -1131,7 +1153,7 @@ __global__ __launch_bounds__(512, 1) void attn_mx_kernel(AttnArgs a) {
     wait_vmem();
     __syncthreads();
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) S[k4] = qk_mx<D, L::KSTR>(smem, qv, k4, n, hh);
+    for (int k4 = 0; k4 < 4; ++k4) S[k4] = qk_mx<D, L::KSTR, FMT>(smem, qv, k4, n, hh);
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
@@ -1139,7 +1161,7 @@ __global__ __launch_bounds__(512, 1) void attn_mx_kernel(AttnArgs a) {
         load_v(t);
         const int key_t = t * kBc;
         // A
-        pv_mx<D>(smem + L::VBASE + ((t + 1) & 1) * L::VBYTES, P, pe, O, alpha, n, hh);
+        pv_mx<D, FMT>(smem + L::VBASE + ((t + 1) & 1) * L::VBYTES, P, pe, O, alpha, n, hh);
         const bool needmask = (tail && t == a.nblk - 1) || (CAUSAL && key_t + kBc - 1 > qbase);
         if (needmask) MaskTileMx<0, 0>::apply(S, kmax - key_t - 32 * hh);
         float mk[4];
@@ -1184,15 +1206,15 @@ __global__ __launch_bounds__(512, 1) void attn_mx_kernel(AttnArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) s4[u] = (p[4 * u] + p[4 * u + 1]) + (p[4 * u + 2] + p[4 * u + 3]);
             part[k4] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-            S[k4] = qk_mx<D, L::KSTR>(kb, qv, k4, n, hh);
-            if (k4 & 1) P[k4 >> 1] = pack_p_mx(pa, p, sc[k4 >> 1]);
+            S[k4] = qk_mx<D, L::KSTR, FMT>(kb, qv, k4, n, hh);
+            if (k4 & 1) P[k4 >> 1] = pack_p_mx<FMT>(pa, p, sc[k4 >> 1]);
             else pa = p;
         }
         l = alpha * l + ((part[0] + part[1]) + (part[2] + part[3]));
         wait_vmem();
         __syncthreads();
     }
-    pv_mx<D>(smem + L::VBASE + ((ntiles + 1) & 1) * L::VBYTES, P, pe, O, alpha, n, hh);
+    pv_mx<D, FMT>(smem + L::VBASE + ((ntiles + 1) & 1) * L::VBYTES, P, pe, O, alpha, n, hh);
     // The matrix instructions read operands from all 64 lanes, but the
     // operand moves feeding them obey EXEC: the final P V must complete
     // before the exit below turns padding-query lanes off, so its results
@@ -1221,13 +1243,18 @@ __global__ __launch_bounds__(512, 1) void attn_mx_kernel(AttnArgs a) {
         }
 }
 
-hipError_t launch_attn_mx(const AttnArgs& args, int B, int d, int causal, hipStream_t s) {
+template <int FMT>
+static const void* attn_mx_fn(int d, int causal) {
+    if (d == 128)
+        return causal ? (const void*)attn_mx_kernel<128, true, FMT> : (const void*)attn_mx_kernel<128, false, FMT>;
+    return causal ? (const void*)attn_mx_kernel<64, true, FMT> : (const void*)attn_mx_kernel<64, false, FMT>;
+}
+
+hipError_t launch_attn_mx(const AttnArgs& args, int B, int d, int causal, int fmt, hipStream_t s) {
     AttnArgs a = args;
     a.nqt = (a.N + 255) / 256;
     a.total = B * a.H * a.nqt;
-    const void* fn;
-    if (d == 128) fn = causal ? (const void*)attn_mx_kernel<128, true> : (const void*)attn_mx_kernel<128, false>;
-    else fn = causal ? (const void*)attn_mx_kernel<64, true> : (const void*)attn_mx_kernel<64, false>;
+    const void* fn = fmt == 4 ? attn_mx_fn<4>(d, causal) : attn_mx_fn<6>(d, causal);
     void* kargs[] = {(void*)&a};
     return hipLaunchKernel(fn, dim3(a.total), dim3(512), kargs, 0, s);
 }

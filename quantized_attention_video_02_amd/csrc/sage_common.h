@@ -113,11 +113,13 @@ hipError_t launch_quant_qk(const u16* q, const u16* k, int B, int H, int N, int 
                            float* qmean, uint64_t* ws, hipStream_t s);
 hipError_t launch_q_bias(const float* qmean, const u16* k, const float* kmean, int B, int H, int N,
                          int d, int layout, float lambda, float* bias, hipStream_t s);
+// MX element format fmt: 6 = E2M3 (MXFP6), 4 = E2M1 (MXFP4)
 hipError_t launch_quant_qk_mx(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
-                              uint8_t* q6, uint8_t* k6, float* kmean, uint64_t* ws, hipStream_t s);
-hipError_t launch_quant_v_mx(const u16* v, int B, int H, int N, int d, int layout, uint8_t* v6,
-                             hipStream_t s);
-hipError_t launch_attn_mx(const AttnArgs& args, int B, int d, int causal, hipStream_t s);
+                              int fmt, uint8_t* q6, uint8_t* k6, float* kmean, uint64_t* ws,
+                              hipStream_t s);
+hipError_t launch_quant_v_mx(const u16* v, int B, int H, int N, int d, int layout, int fmt,
+                             uint8_t* v6, hipStream_t s);
+hipError_t launch_attn_mx(const AttnArgs& args, int B, int d, int causal, int fmt, hipStream_t s);
 hipError_t launch_quant_v(const u16* v, int B, int H, int N, int d, int layout, int pv16,
                           void* vq, float* vscale, float* ws, hipStream_t s);
 hipError_t launch_quant_qkv(const u16* q, const u16* k, const u16* v, int B, int H, int N, int d,

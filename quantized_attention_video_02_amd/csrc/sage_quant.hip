@@ -601,10 +601,44 @@ __device__ inline v8i mx6_block(const float* x) {
     return out;
 }
 
-// Q (blockIdx.z == 0) or smoothed K (z == 1) to MXFP6 per row and 32
+// The same block in E2M1 (FP4), stored as 32 bytes too: byte i (i < 16)
+// holds value i of the block in its low nibble and value 16 + i in its high
+// nibble (the order the FP6 packing gives the elements, so P and V pair up
+// the same way in both formats), the E8M0 byte at offset 24, every other byte
+// zero.  v_cvt_scalef32_pk_fp4_f32 converts two values x / scale to E2M1,
+// rounded to nearest even and saturated at 6, into one byte of a dword.
+__device__ inline v8i mx4_block(const float* x) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    v8i out = v8i{};
+    if (!(amax >= 0x1p-100f)) return out;  // zeros, scale byte 0
+    const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 2;
+    const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t d = 0u;
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[4 * w], x[16 + 4 * w], scale, 0);
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[4 * w + 1], x[17 + 4 * w], scale, 1);
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[4 * w + 2], x[18 + 4 * w], scale, 2);
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[4 * w + 3], x[19 + 4 * w], scale, 3);
+        out[w] = (int)d;
+    }
+    out[6] = e + 127;
+    return out;
+}
+
+// One MX block of element format FMT (6: E2M3, 4: E2M1).
+template <int FMT>
+__device__ inline v8i mx_block(const float* x) {
+    if constexpr (FMT == 4) return mx4_block(x);
+    else return mx6_block(x);
+}
+
+// Q (blockIdx.z == 0) or smoothed K (z == 1) to MX (FMT) per row and 32
 // channels: one thread per (row, block), rows >= N zero.  Output rows of D
 // bytes, [bh][N_pad][D].
-template <int D>
+template <int D, int FMT>
 __global__ __launch_bounds__(kQuantThreads) void quant_qk_mx_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, int H, int N, int N_pad, int layout,
     const float* __restrict__ kmean, uint8_t* __restrict__ q6, uint8_t* __restrict__ k6) {
@@ -632,18 +666,18 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_mx_kernel(
 #pragma unroll
             for (int i = 0; i < 32; ++i) x[i] -= km[i];
         }
-        out = mx6_block(x);
+        out = mx_block<FMT>(x);
     }
     uint8_t* dst = (isk ? k6 : q6) + ((int64_t)bh * N_pad + row) * D + 32 * blk;
     *(uint4*)dst = make_uint4(out[0], out[1], out[2], out[3]);
     *(uint4*)(dst + 16) = make_uint4(out[4], out[5], out[6], out[7]);
 }
 
-// V to MXFP6 per channel and 32 keys, one tile of 128 keys per workgroup:
+// V to MX (FMT) per channel and 32 keys, one tile of 128 keys per workgroup:
 // the tile is staged in LDS channel-major (fp32), then one thread per
 // (channel, block of 32 keys) packs its block.  Output [bh][nblk][D][128]
 // bytes: channel row = the tile's 4 key blocks of 32 bytes; keys >= N are 0.
-template <int D>
+template <int D, int FMT>
 __global__ __launch_bounds__(kQuantThreads) void quant_v_mx_kernel(
     const u16* __restrict__ v, int H, int N, int nblk, int layout, uint8_t* __restrict__ v6) {
     constexpr int CPR = D / 8;
@@ -676,7 +710,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_v_mx_kernel(
         float x[32];
 #pragma unroll
         for (int j = 0; j < 32; ++j) x[j] = tile[c * LSTR + 32 * kb + j];
-        const v8i out = mx6_block(x);
+        const v8i out = mx_block<FMT>(x);
         uint8_t* o = dst + c * kBc + 32 * kb;
         *(uint4*)o = make_uint4(out[0], out[1], out[2], out[3]);
         *(uint4*)(o + 16) = make_uint4(out[4], out[5], out[6], out[7]);
@@ -757,7 +791,8 @@ hipError_t launch_q_bias(const float* qmean, const u16* k, const float* kmean, i
 }
 
 hipError_t launch_quant_qk_mx(const u16* q, const u16* k, int B, int H, int N, int d, int layout,
-                              uint8_t* q6, uint8_t* k6, float* kmean, uint64_t* ws, hipStream_t s) {
+                              int fmt, uint8_t* q6, uint8_t* k6, float* kmean, uint64_t* ws,
+                              hipStream_t s) {
     const int nblk = (N + kBlk - 1) / kBlk, N_pad = nblk * kBlk;
     const int nchunk = (N + kStatsChunk - 1) / kStatsChunk;
     const int BH = B * H;
@@ -775,17 +810,23 @@ hipError_t launch_quant_qk_mx(const u16* q, const u16* k, int B, int H, int N, i
     }
     void* args[] = {(void*)&q, (void*)&k, (void*)&H, (void*)&N, (void*)&N_pad, (void*)&layout,
                     (void*)&kmean, (void*)&q6, (void*)&k6};
-    const void* fn = d == 128 ? (const void*)quant_qk_mx_kernel<128> : (const void*)quant_qk_mx_kernel<64>;
+    const void* fn = fmt == 4 ? (d == 128 ? (const void*)quant_qk_mx_kernel<128, 4>
+                                          : (const void*)quant_qk_mx_kernel<64, 4>)
+                              : (d == 128 ? (const void*)quant_qk_mx_kernel<128, 6>
+                                          : (const void*)quant_qk_mx_kernel<64, 6>);
     const int items = N_pad * (d / 32);
     return launch(fn, dim3((items + kQuantThreads - 1) / kQuantThreads, BH, 2), dim3(kQuantThreads),
                   args, s);
 }
 
-hipError_t launch_quant_v_mx(const u16* v, int B, int H, int N, int d, int layout, uint8_t* v6,
-                             hipStream_t s) {
+hipError_t launch_quant_v_mx(const u16* v, int B, int H, int N, int d, int layout, int fmt,
+                             uint8_t* v6, hipStream_t s) {
     const int nblk = (N + kBc - 1) / kBc;
     void* args[] = {(void*)&v, (void*)&H, (void*)&N, (void*)&nblk, (void*)&layout, (void*)&v6};
-    const void* fn = d == 128 ? (const void*)quant_v_mx_kernel<128> : (const void*)quant_v_mx_kernel<64>;
+    const void* fn = fmt == 4 ? (d == 128 ? (const void*)quant_v_mx_kernel<128, 4>
+                                          : (const void*)quant_v_mx_kernel<64, 4>)
+                              : (d == 128 ? (const void*)quant_v_mx_kernel<128, 6>
+                                          : (const void*)quant_v_mx_kernel<64, 6>);
     return launch(fn, dim3(nblk, B * H), dim3(kQuantThreads), args, s);
 }
 

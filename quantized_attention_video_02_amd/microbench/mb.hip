@@ -1,8 +1,8 @@
 // Microbenchmarks of the MI355X (gfx950) units the attention kernels are
 // bound by: the dense matrix-core rate for INT8, FP8 and FP16 MFMAs, and the
-// v_exp_f32 rate; and two premise checks of the hardware behaviour the
+// v_exp_f32 rate; and premise checks of the hardware behaviour the
 // attention kernels rely on (FP8 matrix-core accumulation, the fp32 -> e4m3
-// convert).  The timing kernels are register-only: each wave runs eight independent
+// and fp32 -> E2M1 converts).  The timing kernels are register-only: each wave runs eight independent
 // accumulation chains (so the matrix core never waits on a result), and one
 // float per thread is stored at the end so nothing is optimised away.
 #include <hip/hip_runtime.h>
@@ -138,6 +138,22 @@ __global__ __launch_bounds__(256) void mb_cvt_e4m3_k(uint32_t first, uint32_t nq
     out[i] = (uint32_t)w;
 }
 
+// Eight consecutive fp32 bit patterns first + 8 i + [0, 8) per thread, each
+// pair (2 j, 2 j + 1) through v_cvt_scalef32_pk_fp4_f32 with the given scale
+// into byte j of one output dword.
+__global__ __launch_bounds__(256) void mb_cvt_fp4_k(uint32_t first, uint32_t noct, float scale,
+                                                    uint32_t* __restrict__ out) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= noct) return;
+    const uint32_t u = first + 8u * i;
+    uint32_t w = 0u;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(u), __uint_as_float(u + 1), scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(u + 2), __uint_as_float(u + 3), scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(u + 4), __uint_as_float(u + 5), scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(u + 6), __uint_as_float(u + 7), scale, 3);
+    out[i] = w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -166,6 +182,21 @@ __attribute__((visibility("default"))) int mb_cvt_e4m3(uint32_t first, uint64_t 
     const uint32_t nquad = (uint32_t)(count / 4);
     hipLaunchKernelGGL(mb_cvt_e4m3_k, dim3((nquad + 255u) / 256u), dim3(256), 0,
                        (hipStream_t)stream, first, nquad, (uint32_t*)out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// out[j] = the byte v_cvt_scalef32_pk_fp4_f32 makes of the fp32 bit patterns
+// first + 2 j and first + 2 j + 1 with the given scale, j < count / 2 (device
+// uint8 buffer of count / 2 bytes, 4-byte aligned).  count: a multiple of 8
+// with first + count <= 2^32.  Returns 0 or -1.
+__attribute__((visibility("default"))) int mb_cvt_fp4(uint32_t first, uint64_t count, float scale,
+                                                      void* out, void* stream) {
+    if (!out || ((uintptr_t)out & 3u) || count == 0 || (count & 7u) ||
+        (uint64_t)first + count > (1ull << 32))
+        return -1;
+    const uint32_t noct = (uint32_t)(count / 8);
+    hipLaunchKernelGGL(mb_cvt_fp4_k, dim3((noct + 255u) / 256u), dim3(256), 0, (hipStream_t)stream,
+                       first, noct, scale, (uint32_t*)out);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -45,18 +45,36 @@ def mx6_unpack_blocks(raw: np.ndarray):
     return codes, raw[..., 24], raw[..., 25:]
 
 
-def mx6_rows(x6: np.ndarray, N: int):
+def mx4_unpack_blocks(raw: np.ndarray):
+    """[..., 32] bytes (one stored E2M1 block each) -> (codes uint8 [..., 32]
+    in value order, E8M0 bytes [...], padding bytes [..., 15]).  Layout from
+    the header: byte i (i < 16) holds value i in its low nibble and value
+    16 + i in its high nibble; bytes 16..23 are zero, byte 24 is the scale,
+    bytes 25..31 are zero."""
+    raw = np.ascontiguousarray(raw, np.uint8)
+    codes = np.empty(raw.shape[:-1] + (32,), np.uint8)
+    codes[..., :16] = raw[..., :16] & 0x0F
+    codes[..., 16:] = raw[..., :16] >> 4
+    pad = np.concatenate([raw[..., 16:24], raw[..., 25:]], axis=-1)
+    return codes, raw[..., 24], pad
+
+
+def _unpack(fmt):
+    return mx4_unpack_blocks if fmt == "mxfp4" else mx6_unpack_blocks
+
+
+def mx6_rows(x6: np.ndarray, N: int, fmt: str = "mxfp6"):
     """q6 / k6 [B,H,N_pad,d] bytes -> (codes [B,H,N,d], E8M0 [B,H,N,d/32], pad)."""
     B, H, Np, d = x6.shape
-    c, e, pad = mx6_unpack_blocks(x6.reshape(B, H, Np, d // 32, 32))
+    c, e, pad = _unpack(fmt)(x6.reshape(B, H, Np, d // 32, 32))
     return c.reshape(B, H, Np, d)[:, :, :N], e[:, :, :N], pad
 
 
-def mx6_v(v6: np.ndarray, N: int):
+def mx6_v(v6: np.ndarray, N: int, fmt: str = "mxfp6"):
     """v6 [B,H,nblk,d,128] bytes -> (codes [B,H,N,d] in key order, E8M0
     [B,H,ceil(N/32),d], pad)."""
     B, H, nblk, d, _ = v6.shape
-    c, e, pad = mx6_unpack_blocks(v6.reshape(B, H, nblk, d, 4, 32))
+    c, e, pad = _unpack(fmt)(v6.reshape(B, H, nblk, d, 4, 32))
     c = np.transpose(c.reshape(B, H, nblk, d, 128), (0, 1, 2, 4, 3)).reshape(B, H, nblk * 128, d)
     e = np.transpose(e, (0, 1, 2, 4, 3)).reshape(B, H, nblk * 4, d)
     return c[:, :, :N], e[:, :, :-(-N // 32)], pad

@@ -277,6 +277,37 @@ def test_status_strings(sage):
     assert L.sage_status_string(12345).decode() == "SAGE_ERR_UNKNOWN"
 
 
+def test_mx4_layout_reader_round_trip():
+    """The tests' reader of the E2M1 block layout against a packer written
+    from the same header text in the opposite direction."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from sage_layouts import mx4_unpack_blocks
+
+    rng = np.random.default_rng(1)
+    vals = rng.integers(0, 16, (5, 32)).astype(np.uint8)
+    scales = rng.integers(0, 256, 5).astype(np.uint8)
+    raw = np.zeros((5, 32), np.uint8)
+    for b in range(5):
+        for i in range(16):
+            raw[b, i] = vals[b, i] | (vals[b, 16 + i] << 4)   # value i low, 16 + i high
+        raw[b, 24] = scales[b]
+    c, e, pad = mx4_unpack_blocks(raw)
+    assert np.array_equal(c, vals) and np.array_equal(e, scales) and not pad.any()
+    raw[0, 20] = 1
+    assert mx4_unpack_blocks(raw)[2].any()
+
+
+def test_mx_format_argument_rejected_before_launch(sage):
+    """The _fmt entry points take SAGE_MX_FP6 (6) or SAGE_MX_FP4 (4) only."""
+    L = sage.lib()
+    p = ct.c_void_p(16)
+    for fmt in (0, 5, 8, -4):
+        assert L.sage_quant_qk_mx_fmt(p, p, 1, 1, 10, 128, 0, fmt, p, p, p, p, 1 << 20, None) == -2
+        assert L.sage_quant_v_mx_fmt(p, 1, 1, 10, 128, 0, fmt, p, None) == -2
+        assert L.sage_attn_fwd_mx_fmt(p, p, p, 1, 1, 10, 128, 0, fmt, 0, 0.1, p, 0, None) == -2
+
+
 def test_mx6_layout_reader_round_trip():
     """The tests' reader of the MX6 block layout against a packer written
     from the same header text in the opposite direction."""

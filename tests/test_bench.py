@@ -89,6 +89,11 @@ def test_record_traffic_of_the_mx_kernel(tmp_path, monkeypatch):
     assert list(data) == ["video_14b_720p/mxfp6"]
     e = data["video_14b_720p/mxfp6"]
     assert e["kernel"] == "attn_mx_kernel" and e["fetch_bytes"] == pytest.approx(700.0 * 1024)
+    # the MXFP4 run of the same kernel goes under its own key
+    bench.record_traffic("video_14b_720p", "fp8", str(tmp_path / "f"), str(tmp_path / "w"),
+                         mx="mxfp4")
+    data = json.load(open(tmp_path / "traffic.json"))
+    assert sorted(data) == ["video_14b_720p/mxfp4", "video_14b_720p/mxfp6"]
 
 
 def test_record_traffic_of_the_backward_sums_its_kernels_per_call(tmp_path, monkeypatch):
@@ -138,12 +143,17 @@ def test_cpu_baseline_of_the_mx_path():
     r = bench.cpu_baseline(wl, "fp8", target_s=0.2, mx=True)
     assert r["value"] > 0 and r["kind"] == "oracle" and r["cores"] == bench.host_cores()
     assert "MXFP6" in r["sample"]
+    r4 = bench.cpu_baseline(wl, "fp8", target_s=0.2, mx="mxfp4", cores=1)
+    assert r4["value"] > 0 and "MXFP4" in r4["sample"]
 
 
 def test_mx_refuses_the_other_variants():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--mx", "--q-smooth"],
                        capture_output=True, text=True, timeout=120)
-    assert r.returncode == 2 and "MXFP6" in r.stderr
+    assert r.returncode == 2 and "MX path" in r.stderr
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--mx", "mxfp5"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "invalid choice" in r.stderr
 
 
 def test_bwd_refuses_the_other_variants_and_samples_the_oracle():
@@ -249,6 +259,13 @@ def test_mx_bench_line():
     assert line["dtype"] == "mxfp6" and rf["kernel"] == "attn_mx_kernel"
     assert rf["peak"] == 10100.0 and rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
     assert "MXFP6" in line["cpu_baseline"]["sample"]
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--mx",
+                        "mxfp4", "--steps", "3", "--warmup", "1", "--no-cpu-baseline"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["dtype"] == "mxfp4" and line["config"]["pv"] == "mxfp4"
+    assert line["roofline"]["kernel"] == "attn_mx_kernel" and line["roofline"]["peak"] == 10100.0
 
 
 @pytest.mark.gpu

@@ -4,8 +4,8 @@
   gives (codes, scales, K mean, V codes) and inside its workspace: each buffer
   sits between two guard bands of a canary byte that must survive, called
   through the C ABI on ragged N, both head sizes, both P V types and both Q
-  scale granularities.
-* Every forward variant returns the same bytes on a repeated call, with other
+  scale granularities; the MX quantization in both element formats likewise.
+* Every forward variant (MXFP4 included) returns the same bytes on a repeated call, with other
   launches of other shapes in between (no state carried between calls, no
   order-dependent reduction).
 """
@@ -100,6 +100,31 @@ def test_quantization_outputs_stay_inside_their_buffers(name, kw, pv, gran, layo
         assert torch.equal(x.body(), y.body()) and torch.equal(x.body(), z.body())
 
 
+MX_CASES = [("tiny", dict(N=333, H=2), "HND"), ("outlier", dict(N=129, B=1, H=1), "NHD")]
+
+
+@pytest.mark.parametrize("fmt", [6, 4])
+@pytest.mark.parametrize("name,kw,layout", MX_CASES)
+def test_mx_quantization_outputs_stay_inside_their_buffers(name, kw, layout, fmt):
+    wl = si.make(name, **kw)
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    q, k, v = ((x if layout == "HND" else x.permute(0, 2, 1, 3)).contiguous().cuda()
+               for x in (wl.q, wl.k, wl.v))
+    L = sage.lib()
+    lay = sage.LAYOUTS[layout]
+    st = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sz = _sizes(B, H, N, d, "fp8")
+    print(f"  case {name} {kw} {layout} fmt {fmt}", flush=True)
+    # q6, k6 as the INT8 codes, k_mean, the Q/K workspace, v6 as the FP8 V codes
+    q6, k6, km, ws, v6 = (Guarded(sz[i]) for i in (0, 2, 4, 7, 5))
+    assert L.sage_quant_qk_mx_fmt(ct.c_void_p(q.data_ptr()), ct.c_void_p(k.data_ptr()), B, H, N,
+                                  d, lay, fmt, q6.ptr, k6.ptr, km.ptr, ws.ptr, sz[7], st) == 0
+    assert L.sage_quant_v_mx_fmt(ct.c_void_p(v.data_ptr()), B, H, N, d, lay, fmt, v6.ptr, st) == 0
+    torch.cuda.synchronize()
+    for i, x in enumerate((q6, k6, km, ws, v6)):
+        assert x.intact(), ("mx buffer", i)
+
+
 def _forward_variants():
     """name -> callable returning the bytes of one forward of that variant."""
     wl = si.make("causal_prefill", B=1, H=2, N=900)
@@ -132,14 +157,14 @@ def _forward_variants():
         o, l = sage.attn_fwd_lse(qz, vq, vs, causal=True, sm_scale=wl.sm_scale)
         return torch.cat([o.float().flatten(), l.flatten()])
 
-    def mx():
-        return sage.attn_fwd_mx(sage.quant_qk_mx(q, k), sage.quant_v_mx(v), causal=True,
-                                sm_scale=wl.sm_scale)
+    def mx(fmt="mxfp6"):
+        return sage.attn_fwd_mx(sage.quant_qk_mx(q, k, fmt=fmt), sage.quant_v_mx(v, fmt=fmt),
+                                causal=True, sm_scale=wl.sm_scale)
 
     return {"dense fp8": lambda: dense(False, "fp8"), "causal fp8": lambda: dense(True, "fp8"),
             "causal fp16": lambda: dense(True, "fp16"), "d64 fp8": lambda: d64("fp8"),
             "d64 fp16": lambda: d64("fp16"), "per-token causal": token, "sparse": sparse,
-            "lse causal": lse, "mxfp6 causal": mx}
+            "lse causal": lse, "mxfp6 causal": mx, "mxfp4 causal": lambda: mx("mxfp4")}
 
 
 def test_every_forward_variant_is_deterministic():

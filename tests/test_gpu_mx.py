@@ -1,5 +1,7 @@
-"""GPU parity of the MXFP6 path (sage_quant_qk_mx, sage_quant_v_mx,
-sage_attn_fwd_mx) against the CPU oracle's MX attention, through the C ABI.
+"""GPU parity of the MX path in both element formats, MXFP6 and MXFP4
+(sage_quant_qk_mx_fmt, sage_quant_v_mx_fmt, sage_attn_fwd_mx_fmt; the plain
+entry points are the MXFP6 forms) against the CPU oracle's MX attention,
+through the C ABI.
 
 Codes and E8M0 scales compared bit for bit (read with the header's layout);
 the fp32 attention output within max-abs 2e-3 and cosine >= 0.9999 of the
@@ -37,15 +39,15 @@ def _to_layout(x, layout):
     return x.contiguous() if layout == "HND" else x.permute(0, 2, 1, 3).contiguous()
 
 
-def _check_quant(mz, v6, oz, ovc, ove, N):
+def _check_quant(mz, v6, oz, ovc, ove, N, fmt="mxfp6"):
     for key in ("q", "k"):
-        c, e, pad = mx6_rows(mz[key + "6"].cpu().numpy(), N)
+        c, e, pad = mx6_rows(mz[key + "6"].cpu().numpy(), N, fmt)
         assert np.array_equal(c, oz[key + "_c"]), key
         assert np.array_equal(e, oz[key + "_e"]), key
         assert not pad.any()
         assert not mz[key + "6"][:, :, N:].any()
     assert np.array_equal(mz["k_mean"].cpu().numpy().view(np.uint32), oz["k_mean"].view(np.uint32))
-    c, e, pad = mx6_v(v6.cpu().numpy(), N)
+    c, e, pad = mx6_v(v6.cpu().numpy(), N, fmt)
     assert np.array_equal(c, ovc) and np.array_equal(e, ove) and not pad.any()
 
 
@@ -59,20 +61,21 @@ MX_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fmt", ["mxfp6", "mxfp4"])
 @pytest.mark.parametrize("name,kw,layout", MX_CASES)
-def test_mx_matches_oracle(sage, orc, name, kw, layout):
-    print(f"[mx parity] {name} {kw} {layout}", flush=True)
+def test_mx_matches_oracle(sage, orc, name, kw, layout, fmt):
+    print(f"[mx parity] {fmt} {name} {kw} {layout}", flush=True)
     wl = si.make(name, **kw)
     qd, kd, vd = (_to_layout(t, layout).cuda() for t in (wl.q, wl.k, wl.v))
-    mz = sage.quant_qk_mx(qd, kd, layout)
-    v6 = sage.quant_v_mx(vd, layout)
+    mz = sage.quant_qk_mx(qd, kd, layout, fmt)
+    v6 = sage.quant_v_mx(vd, layout, fmt)
     out = sage.attn_fwd_mx(mz, v6, causal=wl.causal, sm_scale=wl.sm_scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
     out = to_hnd(out, layout).cpu().numpy()
     q, k, v = codes(wl.q), codes(wl.k), codes(wl.v)
-    oz = orc.mx_quant_qk(q, k, "mxfp6")
-    ovc, ove = orc.mx_quant_v(v, "mxfp6")
-    _check_quant(mz, v6, oz, ovc, ove, wl.N)
+    oz = orc.mx_quant_qk(q, k, fmt)
+    ovc, ove = orc.mx_quant_v(v, fmt)
+    _check_quant(mz, v6, oz, ovc, ove, wl.N, fmt)
     rows = np.arange(wl.N)
     o_or = np.stack([np.stack([orc.mx_attn_rows_head(oz, ovc, ove, b, h, rows, wl.causal, wl.sm_scale)
                                for h in range(wl.H)]) for b in range(wl.B)])
@@ -86,13 +89,14 @@ def test_mx_matches_oracle(sage, orc, name, kw, layout):
     assert abs(c_gpu - c_or) < 2e-4, (c_gpu, c_or)
 
 
-def test_mx_full_size_sampled(sage, orc):
-    """video_14b_720p in MXFP6 at full size (the benchmark's launch
+@pytest.mark.parametrize("fmt", ["mxfp6", "mxfp4"])
+def test_mx_full_size_sampled(sage, orc, fmt):
+    """video_14b_720p in MXFP6 / MXFP4 at full size (the benchmark's launch
     configuration): codes bit-exact on two heads, attention on sampled rows."""
-    print("[mx full-size parity] video_14b_720p", flush=True)
+    print(f"[mx full-size parity] {fmt} video_14b_720p", flush=True)
     wl = si.make("video_14b_720p", device="cuda")
-    mz = sage.quant_qk_mx(wl.q, wl.k)
-    v6 = sage.quant_v_mx(wl.v)
+    mz = sage.quant_qk_mx(wl.q, wl.k, fmt=fmt)
+    v6 = sage.quant_v_mx(wl.v, fmt=fmt)
     out = sage.attn_fwd_mx(mz, v6, sm_scale=wl.sm_scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
     N, nblk = wl.N, -(-wl.N // 128)
@@ -102,11 +106,11 @@ def test_mx_full_size_sampled(sage, orc):
         q = codes(wl.q[b:b + 1, h:h + 1])
         k = codes(wl.k[b:b + 1, h:h + 1])
         v = codes(wl.v[b:b + 1, h:h + 1])
-        oz = orc.mx_quant_qk(q, k, "mxfp6")
-        ovc, ove = orc.mx_quant_v(v, "mxfp6")
+        oz = orc.mx_quant_qk(q, k, fmt)
+        ovc, ove = orc.mx_quant_v(v, fmt)
         sub = {key + "6": mz[key + "6"][b:b + 1, h:h + 1] for key in ("q", "k")}
         sub["k_mean"] = mz["k_mean"][b:b + 1, h:h + 1]
-        _check_quant(sub, v6[b:b + 1, h:h + 1], oz, ovc, ove, N)
+        _check_quant(sub, v6[b:b + 1, h:h + 1], oz, ovc, ove, N, fmt)
         blocks = sorted({0, 1, nblk - 1, int(rng.integers(2, nblk - 1))})
         rows = np.array(sorted({r for blk in blocks
                                 for r in list(range(blk * 128, min(N, blk * 128 + 12))) +
@@ -121,3 +125,31 @@ def test_mx_full_size_sampled(sage, orc):
           f"oracle {_cos(o_or, ref):.6f}")
     assert err <= MAX_ABS and c >= COS_ORACLE, (err, c)
     assert abs(_cos(o_gpu, ref) - _cos(o_or, ref)) < 2e-4
+
+
+def test_plain_entry_points_are_the_mxfp6_forms(sage):
+    """sage_quant_qk_mx, sage_quant_v_mx and sage_attn_fwd_mx (called through
+    the C ABI directly) give the bytes of the _fmt forms with SAGE_MX_FP6."""
+    import ctypes as ct
+
+    wl = si.make("tiny", N=300, H=2)
+    q, k, v = (t.cuda() for t in (wl.q, wl.k, wl.v))
+    mz = sage.quant_qk_mx(q, k, fmt="mxfp6")
+    v6 = sage.quant_v_mx(v, fmt="mxfp6")
+    out = sage.attn_fwd_mx(mz, v6, sm_scale=wl.sm_scale, out_dtype=torch.float32)
+    L = sage.lib()
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    st = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: ct.c_void_p(t.data_ptr())
+    q6, k6, km = torch.empty_like(mz["q6"]), torch.empty_like(mz["k6"]), torch.empty_like(mz["k_mean"])
+    ws = torch.empty_like(mz["workspace"])
+    assert L.sage_quant_qk_mx(p(q), p(k), B, H, N, d, 0, p(q6), p(k6), p(km), p(ws),
+                              ws.numel() * ws.element_size(), st) == 0
+    v6b = torch.empty_like(v6)
+    assert L.sage_quant_v_mx(p(v), B, H, N, d, 0, p(v6b), st) == 0
+    o2 = torch.empty_like(out)
+    assert L.sage_attn_fwd_mx(p(q6), p(k6), p(v6b), B, H, N, d, 0, 0, ct.c_float(wl.sm_scale),
+                              p(o2), 1, st) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(q6, mz["q6"]) and torch.equal(k6, mz["k6"]) and torch.equal(v6b, v6)
+    assert torch.equal(o2.view(torch.int32), out.view(torch.int32))

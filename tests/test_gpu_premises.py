@@ -1,4 +1,4 @@
-"""Two hardware premises the attention kernels are built on, checked on the GPU
+"""Three hardware premises the attention kernels are built on, checked on the GPU
 through the microbenchmark library (quantized_attention_video_02_amd/microbench).
 
 1. How the FP8 matrix core sums (wxsanhe.com TurboDiffusion post, section
@@ -24,6 +24,13 @@ through the microbenchmark library (quantized_attention_video_02_amd/microbench)
    between 448, the largest finite e4m3fn value, and the next step, so larger
    inputs are never produced by the kernels): every such fp32 bit pattern, of
    both signs, against the oracle's encoder.
+3. The fp32 -> E2M1 convert the MXFP4 path packs with
+   (v_cvt_scalef32_pk_fp4_f32: two values into one byte, the first in the low
+   nibble) gives E2M1(x / scale), rounded to nearest with ties to the even
+   code and saturated at 6: every fp32 bit pattern with |x| <= 8 at scale 1
+   (the MX block rule never hands it a larger magnitude), and windows of
+   2^24 patterns at four other power-of-two scales, against the oracle's
+   encoder.
 """
 import ctypes as ct
 import os
@@ -46,6 +53,7 @@ def mb():
     P = ct.c_void_p
     L.mb_f8_mfma.argtypes = [ct.c_int, ct.c_int, P, P, P, P, P]
     L.mb_cvt_e4m3.argtypes = [ct.c_uint32, ct.c_uint64, P, P]
+    L.mb_cvt_fp4.argtypes = [ct.c_uint32, ct.c_uint64, ct.c_float, P, P]
     return L
 
 
@@ -275,3 +283,51 @@ def test_fp32_to_e4m3_convert_every_pattern_up_to_464(mb, orc):
             checked += n
     pool.shutdown()
     assert checked == 2 * top
+
+
+def _check_fp4_window(mb, orc, first, n, scale, buf, pool):
+    """Patterns first .. first + n - 1 through the convert at `scale`, against
+    the oracle's E2M1 code of x / scale (an exact power-of-two division)."""
+    n8 = -(-n // 8) * 8
+    stream = torch.cuda.current_stream()
+    assert mb.mb_cvt_fp4(first, n8, scale, buf.data_ptr(), stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    got = buf[:n8 // 2].cpu().numpy()
+    lo, hi = got & 0x0F, got >> 4
+    codes = np.empty(n8, np.uint8)
+    codes[0::2], codes[1::2] = lo, hi
+    codes = codes[:n]
+    x = np.arange(first, first + n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    y = (x.astype(np.float64) / scale).astype(np.float32)
+    parts = np.array_split(np.arange(n), 8)
+    want = np.concatenate(list(pool.map(lambda ix: orc.f32_to_mx(y[ix[0]:ix[-1] + 1], "mxfp4"),
+                                        parts)))
+    bad = np.flatnonzero(codes != want)
+    assert bad.size == 0, (hex(first + int(bad[0])), scale, int(codes[bad[0]]), int(want[bad[0]]))
+    return n
+
+
+def test_fp32_to_e2m1_convert(mb, orc):
+    """Scale 1: every fp32 bit pattern with |x| <= 8 (0x00000000..0x41000000
+    and the same with the sign bit), in chunks of 2^27.  Scales 2^-20, 2^-3,
+    2^5 and 2^30: windows of up to 2^24 consecutive patterns of both signs
+    starting at 0.5 scale, 2.5 scale and 5.5 scale, up to 8 scale at most
+    (halfway codes, the steps of width 1 and 2, and the saturation above
+    6)."""
+    chunk = 1 << 27
+    buf = torch.empty(chunk // 2, dtype=torch.uint8, device="cuda")
+    pool = ThreadPoolExecutor(8)
+    top = 0x41000000 + 1
+    checked = 0
+    for sign in (0, 0x80000000):
+        for lo in range(0, top, chunk):
+            checked += _check_fp4_window(mb, orc, sign | lo, min(chunk, top - lo), 1.0, buf, pool)
+    assert checked == 2 * top
+    for scale in (2.0 ** -20, 2.0 ** -3, 2.0 ** 5, 2.0 ** 30):
+        end = int(np.float32(8.0 * scale).view(np.uint32))      # |x / scale| <= 8, as above
+        for start in (0.5, 2.5, 5.5):
+            base = int(np.float32(start * scale).view(np.uint32))
+            n = min(1 << 24, end - base + 1)
+            for sign in (0, 0x80000000):
+                _check_fp4_window(mb, orc, sign | base, n, scale, buf, pool)
+    pool.shutdown()

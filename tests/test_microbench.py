@@ -20,6 +20,7 @@ def mb():
     P = ct.c_void_p
     L.mb_f8_mfma.argtypes = [ct.c_int, ct.c_int, P, P, P, P, P]
     L.mb_cvt_e4m3.argtypes = [ct.c_uint32, ct.c_uint64, P, P]
+    L.mb_cvt_fp4.argtypes = [ct.c_uint32, ct.c_uint64, ct.c_float, P, P]
     return L
 
 
@@ -50,3 +51,8 @@ def test_premise_entry_points_refuse_bad_arguments(mb):
     assert mb.mb_cvt_e4m3(0, 6, A, None) == -1                       # not whole quads
     assert mb.mb_cvt_e4m3(0, 0, A, None) == -1
     assert mb.mb_cvt_e4m3(0xFFFFFFF0, 32, A, None) == -1             # past 2^32 patterns
+    assert mb.mb_cvt_fp4(0, 16, 1.0, None, None) == -1
+    assert mb.mb_cvt_fp4(0, 16, 1.0, ct.c_void_p(0x10002), None) == -1  # not 4-byte aligned
+    assert mb.mb_cvt_fp4(0, 12, 1.0, A, None) == -1                     # not whole octets
+    assert mb.mb_cvt_fp4(0, 0, 1.0, A, None) == -1
+    assert mb.mb_cvt_fp4(0xFFFFFFF8, 16, 1.0, A, None) == -1            # past 2^32 patterns
