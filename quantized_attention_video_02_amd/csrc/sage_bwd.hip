@@ -683,24 +683,35 @@ __global__ __launch_bounds__(64 * dkdv_waves<MODE>(), MODE == kDV ? 2 : 1) void 
                 for (int q4 = 0; q4 < 4; ++q4)
                     S[q4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[q4][kk], kf[kk], S[q4], 0, 0, 0);
         }
+        // (p of every entry first, the mask of a tile that needs one applied
+        // to the block's 16 values after them: one uniform branch per block
+        // instead of a divergent one around each exp2)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
+        for (int q4 = 0; q4 < 4; ++q4) {
+            float pq[16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float4 L4 = *(const float4*)&recL[32 * q4 + 8 * i + 4 * hh];
                 const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-                float pv[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * i + j;
-                    const int q = qt * kBlk + 32 * q4 + 8 * i + 4 * hh + j;
-                    const bool ok = !needmask || (kvalid && (!CAUSAL || kj <= q));
-                    pv[j] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[q4][r], c, -Lv[j])) : 0.0f;
+                for (int j = 0; j < 4; ++j)
+                    pq[4 * i + j] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[q4][4 * i + j], c, -Lv[j]));
+            }
+            if (needmask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int q = qt * kBlk + 32 * q4 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    const bool ok = kvalid && (!CAUSAL || kj <= q);
+                    pq[r] = ok ? pq[r] : 0.0f;
                 }
-                int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0] * 448.0f, pv[1] * 448.0f, 0, false);
-                w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2] * 448.0f, pv[3] * 448.0f, w, true);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(pq[4 * i] * 448.0f, pq[4 * i + 1] * 448.0f, 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(pq[4 * i + 2] * 448.0f, pq[4 * i + 3] * 448.0f, w, true);
                 P8[q4 >> 1][(q4 & 1) * 4 + i] = w;
             }
+        }
         }
         // B(qt) complete for this wave (A(qt + 1), issued after it, may still
         // be in flight); the next barrier (in tile_scale for dK) makes it so
