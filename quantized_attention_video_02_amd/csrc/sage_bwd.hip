@@ -265,7 +265,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
     const int n = lane & 31, hh = lane >> 5;
     const int wg = xcd_remap(blockIdx.x, a.total);
     const int nqg = (a.nblk + 1) / 2;  // workgroups per head
-    const int bh = wg / nqg, qg = wg - bh * nqg;
+    const int bh = wg / nqg;
+    int qg = wg - bh * nqg;
+    // causal: the pair sweeps 2 qg + 2 key tiles, so the longest sweeps are
+    // dispatched first (the key sweeps are longest for the first key blocks
+    // already)
+    if (CAUSAL) qg = nqg - 1 - qg;
     const int H = a.H, N = a.N, b = bh / H, h = bh - b * H;
     const int qb = 2 * qg + (wave >> 2);  // this wave's query block
     const bool qbvalid = qb < a.nblk;     // (the second block of the last pair may not exist)
