@@ -813,9 +813,10 @@ static hipError_t launch_attn_bwd_d(const BwdPrep& pp, const BwdArgs& args, int 
     void* kq[] = {(void*)&aq};
     const void* fq = causal ? (const void*)bwd_dq_kernel<D, true> : (const void*)bwd_dq_kernel<D, false>;
     if ((e = hipLaunchKernel(fq, dim3(aq.total), dim3(512), kq, 0, s)) != hipSuccess) return e;
-    // dV sweep: one workgroup per key block
+    // dV sweep: one workgroup per key block (or pair of them with 8 waves)
     BwdArgs av = args;
-    av.total = BH * args.nblk;
+    constexpr int kbw_v = dkdv_waves<kDV>() / 4;
+    av.total = BH * ((args.nblk + kbw_v - 1) / kbw_v);
     void* kv[] = {(void*)&av};
     const void* fv = causal ? (const void*)bwd_dkdv_kernel<D, true, kDV>
                             : (const void*)bwd_dkdv_kernel<D, false, kDV>;
