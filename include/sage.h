@@ -269,7 +269,8 @@ int sage_attn_fwd_lse(const int8_t* q8, const float* q_scale, const int8_t* k8,
  *       zero, so smoothing leaves dQ unchanged in exact arithmetic)
  *   P = exp2(fma(S, c, -lse_i)), c = fp32(fp32(q_scale * lambda) * k_scale)
  *   dP = f16(dO) . f16(V)^T (FP16 matrix cores, FP32 accumulation)
- *   D_i = dO_i . O_i;  dS = fp32(P * fp32(dP - D_i))
+ *   D_i = dO_i . O_i;  dS = fp32(P * fp32(dP - D_i)) (the FP16 product's
+ *       accumulation starts at -D_i, so dP - D_i leaves the matrix core)
  *   dV += (dO8^T . e4m3(448 P)) * fp32(s_do / 448): dO in FP8 e4m3 per block
  *         of 128 rows (absmax / 448 scale), P at the forward's static scale
  *   dS8 = INT8 of dS per tile pair (absmax / 127 scale s_ds)

@@ -4,7 +4,8 @@
   gives (codes, scales, K mean, V codes) and inside its workspace: each buffer
   sits between two guard bands of a canary byte that must survive, called
   through the C ABI on ragged N, both head sizes, both P V types and both Q
-  scale granularities; the MX quantization in both element formats likewise.
+  scale granularities; the MX quantization in both element formats, the
+  training forward and the backward likewise.
 * Every forward variant (MXFP4 included) returns the same bytes on a repeated call, with other
   launches of other shapes in between (no state carried between calls, no
   order-dependent reduction).
@@ -123,6 +124,38 @@ def test_mx_quantization_outputs_stay_inside_their_buffers(name, kw, layout, fmt
     torch.cuda.synchronize()
     for i, x in enumerate((q6, k6, km, ws, v6)):
         assert x.intact(), ("mx buffer", i)
+
+
+@pytest.mark.parametrize("name,kw,causal", [("tiny", dict(N=333, H=2), False),
+                                             ("outlier", dict(N=300, B=1, H=2), True)])
+def test_training_outputs_stay_inside_their_buffers(name, kw, causal):
+    """sage_attn_fwd_lse (output and log-sum-exp) and sage_attn_bwd (dq, dk,
+    dv and the workspace) write inside their buffers."""
+    wl = si.make(name, **kw)
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    q, k, v = (x.contiguous().cuda() for x in (wl.q, wl.k, wl.v))
+    do = si.output_grad(wl).contiguous().cuda()
+    L = sage.lib()
+    st = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+    print(f"  case {name} {kw} causal={causal}", flush=True)
+    qz = sage.quant_qk(q, k)
+    vq, vs = sage.quant_v(v)
+    p = lambda t: ct.c_void_p(t.data_ptr())
+    o, lse = Guarded(B * H * N * d * 2), Guarded(B * H * N * 4)
+    assert L.sage_attn_fwd_lse(p(qz["q8"]), p(qz["q_scale"]), p(qz["k8"]), p(qz["k_scale"]), p(vq),
+                               p(vs), B, H, N, d, 0, int(causal), wl.sm_scale, 0, o.ptr, 0,
+                               lse.ptr, st) == 0
+    n = ct.c_size_t()
+    assert L.sage_bwd_sizes(B, H, N, d, ct.byref(n)) == 0
+    dq, dk, dv = (Guarded(B * H * N * d * 4) for _ in range(3))
+    ws = Guarded(n.value)
+    assert L.sage_attn_bwd(p(qz["q8"]), p(qz["q_scale"]), p(qz["k8"]), p(qz["k_scale"]), p(v),
+                           o.ptr, p(do), lse.ptr, B, H, N, d, 0, int(causal), wl.sm_scale,
+                           dq.ptr, dk.ptr, dv.ptr, ws.ptr, n.value, st) == 0
+    torch.cuda.synchronize()
+    for i, x in enumerate((o, lse, dq, dk, dv, ws)):
+        assert x.intact(), ("training buffer", i)
+    assert torch.isfinite(dq.body().view(torch.float32)).all()
 
 
 def _forward_variants():
